@@ -1,0 +1,106 @@
+"""Seeded synthetic inputs and the named workloads.
+
+This module only draws numbers and describes shapes: it holds none of the
+attention arithmetic, so both the GPU path's tests and the CPU oracle can take
+their inputs from it.
+
+Recipe (the same for every workload): one CPU ``torch.Generator`` seeded with
+``seed``; ``torch.randn`` in float32 for Q, K, V and (for a backward pass) dO,
+drawn in that order, each rounded to bfloat16 (round-to-nearest-even).  For the
+long-sequence workload every query row whose 0-based index is a multiple of 64
+is multiplied by 8 after rounding (exact in bfloat16), which makes the running
+row maximum jump and forces rescaling of the accumulators.  The softmax scale is
+1/sqrt(d) rounded to float32.
+"""
+from __future__ import annotations
+
+import hashlib
+import math
+from dataclasses import dataclass, field
+
+import numpy as np
+import torch
+
+
+@dataclass(frozen=True)
+class Workload:
+    name: str
+    B: int
+    H: int
+    N: int
+    d: int
+    causal: bool
+    backward: bool = False
+    boost_every: int = 0      # multiply query rows i % boost_every == 0 by `boost`
+    boost: float = 8.0
+    seed: int = 0
+    Nk: int | None = None     # key length when it differs from the query length
+    note: str = field(default="", compare=False)
+
+    @property
+    def nq(self) -> int:
+        return self.N
+
+    @property
+    def nk(self) -> int:
+        return self.N if self.Nk is None else self.Nk
+
+    @property
+    def scale(self) -> float:
+        return softmax_scale(self.d)
+
+    def describe(self) -> str:
+        kind = "fwd+bwd" if self.backward else "fwd"
+        mask = "causal" if self.causal else "non-causal"
+        s = "%s %s B=%d H=%d N=%d d=%d" % (kind, mask, self.B, self.H, self.N, self.d)
+        if self.Nk is not None:
+            s += " Nk=%d" % self.Nk
+        if self.boost_every:
+            s += " (every %dth query row x%g)" % (self.boost_every, self.boost)
+        return s
+
+
+WORKLOADS = {
+    "c1": Workload("c1", 1, 1, 256, 64, False, note="single head forward, seed 0"),
+    "c2": Workload("c2", 4, 16, 2048, 64, False),
+    "c3": Workload("c3", 2, 32, 4096, 128, True),
+    "c4": Workload("c4", 1, 16, 16384, 128, True, boost_every=64),
+    "c5": Workload("c5", 2, 16, 4096, 128, True, backward=True),
+}
+
+
+def softmax_scale(d: int) -> float:
+    """1/sqrt(d) rounded to float32 (returned as the Python float of that value)."""
+    return float(np.float32(1.0 / math.sqrt(d)))
+
+
+def make_inputs(B: int, H: int, nq: int, d: int, *, nk: int | None = None, seed: int = 0,
+                backward: bool = False, boost_every: int = 0, boost: float = 8.0) -> dict:
+    """Draw Q, K, V (and dO when ``backward``) as bfloat16 CPU tensors.
+
+    Shapes: q and do ``[B, H, nq, d]``; k and v ``[B, H, nk, d]``."""
+    nk = nq if nk is None else nk
+    g = torch.Generator().manual_seed(seed)
+    q = torch.randn(B, H, nq, d, generator=g, dtype=torch.float32).to(torch.bfloat16)
+    k = torch.randn(B, H, nk, d, generator=g, dtype=torch.float32).to(torch.bfloat16)
+    v = torch.randn(B, H, nk, d, generator=g, dtype=torch.float32).to(torch.bfloat16)
+    out = {"q": q, "k": k, "v": v}
+    if backward:
+        out["do"] = torch.randn(B, H, nq, d, generator=g, dtype=torch.float32).to(torch.bfloat16)
+    if boost_every:
+        out["q"][:, :, ::boost_every, :] *= boost
+    return out
+
+
+def workload_inputs(w: Workload) -> dict:
+    return make_inputs(w.B, w.H, w.nq, w.d, nk=w.nk, seed=w.seed, backward=w.backward,
+                       boost_every=w.boost_every, boost=w.boost)
+
+
+def inputs_sha256(tensors: dict) -> str:
+    """SHA-256 over the raw bytes of the tensors, in key order q, k, v, do."""
+    h = hashlib.sha256()
+    for key in ("q", "k", "v", "do"):
+        if key in tensors:
+            h.update(tensors[key].contiguous().view(torch.int16).numpy().tobytes())
+    return h.hexdigest()
