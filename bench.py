@@ -1,0 +1,226 @@
+#!/usr/bin/env python3
+"""Benchmark: attention forward + backward throughput on one MI355X.
+
+One step is one pass of the whole path over resident synthetic inputs: the fused
+forward kernel, then the backward preprocess, dK/dV and dQ kernels (the same four
+launches attn_bwd makes).  The default workload is the forward+backward causal case
+B=2, H=16, N=4096, d=128; ``--workload c2|c3|c4`` times forward-only workloads.
+
+FLOP convention: 4*B*H*N^2*d for the forward, halved when causal; the backward counts
+2.5x the forward.  Printed: one JSON line with the whole-job TFLOP/s, the dominant
+kernel's roofline (achieved algorithmic TFLOP/s against the bf16 dense MFMA peak,
+measured with HIP events on the launch stream) and the fp64 CPU oracle timed on a
+bounded sample of the same workload on the host cores.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "attention fwd/bwd TFLOP/s on 1 MI355X and % of bf16 MFMA peak"
+PEAK_BF16_TFLOPS = 2516.6   # 256 CUs x 2.4 GHz x 4096 dense bf16 FLOP/clk/CU
+PEAK_HBM_GBS = 8000.0
+KERNEL_SOURCES = ["attn_device.h", "attn_fwd.hip", "attn_bwd.hip"]
+
+
+def fwd_flop(B, H, N, d, causal) -> float:
+    """Forward FLOP by the convention: 4*B*H*N^2*d, halved when causal."""
+    return 4.0 * B * H * N * N * d * (0.5 if causal else 1.0)
+
+
+def step_flop(B, H, N, d, causal, backward) -> float:
+    return fwd_flop(B, H, N, d, causal) * (3.5 if backward else 1.0)
+
+
+def kernel_algorithmic_flop(kernel, B, H, N, d, causal) -> float:
+    """Algorithmic FLOP one launch performs, in units of one N x N x d product (the
+    forward is two of them): fwd 2 (QK^T, PV); dkdv 4 (the recomputed S, dP, dV, dK);
+    dq 1 (dQ; its recomputed S and dP are counted in dkdv); preprocess 0."""
+    unit = fwd_flop(B, H, N, d, causal) / 2.0
+    return unit * {"fwd": 2, "dkdv": 4, "dq": 1, "preprocess": 0}[kernel]
+
+
+def kernel_source_sha() -> str:
+    h = hashlib.sha256()
+    for name in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, "tiled_online_softmax_02_amd", "csrc", name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def stored_traffic(kernel: str, workload: str):
+    """HBM bytes per launch from committed rocprofv3 counter summaries, or None when the
+    kernel sources changed since the counters were taken."""
+    path = os.path.join(ROOT, "profiles", "hbm_traffic_%s_%s.txt" % (kernel, workload))
+    if not os.path.exists(path):
+        return None
+    try:
+        rec = json.loads(open(path).read().split("JSON:", 1)[1].strip().splitlines()[0])
+    except Exception:
+        return None
+    if rec.get("kernel_source_sha") != kernel_source_sha():
+        return None
+    return rec.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(w, budget_s: float):
+    """Time the fp64 CPU oracle on whole heads of the workload until ~budget_s of work."""
+    import numpy as np
+    import oracle
+    from tiled_online_softmax_02_amd.inputs import make_inputs
+
+    threads = max(1, min(len(os.sched_getaffinity(0)), 16))
+    inp = make_inputs(1, 1, w.N, w.d, seed=w.seed + 1000, backward=w.backward,
+                      boost_every=w.boost_every, boost=w.boost)
+    f64 = {k: t.to(dtype=__import__("torch").float64).numpy() for k, t in inp.items()}
+    # one head first, to size the sample
+    t0 = time.perf_counter()
+    oracle.attn_fwd(f64["q"], f64["k"], f64["v"], w.causal, w.scale, nthreads=1)
+    if w.backward:
+        oracle.attn_bwd_matmul(f64["q"], f64["k"], f64["v"], f64["do"], w.causal, w.scale)
+    one = time.perf_counter() - t0
+    heads = int(max(1, min(w.B * w.H, threads, budget_s // max(one, 1e-3))))
+    inp = make_inputs(1, heads, w.N, w.d, seed=w.seed + 1001, backward=w.backward,
+                      boost_every=w.boost_every, boost=w.boost)
+    f64 = {k: t.to(dtype=__import__("torch").float64).numpy() for k, t in inp.items()}
+    t0 = time.perf_counter()
+    oracle.attn_fwd(f64["q"], f64["k"], f64["v"], w.causal, w.scale, nthreads=min(threads, heads))
+    if w.backward:
+        oracle.attn_bwd_matmul(f64["q"], f64["k"], f64["v"], f64["do"], w.causal, w.scale)
+    dt = time.perf_counter() - t0
+    flop = step_flop(1, heads, w.N, w.d, w.causal, w.backward)
+    return {
+        "value": flop / dt / 1e12,
+        "unit": "TFLOP/s",
+        "cores": min(threads, heads) if not w.backward else threads,
+        "kind": "oracle",
+        "sample": "%d of %d heads (%s per head), same FLOP convention, %.1f s wall; forward by the plain "
+                  "fp64 C definition (one thread per head), backward by fp64 numpy matmuls"
+                  % (heads, w.B * w.H, "N=%d d=%d" % (w.N, w.d), dt),
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="c5", choices=["c2", "c3", "c4", "c5"])
+    ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle work for the CPU baseline")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py measures one GPU only: the path runs on a single MI355X and this build has no "
+              "multi-GPU code; run with --gpus 1", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import tiled_online_softmax_02_amd as A
+    from tiled_online_softmax_02_amd.inputs import WORKLOADS, workload_inputs
+
+    w = WORKLOADS[args.workload]
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    inp = workload_inputs(w)
+    q, k, v = (inp[n].to(dev) for n in ("q", "k", "v"))
+    B, H, N, d = q.shape
+    causal, scale = w.causal, w.scale
+    o = torch.empty_like(q)
+    lse = torch.empty((B, H, N), dtype=torch.float32, device=dev)
+    if w.backward:
+        do = inp["do"].to(dev)
+        dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+        delta = torch.empty_like(lse)
+
+    # A plain copy of known size, outside the timed region: under rocprofv3 --pmc its
+    # FETCH_SIZE / WRITE_SIZE calibrate the counters against known bytes.
+    cal_src = torch.empty(64 << 20, dtype=torch.int32, device=dev).fill_(1)
+    cal_dst = torch.empty_like(cal_src)
+    cal_dst.copy_(cal_src)
+    torch.cuda.synchronize()
+    del cal_src, cal_dst
+
+    kernels = ["fwd"] + (["preprocess", "dkdv", "dq"] if w.backward else [])
+    ev = {kname: [] for kname in kernels}
+
+    def step(record):
+        e = [torch.cuda.Event(enable_timing=True) for _ in range(len(kernels) + 1)] if record else None
+        if record:
+            e[0].record()
+        A.attn_fwd(q, k, v, o, lse, B, H, N, d, causal, scale)
+        if record:
+            e[1].record()
+        if w.backward:
+            A.attn_bwd_preprocess(o, do, delta, B, H, N, d)
+            if record:
+                e[2].record()
+            A.attn_bwd_dkdv(q, k, v, do, lse, delta, dk, dv, B, H, N, d, causal, scale)
+            if record:
+                e[3].record()
+            A.attn_bwd_dq(q, k, v, do, lse, delta, dq, B, H, N, d, causal, scale)
+            if record:
+                e[4].record()
+        if record:
+            for i, kname in enumerate(kernels):
+                ev[kname].append((e[i], e[i + 1]))
+
+    for _ in range(args.warmup):
+        step(False)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step(True)
+    torch.cuda.synchronize()
+    dt = time.perf_counter() - t0
+    ms_per_step = dt * 1e3 / args.steps
+
+    kernel_ms = {kname: sum(a.elapsed_time(b) for a, b in pairs) / len(pairs) for kname, pairs in ev.items()}
+    flop = step_flop(B, H, N, d, causal, w.backward)
+    value = flop / (ms_per_step * 1e-3) / 1e12
+    dom = max(kernels, key=lambda kname: kernel_ms[kname])
+    achieved = kernel_algorithmic_flop(dom, B, H, N, d, causal) / (kernel_ms[dom] * 1e-3) / 1e12
+
+    fwd_t = fwd_flop(B, H, N, d, causal) / (kernel_ms["fwd"] * 1e-3) / 1e12
+    out = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": w.describe(), "B": B, "H": H, "N": N, "d": d, "causal": causal,
+                   "scale": scale, "global_batch": B, "seq_len": N, "parallelism": "single GPU"},
+        "pct_of_peak": round(100.0 * value / PEAK_BF16_TFLOPS, 2),
+        "fwd_tflops": round(fwd_t, 2),
+        "kernel_ms": {kname: round(t, 4) for kname, t in kernel_ms.items()},
+        "roofline": {"kernel": dom, "bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+                     "traffic": stored_traffic(dom, w.name)},
+    }
+    if w.backward:
+        out["bwd_tflops"] = round(2.5 * fwd_flop(B, H, N, d, causal)
+                                  / (sum(kernel_ms[x] for x in ("preprocess", "dkdv", "dq")) * 1e-3) / 1e12, 2)
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(w, args.cpu_budget)
+    else:
+        out["cpu_baseline"] = None
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,104 @@
+/*
+ * attn.h -- C ABI of the gfx950 (MI355X) attention library libattn.so.
+ *
+ * The library computes exact scaled-dot-product attention,
+ *     O = softmax(scale * Q K^T [+ causal mask]) V,
+ * and its gradients.  The forward pass is one fused tiled kernel that keeps,
+ * for every query row, a running maximum m and a running exponential sum l and
+ * never writes the N x N score matrix S or probability matrix P to memory
+ * ("digest_existing.txt", answer q02_flashattention, sections 1 and 2: S and
+ * P need not be materialised; the merge rule m = max(m1, m2),
+ * l = e^(m1-m) l1 + e^(m2-m) l2).  The backward pass regenerates P from the
+ * inputs and the per-row log-sum-exp saved by the forward pass
+ * ("GPU Programming and Kernel Optimization", item 58).
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * Tensors are device pointers to dense row-major arrays:
+ *   q, k, v, o, dout, dq, dk, dv : bfloat16 (raw 16-bit patterns), [B, H, N, d]
+ *   lse, delta                   : float32, [B, H, N]
+ * lse is the natural log of sum_j exp(scale * <q_i, k_j>) over the keys j that
+ * query i sees; delta is D_i = sum_c dout[i][c] * o[i][c].
+ * Causal masking (causal = 1) hides key j from query i when j > i.
+ * scale is the factor applied to the dot products (usually 1/sqrt(d)).
+ *
+ * Ownership: the caller owns every buffer.  The library neither allocates,
+ * frees nor keeps any pointer after a call returns.  Outputs must not overlap
+ * inputs or each other.
+ *
+ * Asynchrony: a successful call only enqueues kernels on `stream` (a
+ * hipStream_t; NULL means the default stream) and returns; completion is
+ * observed by the caller through the stream.  Calls on one stream run in order.
+ *
+ * Errors: every entry point checks its arguments on the host before any HIP
+ * call.  On a nonzero status nothing was enqueued and no output was touched.
+ * The library never aborts or prints.  An empty problem (B, H or N equal to 0)
+ * is valid, enqueues nothing and returns ATTN_OK (its pointers may be NULL).
+ * Sizes: B, H, N >= 0; d in {64, 128}; B*H*N*d < 2^62; N*d < 2^31.
+ * Pointers must be 16-byte aligned.
+ */
+#ifndef ATTN_H_
+#define ATTN_H_
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum attn_status {
+    ATTN_OK = 0,
+    ATTN_ERR_NULLPTR = 1,        /* a required pointer is NULL (non-empty problem) */
+    ATTN_ERR_BAD_SHAPE = 2,      /* B, H or N negative, or a size limit exceeded */
+    ATTN_ERR_UNSUPPORTED_D = 3,  /* head dimension d is not 64 or 128 */
+    ATTN_ERR_MISALIGNED = 4,     /* a pointer is not 16-byte aligned */
+    ATTN_ERR_BAD_SCALE = 5,      /* scale is not finite or not > 0 */
+    ATTN_ERR_BAD_ARG = 6,        /* causal is not 0 or 1 */
+    ATTN_ERR_ALIAS = 7,          /* an output overlaps an input or another output */
+    ATTN_ERR_HIP = 8             /* the HIP runtime reported an error at launch */
+};
+
+/* Forward pass.  Reads q, k, v; writes o [B,H,N,d] (bf16, rounded to nearest
+ * even) and lse [B,H,N] (fp32, natural log).  One kernel launch. */
+int attn_fwd(const void *q, const void *k, const void *v, void *o, float *lse,
+             int B, int H, int N, int d, int causal, float scale, void *stream);
+
+/* Backward pass: enqueues attn_bwd_preprocess, attn_bwd_dkdv and attn_bwd_dq
+ * in that order on `stream`.  Reads q, k, v, o, dout and the lse written by
+ * attn_fwd with the same q, k, v, causal and scale; writes dq, dk, dv
+ * [B,H,N,d] (bf16) and delta [B,H,N] (fp32), a caller-owned workspace that
+ * holds D on return. */
+int attn_bwd(const void *q, const void *k, const void *v, const void *o, const void *dout,
+             const float *lse, void *dq, void *dk, void *dv, float *delta,
+             int B, int H, int N, int d, int causal, float scale, void *stream);
+
+/* Backward step 1: delta[i] = sum_c dout[i][c] * o[i][c] (fp32 products and
+ * sums of the bf16 inputs).  Memory-bound; one kernel launch. */
+int attn_bwd_preprocess(const void *o, const void *dout, float *delta,
+                        int B, int H, int N, int d, void *stream);
+
+/* Backward step 2: for every key block, loops over the query blocks that see
+ * it, regenerates P = exp(scale * Q K^T - lse) and accumulates
+ * dv = P^T dout and dk = scale * dS^T q with dS = P * (dout V^T - delta).
+ * Writes dk and dv; one kernel launch. */
+int attn_bwd_dkdv(const void *q, const void *k, const void *v, const void *dout,
+                  const float *lse, const float *delta, void *dk, void *dv,
+                  int B, int H, int N, int d, int causal, float scale, void *stream);
+
+/* Backward step 3: for every query block, loops over the key blocks it sees,
+ * regenerates P and dS as above and accumulates dq = scale * dS k.  Writes dq;
+ * one kernel launch.  No atomics: results are bitwise reproducible. */
+int attn_bwd_dq(const void *q, const void *k, const void *v, const void *dout,
+                const float *lse, const float *delta, void *dq,
+                int B, int H, int N, int d, int causal, float scale, void *stream);
+
+/* Static, NUL-terminated description of a status code (never NULL). */
+const char *attn_status_string(int status);
+
+/* The hipError_t value behind the last ATTN_ERR_HIP returned on the calling
+ * thread (0 if none). */
+int attn_last_hip_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* ATTN_H_ */

@@ -178,3 +178,33 @@ def attn_bwd(q, k, v, dout, causal: bool, scale: float, nthreads: int | None = N
     _check(_load().oracle_attn_bwd(_p(q), _p(k), _p(v), _p(dout), _p(dq), _p(dk), _p(dv), _p(dvec), B, H, nq, nk,
                                    d, int(bool(causal)), float(scale), nthreads or default_threads()), "attn_bwd")
     return dq, dk, dv, dvec
+
+
+def attn_bwd_matmul(q, k, v, dout, causal: bool, scale: float, nthreads: int | None = None):
+    """The same backward formulas as :func:`attn_bwd`, with each product done by numpy's fp64 matmul.
+
+    P comes from the definitional forward pass (:func:`attn_fwd` with ``want_p``); then, per head,
+    dV = P^T dO, dP = dO V^T, D = rowsum(P * dP), dS = P * (dP - D), dQ = scale dS K,
+    dK = scale dS^T Q.  Used for large heads, where the plain loops of :func:`attn_bwd` are slow.
+    Returns (dQ, dK, dV, D)."""
+    q, k, v, dout = _f64(q), _f64(k), _f64(v), _f64(dout)
+    B, H, nq, d = q.shape
+    nk = k.shape[2]
+    dq = np.empty_like(q)
+    dk = np.empty_like(k)
+    dv = np.empty_like(v)
+    dvec = np.empty((B, H, nq))
+    for b in range(B):
+        for h in range(H):
+            sl = (slice(b, b + 1), slice(h, h + 1))
+            _, _, p = attn_fwd(q[sl], k[sl], v[sl], causal, scale, want_p=True, nthreads=1)
+            p = p[0, 0]
+            g = dout[b, h]
+            dv[b, h] = p.T @ g
+            dp = g @ v[b, h].T
+            D = (p * dp).sum(axis=1)
+            ds = p * (dp - D[:, None])
+            dq[b, h] = scale * (ds @ k[b, h])
+            dk[b, h] = scale * (ds.T @ q[b, h])
+            dvec[b, h] = D
+    return dq, dk, dv, dvec

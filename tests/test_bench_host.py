@@ -1,0 +1,35 @@
+"""Host-side logic of bench.py (no GPU): the FLOP convention and the multi-GPU refusal."""
+import json
+import os
+import subprocess
+import sys
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+sys.path.insert(0, ROOT)
+import bench  # noqa: E402
+
+
+def test_flop_convention_reproduces_the_pages_throughputs():
+    with open(os.path.join(ROOT, "tests", "golden", "flop_convention.json")) as f:
+        g = json.load(f)
+    for c in g["cases"]:
+        tflops = bench.fwd_flop(c["B"], c["H"], c["N"], c["d"], c["causal"]) / (c["ms"] * 1e-3) / 1e12
+        # the printed figures carry 3-4 significant digits
+        assert tflops == pytest.approx(c["tflops"], rel=3e-3), c
+
+
+def test_causal_halves_and_backward_is_two_and_a_half_forwards():
+    f = bench.fwd_flop(2, 16, 4096, 128, False)
+    assert bench.fwd_flop(2, 16, 4096, 128, True) == f / 2
+    assert bench.step_flop(2, 16, 4096, 128, True, True) == pytest.approx(3.5 * f / 2)
+    # per-kernel algorithmic counts add up to the whole step
+    parts = sum(bench.kernel_algorithmic_flop(k, 2, 16, 4096, 128, True) for k in ("fwd", "preprocess", "dkdv", "dq"))
+    assert parts == pytest.approx(bench.step_flop(2, 16, 4096, 128, True, True))
+
+
+def test_more_than_one_gpu_is_refused_with_a_message():
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"], capture_output=True,
+                       text=True, timeout=120)
+    assert r.returncode == 2 and "one GPU" in r.stderr

@@ -1,0 +1,126 @@
+"""The C ABI without a GPU: the library loads, exports what include/attn.h declares, and
+rejects bad arguments on the host before any HIP call.
+
+Every call below fails validation, so nothing is ever launched (fake pointers are never
+dereferenced).  Calls that would pass validation are not made here.
+"""
+import os
+import re
+
+import pytest
+
+import tiled_online_softmax_02_amd as A
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "attn.h")
+
+# fake, 16-byte aligned, never dereferenced device addresses (distinct, non-overlapping)
+P = [0x7f0000000000 + i * (1 << 36) for i in range(12)]
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(A.LIB_PATH):
+        from tiled_online_softmax_02_amd import build
+        build.build()
+    return A.library()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(attn_\w+)\s*\(", text, re.M)))
+
+
+def test_header_declares_the_expected_entry_points():
+    assert declared_functions() == sorted([
+        "attn_fwd", "attn_bwd", "attn_bwd_preprocess", "attn_bwd_dkdv", "attn_bwd_dq",
+        "attn_status_string", "attn_last_hip_error"])
+
+
+def test_library_exports_every_declared_symbol(lib):
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+
+
+def test_status_strings(lib):
+    for code in range(0, 9):
+        s = A.attn_status_string(code)
+        assert s and s != "unknown status"
+    assert A.attn_status_string(99) == "unknown status"
+    assert lib.attn_last_hip_error() == 0
+
+
+def fwd(lib, q=P[0], k=P[1], v=P[2], o=P[3], lse=P[4], B=1, H=1, N=64, d=64, causal=0, scale=0.125):
+    return lib.attn_fwd(q, k, v, o, lse, B, H, N, d, causal, scale, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(B=-1), A.ATTN_ERR_BAD_SHAPE),
+    (dict(H=-3), A.ATTN_ERR_BAD_SHAPE),
+    (dict(N=-1), A.ATTN_ERR_BAD_SHAPE),
+    (dict(d=96), A.ATTN_ERR_UNSUPPORTED_D),
+    (dict(d=0), A.ATTN_ERR_UNSUPPORTED_D),
+    (dict(d=256), A.ATTN_ERR_UNSUPPORTED_D),
+    (dict(N=1 << 24, d=128), A.ATTN_ERR_BAD_SHAPE),   # N*d = 2^31
+    (dict(causal=2), A.ATTN_ERR_BAD_ARG),
+    (dict(causal=-1), A.ATTN_ERR_BAD_ARG),
+    (dict(scale=0.0), A.ATTN_ERR_BAD_SCALE),
+    (dict(scale=-0.125), A.ATTN_ERR_BAD_SCALE),
+    (dict(scale=float("nan")), A.ATTN_ERR_BAD_SCALE),
+    (dict(scale=float("inf")), A.ATTN_ERR_BAD_SCALE),
+    (dict(q=None), A.ATTN_ERR_NULLPTR),
+    (dict(lse=None), A.ATTN_ERR_NULLPTR),
+    (dict(k=P[1] + 2), A.ATTN_ERR_MISALIGNED),
+    (dict(o=P[3] + 8), A.ATTN_ERR_MISALIGNED),
+    (dict(o=P[0]), A.ATTN_ERR_ALIAS),                  # o == q
+    (dict(lse=P[2] + 64), A.ATTN_ERR_ALIAS),           # lse inside v
+    (dict(o=P[2] + 8192 - 16), A.ATTN_ERR_ALIAS),      # o overlaps the tail of v (64*64*2 bytes)
+])
+def test_forward_argument_checks(lib, kw, status):
+    assert fwd(lib, **kw) == status
+
+
+def test_empty_problems_are_valid_no_ops(lib):
+    # nothing is launched, pointers may be NULL
+    assert fwd(lib, q=None, k=None, v=None, o=None, lse=None, B=0) == A.ATTN_OK
+    assert fwd(lib, q=None, k=None, v=None, o=None, lse=None, N=0) == A.ATTN_OK
+    assert lib.attn_bwd(*([None] * 10), 1, 0, 64, 128, 1, 0.1, None) == A.ATTN_OK
+    assert lib.attn_bwd_preprocess(None, None, None, 0, 1, 1, 64, None) == A.ATTN_OK
+    # an empty problem is still checked for d, causal and scale
+    assert fwd(lib, B=0, d=80) == A.ATTN_ERR_UNSUPPORTED_D
+    assert fwd(lib, N=0, scale=0.0) == A.ATTN_ERR_BAD_SCALE
+
+
+def test_backward_argument_checks(lib):
+    args = [P[0], P[1], P[2], P[3], P[4], P[5], P[6], P[7], P[8], P[9]]
+
+    def bwd(**kw):
+        a = list(args)
+        for i, val in kw.get("ptr", {}).items():
+            a[i] = val
+        return lib.attn_bwd(*a, kw.get("B", 2), kw.get("H", 2), kw.get("N", 128), kw.get("d", 128),
+                            kw.get("causal", 1), kw.get("scale", 0.088), None)
+
+    assert bwd(d=32) == A.ATTN_ERR_UNSUPPORTED_D
+    assert bwd(scale=float("nan")) == A.ATTN_ERR_BAD_SCALE
+    assert bwd(causal=5) == A.ATTN_ERR_BAD_ARG
+    assert bwd(ptr={9: None}) == A.ATTN_ERR_NULLPTR      # delta workspace
+    assert bwd(ptr={6: P[0]}) == A.ATTN_ERR_ALIAS        # dq == q
+    assert bwd(ptr={7: P[6]}) == A.ATTN_ERR_ALIAS        # dk == dq
+    assert bwd(ptr={9: P[5]}) == A.ATTN_ERR_ALIAS        # delta == lse
+    assert bwd(ptr={8: P[8] + 4}) == A.ATTN_ERR_MISALIGNED
+    # the three step entry points check their own arguments
+    assert lib.attn_bwd_preprocess(P[0], P[1], P[0], 1, 1, 64, 64, None) == A.ATTN_ERR_ALIAS
+    assert lib.attn_bwd_preprocess(P[0], None, P[2], 1, 1, 64, 64, None) == A.ATTN_ERR_NULLPTR
+    assert lib.attn_bwd_dkdv(P[0], P[1], P[2], P[3], P[4], P[5], P[6], P[6], 1, 1, 64, 64, 0, 0.125,
+                             None) == A.ATTN_ERR_ALIAS
+    assert lib.attn_bwd_dq(P[0], P[1], P[2], P[3], P[4], P[5], P[6], 1, 1, 64, 64, 0, 0.0,
+                           None) == A.ATTN_ERR_BAD_SCALE
+    assert lib.attn_bwd_dq(P[0], P[1], P[2], P[3], P[4], P[5], P[6], 1, 1, 64, 100, 0, 0.1,
+                           None) == A.ATTN_ERR_UNSUPPORTED_D
+
+
+def test_python_binding_raises_with_status(lib):
+    with pytest.raises(A.AttnError) as e:
+        A.attn_fwd(P[0], P[1], P[2], P[3], P[4], 1, 1, 64, 64, False, -1.0)
+    assert e.value.status == A.ATTN_ERR_BAD_SCALE

@@ -305,3 +305,35 @@ def test_argument_errors_are_reported():
         oracle.attn_fwd_blockwise(rand(4, 2), rand(4, 2), rand(4, 2), False, 1.0, 0, 2)
     with pytest.raises(ValueError):
         oracle.online_merge(rand(5), [3, 2])
+
+
+@pytest.mark.parametrize("nq,nk,causal", [(6, 6, True), (5, 8, True), (7, 4, False)])
+def test_matmul_backward_matches_finite_differences_and_loops(nq, nk, causal):
+    d = 3
+    q, k, v, dout = rand(1, 1, nq, d), rand(1, 1, nk, d), rand(1, 1, nk, d), rand(1, 1, nq, d)
+    scale = 0.45
+    ref = oracle.attn_bwd(q, k, v, dout, causal, scale, nthreads=1)
+    got = oracle.attn_bwd_matmul(q, k, v, dout, causal, scale)
+    for a, b in zip(got, ref):
+        np.testing.assert_allclose(a, b, rtol=1e-12, atol=1e-13)
+    h = 1e-6
+    for name, x, g in (("q", q, got[0]), ("k", k, got[1]), ("v", v, got[2])):
+        fd = np.empty_like(x)
+        for idx in np.ndindex(x.shape):
+            xp, xm = x.copy(), x.copy()
+            xp[idx] += h
+            xm[idx] -= h
+            args = {"q": q, "k": k, "v": v}
+            fd[idx] = (loss(**{**args, name: xp}, dout=dout, causal=causal, scale=scale)
+                       - loss(**{**args, name: xm}, dout=dout, causal=causal, scale=scale)) / (2 * h)
+        assert np.abs(fd - g).max() <= 1e-6 * np.abs(g).max()
+
+
+def test_matmul_backward_matches_loops_on_a_multi_head_case():
+    B, H, N, d = 2, 2, 40, 16
+    q, k, v, dout = rand(B, H, N, d), rand(B, H, N, d), rand(B, H, N, d), rand(B, H, N, d)
+    for causal in (False, True):
+        ref = oracle.attn_bwd(q, k, v, dout, causal, 0.25)
+        got = oracle.attn_bwd_matmul(q, k, v, dout, causal, 0.25)
+        for a, b in zip(got, ref):
+            np.testing.assert_allclose(a, b, rtol=1e-11, atol=1e-12)

@@ -1,0 +1,173 @@
+"""Python binding of libattn.so, the gfx950 attention library (C ABI in include/attn.h).
+
+The functions named like the C entry points (``attn_fwd``, ``attn_bwd``,
+``attn_bwd_preprocess``, ``attn_bwd_dkdv``, ``attn_bwd_dq``,
+``attn_status_string``) only marshal arguments: tensors become device
+pointers, ``stream=None`` becomes the current PyTorch stream of the tensors'
+device, and a nonzero status becomes :class:`AttnError`.  Every step of the
+computation runs in the library's HIP kernels; there is no fallback.  If the
+library has not been built the first call raises.
+
+``fwd`` and ``bwd`` are conveniences that check dtypes, devices and
+contiguity and allocate the outputs with ``torch.empty``.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import threading
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libattn.so")
+
+ATTN_OK = 0
+ATTN_ERR_NULLPTR = 1
+ATTN_ERR_BAD_SHAPE = 2
+ATTN_ERR_UNSUPPORTED_D = 3
+ATTN_ERR_MISALIGNED = 4
+ATTN_ERR_BAD_SCALE = 5
+ATTN_ERR_BAD_ARG = 6
+ATTN_ERR_ALIAS = 7
+ATTN_ERR_HIP = 8
+
+_lock = threading.Lock()
+_lib = None
+
+_P = ctypes.c_void_p
+_I = ctypes.c_int
+_F = ctypes.c_float
+
+_SIGNATURES = {
+    "attn_fwd": [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _F, _P],
+    "attn_bwd": [_P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _F, _P],
+    "attn_bwd_preprocess": [_P, _P, _P, _I, _I, _I, _I, _P],
+    "attn_bwd_dkdv": [_P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _F, _P],
+    "attn_bwd_dq": [_P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _F, _P],
+}
+
+
+class AttnError(RuntimeError):
+    def __init__(self, name: str, status: int):
+        self.status = status
+        msg = "%s failed with status %d: %s" % (name, status, attn_status_string(status))
+        if status == ATTN_ERR_HIP:
+            msg += " (hipError_t %d)" % library().attn_last_hip_error()
+        super().__init__(msg)
+
+
+def library() -> ctypes.CDLL:
+    """Load libattn.so (once).  Raises if it has not been built."""
+    global _lib
+    with _lock:
+        if _lib is None:
+            if not os.path.exists(LIB_PATH):
+                raise RuntimeError("libattn.so is not built (%s); build it with "
+                                   "`python -m tiled_online_softmax_02_amd.build`" % LIB_PATH)
+            lib = ctypes.CDLL(LIB_PATH)
+            for name, args in _SIGNATURES.items():
+                fn = getattr(lib, name)
+                fn.argtypes = args
+                fn.restype = _I
+            lib.attn_status_string.argtypes = [_I]
+            lib.attn_status_string.restype = ctypes.c_char_p
+            lib.attn_last_hip_error.argtypes = []
+            lib.attn_last_hip_error.restype = _I
+            _lib = lib
+    return _lib
+
+
+def _ptr(x):
+    if x is None:
+        return None
+    if isinstance(x, torch.Tensor):
+        return x.data_ptr() or None
+    return int(x) or None
+
+
+def _stream(stream, *tensors):
+    if stream is not None:
+        return stream.cuda_stream if isinstance(stream, torch.cuda.Stream) else int(stream)
+    for t in tensors:
+        if isinstance(t, torch.Tensor) and t.is_cuda:
+            return torch.cuda.current_stream(t.device).cuda_stream
+    return None
+
+
+def _call(name: str, *args) -> None:
+    rc = getattr(library(), name)(*args)
+    if rc != ATTN_OK:
+        raise AttnError(name, rc)
+
+
+def attn_status_string(status: int) -> str:
+    return library().attn_status_string(int(status)).decode()
+
+
+def attn_fwd(q, k, v, o, lse, B, H, N, d, causal, scale, stream=None) -> None:
+    _call("attn_fwd", _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, H, N, d, int(causal), float(scale),
+          _stream(stream, q, o))
+
+
+def attn_bwd(q, k, v, o, dout, lse, dq, dk, dv, delta, B, H, N, d, causal, scale, stream=None) -> None:
+    _call("attn_bwd", _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(dout), _ptr(lse), _ptr(dq), _ptr(dk), _ptr(dv),
+          _ptr(delta), B, H, N, d, int(causal), float(scale), _stream(stream, q, dq))
+
+
+def attn_bwd_preprocess(o, dout, delta, B, H, N, d, stream=None) -> None:
+    _call("attn_bwd_preprocess", _ptr(o), _ptr(dout), _ptr(delta), B, H, N, d, _stream(stream, o, delta))
+
+
+def attn_bwd_dkdv(q, k, v, dout, lse, delta, dk, dv, B, H, N, d, causal, scale, stream=None) -> None:
+    _call("attn_bwd_dkdv", _ptr(q), _ptr(k), _ptr(v), _ptr(dout), _ptr(lse), _ptr(delta), _ptr(dk), _ptr(dv),
+          B, H, N, d, int(causal), float(scale), _stream(stream, q, dk))
+
+
+def attn_bwd_dq(q, k, v, dout, lse, delta, dq, B, H, N, d, causal, scale, stream=None) -> None:
+    _call("attn_bwd_dq", _ptr(q), _ptr(k), _ptr(v), _ptr(dout), _ptr(lse), _ptr(delta), _ptr(dq), B, H, N, d,
+          int(causal), float(scale), _stream(stream, q, dq))
+
+
+def _check_inputs(*ts):
+    ref = ts[0]
+    if ref.dim() != 4:
+        raise ValueError("expected [B, H, N, d] tensors")
+    for t in ts:
+        if t.dtype != torch.bfloat16:
+            raise TypeError("tensors must be bfloat16")
+        if not t.is_cuda or t.device != ref.device:
+            raise ValueError("tensors must be on the same GPU")
+        if not t.is_contiguous():
+            raise ValueError("tensors must be contiguous")
+        if t.shape != ref.shape:
+            raise ValueError("q, k, v (and o, dO) must have the same shape [B, H, N, d]")
+
+
+def default_scale(d: int) -> float:
+    import numpy as np
+    return float(np.float32(1.0 / (d ** 0.5)))
+
+
+def fwd(q, k, v, causal: bool = False, scale: float | None = None, stream=None):
+    """Forward pass; returns (o bf16 [B,H,N,d], lse fp32 [B,H,N])."""
+    _check_inputs(q, k, v)
+    B, H, N, d = q.shape
+    scale = default_scale(d) if scale is None else scale
+    o = torch.empty_like(q)
+    lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
+    attn_fwd(q, k, v, o, lse, B, H, N, d, causal, scale, stream)
+    return o, lse
+
+
+def bwd(q, k, v, o, dout, lse, causal: bool = False, scale: float | None = None, stream=None):
+    """Backward pass; returns (dq, dk, dv) bf16 [B,H,N,d]."""
+    _check_inputs(q, k, v, o, dout)
+    B, H, N, d = q.shape
+    if lse.dtype != torch.float32 or tuple(lse.shape) != (B, H, N) or not lse.is_contiguous():
+        raise ValueError("lse must be a contiguous float32 [B, H, N] tensor")
+    scale = default_scale(d) if scale is None else scale
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    delta = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
+    attn_bwd(q, k, v, o, dout, lse, dq, dk, dv, delta, B, H, N, d, causal, scale, stream)
+    return dq, dk, dv

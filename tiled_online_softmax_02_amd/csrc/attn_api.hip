@@ -1,0 +1,230 @@
+// attn_api.hip -- the C ABI declared in include/attn.h: host-side argument
+// checks, then kernel launches on the caller's stream.  Nothing here allocates
+// device memory, synchronises or prints.
+#include <math.h>
+#include <stdint.h>
+
+#include "../../include/attn.h"
+#include "attn_launch.h"
+
+namespace {
+
+thread_local int g_last_hip_error = 0;
+
+struct Range {
+    uintptr_t lo, hi;  // [lo, hi)
+};
+
+Range range_of(const void *p, long long bytes) { return Range{(uintptr_t)p, (uintptr_t)p + (uintptr_t)bytes}; }
+
+bool overlap(Range a, Range b) { return a.lo < b.hi && b.lo < a.hi; }
+
+bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
+
+// Shape rules shared by every entry point.  Sets *empty when there is nothing to compute.
+int check_shape(int B, int H, int N, int d, bool *empty)
+{
+    if (B < 0 || H < 0 || N < 0) return ATTN_ERR_BAD_SHAPE;
+    if (d != 64 && d != 128) return ATTN_ERR_UNSUPPORTED_D;
+    const long long rows = (long long)B * H * N;
+    if (rows > ((1LL << 62) / d)) return ATTN_ERR_BAD_SHAPE;
+    if ((long long)N * d >= (1LL << 31)) return ATTN_ERR_BAD_SHAPE;
+    // work-group counts of the launches must fit a 32-bit grid
+    if (attn::fwd_grid_size(B, H, N) >= (1LL << 31) || attn::bwd_dkdv_grid_size(B, H, N) >= (1LL << 31) ||
+        attn::bwd_dq_grid_size(B, H, N) >= (1LL << 31) || rows / 16 >= (1LL << 31))
+        return ATTN_ERR_BAD_SHAPE;
+    *empty = (rows == 0);
+    return ATTN_OK;
+}
+
+int check_scale(float scale) { return (isfinite(scale) && scale > 0.f) ? ATTN_OK : ATTN_ERR_BAD_SCALE; }
+
+int check_causal(int causal) { return (causal == 0 || causal == 1) ? ATTN_OK : ATTN_ERR_BAD_ARG; }
+
+// Pointers: non-null and 16-byte aligned.
+int check_ptrs(const void *const *ptrs, int n)
+{
+    for (int i = 0; i < n; ++i)
+        if (!ptrs[i]) return ATTN_ERR_NULLPTR;
+    for (int i = 0; i < n; ++i)
+        if (!aligned16(ptrs[i])) return ATTN_ERR_MISALIGNED;
+    return ATTN_OK;
+}
+
+// Every output range must be disjoint from every input range and from the other outputs.
+int check_alias(const Range *in, int nin, const Range *out, int nout)
+{
+    for (int i = 0; i < nout; ++i) {
+        for (int j = 0; j < nin; ++j)
+            if (overlap(out[i], in[j])) return ATTN_ERR_ALIAS;
+        for (int j = i + 1; j < nout; ++j)
+            if (overlap(out[i], out[j])) return ATTN_ERR_ALIAS;
+    }
+    return ATTN_OK;
+}
+
+int hip_status(hipError_t e)
+{
+    if (e == hipSuccess) return ATTN_OK;
+    g_last_hip_error = (int)e;
+    return ATTN_ERR_HIP;
+}
+
+#define RETURN_IF(x)               \
+    do {                           \
+        const int rc_ = (x);       \
+        if (rc_ != ATTN_OK) return rc_; \
+    } while (0)
+
+int validate_common(int B, int H, int N, int d, int causal, float scale, bool *empty)
+{
+    RETURN_IF(check_shape(B, H, N, d, empty));
+    RETURN_IF(check_causal(causal));
+    RETURN_IF(check_scale(scale));
+    return ATTN_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int attn_fwd(const void *q, const void *k, const void *v, void *o, float *lse, int B, int H, int N, int d, int causal,
+             float scale, void *stream)
+{
+    bool empty = false;
+    RETURN_IF(validate_common(B, H, N, d, causal, scale, &empty));
+    if (empty) return ATTN_OK;
+    const void *ptrs[] = {q, k, v, o, lse};
+    RETURN_IF(check_ptrs(ptrs, 5));
+    const long long tb = (long long)B * H * N * d * 2, lb = (long long)B * H * N * 4;
+    const Range in[] = {range_of(q, tb), range_of(k, tb), range_of(v, tb)};
+    const Range out[] = {range_of(o, tb), range_of(lse, lb)};
+    RETURN_IF(check_alias(in, 3, out, 2));
+    attn::FwdArgs a{q, k, v, o, lse, B, H, N, d, causal, scale, stream};
+    return hip_status(attn::launch_fwd(a));
+}
+
+int attn_bwd_preprocess(const void *o, const void *dout, float *delta, int B, int H, int N, int d, void *stream)
+{
+    bool empty = false;
+    RETURN_IF(check_shape(B, H, N, d, &empty));
+    if (empty) return ATTN_OK;
+    const void *ptrs[] = {o, dout, delta};
+    RETURN_IF(check_ptrs(ptrs, 3));
+    const long long tb = (long long)B * H * N * d * 2, lb = (long long)B * H * N * 4;
+    const Range in[] = {range_of(o, tb), range_of(dout, tb)};
+    const Range out[] = {range_of(delta, lb)};
+    RETURN_IF(check_alias(in, 2, out, 1));
+    attn::BwdArgs a{};
+    a.o = o;
+    a.dout = dout;
+    a.delta = delta;
+    a.B = B;
+    a.H = H;
+    a.N = N;
+    a.d = d;
+    a.stream = stream;
+    return hip_status(attn::launch_bwd_preprocess(a));
+}
+
+int attn_bwd_dkdv(const void *q, const void *k, const void *v, const void *dout, const float *lse, const float *delta,
+                  void *dk, void *dv, int B, int H, int N, int d, int causal, float scale, void *stream)
+{
+    bool empty = false;
+    RETURN_IF(validate_common(B, H, N, d, causal, scale, &empty));
+    if (empty) return ATTN_OK;
+    const void *ptrs[] = {q, k, v, dout, lse, delta, dk, dv};
+    RETURN_IF(check_ptrs(ptrs, 8));
+    const long long tb = (long long)B * H * N * d * 2, lb = (long long)B * H * N * 4;
+    const Range in[] = {range_of(q, tb),    range_of(k, tb),     range_of(v, tb),
+                        range_of(dout, tb), range_of(lse, lb),   range_of(delta, lb)};
+    const Range out[] = {range_of(dk, tb), range_of(dv, tb)};
+    RETURN_IF(check_alias(in, 6, out, 2));
+    attn::BwdArgs a{};
+    a.q = q;
+    a.k = k;
+    a.v = v;
+    a.dout = dout;
+    a.lse = lse;
+    a.delta = (float *)delta;
+    a.dk = dk;
+    a.dv = dv;
+    a.B = B;
+    a.H = H;
+    a.N = N;
+    a.d = d;
+    a.causal = causal;
+    a.scale = scale;
+    a.stream = stream;
+    return hip_status(attn::launch_bwd_dkdv(a));
+}
+
+int attn_bwd_dq(const void *q, const void *k, const void *v, const void *dout, const float *lse, const float *delta,
+                void *dq, int B, int H, int N, int d, int causal, float scale, void *stream)
+{
+    bool empty = false;
+    RETURN_IF(validate_common(B, H, N, d, causal, scale, &empty));
+    if (empty) return ATTN_OK;
+    const void *ptrs[] = {q, k, v, dout, lse, delta, dq};
+    RETURN_IF(check_ptrs(ptrs, 7));
+    const long long tb = (long long)B * H * N * d * 2, lb = (long long)B * H * N * 4;
+    const Range in[] = {range_of(q, tb),    range_of(k, tb),   range_of(v, tb),
+                        range_of(dout, tb), range_of(lse, lb), range_of(delta, lb)};
+    const Range out[] = {range_of(dq, tb)};
+    RETURN_IF(check_alias(in, 6, out, 1));
+    attn::BwdArgs a{};
+    a.q = q;
+    a.k = k;
+    a.v = v;
+    a.dout = dout;
+    a.lse = lse;
+    a.delta = (float *)delta;
+    a.dq = dq;
+    a.B = B;
+    a.H = H;
+    a.N = N;
+    a.d = d;
+    a.causal = causal;
+    a.scale = scale;
+    a.stream = stream;
+    return hip_status(attn::launch_bwd_dq(a));
+}
+
+int attn_bwd(const void *q, const void *k, const void *v, const void *o, const void *dout, const float *lse, void *dq,
+             void *dk, void *dv, float *delta, int B, int H, int N, int d, int causal, float scale, void *stream)
+{
+    bool empty = false;
+    RETURN_IF(validate_common(B, H, N, d, causal, scale, &empty));
+    if (empty) return ATTN_OK;
+    const void *ptrs[] = {q, k, v, o, dout, lse, dq, dk, dv, delta};
+    RETURN_IF(check_ptrs(ptrs, 10));
+    const long long tb = (long long)B * H * N * d * 2, lb = (long long)B * H * N * 4;
+    const Range in[] = {range_of(q, tb), range_of(k, tb),    range_of(v, tb),
+                        range_of(o, tb), range_of(dout, tb), range_of(lse, lb)};
+    const Range out[] = {range_of(dq, tb), range_of(dk, tb), range_of(dv, tb), range_of(delta, lb)};
+    RETURN_IF(check_alias(in, 6, out, 4));
+    attn::BwdArgs a{q, k, v, o, dout, lse, dq, dk, dv, delta, B, H, N, d, causal, scale, stream};
+    RETURN_IF(hip_status(attn::launch_bwd_preprocess(a)));
+    RETURN_IF(hip_status(attn::launch_bwd_dkdv(a)));
+    return hip_status(attn::launch_bwd_dq(a));
+}
+
+const char *attn_status_string(int status)
+{
+    switch (status) {
+    case ATTN_OK: return "ok";
+    case ATTN_ERR_NULLPTR: return "a required pointer is NULL";
+    case ATTN_ERR_BAD_SHAPE: return "bad shape: B, H, N must be >= 0 and within the size limits";
+    case ATTN_ERR_UNSUPPORTED_D: return "unsupported head dimension: d must be 64 or 128";
+    case ATTN_ERR_MISALIGNED: return "a pointer is not 16-byte aligned";
+    case ATTN_ERR_BAD_SCALE: return "scale must be finite and > 0";
+    case ATTN_ERR_BAD_ARG: return "causal must be 0 or 1";
+    case ATTN_ERR_ALIAS: return "an output overlaps an input or another output";
+    case ATTN_ERR_HIP: return "the HIP runtime reported an error at launch";
+    default: return "unknown status";
+    }
+}
+
+int attn_last_hip_error(void) { return g_last_hip_error; }
+
+}  // extern "C"

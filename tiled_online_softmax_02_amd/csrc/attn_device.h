@@ -1,0 +1,107 @@
+// attn_device.h -- device-side building blocks shared by the gfx950 attention kernels.
+//
+// Matrix-core conventions (CDNA4, wave64).  All products use
+// v_mfma_f32_32x32x16_bf16: C[32x32] += A[32x16] * B[16x32] with, for lane l
+// (h = l / 32, c = l % 32):
+//   A operand  : 8 bf16  A[c][8h + e],            e = 0..7
+//   B operand  : 8 bf16  B[8h + e][c]
+//   accumulator: 16 fp32 C[8(r/4) + 4h + r%4][c], r = 0..15
+// A product whose reduction runs over a tile's rows (keys or queries) takes its
+// reduction slot s = 8h + e to mean row 8(e/4) + 4h + e%4 of a 16-row group.
+// With that choice, accumulator registers 8t'..8t'+7 (t' = 0, 1) of a 32-row
+// block are exactly the B operand of the 16-row group t' of that block, so a
+// probability or gradient tile computed in registers feeds the next product
+// without any cross-lane movement.  The other operand of such a product is
+// read from LDS with ds_read_b64_tr_b16 (a transposing LDS read), see
+// lds_read_tr_rows below.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace attn {
+
+typedef __bf16 bf16;
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) char lds_char;
+
+constexpr float kLog2e = 1.44269504088896340736f;
+
+__device__ __forceinline__ f32x16 mfma(bf16x8 a, bf16x8 b, f32x16 c)
+{
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ f32x16 zero16()
+{
+    f32x16 z;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) z[i] = 0.f;
+    return z;
+}
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// 16-byte LDS read at byte offset `off` of `base`.
+__device__ __forceinline__ bf16x8 lds_read16(const lds_char *base, int off)
+{
+    return *(const __attribute__((address_space(3))) bf16x8 *)(base + off);
+}
+
+__device__ __forceinline__ void lds_write16(lds_char *base, int off, u32x4 v)
+{
+    *(__attribute__((address_space(3))) u32x4 *)(base + off) = v;
+}
+
+// ds_read_b64_tr_b16: within each group of 16 lanes, lane i receives element
+// (i % 4) of the 8-byte chunks addressed by lanes 4e + i/4 (e = 0..3).
+__device__ __forceinline__ bf16x4 lds_read_tr(const lds_char *base, int off)
+{
+    i16x4 r = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (__attribute__((address_space(3))) i16x4 *)(base + off));
+    return __builtin_bit_cast(bf16x4, r);
+}
+
+// A operand (32 columns x 16 reduction rows, transposed) for a product that
+// reduces over rows r0 .. r0+15 of a row-major LDS tile of 16-bit elements with
+// row stride `rs` bytes, taking columns c0 .. c0+31.  Lane l gets column
+// c0 + l%32 at reduction slots 8h + e -> rows r0 + 8(e/4) + 4h + e%4.
+// Each lane addresses, for its group G = l/16 and index s = l%16, row
+// r0 + 4(G/2) + s/4 (and +8), columns c0 + 16(G%2) + 4(s%4) .. +3.
+__device__ __forceinline__ bf16x8 lds_read_tr_rows(const lds_char *base, int rs, int r0, int c0, int lane)
+{
+    const int G = lane >> 4, s = lane & 15;
+    const int row = r0 + 4 * (G >> 1) + (s >> 2);
+    const int col = c0 + 16 * (G & 1) + 4 * (s & 3);
+    const bf16x4 lo = lds_read_tr(base, row * rs + col * 2);
+    const bf16x4 hi = lds_read_tr(base, (row + 8) * rs + col * 2);
+    return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+}
+
+// Eight consecutive accumulator registers (8t' .. 8t'+7 of a 32x32 block),
+// rounded to bf16 (nearest even): the B operand of a row-reduction product.
+__device__ __forceinline__ bf16x8 pack_bf16(const f32x16 &acc, int half)
+{
+    bf16x8 r;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) r[e] = (bf16)acc[8 * half + e];
+    return r;
+}
+
+// Workgroups are dispatched round-robin over the 8 XCDs of the chip, each with
+// its own L2.  Map dispatch index g to a work id so that every XCD receives a
+// contiguous range of work ids (work that shares K/V then shares an L2).
+__device__ __forceinline__ int xcd_remap(int g, int G)
+{
+    constexpr int NX = 8;
+    const int per = G / NX, rem = G % NX;
+    const int x = g % NX, i = g / NX;
+    return x * per + (x < rem ? x : rem) + i;
+}
+
+}  // namespace attn

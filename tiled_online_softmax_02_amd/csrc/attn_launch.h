@@ -1,0 +1,37 @@
+// attn_launch.h -- internal interface between the C ABI (attn_api.hip) and the
+// kernel files.  Arguments have already been validated when these are called.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+namespace attn {
+
+struct FwdArgs {
+    const void *q, *k, *v;
+    void *o;
+    float *lse;
+    int B, H, N, d, causal;
+    float scale;
+    void *stream;
+};
+
+struct BwdArgs {
+    const void *q, *k, *v, *o, *dout;
+    const float *lse;
+    void *dq, *dk, *dv;
+    float *delta;
+    int B, H, N, d, causal;
+    float scale;
+    void *stream;
+};
+
+hipError_t launch_fwd(const FwdArgs &a);
+hipError_t launch_bwd_preprocess(const BwdArgs &a);
+hipError_t launch_bwd_dkdv(const BwdArgs &a);
+hipError_t launch_bwd_dq(const BwdArgs &a);
+
+long long fwd_grid_size(int B, int H, int N);
+long long bwd_dkdv_grid_size(int B, int H, int N);
+long long bwd_dq_grid_size(int B, int H, int N);
+
+}  // namespace attn
