@@ -34,7 +34,7 @@
  * call.  On a nonzero status nothing was enqueued and no output was touched.
  * The library never aborts or prints.  An empty problem (B, H or N equal to 0)
  * is valid, enqueues nothing and returns ATTN_OK (its pointers may be NULL).
- * Sizes: B, H, N >= 0; d in {64, 128}; B*H*N*d < 2^62; N*d < 2^31.
+ * Sizes: B, H, N >= 0; d in {64, 128}; B*H*N*d < 2^62; (N + 256)*d*2 < 2^32.
  * Pointers must be 16-byte aligned.
  */
 #ifndef ATTN_H_

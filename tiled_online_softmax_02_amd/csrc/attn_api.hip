@@ -28,7 +28,8 @@ int check_shape(int B, int H, int N, int d, bool *empty)
     if (d != 64 && d != 128) return ATTN_ERR_UNSUPPORTED_D;
     const long long rows = (long long)B * H * N;
     if (rows > ((1LL << 62) / d)) return ATTN_ERR_BAD_SHAPE;
-    if ((long long)N * d >= (1LL << 31)) return ATTN_ERR_BAD_SHAPE;
+    // per-head byte offsets, including the padding rows of the last tile, are 32-bit
+    if ((long long)(N + 256) * d * 2 > 0xFFFFFFFFLL) return ATTN_ERR_BAD_SHAPE;
     // work-group counts of the launches must fit a 32-bit grid
     if (attn::fwd_grid_size(B, H, N) >= (1LL << 31) || attn::bwd_dkdv_grid_size(B, H, N) >= (1LL << 31) ||
         attn::bwd_dq_grid_size(B, H, N) >= (1LL << 31) || rows / 16 >= (1LL << 31))

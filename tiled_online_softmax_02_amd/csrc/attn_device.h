@@ -105,3 +105,21 @@ __device__ __forceinline__ int xcd_remap(int g, int G)
 }
 
 }  // namespace attn
+
+namespace attn {
+
+// Buffer resource over [base, base + bytes): loads beyond `bytes` return zeros,
+// which gives ragged tiles their zero padding without branches.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base, uint32_t bytes)
+{
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, (int)bytes, 0x00020000);
+}
+
+__device__ __forceinline__ u32x4 buffer_load16(__amdgpu_buffer_rsrc_t r, uint32_t byte_off)
+{
+    return __builtin_amdgcn_raw_buffer_load_b128(r, (int)byte_off, 0, 0);
+}
+
+__device__ __forceinline__ int wave_uniform(int x) { return __builtin_amdgcn_readfirstlane(x); }
+
+}  // namespace attn
