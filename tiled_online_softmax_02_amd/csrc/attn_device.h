@@ -123,3 +123,72 @@ __device__ __forceinline__ u32x4 buffer_load16(__amdgpu_buffer_rsrc_t r, uint32_
 __device__ __forceinline__ int wave_uniform(int x) { return __builtin_amdgcn_readfirstlane(x); }
 
 }  // namespace attn
+
+namespace attn {
+
+// Swizzled LDS tiles: rows of D bf16 (2*D bytes, no padding) whose 16-byte
+// chunks are permuted per row, physical chunk = logical chunk ^ lds_swz<D>(row).
+// The map XORs fixed chunk masks selected by the low four row bits; it keeps both
+// access patterns of the kernels free of bank conflicts: 16-byte reads of one
+// chunk column by 16 consecutive rows, and the transposing 8-byte reads of
+// 4 consecutive rows x 4 consecutive chunks.  Only bits 0..3 of the row matter,
+// so the map is linear over row blocks aligned to 16.
+template <int D>
+__device__ __forceinline__ int lds_swz(int r)
+{
+    constexpr int m0 = D == 128 ? 4 : 2, m1 = D == 128 ? 10 : 4, m2 = 1, m3 = 2;
+    return ((r & 1) ? m0 : 0) ^ ((r & 2) ? m1 : 0) ^ ((r & 4) ? m2 : 0) ^ ((r & 8) ? m3 : 0);
+}
+
+// Byte offset of logical 16-byte chunk `chunk` of row `row` in a swizzled tile.
+template <int D>
+__device__ __forceinline__ int swz_off(int row, int chunk)
+{
+    return row * (2 * D) + 16 * (chunk ^ lds_swz<D>(row));
+}
+
+// Direct global -> LDS load: every lane fetches 16 bytes at `byte_off` of the
+// buffer and the wave writes its 64 x 16 bytes contiguously at `lds_dst`
+// (lane i at lds_dst + 16 i).  Loads past the buffer end write zeros.
+__device__ __forceinline__ void buffer_load_lds16(__amdgpu_buffer_rsrc_t r, lds_char *lds_dst, uint32_t byte_off)
+{
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void *)lds_dst, 16, byte_off, 0,
+                                             0, 0);
+}
+
+// Wait until this wave's vector-memory loads (including direct LDS loads) are done.
+__device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+
+// Load rows [row0, row0 + 64) of a row-major [*, D] bf16 matrix into a swizzled
+// LDS tile with direct loads; all NW waves of the workgroup take part.
+// Each wave instruction covers 1 KB = 1024 / (2 D) whole rows.
+template <int D, int NW>
+__device__ __forceinline__ void load_tile_lds(__amdgpu_buffer_rsrc_t r, lds_char *tile, int row0, int wave, int lane)
+{
+    constexpr int RB = 2 * D;           // bytes per row
+    constexpr int RPI = 1024 / RB;      // rows per wave instruction
+    constexpr int NI = 64 / RPI / NW;   // instructions per wave for 64 rows
+    static_assert(NI >= 1 && NI * RPI * NW == 64, "64-row tile must split evenly over the waves");
+    const int lr = lane / (RB / 16), p = lane % (RB / 16);
+#pragma unroll
+    for (int i = 0; i < NI; ++i) {
+        const int r0 = (wave * NI + i) * RPI;  // first tile row of this instruction
+        const int row = r0 + lr;
+        const int chunk = p ^ lds_swz<D>(row);
+        buffer_load_lds16(r, tile + r0 * RB, (uint32_t)((row0 + row) * RB + 16 * chunk));
+    }
+}
+
+// lds_read_tr_rows for a swizzled tile.
+template <int D>
+__device__ __forceinline__ bf16x8 lds_read_tr_rows_swz(const lds_char *base, int r0, int c0, int lane)
+{
+    const int G = lane >> 4, s = lane & 15;
+    const int row = r0 + 4 * (G >> 1) + (s >> 2);
+    const int byte = 2 * (c0 + 16 * (G & 1) + 4 * (s & 3));
+    const bf16x4 lo = lds_read_tr(base, swz_off<D>(row, byte >> 4) + (byte & 15));
+    const bf16x4 hi = lds_read_tr(base, swz_off<D>(row + 8, byte >> 4) + (byte & 15));
+    return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+}
+
+}  // namespace attn

@@ -11,8 +11,9 @@
 // gfx950 mapping:
 //   * one workgroup of 4 waves per block of 128 query rows; each wave owns 32
 //     rows and holds their Q fragments in VGPRs for the whole loop;
-//   * key/value blocks of 64 rows are double-buffered through LDS with 16-byte
-//     buffer loads (rows past N read as zeros); K runs one block ahead of V, so
+//   * key/value blocks of 64 rows are double-buffered through swizzled LDS tiles
+//     filled by direct global->LDS buffer loads (rows past N read as zeros, no
+//     staging registers, no LDS store instructions); K runs one block ahead of V, so
 //     the scores of block j+1 are computed on the matrix cores while the
 //     vector units exponentiate block j;
 //   * scores are computed transposed, S^T = K Q^T, so each lane holds 32 keys
@@ -31,27 +32,27 @@
 #include "attn_device.h"
 #include "attn_launch.h"
 
+#include <type_traits>
+
 namespace attn {
 
 namespace {
 
-constexpr int kFwdBM = 128;  // query rows per workgroup
-constexpr int kFwdBN = 64;   // keys per streamed block
-constexpr int kThreads = 256;
+constexpr int kFwdWaves = 4;               // waves per workgroup, 32 query rows each
+constexpr int kFwdBM = 32 * kFwdWaves;     // query rows per workgroup
+constexpr int kFwdBN = 64;                 // keys per streamed block
+constexpr int kThreads = 64 * kFwdWaves;
 constexpr float kRescaleLog2 = 8.0f;
 
 template <int D>
 struct FwdSmem {
-    static constexpr int KRS = D * 2 + 16;  // K row stride in bytes
-    static constexpr int VRS = D * 2 + 64;  // V row stride in bytes
-    static constexpr int KBYTES = kFwdBN * KRS;
-    static constexpr int VBYTES = kFwdBN * VRS;
-    static constexpr int OFF_V = 2 * KBYTES;  // two K stages, then two V stages
-    static constexpr int TOTAL = 2 * KBYTES + 2 * VBYTES;
+    static constexpr int TILE = kFwdBN * D * 2;  // one swizzled K or V block
+    static constexpr int OFF_V = 2 * TILE;       // two K stages, then two V stages
+    static constexpr int TOTAL = 4 * TILE;
 };
 
 template <int D, bool CAUSAL>
-__global__ __launch_bounds__(kThreads, 2) void fwd_kernel(const bf16 *__restrict__ Q, const bf16 *__restrict__ K,
+__global__ __launch_bounds__(kThreads, 8 / kFwdWaves) void fwd_kernel(const bf16 *__restrict__ Q, const bf16 *__restrict__ K,
                                                           const bf16 *__restrict__ V, bf16 *__restrict__ O,
                                                           float *__restrict__ LSE, int N, int n_qtiles, float scale,
                                                           float c_log2)
@@ -59,11 +60,9 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_kernel(const bf16 *__restrict
     using L = FwdSmem<D>;
     constexpr int NKS = D / 16;          // reduction steps over d for S^T
     constexpr int NDB = D / 32;          // 32-wide column blocks of O
-    constexpr int CPR = D / 8;           // 16-byte chunks per row
-    constexpr int RPP = kThreads / CPR;  // rows per load pass
-    constexpr int NP = kFwdBN / RPP;     // load passes per block
-    __shared__ __attribute__((aligned(16))) char smem_raw[L::TOTAL];
-    lds_char *smem = (lds_char *)smem_raw;
+    // one LDS array per stage, so that reads of one stage are known not to alias the
+    // direct loads into the other (no wait on those loads before the reads)
+    __shared__ __attribute__((aligned(16))) char k0_raw[L::TILE], k1_raw[L::TILE], v0_raw[L::TILE], v1_raw[L::TILE];
 
     const int id = xcd_remap(blockIdx.x, gridDim.x);
     const int head = id / n_qtiles;
@@ -100,58 +99,65 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_kernel(const bf16 *__restrict
     const int kv_end = CAUSAL ? min(N, q0 + kFwdBM) : N;
     const int nt = (kv_end + kFwdBN - 1) / kFwdBN;
 
-    // Cooperative block loader: thread -> (row within pass, 16-byte chunk).
-    const int ld_row = tid / CPR, ld_chk = tid % CPR;
-    u32x4 kreg[NP], vreg[NP];
-    auto gload = [&](const __amdgpu_buffer_rsrc_t &r, int j, u32x4 *regs) {
-#pragma unroll
-        for (int p = 0; p < NP; ++p) {
-            const int row = j * kFwdBN + p * RPP + ld_row;
-            regs[p] = buffer_load16(r, (uint32_t)(row * D + 8 * ld_chk) * 2u);
-        }
-    };
-    auto swrite = [&](int off, int rs, const u32x4 *regs) {
-#pragma unroll
-        for (int p = 0; p < NP; ++p) lds_write16(smem + off, (p * RPP + ld_row) * rs + 16 * ld_chk, regs[p]);
-    };
-    auto kstage = [&](int j) { return smem + (j & 1) * L::KBYTES; };
-    auto vstage = [&](int j) { return smem + L::OFF_V + (j & 1) * L::VBYTES; };
+    // Key / value blocks go straight from global memory into swizzled LDS tiles.
+    // stage of block j is j & 1; callers pass the parity as a compile-time constant
+    auto kstage = [&](auto par) { return (lds_char *)(decltype(par)::value ? k1_raw : k0_raw); };
+    auto vstage = [&](auto par) { return (lds_char *)(decltype(par)::value ? v1_raw : v0_raw); };
+    auto load_k = [&](int j, auto par) { load_tile_lds<D, kFwdWaves>(rk, kstage(par), j * kFwdBN, w, lane); };
+    auto load_v = [&](int j, auto par) { load_tile_lds<D, kFwdWaves>(rv, vstage(par), j * kFwdBN, w, lane); };
 
     // S^T block (64 keys x 32 queries) of key block j
-    auto scores = [&](int j, f32x16 *s) {
-        const lds_char *ks = kstage(j);
+    auto scores = [&](auto par, f32x16 *s) {
+        const lds_char *ks = kstage(par);
         s[0] = zero16();
         s[1] = zero16();
 #pragma unroll
         for (int kst = 0; kst < NKS; ++kst) {
 #pragma unroll
             for (int kb = 0; kb < 2; ++kb) {
-                const bf16x8 a = lds_read16(ks, (32 * kb + c32) * L::KRS + 32 * kst + 16 * h);
+                const bf16x8 a = lds_read16(ks, swz_off<D>(32 * kb + c32, 2 * kst + h));
                 s[kb] = mfma(a, qf[kst], s[kb]);
             }
         }
     };
 
+    // maximum over this lane's 32 keys of a score block (one half of the row's 64 keys)
+    auto local_max = [&](const f32x16 *sc) {
+        float m = fmaxf(sc[0][0], sc[0][1]);
+#pragma unroll
+        for (int r = 2; r < 16; ++r) m = fmaxf(m, sc[0][r]);
+#pragma unroll
+        for (int r = 0; r < 16; ++r) m = fmaxf(m, sc[1][r]);
+        return m;
+    };
+    float mloc = -__builtin_inff();  // local maximum of the block whose scores are current
+
     auto active = [&](int j) { return (qw0 < N) && (!CAUSAL || j * kFwdBN <= qw0 + 31); };
 
     // prologue: K0, V0 and K1 in LDS, scores of block 0 in registers
-    gload(rk, 0, kreg);
-    gload(rv, 0, vreg);
-    swrite(0, L::KRS, kreg);
-    swrite(L::OFF_V, L::VRS, vreg);
-    if (nt > 1) {
-        gload(rk, 1, kreg);
-        swrite(L::KBYTES, L::KRS, kreg);
-    }
+    using P0 = std::integral_constant<int, 0>;
+    using P1 = std::integral_constant<int, 1>;
+    load_k(0, P0{});
+    load_v(0, P0{});
+    load_k(1, P1{});
+    wait_vmem();
     __syncthreads();
     f32x16 sa[2], sb[2];
-    if (active(0)) scores(0, sa);
+    if (active(0)) {
+        scores(P0{}, sa);
+        mloc = local_max(sa);
+    }
 
     // One pipeline step on key block j: scores of j are in `cur`, scores of j+1 go to `nxt`.
-    auto step = [&](int j, f32x16 *cur, f32x16 *nxt) {
+    auto step = [&](int j, auto par, f32x16 *cur, f32x16 *nxt) {
+        using PN = std::integral_constant<int, 1 - decltype(par)::value>;  // parity of j + 1
         const bool more = j + 1 < nt;
-        if (j + 2 < nt) gload(rk, j + 2, kreg);
-        if (more) gload(rv, j + 1, vreg);
+        // K of block j+2 replaces K of block j (last read one step ago), V of block j+1
+        // replaces V of block j-1: both stages are free since the previous barrier.  The
+        // loads are issued every step (past the last block they fetch zeros that are never
+        // read) so that they can be spread between the matrix instructions below.
+        load_k(j + 2, par);
+        load_v(j + 1, PN{});
         if (active(j)) {
             const int k0 = j * kFwdBN;
             if ((CAUSAL && (k0 + kFwdBN - 1 > qw0)) || (k0 + kFwdBN > N)) {
@@ -163,17 +169,15 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_kernel(const bf16 *__restrict
                         if ((CAUSAL && key > qrow) || key >= N) cur[kb][r] = -__builtin_inff();
                     }
                 }
+                mloc = local_max(cur);
             }
-            float mx = cur[0][0];
-#pragma unroll
-            for (int r = 1; r < 16; ++r) mx = fmaxf(mx, cur[0][r]);
-#pragma unroll
-            for (int r = 0; r < 16; ++r) mx = fmaxf(mx, cur[1][r]);
-            mx = fmaxf(mx, __shfl_xor(mx, 32));
-            // move the offset only when some row's maximum outgrows it (or it is still -inf)
-            const bool grow = mx > m_run + grow_thr;
-            if (__builtin_amdgcn_ballot_w64(grow)) {
-                const float m_new = grow ? mx : m_run;
+            // Rescale check without a cross-lane exchange in the common case: each half of the
+            // wave compares the maximum of its own 32 keys with the offset; only when some lane
+            // outgrows it are the two halves' maxima combined and the offset moved.
+            if (__builtin_amdgcn_ballot_w64(mloc > m_run + grow_thr)) {
+                const float mrow = fmaxf(mloc, __shfl_xor(mloc, 32));
+                const bool grow = mrow > m_run + grow_thr;  // identical for both halves of a row
+                const float m_new = grow ? mrow : m_run;
                 const float alpha = grow ? fast_exp2((m_run - m_new) * c_log2) : 1.f;
                 m_run = m_new;
                 msc = (m_run == -__builtin_inff()) ? 0.f : m_run * c_log2;
@@ -185,58 +189,65 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_kernel(const bf16 *__restrict
                 }
             }
             // scores of block j+1 on the matrix cores, probabilities of block j on the vector units
-            scores(more ? j + 1 : j, nxt);
-            float rs = 0.f;
+            scores(PN{}, nxt);  // past the last block: garbage scores that are never used
             bf16x8 pb[kFwdBN / 16];
 #pragma unroll
             for (int kb = 0; kb < 2; ++kb) {
 #pragma unroll
                 for (int r = 0; r < 16; ++r) {
-                                        const float e = fast_exp2(fmaf(cur[kb][r], c_log2, -msc));
-                    rs += e;
-                    pb[2 * kb + (r >> 3)][r & 7] = (bf16)e;
+                    cur[kb][r] = fast_exp2(fmaf(cur[kb][r], c_log2, -msc));
+                    pb[2 * kb + (r >> 3)][r & 7] = (bf16)cur[kb][r];
                 }
             }
-            l_run += rs;
             // O^T += V^T P^T over 4 groups of 16 keys
-            const lds_char *vs = vstage(j);
+            const lds_char *vs = vstage(par);
 #pragma unroll
             for (int t = 0; t < kFwdBN / 16; ++t) {
 #pragma unroll
                 for (int db = 0; db < NDB; ++db) {
-                    const bf16x8 a = lds_read_tr_rows(vs, L::VRS, 16 * t, 32 * db, lane);
+                    const bf16x8 a = lds_read_tr_rows_swz<D>(vs, 16 * t, 32 * db, lane);
                     oacc[db] = mfma(a, pb[t], oacc[db]);
                 }
             }
-            // Issue order for the block above: each score MFMA is followed by the K read two
-            // MFMAs ahead and a slice of the exponential work; the first V reads are issued
-            // before the P V MFMAs, each of which then issues the reads two MFMAs ahead.
+            // while the P V products run: this half's exp-sum of block j and its maximum of block j+1
+            float rs = 0.f;
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb) {
+#pragma unroll
+                for (int r = 0; r < 16; ++r) rs += cur[kb][r];
+            }
+            l_run += rs;
+            mloc = local_max(nxt);
+            // Issue order for the block above: score MFMAs interleaved with K reads, the first
+            // V reads, the exponentials and the block loads; P V MFMAs interleaved with the
+            // remaining V reads, the sums and the next maximum.
+            constexpr int NSM = 2 * NKS;                  // score MFMAs
+            constexpr int NPV = (kFwdBN / 16) * NDB;      // P V MFMAs
             __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
 #pragma unroll
-            for (int i = 0; i < 2 * NKS; ++i) {
+            for (int i = 0; i < NSM; ++i) {
                 __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
                 __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-                __builtin_amdgcn_sched_group_barrier(0x002, 128 / (2 * NKS), 0);
+                if (i >= NSM - 2) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+                __builtin_amdgcn_sched_group_barrier(0x002, 80 / NSM, 0);
             }
-            __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
 #pragma unroll
-            for (int i = 0; i < (kFwdBN / 16) * NDB; ++i) {
+            for (int i = 0; i < NPV; ++i) {
                 __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
                 __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
-                __builtin_amdgcn_sched_group_barrier(0x002, 1, 0);
+                __builtin_amdgcn_sched_group_barrier(0x002, 48 / NPV, 0);
             }
         }
-        if (j + 2 < nt) swrite((j & 1) * L::KBYTES, L::KRS, kreg);
-        if (more) swrite(L::OFF_V + ((j + 1) & 1) * L::VBYTES, L::VRS, vreg);
+        wait_vmem();
         __syncthreads();
     };
 
     int j = 0;
     for (; j + 1 < nt; j += 2) {
-        step(j, sa, sb);
-        step(j + 1, sb, sa);
+        step(j, P0{}, sa, sb);
+        step(j + 1, P1{}, sb, sa);
     }
-    if (j < nt) step(j, sa, sb);
+    if (j < nt) step(j, P0{}, sa, sb);
 
     // epilogue: O = acc / l (bf16, nearest even), lse = m*scale + ln(l)
     const float l_tot = l_run + __shfl_xor(l_run, 32);
