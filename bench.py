@@ -15,7 +15,6 @@ bounded sample of the same workload on the host cores.
 from __future__ import annotations
 
 import argparse
-import hashlib
 import json
 import os
 import sys
@@ -28,7 +27,6 @@ if ROOT not in sys.path:
 METRIC = "attention fwd/bwd TFLOP/s on 1 MI355X and % of bf16 MFMA peak"
 PEAK_BF16_TFLOPS = 2516.6   # 256 CUs x 2.4 GHz x 4096 dense bf16 FLOP/clk/CU
 PEAK_HBM_GBS = 8000.0
-KERNEL_SOURCES = ["attn_device.h", "attn_fwd.hip", "attn_bwd.hip"]
 
 
 def fwd_flop(B, H, N, d, causal) -> float:
@@ -48,14 +46,6 @@ def kernel_algorithmic_flop(kernel, B, H, N, d, causal) -> float:
     return unit * {"fwd": 2, "dkdv": 4, "dq": 1, "preprocess": 0}[kernel]
 
 
-def kernel_source_sha() -> str:
-    h = hashlib.sha256()
-    for name in KERNEL_SOURCES:
-        with open(os.path.join(ROOT, "tiled_online_softmax_02_amd", "csrc", name), "rb") as f:
-            h.update(f.read())
-    return h.hexdigest()[:16]
-
-
 def stored_traffic(kernel: str, workload: str):
     """HBM bytes per launch from committed rocprofv3 counter summaries, or None when the
     kernel sources changed since the counters were taken."""
@@ -66,6 +56,7 @@ def stored_traffic(kernel: str, workload: str):
         rec = json.loads(open(path).read().split("JSON:", 1)[1].strip().splitlines()[0])
     except Exception:
         return None
+    from tiled_online_softmax_02_amd.profiling import kernel_source_sha
     if rec.get("kernel_source_sha") != kernel_source_sha():
         return None
     return rec.get("hbm_bytes_per_launch")

@@ -1,0 +1,111 @@
+"""Summaries of rocprofv3 output for the attention kernels.
+
+``python -m tiled_online_softmax_02_amd.profiling stats <kernel_stats.csv> <out.txt> "<command>"``
+    writes the per-kernel average durations of a ``rocprofv3 --kernel-trace --stats`` run.
+
+``python -m tiled_online_softmax_02_amd.profiling traffic <fetch.csv> <write.csv> <workload> <out_dir> "<commands>"``
+    turns two ``rocprofv3 --pmc FETCH_SIZE`` / ``--pmc WRITE_SIZE`` runs of ``bench.py`` into
+    HBM bytes per launch for each attention kernel.  Both counters are scaled by what they read
+    for the plain device-to-device copy that bench.py performs before its timed region (its
+    size is known: 256 MiB read, 256 MiB written), which calibrates the counter units.
+    One file ``hbm_traffic_<kernel>_<workload>.txt`` is written per kernel; bench.py reports it
+    as ``roofline.traffic`` while the kernel sources are unchanged.
+"""
+from __future__ import annotations
+
+import csv
+import hashlib
+import json
+import os
+import sys
+from collections import defaultdict
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+KERNEL_SOURCES = ["attn_device.h", "attn_fwd.hip", "attn_bwd.hip"]
+CALIBRATION_BYTES = 256 << 20   # bench.py copies 64 Mi int32 values before timing
+SHORT = {"fwd_kernel": "fwd", "bwd_dkdv_kernel": "dkdv", "bwd_dq_kernel": "dq",
+         "bwd_preprocess_kernel": "preprocess"}
+
+
+def kernel_source_sha() -> str:
+    h = hashlib.sha256()
+    for name in KERNEL_SOURCES:
+        with open(os.path.join(PKG, "csrc", name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def short_name(full: str) -> str | None:
+    for key, short in SHORT.items():
+        if key in full:
+            return short
+    return None
+
+
+def stats_summary(stats_csv: str, command: str) -> str:
+    rows = list(csv.DictReader(open(stats_csv)))
+    total = sum(float(r["TotalDurationNs"]) for r in rows)
+    lines = ["rocprofv3 --kernel-trace --stats summary", "command: " + command, "",
+             "%-12s %6s %12s %12s %12s %7s" % ("kernel", "calls", "avg_us", "min_us", "max_us", "pct")]
+    for r in rows:
+        name = short_name(r["Name"]) or r["Name"][:40]
+        lines.append("%-12s %6s %12.2f %12.2f %12.2f %7.2f" % (
+            name, r["Calls"], float(r["AverageNs"]) / 1e3, float(r["MinNs"]) / 1e3, float(r["MaxNs"]) / 1e3,
+            100.0 * float(r["TotalDurationNs"]) / total))
+    lines.append("")
+    lines.append("kernel source sha (attn_device.h, attn_fwd.hip, attn_bwd.hip): " + kernel_source_sha())
+    return "\n".join(lines) + "\n"
+
+
+def counter_per_kernel(path: str, counter: str):
+    """Average counter value (KiB) per dispatch for each attention kernel, plus the copy kernel."""
+    vals = defaultdict(list)
+    for r in csv.DictReader(open(path)):
+        if r["Counter_Name"] != counter:
+            continue
+        name = r["Kernel_Name"]
+        key = short_name(name) or ("copy" if "copyBuffer" in name else None)
+        if key:
+            vals[key].append(float(r["Counter_Value"]))
+    return {k: sum(v) / len(v) for k, v in vals.items()}
+
+
+def traffic_summaries(fetch_csv: str, write_csv: str, workload: str, out_dir: str, commands: str) -> list[str]:
+    fetch = counter_per_kernel(fetch_csv, "FETCH_SIZE")
+    write = counter_per_kernel(write_csv, "WRITE_SIZE")
+    f_factor = CALIBRATION_BYTES / (fetch["copy"] * 1024.0)
+    w_factor = CALIBRATION_BYTES / (write["copy"] * 1024.0)
+    sha = kernel_source_sha()
+    written = []
+    for k in sorted(set(fetch) & set(write)):
+        if k == "copy":
+            continue
+        fb = fetch[k] * 1024.0 * f_factor
+        wb = write[k] * 1024.0 * w_factor
+        rec = {"kernel": k, "workload": workload, "hbm_bytes_per_launch": fb + wb, "fetch_bytes": fb,
+               "write_bytes": wb, "fetch_kib_raw": fetch[k], "write_kib_raw": write[k],
+               "fetch_scale": f_factor, "write_scale": w_factor, "kernel_source_sha": sha}
+        text = "\n".join([
+            "HBM traffic per launch of the %s kernel, workload %s" % (k, workload),
+            "commands: " + commands,
+            "calibration: device copy of %d bytes reads FETCH_SIZE=%.1f KiB, WRITE_SIZE=%.1f KiB"
+            % (CALIBRATION_BYTES, fetch["copy"], write["copy"]),
+            "scale factors: fetch x%.4f, write x%.4f" % (f_factor, w_factor),
+            "fetch %.1f MiB + write %.1f MiB = %.1f MiB per launch" % (fb / 2**20, wb / 2**20, (fb + wb) / 2**20),
+            "JSON: " + json.dumps(rec), ""])
+        path = os.path.join(out_dir, "hbm_traffic_%s_%s.txt" % (k, workload))
+        with open(path, "w") as f:
+            f.write(text)
+        written.append(path)
+    return written
+
+
+if __name__ == "__main__":
+    if sys.argv[1] == "stats":
+        with open(sys.argv[3], "w") as f:
+            f.write(stats_summary(sys.argv[2], sys.argv[4]))
+    elif sys.argv[1] == "traffic":
+        for p in traffic_summaries(sys.argv[2], sys.argv[3], sys.argv[4], sys.argv[5], sys.argv[6]):
+            print(p)
+    else:
+        raise SystemExit(__doc__)
