@@ -22,6 +22,8 @@
 #include "attn_device.h"
 #include "attn_launch.h"
 
+#include <type_traits>
+
 namespace attn {
 
 namespace {
@@ -56,61 +58,46 @@ __global__ __launch_bounds__(kThreads) void bwd_preprocess_kernel(const bf16 *__
 constexpr int kKvBN = 128;  // keys per workgroup (32 per wave)
 constexpr int kKvBM = 64;   // queries per streamed block
 
-template <int D>
-struct KvSmem {
-    static constexpr int RS = D * 2 + 16;  // Q / dO row stride in bytes
-    static constexpr int QBYTES = kKvBM * RS;
-    static constexpr int OFF_DO = QBYTES;
-    static constexpr int OFF_LSE = 2 * QBYTES;            // kKvBM floats: lse * log2(e)
-    static constexpr int OFF_D = OFF_LSE + 4 * kKvBM;     // kKvBM floats: D
-    static constexpr int STAGE = OFF_D + 4 * kKvBM;
-    static constexpr int TOTAL = 2 * STAGE;
-};
-
 template <int D, bool CAUSAL>
 __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(
     const bf16 *__restrict__ Q, const bf16 *__restrict__ K, const bf16 *__restrict__ V, const bf16 *__restrict__ dO,
     const float *__restrict__ LSE, const float *__restrict__ Dl, bf16 *__restrict__ dK, bf16 *__restrict__ dV, int N,
     int n_ktiles, float scale, float c_log2)
 {
-    using L = KvSmem<D>;
     constexpr int NKS = D / 16;
     constexpr int NDB = D / 32;
-    constexpr int CPR = D / 8;
-    constexpr int RPP = kThreads / CPR;
-    constexpr int NP = kKvBM / RPP;
-    __shared__ __attribute__((aligned(16))) char smem_raw[L::TOTAL];
-    lds_char *smem = (lds_char *)smem_raw;
+    constexpr int TILE = kKvBM * D * 2;
+    // One LDS array per stage and operand (swizzled tiles filled by direct loads): reads of
+    // one stage are known not to alias the loads in flight into the other.
+    __shared__ __attribute__((aligned(16))) char q0_raw[TILE], q1_raw[TILE], g0_raw[TILE], g1_raw[TILE];
+    __shared__ __attribute__((aligned(16))) float s0_raw[2 * kKvBM], s1_raw[2 * kKvBM];  // lse, then D
 
     const int id = xcd_remap(blockIdx.x, gridDim.x);
     const int head = id / n_ktiles;
     const int ktile = id - head * n_ktiles;  // causal: key block 0 sees the most queries and goes first
 
     const int tid = threadIdx.x;
-    const int lane = tid & 63, w = tid >> 6, h = lane >> 5, c32 = lane & 31;
+    const int lane = tid & 63, h = lane >> 5, c32 = lane & 31;
+    const int w = wave_uniform(tid >> 6);
     const size_t hoff = (size_t)head * (size_t)N * D;
-    const bf16 *Qh = Q + hoff, *Kh = K + hoff, *Vh = V + hoff, *dOh = dO + hoff;
-    const float *LSEh = LSE + (size_t)head * N, *Dh = Dl + (size_t)head * N;
+    const uint32_t head_bytes = (uint32_t)N * D * 2;
+    const __amdgpu_buffer_rsrc_t rq = make_rsrc(Q + hoff, head_bytes);
+    const __amdgpu_buffer_rsrc_t rk = make_rsrc(K + hoff, head_bytes);
+    const __amdgpu_buffer_rsrc_t rv = make_rsrc(V + hoff, head_bytes);
+    const __amdgpu_buffer_rsrc_t rg = make_rsrc(dO + hoff, head_bytes);
+    const __amdgpu_buffer_rsrc_t rl = make_rsrc(LSE + (size_t)head * N, (uint32_t)N * 4);
+    const __amdgpu_buffer_rsrc_t rd = make_rsrc(Dl + (size_t)head * N, (uint32_t)N * 4);
 
     const int k0 = ktile * kKvBN;
-    const int kw0 = k0 + 32 * w;
+    const int kw0 = k0 + 32 * w;  // wave-uniform
     const int key = kw0 + c32;
-    const bool key_ok = key < N;
 
-    // K and V fragments (B operands of S = Q K^T and dP = dO V^T): lane holds row `key`.
+    // K and V fragments (B operands of S = Q K^T and dP = dO V^T): lane holds row `key` (zeros past N).
     bf16x8 kf[NKS], vf[NKS];
 #pragma unroll
     for (int ks = 0; ks < NKS; ++ks) {
-        if (key_ok) {
-            kf[ks] = *(const bf16x8 *)(Kh + (size_t)key * D + 16 * ks + 8 * h);
-            vf[ks] = *(const bf16x8 *)(Vh + (size_t)key * D + 16 * ks + 8 * h);
-        } else {
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                kf[ks][e] = (bf16)0.f;
-                vf[ks][e] = (bf16)0.f;
-            }
-        }
+        kf[ks] = __builtin_bit_cast(bf16x8, buffer_load16(rk, (uint32_t)(key * D + 16 * ks + 8 * h) * 2u));
+        vf[ks] = __builtin_bit_cast(bf16x8, buffer_load16(rv, (uint32_t)(key * D + 16 * ks + 8 * h) * 2u));
     }
 
     f32x16 dk[NDB], dv[NDB];
@@ -123,59 +110,34 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(
     const int q_start = CAUSAL ? (k0 / kKvBM) * kKvBM : 0;
     const int nsteps = (N > q_start) ? (N - q_start + kKvBM - 1) / kKvBM : 0;
 
-    const int ld_row = tid / CPR, ld_chk = tid % CPR;
-    u32x4 qreg[NP], oreg[NP];
-    float lreg = 0.f, dreg = 0.f;
-    auto gload = [&](int i) {
+    auto qst = [&](auto par) { return (lds_char *)(decltype(par)::value ? q1_raw : q0_raw); };
+    auto gst = [&](auto par) { return (lds_char *)(decltype(par)::value ? g1_raw : g0_raw); };
+    auto sst = [&](auto par) { return (lds_char *)(decltype(par)::value ? s1_raw : s0_raw); };
+    // Q, dO, lse and D of query block i.  Rows past N read as zeros: such a row has Q = dO = 0,
+    // so its P = exp2(0 - 0) = 1 meets zero operands in every product and contributes nothing.
+    auto load_blk = [&](int i, auto par) {
         const int qs = q_start + i * kKvBM;
-#pragma unroll
-        for (int p = 0; p < NP; ++p) {
-            const int row = qs + p * RPP + ld_row;
-            if (row < N) {
-                qreg[p] = *(const u32x4 *)(Qh + (size_t)row * D + 8 * ld_chk);
-                oreg[p] = *(const u32x4 *)(dOh + (size_t)row * D + 8 * ld_chk);
-            } else {
-                qreg[p] = u32x4{0u, 0u, 0u, 0u};
-                oreg[p] = u32x4{0u, 0u, 0u, 0u};
-            }
-        }
-        if (tid < kKvBM) {
-            const int row = qs + tid;
-            // rows beyond N get lse = +inf so that their probabilities are exactly 0
-            lreg = (row < N) ? LSEh[row] * kLog2e : __builtin_inff();
-            dreg = (row < N) ? Dh[row] : 0.f;
-        }
-    };
-    auto swrite = [&](int stage) {
-        lds_char *base = smem + stage * L::STAGE;
-#pragma unroll
-        for (int p = 0; p < NP; ++p) {
-            const int r = p * RPP + ld_row;
-            lds_write16(base, r * L::RS + 16 * ld_chk, qreg[p]);
-            lds_write16(base + L::OFF_DO, r * L::RS + 16 * ld_chk, oreg[p]);
-        }
-        if (tid < kKvBM) {
-            *(__attribute__((address_space(3))) float *)(base + L::OFF_LSE + 4 * tid) = lreg;
-            *(__attribute__((address_space(3))) float *)(base + L::OFF_D + 4 * tid) = dreg;
-        }
+        load_tile_lds<D, 4>(rq, qst(par), qs, w, lane);
+        load_tile_lds<D, 4>(rg, gst(par), qs, w, lane);
+        if (w == 0 && lane < 16) buffer_load_lds16(rl, sst(par), (uint32_t)(qs + 4 * lane) * 4u);
+        if (w == 1 && lane < 16) buffer_load_lds16(rd, sst(par) + 4 * kKvBM, (uint32_t)(qs + 4 * lane) * 4u);
     };
 
-    if (nsteps > 0) {
-        gload(0);
-        swrite(0);
-    }
+    using P0 = std::integral_constant<int, 0>;
+    using P1 = std::integral_constant<int, 1>;
+    load_blk(0, P0{});
+    wait_vmem();
     __syncthreads();
 
-    for (int i = 0; i < nsteps; ++i) {
-        if (i + 1 < nsteps) gload(i + 1);
-        const lds_char *qs_l = smem + (i & 1) * L::STAGE;
-        const lds_char *do_l = qs_l + L::OFF_DO;
-        const lds_char *lse_l = qs_l + L::OFF_LSE;
-        const lds_char *d_l = qs_l + L::OFF_D;
+    auto step = [&](int i, auto par) {
+        using PN = std::integral_constant<int, 1 - decltype(par)::value>;
+        load_blk(i + 1, PN{});  // past the last block: zeros into the free stage, never read
+        const lds_char *q_l = qst(par);
+        const lds_char *g_l = gst(par);
+        const lds_char *st_l = sst(par);
         const int qs = q_start + i * kKvBM;
         // some query of this block sees some key of this wave
-        const bool active = (kw0 < N) && (!CAUSAL || qs + kKvBM - 1 >= kw0);
-        if (active) {
+        if ((kw0 < N) && (!CAUSAL || qs + kKvBM - 1 >= kw0)) {
             // S = Q K^T and dP = dO V^T, two 32-query blocks
             f32x16 s[2] = {zero16(), zero16()};
             f32x16 dp[2] = {zero16(), zero16()};
@@ -183,46 +145,53 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(
             for (int kst = 0; kst < NKS; ++kst) {
 #pragma unroll
                 for (int qb = 0; qb < 2; ++qb) {
-                    const int off = (32 * qb + c32) * L::RS + 32 * kst + 16 * h;
-                    s[qb] = mfma(lds_read16(qs_l, off), kf[kst], s[qb]);
-                    dp[qb] = mfma(lds_read16(do_l, off), vf[kst], dp[qb]);
+                    const int off = swz_off<D>(32 * qb + c32, 2 * kst + h);
+                    s[qb] = mfma(lds_read16(q_l, off), kf[kst], s[qb]);
+                    dp[qb] = mfma(lds_read16(g_l, off), vf[kst], dp[qb]);
                 }
             }
             const bool need_mask = CAUSAL && (qs < kw0 + 31);
+            bf16x8 pb[4], sb[4];
 #pragma unroll
             for (int qb = 0; qb < 2; ++qb) {
 #pragma unroll
                 for (int g = 0; g < 4; ++g) {
                     const int qloc = 32 * qb + 8 * g + 4 * h;  // first of 4 consecutive queries
-                    const f32x4 l4 = *(const __attribute__((address_space(3))) f32x4 *)(lse_l + 4 * qloc);
-                    const f32x4 d4 = *(const __attribute__((address_space(3))) f32x4 *)(d_l + 4 * qloc);
+                    const f32x4 l4 = *(const __attribute__((address_space(3))) f32x4 *)(st_l + 4 * qloc);
+                    const f32x4 d4 = *(const __attribute__((address_space(3))) f32x4 *)(st_l + 4 * (kKvBM + qloc));
 #pragma unroll
                     for (int u = 0; u < 4; ++u) {
                         const int r = 4 * g + u;
-                        float p = fast_exp2(fmaf(s[qb][r], c_log2, -l4[u]));
+                        float p = fast_exp2(fmaf(s[qb][r], c_log2, -l4[u] * kLog2e));
                         if (need_mask && (qs + qloc + u < key)) p = 0.f;
-                        s[qb][r] = p;
-                        dp[qb][r] = p * (dp[qb][r] - d4[u]);
+                        const float ds = p * (dp[qb][r] - d4[u]);
+                        pb[2 * qb + (r >> 3)][r & 7] = (bf16)p;
+                        sb[2 * qb + (r >> 3)][r & 7] = (bf16)ds;
                     }
                 }
             }
             // dV^T += dO^T P and dK^T += Q^T dS over 4 groups of 16 queries
 #pragma unroll
             for (int t = 0; t < kKvBM / 16; ++t) {
-                const bf16x8 pb = pack_bf16(s[t >> 1], t & 1);
-                const bf16x8 sb = pack_bf16(dp[t >> 1], t & 1);
 #pragma unroll
                 for (int db = 0; db < NDB; ++db) {
-                    dv[db] = mfma(lds_read_tr_rows(do_l, L::RS, 16 * t, 32 * db, lane), pb, dv[db]);
-                    dk[db] = mfma(lds_read_tr_rows(qs_l, L::RS, 16 * t, 32 * db, lane), sb, dk[db]);
+                    dv[db] = mfma(lds_read_tr_rows_swz<D>(g_l, 16 * t, 32 * db, lane), pb[t], dv[db]);
+                    dk[db] = mfma(lds_read_tr_rows_swz<D>(q_l, 16 * t, 32 * db, lane), sb[t], dk[db]);
                 }
             }
         }
-        if (i + 1 < nsteps) swrite((i + 1) & 1);
+        wait_vmem();
         __syncthreads();
-    }
+    };
 
-    if (key_ok) {
+    int i = 0;
+    for (; i + 1 < nsteps; i += 2) {
+        step(i, P0{});
+        step(i + 1, P1{});
+    }
+    if (i < nsteps) step(i, P0{});
+
+    if (key < N) {
         bf16 *dkrow = dK + hoff + (size_t)key * D;
         bf16 *dvrow = dV + hoff + (size_t)key * D;
 #pragma unroll
@@ -247,28 +216,16 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(
 constexpr int kQBM = 128;  // queries per workgroup (32 per wave)
 constexpr int kQBN = 64;   // keys per streamed block
 
-template <int D>
-struct QSmem {
-    static constexpr int RS = D * 2 + 16;
-    static constexpr int KBYTES = kQBN * RS;
-    static constexpr int STAGE = 2 * KBYTES;  // K then V
-    static constexpr int TOTAL = 2 * STAGE;
-};
-
 template <int D, bool CAUSAL>
 __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(
     const bf16 *__restrict__ Q, const bf16 *__restrict__ K, const bf16 *__restrict__ V, const bf16 *__restrict__ dO,
     const float *__restrict__ LSE, const float *__restrict__ Dl, bf16 *__restrict__ dQ, int N, int n_qtiles,
     float scale, float c_log2)
 {
-    using L = QSmem<D>;
     constexpr int NKS = D / 16;
     constexpr int NDB = D / 32;
-    constexpr int CPR = D / 8;
-    constexpr int RPP = kThreads / CPR;
-    constexpr int NP = kQBN / RPP;
-    __shared__ __attribute__((aligned(16))) char smem_raw[L::TOTAL];
-    lds_char *smem = (lds_char *)smem_raw;
+    constexpr int TILE = kQBN * D * 2;
+    __shared__ __attribute__((aligned(16))) char k0_raw[TILE], k1_raw[TILE], v0_raw[TILE], v1_raw[TILE];
 
     const int id = xcd_remap(blockIdx.x, gridDim.x);
     const int head = id / n_qtiles;
@@ -276,28 +233,25 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(
     const int qtile = CAUSAL ? (n_qtiles - 1 - t_in) : t_in;
 
     const int tid = threadIdx.x;
-    const int lane = tid & 63, w = tid >> 6, h = lane >> 5, c32 = lane & 31;
+    const int lane = tid & 63, h = lane >> 5, c32 = lane & 31;
+    const int w = wave_uniform(tid >> 6);
     const size_t hoff = (size_t)head * (size_t)N * D;
-    const bf16 *Qh = Q + hoff, *Kh = K + hoff, *Vh = V + hoff, *dOh = dO + hoff;
+    const uint32_t head_bytes = (uint32_t)N * D * 2;
+    const __amdgpu_buffer_rsrc_t rq = make_rsrc(Q + hoff, head_bytes);
+    const __amdgpu_buffer_rsrc_t rk = make_rsrc(K + hoff, head_bytes);
+    const __amdgpu_buffer_rsrc_t rv = make_rsrc(V + hoff, head_bytes);
+    const __amdgpu_buffer_rsrc_t rg = make_rsrc(dO + hoff, head_bytes);
 
     const int q0 = qtile * kQBM;
-    const int qw0 = q0 + 32 * w;
+    const int qw0 = q0 + 32 * w;  // wave-uniform
     const int qrow = qw0 + c32;
     const bool row_ok = qrow < N;
 
     bf16x8 qf[NKS], gf[NKS];
 #pragma unroll
     for (int ks = 0; ks < NKS; ++ks) {
-        if (row_ok) {
-            qf[ks] = *(const bf16x8 *)(Qh + (size_t)qrow * D + 16 * ks + 8 * h);
-            gf[ks] = *(const bf16x8 *)(dOh + (size_t)qrow * D + 16 * ks + 8 * h);
-        } else {
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                qf[ks][e] = (bf16)0.f;
-                gf[ks][e] = (bf16)0.f;
-            }
-        }
+        qf[ks] = __builtin_bit_cast(bf16x8, buffer_load16(rq, (uint32_t)(qrow * D + 16 * ks + 8 * h) * 2u));
+        gf[ks] = __builtin_bit_cast(bf16x8, buffer_load16(rg, (uint32_t)(qrow * D + 16 * ks + 8 * h) * 2u));
     }
     const float lse2 = row_ok ? LSE[(size_t)head * N + qrow] * kLog2e : __builtin_inff();
     const float dval = row_ok ? Dl[(size_t)head * N + qrow] : 0.f;
@@ -309,55 +263,39 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(
     const int kv_end = CAUSAL ? min(N, q0 + kQBM) : N;
     const int nt = (kv_end + kQBN - 1) / kQBN;
 
-    const int ld_row = tid / CPR, ld_chk = tid % CPR;
-    u32x4 kreg[NP], vreg[NP];
-    auto gload = [&](int j) {
-#pragma unroll
-        for (int p = 0; p < NP; ++p) {
-            const int row = j * kQBN + p * RPP + ld_row;
-            if (row < N) {
-                kreg[p] = *(const u32x4 *)(Kh + (size_t)row * D + 8 * ld_chk);
-                vreg[p] = *(const u32x4 *)(Vh + (size_t)row * D + 8 * ld_chk);
-            } else {
-                kreg[p] = u32x4{0u, 0u, 0u, 0u};
-                vreg[p] = u32x4{0u, 0u, 0u, 0u};
-            }
-        }
-    };
-    auto swrite = [&](int stage) {
-        lds_char *ks = smem + stage * L::STAGE;
-        lds_char *vs = ks + L::KBYTES;
-#pragma unroll
-        for (int p = 0; p < NP; ++p) {
-            const int r = p * RPP + ld_row;
-            lds_write16(ks, r * L::RS + 16 * ld_chk, kreg[p]);
-            lds_write16(vs, r * L::RS + 16 * ld_chk, vreg[p]);
-        }
+    auto kst_l = [&](auto par) { return (lds_char *)(decltype(par)::value ? k1_raw : k0_raw); };
+    auto vst_l = [&](auto par) { return (lds_char *)(decltype(par)::value ? v1_raw : v0_raw); };
+    auto load_blk = [&](int j, auto par) {
+        load_tile_lds<D, 4>(rk, kst_l(par), j * kQBN, w, lane);
+        load_tile_lds<D, 4>(rv, vst_l(par), j * kQBN, w, lane);
     };
 
-    gload(0);
-    swrite(0);
+    using P0 = std::integral_constant<int, 0>;
+    using P1 = std::integral_constant<int, 1>;
+    load_blk(0, P0{});
+    wait_vmem();
     __syncthreads();
 
-    for (int j = 0; j < nt; ++j) {
-        if (j + 1 < nt) gload(j + 1);
-        const lds_char *ks = smem + (j & 1) * L::STAGE;
-        const lds_char *vs = ks + L::KBYTES;
+    auto step = [&](int j, auto par) {
+        using PN = std::integral_constant<int, 1 - decltype(par)::value>;
+        load_blk(j + 1, PN{});  // past the last block: zeros into the free stage, never read
+        const lds_char *ks = kst_l(par);
+        const lds_char *vs = vst_l(par);
         const int k0 = j * kQBN;
-        const bool active = (qw0 < N) && (!CAUSAL || k0 <= qw0 + 31);
-        if (active) {
+        if ((qw0 < N) && (!CAUSAL || k0 <= qw0 + 31)) {
             f32x16 s[2] = {zero16(), zero16()};
             f32x16 dp[2] = {zero16(), zero16()};
 #pragma unroll
             for (int kst = 0; kst < NKS; ++kst) {
 #pragma unroll
                 for (int kb = 0; kb < 2; ++kb) {
-                    const int off = (32 * kb + c32) * L::RS + 32 * kst + 16 * h;
+                    const int off = swz_off<D>(32 * kb + c32, 2 * kst + h);
                     s[kb] = mfma(lds_read16(ks, off), qf[kst], s[kb]);
                     dp[kb] = mfma(lds_read16(vs, off), gf[kst], dp[kb]);
                 }
             }
             const bool need_mask = (CAUSAL && (k0 + kQBN - 1 > qw0)) || (k0 + kQBN > N);
+            bf16x8 sb[4];
 #pragma unroll
             for (int kb = 0; kb < 2; ++kb) {
 #pragma unroll
@@ -367,21 +305,27 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(
                         const int kk = k0 + 32 * kb + 8 * (r >> 2) + 4 * h + (r & 3);
                         if ((CAUSAL && kk > qrow) || kk >= N) p = 0.f;
                     }
-                    dp[kb][r] = p * (dp[kb][r] - dval);
+                    sb[2 * kb + (r >> 3)][r & 7] = (bf16)(p * (dp[kb][r] - dval));
                 }
             }
             // dQ^T += K^T dS^T over 4 groups of 16 keys
 #pragma unroll
             for (int t = 0; t < kQBN / 16; ++t) {
-                const bf16x8 sb = pack_bf16(dp[t >> 1], t & 1);
 #pragma unroll
                 for (int db = 0; db < NDB; ++db)
-                    dq[db] = mfma(lds_read_tr_rows(ks, L::RS, 16 * t, 32 * db, lane), sb, dq[db]);
+                    dq[db] = mfma(lds_read_tr_rows_swz<D>(ks, 16 * t, 32 * db, lane), sb[t], dq[db]);
             }
         }
-        if (j + 1 < nt) swrite((j + 1) & 1);
+        wait_vmem();
         __syncthreads();
+    };
+
+    int j = 0;
+    for (; j + 1 < nt; j += 2) {
+        step(j, P0{});
+        step(j + 1, P1{});
     }
+    if (j < nt) step(j, P0{});
 
     if (row_ok) {
         bf16 *qrow_p = dQ + hoff + (size_t)qrow * D;
