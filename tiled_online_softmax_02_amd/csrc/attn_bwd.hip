@@ -72,9 +72,8 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(
     __shared__ __attribute__((aligned(16))) char q0_raw[TILE], q1_raw[TILE], g0_raw[TILE], g1_raw[TILE];
     __shared__ __attribute__((aligned(16))) float s0_raw[2 * kKvBM], s1_raw[2 * kKvBM];  // lse, then D
 
-    const int id = xcd_remap(blockIdx.x, gridDim.x);
-    const int head = id / n_ktiles;
-    const int ktile = id - head * n_ktiles;  // causal: key block 0 sees the most queries and goes first
+    int head, ktile;
+    work_item(blockIdx.x, n_ktiles, head, ktile);  // causal: key block 0 sees the most queries and goes first
 
     const int tid = threadIdx.x;
     const int lane = tid & 63, h = lane >> 5, c32 = lane & 31;
@@ -110,12 +109,12 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(
     const int q_start = CAUSAL ? (k0 / kKvBM) * kKvBM : 0;
     const int nsteps = (N > q_start) ? (N - q_start + kKvBM - 1) / kKvBM : 0;
 
-    auto qst = [&](auto par) { return (lds_char *)(decltype(par)::value ? q1_raw : q0_raw); };
-    auto gst = [&](auto par) { return (lds_char *)(decltype(par)::value ? g1_raw : g0_raw); };
-    auto sst = [&](auto par) { return (lds_char *)(decltype(par)::value ? s1_raw : s0_raw); };
+    auto qst = [&](auto par) __attribute__((always_inline)) { return (lds_char *)(decltype(par)::value ? q1_raw : q0_raw); };
+    auto gst = [&](auto par) __attribute__((always_inline)) { return (lds_char *)(decltype(par)::value ? g1_raw : g0_raw); };
+    auto sst = [&](auto par) __attribute__((always_inline)) { return (lds_char *)(decltype(par)::value ? s1_raw : s0_raw); };
     // Q, dO, lse and D of query block i.  Rows past N read as zeros: such a row has Q = dO = 0,
     // so its P = exp2(0 - 0) = 1 meets zero operands in every product and contributes nothing.
-    auto load_blk = [&](int i, auto par) {
+    auto load_blk = [&](int i, auto par) __attribute__((always_inline)) {
         const int qs = q_start + i * kKvBM;
         load_tile_lds<D, 4>(rq, qst(par), qs, w, lane);
         load_tile_lds<D, 4>(rg, gst(par), qs, w, lane);
@@ -129,7 +128,7 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(
     wait_vmem();
     __syncthreads();
 
-    auto step = [&](int i, auto par) {
+    auto step = [&](int i, auto par) __attribute__((always_inline)) {
         using PN = std::integral_constant<int, 1 - decltype(par)::value>;
         load_blk(i + 1, PN{});  // past the last block: zeros into the free stage, never read
         const lds_char *q_l = qst(par);
@@ -227,9 +226,8 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(
     constexpr int TILE = kQBN * D * 2;
     __shared__ __attribute__((aligned(16))) char k0_raw[TILE], k1_raw[TILE], v0_raw[TILE], v1_raw[TILE];
 
-    const int id = xcd_remap(blockIdx.x, gridDim.x);
-    const int head = id / n_qtiles;
-    const int t_in = id - head * n_qtiles;
+    int head, t_in;
+    work_item(blockIdx.x, n_qtiles, head, t_in);
     const int qtile = CAUSAL ? (n_qtiles - 1 - t_in) : t_in;
 
     const int tid = threadIdx.x;
@@ -263,9 +261,9 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(
     const int kv_end = CAUSAL ? min(N, q0 + kQBM) : N;
     const int nt = (kv_end + kQBN - 1) / kQBN;
 
-    auto kst_l = [&](auto par) { return (lds_char *)(decltype(par)::value ? k1_raw : k0_raw); };
-    auto vst_l = [&](auto par) { return (lds_char *)(decltype(par)::value ? v1_raw : v0_raw); };
-    auto load_blk = [&](int j, auto par) {
+    auto kst_l = [&](auto par) __attribute__((always_inline)) { return (lds_char *)(decltype(par)::value ? k1_raw : k0_raw); };
+    auto vst_l = [&](auto par) __attribute__((always_inline)) { return (lds_char *)(decltype(par)::value ? v1_raw : v0_raw); };
+    auto load_blk = [&](int j, auto par) __attribute__((always_inline)) {
         load_tile_lds<D, 4>(rk, kst_l(par), j * kQBN, w, lane);
         load_tile_lds<D, 4>(rv, vst_l(par), j * kQBN, w, lane);
     };
@@ -276,7 +274,7 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(
     wait_vmem();
     __syncthreads();
 
-    auto step = [&](int j, auto par) {
+    auto step = [&](int j, auto par) __attribute__((always_inline)) {
         using PN = std::integral_constant<int, 1 - decltype(par)::value>;
         load_blk(j + 1, PN{});  // past the last block: zeros into the free stage, never read
         const lds_char *ks = kst_l(par);

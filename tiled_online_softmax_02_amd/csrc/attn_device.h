@@ -104,6 +104,26 @@ __device__ __forceinline__ int xcd_remap(int g, int G)
     return x * per + (x < rem ? x : rem) + i;
 }
 
+// Work item of workgroup g when the grid holds n_heads * n_tiles workgroups: a head and
+// the position t of its tile in issue order (t = 0 goes out first).  When n_heads is a
+// multiple of the 8 XCDs, items go out position-major (position 0 of every head, then
+// position 1, ...): dispatch is then longest-first over the whole grid when position 0
+// is the largest tile, and head h always lands on XCD h % 8, so that its K and V stay in
+// one L2.  Otherwise every XCD takes a contiguous head-major range of items.
+__device__ __forceinline__ void work_item(int g, int n_tiles, int &head, int &t)
+{
+    const int G = (int)gridDim.x;
+    const int n_heads = G / n_tiles;
+    if ((n_heads & 7) == 0) {
+        t = g / n_heads;
+        head = g - t * n_heads;
+    } else {
+        const int id = xcd_remap(g, G);
+        head = id / n_tiles;
+        t = id - head * n_tiles;
+    }
+}
+
 }  // namespace attn
 
 namespace attn {
@@ -159,16 +179,27 @@ __device__ __forceinline__ void buffer_load_lds16(__amdgpu_buffer_rsrc_t r, lds_
 // Wait until this wave's vector-memory loads (including direct LDS loads) are done.
 __device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 
-// Load rows [row0, row0 + 64) of a row-major [*, D] bf16 matrix into a swizzled
+// Workgroup barrier that first waits until at most N of this wave's vector-memory loads
+// (direct LDS loads included) are outstanding and all its LDS accesses are done.  Unlike
+// __syncthreads() it carries no release fence, which would wait for every load in flight;
+// the "memory" clobber keeps the compiler from moving memory accesses across it.
+template <int N>
+__device__ __forceinline__ void barrier_wait_vmem_upto()
+{
+    static_assert(N >= 0 && N < 16, "vmcnt field is 4 bits here");
+    asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(N) : "memory");
+}
+
+// Load rows [row0, row0 + ROWS) of a row-major [*, D] bf16 matrix into a swizzled
 // LDS tile with direct loads; all NW waves of the workgroup take part.
 // Each wave instruction covers 1 KB = 1024 / (2 D) whole rows.
-template <int D, int NW>
+template <int D, int NW, int ROWS = 64>
 __device__ __forceinline__ void load_tile_lds(__amdgpu_buffer_rsrc_t r, lds_char *tile, int row0, int wave, int lane)
 {
-    constexpr int RB = 2 * D;           // bytes per row
-    constexpr int RPI = 1024 / RB;      // rows per wave instruction
-    constexpr int NI = 64 / RPI / NW;   // instructions per wave for 64 rows
-    static_assert(NI >= 1 && NI * RPI * NW == 64, "64-row tile must split evenly over the waves");
+    constexpr int RB = 2 * D;            // bytes per row
+    constexpr int RPI = 1024 / RB;       // rows per wave instruction
+    constexpr int NI = ROWS / RPI / NW;  // instructions per wave for the tile
+    static_assert(NI >= 1 && NI * RPI * NW == ROWS, "tile must split evenly over the waves");
     const int lr = lane / (RB / 16), p = lane % (RB / 16);
 #pragma unroll
     for (int i = 0; i < NI; ++i) {

@@ -9,8 +9,9 @@
 // end.  S and P never leave the chip.
 //
 // gfx950 mapping:
-//   * one workgroup of 4 waves per block of 128 query rows; each wave owns 32
-//     rows and holds their Q fragments in VGPRs for the whole loop;
+//   * one workgroup of 8 waves (d = 128) or 4 waves (d = 64) per block of query
+//     rows; each wave owns 32 rows and holds their Q fragments in VGPRs for the
+//     whole loop;
 //   * key/value blocks of 64 rows are double-buffered through swizzled LDS tiles
 //     filled by direct global->LDS buffer loads (rows past N read as zeros, no
 //     staging registers, no LDS store instructions); K runs one block ahead of V, so
@@ -38,10 +39,13 @@ namespace attn {
 
 namespace {
 
-constexpr int kFwdWaves = 4;               // waves per workgroup, 32 query rows each
-constexpr int kFwdBM = 32 * kFwdWaves;     // query rows per workgroup
+// Waves per workgroup (32 query rows each): 8 at d = 128, where two waves per SIMD come from
+// the same workgroup and share each K/V block loaded into LDS; 4 at d = 64.
+template <int D>
+constexpr int fwd_waves() { return D == 128 ? 8 : 4; }
+template <int D>
+constexpr int fwd_bm() { return 32 * fwd_waves<D>(); }
 constexpr int kFwdBN = 64;                 // keys per streamed block
-constexpr int kThreads = 64 * kFwdWaves;
 constexpr float kRescaleLog2 = 8.0f;
 
 template <int D>
@@ -52,21 +56,22 @@ struct FwdSmem {
 };
 
 template <int D, bool CAUSAL>
-__global__ __launch_bounds__(kThreads, 8 / kFwdWaves) void fwd_kernel(const bf16 *__restrict__ Q, const bf16 *__restrict__ K,
+__global__ __launch_bounds__(64 * fwd_waves<D>(), 8 / fwd_waves<D>()) void fwd_kernel(const bf16 *__restrict__ Q, const bf16 *__restrict__ K,
                                                           const bf16 *__restrict__ V, bf16 *__restrict__ O,
                                                           float *__restrict__ LSE, int N, int n_qtiles, float scale,
                                                           float c_log2)
 {
     using L = FwdSmem<D>;
+    constexpr int kFwdWaves = fwd_waves<D>();
+    constexpr int kFwdBM = fwd_bm<D>();
     constexpr int NKS = D / 16;          // reduction steps over d for S^T
     constexpr int NDB = D / 32;          // 32-wide column blocks of O
     // one LDS array per stage, so that reads of one stage are known not to alias the
     // direct loads into the other (no wait on those loads before the reads)
     __shared__ __attribute__((aligned(16))) char k0_raw[L::TILE], k1_raw[L::TILE], v0_raw[L::TILE], v1_raw[L::TILE];
 
-    const int id = xcd_remap(blockIdx.x, gridDim.x);
-    const int head = id / n_qtiles;
-    const int t_in = id - head * n_qtiles;
+    int head, t_in;
+    work_item(blockIdx.x, n_qtiles, head, t_in);
     const int qtile = CAUSAL ? (n_qtiles - 1 - t_in) : t_in;  // causal: longest rows first
 
     const int tid = threadIdx.x;
@@ -101,13 +106,13 @@ __global__ __launch_bounds__(kThreads, 8 / kFwdWaves) void fwd_kernel(const bf16
 
     // Key / value blocks go straight from global memory into swizzled LDS tiles.
     // stage of block j is j & 1; callers pass the parity as a compile-time constant
-    auto kstage = [&](auto par) { return (lds_char *)(decltype(par)::value ? k1_raw : k0_raw); };
-    auto vstage = [&](auto par) { return (lds_char *)(decltype(par)::value ? v1_raw : v0_raw); };
-    auto load_k = [&](int j, auto par) { load_tile_lds<D, kFwdWaves>(rk, kstage(par), j * kFwdBN, w, lane); };
-    auto load_v = [&](int j, auto par) { load_tile_lds<D, kFwdWaves>(rv, vstage(par), j * kFwdBN, w, lane); };
+    auto kstage = [&](auto par) __attribute__((always_inline)) { return (lds_char *)(decltype(par)::value ? k1_raw : k0_raw); };
+    auto vstage = [&](auto par) __attribute__((always_inline)) { return (lds_char *)(decltype(par)::value ? v1_raw : v0_raw); };
+    auto load_k = [&](int j, auto par) __attribute__((always_inline)) { load_tile_lds<D, kFwdWaves>(rk, kstage(par), j * kFwdBN, w, lane); };
+    auto load_v = [&](int j, auto par) __attribute__((always_inline)) { load_tile_lds<D, kFwdWaves>(rv, vstage(par), j * kFwdBN, w, lane); };
 
     // S^T block (64 keys x 32 queries) of key block j
-    auto scores = [&](auto par, f32x16 *s) {
+    auto scores = [&](auto par, f32x16 *s) __attribute__((always_inline)) {
         const lds_char *ks = kstage(par);
         s[0] = zero16();
         s[1] = zero16();
@@ -122,7 +127,7 @@ __global__ __launch_bounds__(kThreads, 8 / kFwdWaves) void fwd_kernel(const bf16
     };
 
     // maximum over this lane's 32 keys of a score block (one half of the row's 64 keys)
-    auto local_max = [&](const f32x16 *sc) {
+    auto local_max = [&](const f32x16 *sc) __attribute__((always_inline)) {
         float m = fmaxf(sc[0][0], sc[0][1]);
 #pragma unroll
         for (int r = 2; r < 16; ++r) m = fmaxf(m, sc[0][r]);
@@ -132,7 +137,7 @@ __global__ __launch_bounds__(kThreads, 8 / kFwdWaves) void fwd_kernel(const bf16
     };
     float mloc = -__builtin_inff();  // local maximum of the block whose scores are current
 
-    auto active = [&](int j) { return (qw0 < N) && (!CAUSAL || j * kFwdBN <= qw0 + 31); };
+    auto active = [&](int j) __attribute__((always_inline)) { return (qw0 < N) && (!CAUSAL || j * kFwdBN <= qw0 + 31); };
 
     // prologue: K0, V0 and K1 in LDS, scores of block 0 in registers
     using P0 = std::integral_constant<int, 0>;
@@ -149,15 +154,9 @@ __global__ __launch_bounds__(kThreads, 8 / kFwdWaves) void fwd_kernel(const bf16
     }
 
     // One pipeline step on key block j: scores of j are in `cur`, scores of j+1 go to `nxt`.
-    auto step = [&](int j, auto par, f32x16 *cur, f32x16 *nxt) {
+    auto step = [&](int j, auto par, f32x16 *cur, f32x16 *nxt) __attribute__((always_inline)) {
         using PN = std::integral_constant<int, 1 - decltype(par)::value>;  // parity of j + 1
         const bool more = j + 1 < nt;
-        // K of block j+2 replaces K of block j (last read one step ago), V of block j+1
-        // replaces V of block j-1: both stages are free since the previous barrier.  The
-        // loads are issued every step (past the last block they fetch zeros that are never
-        // read) so that they can be spread between the matrix instructions below.
-        load_k(j + 2, par);
-        load_v(j + 1, PN{});
         if (active(j)) {
             const int k0 = j * kFwdBN;
             if ((CAUSAL && (k0 + kFwdBN - 1 > qw0)) || (k0 + kFwdBN > N)) {
@@ -189,7 +188,14 @@ __global__ __launch_bounds__(kThreads, 8 / kFwdWaves) void fwd_kernel(const bf16
                 }
             }
             // scores of block j+1 on the matrix cores, probabilities of block j on the vector units
+            __builtin_amdgcn_s_setprio(1);
             scores(PN{}, nxt);  // past the last block: garbage scores that are never used
+            // K of block j+2 replaces K of block j (last read one step ago), V of block j+1
+            // replaces V of block j-1: both stages are free since the previous barrier.  The
+            // loads are issued every step (past the last block they fetch zeros that are never
+            // read), after the score MFMAs so that their issue overlaps matrix work.
+            load_k(j + 2, par);
+            load_v(j + 1, PN{});
             bf16x8 pb[kFwdBN / 16];
 #pragma unroll
             for (int kb = 0; kb < 2; ++kb) {
@@ -218,25 +224,10 @@ __global__ __launch_bounds__(kThreads, 8 / kFwdWaves) void fwd_kernel(const bf16
             }
             l_run += rs;
             mloc = local_max(nxt);
-            // Issue order for the block above: score MFMAs interleaved with K reads, the first
-            // V reads, the exponentials and the block loads; P V MFMAs interleaved with the
-            // remaining V reads, the sums and the next maximum.
-            constexpr int NSM = 2 * NKS;                  // score MFMAs
-            constexpr int NPV = (kFwdBN / 16) * NDB;      // P V MFMAs
-            __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
-#pragma unroll
-            for (int i = 0; i < NSM; ++i) {
-                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-                __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-                if (i >= NSM - 2) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
-                __builtin_amdgcn_sched_group_barrier(0x002, 80 / NSM, 0);
-            }
-#pragma unroll
-            for (int i = 0; i < NPV; ++i) {
-                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-                __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
-                __builtin_amdgcn_sched_group_barrier(0x002, 48 / NPV, 0);
-            }
+            __builtin_amdgcn_s_setprio(0);
+        } else {
+            load_k(j + 2, par);
+            load_v(j + 1, PN{});
         }
         wait_vmem();
         __syncthreads();
@@ -272,6 +263,8 @@ __global__ __launch_bounds__(kThreads, 8 / kFwdWaves) void fwd_kernel(const bf16
 template <int D, bool CAUSAL>
 hipError_t launch_fwd_t(const FwdArgs &a)
 {
+    constexpr int kFwdBM = fwd_bm<D>();
+    constexpr int kThreads = 64 * fwd_waves<D>();
     const int n_qtiles = (a.N + kFwdBM - 1) / kFwdBM;
     const long long G = (long long)a.B * a.H * n_qtiles;
     const float c_log2 = a.scale * kLog2e;
@@ -289,6 +282,6 @@ hipError_t launch_fwd(const FwdArgs &a)
     return a.causal ? launch_fwd_t<128, true>(a) : launch_fwd_t<128, false>(a);
 }
 
-long long fwd_grid_size(int B, int H, int N) { return (long long)B * H * ((N + kFwdBM - 1) / kFwdBM); }
+long long fwd_grid_size(int B, int H, int N) { return (long long)B * H * ((N + fwd_bm<64>() - 1) / fwd_bm<64>()); }
 
 }  // namespace attn
