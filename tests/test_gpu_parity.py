@@ -77,6 +77,8 @@ SMALL = [
     (1, 1, 1, 64, False), (1, 2, 1, 128, True), (1, 1, 17, 64, True), (2, 1, 63, 128, False),
     (1, 2, 64, 64, True), (1, 1, 65, 128, True), (2, 3, 100, 64, False), (1, 2, 128, 128, True),
     (2, 2, 200, 128, True), (1, 3, 257, 64, True), (1, 1, 300, 128, False), (2, 2, 384, 64, False),
+    # odd and even counts of query / key blocks per head under the causal mask, ragged tails
+    (1, 2, 600, 128, True), (1, 1, 777, 64, True), (2, 1, 1100, 128, True), (1, 1, 1024, 64, True),
 ]
 
 

@@ -29,7 +29,8 @@
 //     lse = m + ln l are unchanged because acc and l share the offset;
 //   * causal: key blocks above the diagonal are never loaded, waves skip the
 //     blocks that lie wholly above their own rows, masking runs only on blocks
-//     that cross the diagonal, and query blocks are issued longest first.
+//     that cross the diagonal, and each workgroup takes a long and a short query
+//     block (T-1-p and p of T), so that all workgroups carry equal work.
 #include "attn_device.h"
 #include "attn_launch.h"
 
@@ -70,9 +71,12 @@ __global__ __launch_bounds__(64 * fwd_waves<D>(), 8 / fwd_waves<D>()) void fwd_k
     // direct loads into the other (no wait on those loads before the reads)
     __shared__ __attribute__((aligned(16))) char k0_raw[L::TILE], k1_raw[L::TILE], v0_raw[L::TILE], v1_raw[L::TILE];
 
-    int head, t_in;
-    work_item(blockIdx.x, n_qtiles, head, t_in);
-    const int qtile = CAUSAL ? (n_qtiles - 1 - t_in) : t_in;  // causal: longest rows first
+    // Causal: workgroup `pos` of a head takes query blocks T-1-pos and then pos (T = n_qtiles),
+    // so every workgroup but a middle one does the same T+1 blocks' worth of work and the
+    // grid needs no longest-first balancing.  Non-causal: one query block per workgroup.
+    const int n_pos = CAUSAL ? (n_qtiles + 1) / 2 : n_qtiles;
+    int head, pos;
+    work_item(blockIdx.x, n_pos, head, pos);
 
     const int tid = threadIdx.x;
     const int lane = tid & 63, h = lane >> 5, c32 = lane & 31;
@@ -83,180 +87,187 @@ __global__ __launch_bounds__(64 * fwd_waves<D>(), 8 / fwd_waves<D>()) void fwd_k
     const __amdgpu_buffer_rsrc_t rk = make_rsrc(K + hoff, head_bytes);
     const __amdgpu_buffer_rsrc_t rv = make_rsrc(V + hoff, head_bytes);
 
-    const int q0 = qtile * kFwdBM;
-    const int qw0 = q0 + 32 * w;  // wave-uniform
-    const int qrow = qw0 + c32;
+    for (int pass = 0; pass < (CAUSAL ? 2 : 1); ++pass) {
+        const int qtile = pass == 0 ? (CAUSAL ? n_qtiles - 1 - pos : pos) : pos;
+        if (pass == 1 && qtile == n_qtiles - 1 - pos) break;  // odd T: the middle block is alone
+        const int q0 = qtile * kFwdBM;
+        const int qw0 = q0 + 32 * w;  // wave-uniform
+        const int qrow = qw0 + c32;
 
-    // Q fragments: B operand of S^T = K Q^T, lane holds Q[qrow][16ks + 8h .. +7] (zeros past N).
-    bf16x8 qf[NKS];
+        // Q fragments: B operand of S^T = K Q^T, lane holds Q[qrow][16ks + 8h .. +7] (zeros past N).
+        bf16x8 qf[NKS];
 #pragma unroll
-    for (int ks = 0; ks < NKS; ++ks)
-        qf[ks] = __builtin_bit_cast(bf16x8, buffer_load16(rq, (uint32_t)(qrow * D + 16 * ks + 8 * h) * 2u));
+        for (int ks = 0; ks < NKS; ++ks)
+            qf[ks] = __builtin_bit_cast(bf16x8, buffer_load16(rq, (uint32_t)(qrow * D + 16 * ks + 8 * h) * 2u));
 
-    f32x16 oacc[NDB];
+        f32x16 oacc[NDB];
 #pragma unroll
-    for (int i = 0; i < NDB; ++i) oacc[i] = zero16();
-    float m_run = -__builtin_inff();  // exponent offset (raw score units)
-    float msc = 0.f;                   // m_run * c_log2, 0 while m_run = -inf
-    float l_run = 0.f;
-    const float grow_thr = kRescaleLog2 / c_log2;
+        for (int i = 0; i < NDB; ++i) oacc[i] = zero16();
+        float m_run = -__builtin_inff();  // exponent offset (raw score units)
+        float msc = 0.f;                   // m_run * c_log2, 0 while m_run = -inf
+        float l_run = 0.f;
+        const float grow_thr = kRescaleLog2 / c_log2;
 
-    const int kv_end = CAUSAL ? min(N, q0 + kFwdBM) : N;
-    const int nt = (kv_end + kFwdBN - 1) / kFwdBN;
+        const int kv_end = CAUSAL ? min(N, q0 + kFwdBM) : N;
+        const int nt = (kv_end + kFwdBN - 1) / kFwdBN;
 
-    // Key / value blocks go straight from global memory into swizzled LDS tiles.
-    // stage of block j is j & 1; callers pass the parity as a compile-time constant
-    auto kstage = [&](auto par) __attribute__((always_inline)) { return (lds_char *)(decltype(par)::value ? k1_raw : k0_raw); };
-    auto vstage = [&](auto par) __attribute__((always_inline)) { return (lds_char *)(decltype(par)::value ? v1_raw : v0_raw); };
-    auto load_k = [&](int j, auto par) __attribute__((always_inline)) { load_tile_lds<D, kFwdWaves>(rk, kstage(par), j * kFwdBN, w, lane); };
-    auto load_v = [&](int j, auto par) __attribute__((always_inline)) { load_tile_lds<D, kFwdWaves>(rv, vstage(par), j * kFwdBN, w, lane); };
+        // Key / value blocks go straight from global memory into swizzled LDS tiles.
+        // stage of block j is j & 1; callers pass the parity as a compile-time constant
+        auto kstage = [&](auto par) __attribute__((always_inline)) { return (lds_char *)(decltype(par)::value ? k1_raw : k0_raw); };
+        auto vstage = [&](auto par) __attribute__((always_inline)) { return (lds_char *)(decltype(par)::value ? v1_raw : v0_raw); };
+        auto load_k = [&](int j, auto par) __attribute__((always_inline)) { load_tile_lds<D, kFwdWaves>(rk, kstage(par), j * kFwdBN, w, lane); };
+        auto load_v = [&](int j, auto par) __attribute__((always_inline)) { load_tile_lds<D, kFwdWaves>(rv, vstage(par), j * kFwdBN, w, lane); };
 
-    // S^T block (64 keys x 32 queries) of key block j
-    auto scores = [&](auto par, f32x16 *s) __attribute__((always_inline)) {
-        const lds_char *ks = kstage(par);
-        s[0] = zero16();
-        s[1] = zero16();
+        // S^T block (64 keys x 32 queries) of key block j
+        auto scores = [&](auto par, f32x16 *s) __attribute__((always_inline)) {
+            const lds_char *ks = kstage(par);
+            s[0] = zero16();
+            s[1] = zero16();
 #pragma unroll
-        for (int kst = 0; kst < NKS; ++kst) {
+            for (int kst = 0; kst < NKS; ++kst) {
 #pragma unroll
-            for (int kb = 0; kb < 2; ++kb) {
-                const bf16x8 a = lds_read16(ks, swz_off<D>(32 * kb + c32, 2 * kst + h));
-                s[kb] = mfma(a, qf[kst], s[kb]);
+                for (int kb = 0; kb < 2; ++kb) {
+                    const bf16x8 a = lds_read16(ks, swz_off<D>(32 * kb + c32, 2 * kst + h));
+                    s[kb] = mfma(a, qf[kst], s[kb]);
+                }
             }
+        };
+
+        // maximum over this lane's 32 keys of a score block (one half of the row's 64 keys)
+        auto local_max = [&](const f32x16 *sc) __attribute__((always_inline)) {
+            float m = fmaxf(sc[0][0], sc[0][1]);
+#pragma unroll
+            for (int r = 2; r < 16; ++r) m = fmaxf(m, sc[0][r]);
+#pragma unroll
+            for (int r = 0; r < 16; ++r) m = fmaxf(m, sc[1][r]);
+            return m;
+        };
+        float mloc = -__builtin_inff();  // local maximum of the block whose scores are current
+
+        auto active = [&](int j) __attribute__((always_inline)) { return (qw0 < N) && (!CAUSAL || j * kFwdBN <= qw0 + 31); };
+
+        // prologue: K0, V0 and K1 in LDS, scores of block 0 in registers
+        using P0 = std::integral_constant<int, 0>;
+        using P1 = std::integral_constant<int, 1>;
+        load_k(0, P0{});
+        load_v(0, P0{});
+        load_k(1, P1{});
+        wait_vmem();
+        __syncthreads();
+        f32x16 sa[2], sb[2];
+        if (active(0)) {
+            scores(P0{}, sa);
+            mloc = local_max(sa);
         }
-    };
+        // the first step loads K of block 2 into the stage of K0: every wave must be done
+        // reading K0 first (rows past N come back as zeros almost at once)
+        __syncthreads();
 
-    // maximum over this lane's 32 keys of a score block (one half of the row's 64 keys)
-    auto local_max = [&](const f32x16 *sc) __attribute__((always_inline)) {
-        float m = fmaxf(sc[0][0], sc[0][1]);
+        // One pipeline step on key block j: scores of j are in `cur`, scores of j+1 go to `nxt`.
+        auto step = [&](int j, auto par, f32x16 *cur, f32x16 *nxt) __attribute__((always_inline)) {
+            using PN = std::integral_constant<int, 1 - decltype(par)::value>;  // parity of j + 1
+            const bool more = j + 1 < nt;
+            if (active(j)) {
+                const int k0 = j * kFwdBN;
+                if ((CAUSAL && (k0 + kFwdBN - 1 > qw0)) || (k0 + kFwdBN > N)) {
 #pragma unroll
-        for (int r = 2; r < 16; ++r) m = fmaxf(m, sc[0][r]);
+                    for (int kb = 0; kb < 2; ++kb) {
 #pragma unroll
-        for (int r = 0; r < 16; ++r) m = fmaxf(m, sc[1][r]);
-        return m;
-    };
-    float mloc = -__builtin_inff();  // local maximum of the block whose scores are current
-
-    auto active = [&](int j) __attribute__((always_inline)) { return (qw0 < N) && (!CAUSAL || j * kFwdBN <= qw0 + 31); };
-
-    // prologue: K0, V0 and K1 in LDS, scores of block 0 in registers
-    using P0 = std::integral_constant<int, 0>;
-    using P1 = std::integral_constant<int, 1>;
-    load_k(0, P0{});
-    load_v(0, P0{});
-    load_k(1, P1{});
-    wait_vmem();
-    __syncthreads();
-    f32x16 sa[2], sb[2];
-    if (active(0)) {
-        scores(P0{}, sa);
-        mloc = local_max(sa);
-    }
-
-    // One pipeline step on key block j: scores of j are in `cur`, scores of j+1 go to `nxt`.
-    auto step = [&](int j, auto par, f32x16 *cur, f32x16 *nxt) __attribute__((always_inline)) {
-        using PN = std::integral_constant<int, 1 - decltype(par)::value>;  // parity of j + 1
-        const bool more = j + 1 < nt;
-        if (active(j)) {
-            const int k0 = j * kFwdBN;
-            if ((CAUSAL && (k0 + kFwdBN - 1 > qw0)) || (k0 + kFwdBN > N)) {
+                        for (int r = 0; r < 16; ++r) {
+                            const int key = k0 + 32 * kb + 8 * (r >> 2) + 4 * h + (r & 3);
+                            if ((CAUSAL && key > qrow) || key >= N) cur[kb][r] = -__builtin_inff();
+                        }
+                    }
+                    mloc = local_max(cur);
+                }
+                // Rescale check without a cross-lane exchange in the common case: each half of the
+                // wave compares the maximum of its own 32 keys with the offset; only when some lane
+                // outgrows it are the two halves' maxima combined and the offset moved.
+                if (__builtin_amdgcn_ballot_w64(mloc > m_run + grow_thr)) {
+                    const float mrow = fmaxf(mloc, __shfl_xor(mloc, 32));
+                    const bool grow = mrow > m_run + grow_thr;  // identical for both halves of a row
+                    const float m_new = grow ? mrow : m_run;
+                    const float alpha = grow ? fast_exp2((m_run - m_new) * c_log2) : 1.f;
+                    m_run = m_new;
+                    msc = (m_run == -__builtin_inff()) ? 0.f : m_run * c_log2;
+                    l_run *= alpha;
+#pragma unroll
+                    for (int db = 0; db < NDB; ++db) {
+#pragma unroll
+                        for (int r = 0; r < 16; ++r) oacc[db][r] *= alpha;
+                    }
+                }
+                // scores of block j+1 on the matrix cores, probabilities of block j on the vector units
+                __builtin_amdgcn_s_setprio(1);
+                scores(PN{}, nxt);  // past the last block: garbage scores that are never used
+                // K of block j+2 replaces K of block j (last read one step ago), V of block j+1
+                // replaces V of block j-1: both stages are free since the previous barrier.  The
+                // loads are issued every step (past the last block they fetch zeros that are never
+                // read), after the score MFMAs so that their issue overlaps matrix work.
+                load_k(j + 2, par);
+                load_v(j + 1, PN{});
+                bf16x8 pb[kFwdBN / 16];
 #pragma unroll
                 for (int kb = 0; kb < 2; ++kb) {
 #pragma unroll
                     for (int r = 0; r < 16; ++r) {
-                        const int key = k0 + 32 * kb + 8 * (r >> 2) + 4 * h + (r & 3);
-                        if ((CAUSAL && key > qrow) || key >= N) cur[kb][r] = -__builtin_inff();
+                        cur[kb][r] = fast_exp2(fmaf(cur[kb][r], c_log2, -msc));
+                        pb[2 * kb + (r >> 3)][r & 7] = (bf16)cur[kb][r];
                     }
                 }
-                mloc = local_max(cur);
-            }
-            // Rescale check without a cross-lane exchange in the common case: each half of the
-            // wave compares the maximum of its own 32 keys with the offset; only when some lane
-            // outgrows it are the two halves' maxima combined and the offset moved.
-            if (__builtin_amdgcn_ballot_w64(mloc > m_run + grow_thr)) {
-                const float mrow = fmaxf(mloc, __shfl_xor(mloc, 32));
-                const bool grow = mrow > m_run + grow_thr;  // identical for both halves of a row
-                const float m_new = grow ? mrow : m_run;
-                const float alpha = grow ? fast_exp2((m_run - m_new) * c_log2) : 1.f;
-                m_run = m_new;
-                msc = (m_run == -__builtin_inff()) ? 0.f : m_run * c_log2;
-                l_run *= alpha;
+                // O^T += V^T P^T over 4 groups of 16 keys
+                const lds_char *vs = vstage(par);
 #pragma unroll
-                for (int db = 0; db < NDB; ++db) {
+                for (int t = 0; t < kFwdBN / 16; ++t) {
 #pragma unroll
-                    for (int r = 0; r < 16; ++r) oacc[db][r] *= alpha;
+                    for (int db = 0; db < NDB; ++db) {
+                        const bf16x8 a = lds_read_tr_rows_swz<D>(vs, 16 * t, 32 * db, lane);
+                        oacc[db] = mfma(a, pb[t], oacc[db]);
+                    }
                 }
-            }
-            // scores of block j+1 on the matrix cores, probabilities of block j on the vector units
-            __builtin_amdgcn_s_setprio(1);
-            scores(PN{}, nxt);  // past the last block: garbage scores that are never used
-            // K of block j+2 replaces K of block j (last read one step ago), V of block j+1
-            // replaces V of block j-1: both stages are free since the previous barrier.  The
-            // loads are issued every step (past the last block they fetch zeros that are never
-            // read), after the score MFMAs so that their issue overlaps matrix work.
-            load_k(j + 2, par);
-            load_v(j + 1, PN{});
-            bf16x8 pb[kFwdBN / 16];
+                // while the P V products run: this half's exp-sum of block j and its maximum of block j+1
+                float rs = 0.f;
 #pragma unroll
-            for (int kb = 0; kb < 2; ++kb) {
+                for (int kb = 0; kb < 2; ++kb) {
 #pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    cur[kb][r] = fast_exp2(fmaf(cur[kb][r], c_log2, -msc));
-                    pb[2 * kb + (r >> 3)][r & 7] = (bf16)cur[kb][r];
+                    for (int r = 0; r < 16; ++r) rs += cur[kb][r];
                 }
+                l_run += rs;
+                mloc = local_max(nxt);
+                __builtin_amdgcn_s_setprio(0);
+            } else {
+                load_k(j + 2, par);
+                load_v(j + 1, PN{});
             }
-            // O^T += V^T P^T over 4 groups of 16 keys
-            const lds_char *vs = vstage(par);
-#pragma unroll
-            for (int t = 0; t < kFwdBN / 16; ++t) {
-#pragma unroll
-                for (int db = 0; db < NDB; ++db) {
-                    const bf16x8 a = lds_read_tr_rows_swz<D>(vs, 16 * t, 32 * db, lane);
-                    oacc[db] = mfma(a, pb[t], oacc[db]);
-                }
-            }
-            // while the P V products run: this half's exp-sum of block j and its maximum of block j+1
-            float rs = 0.f;
-#pragma unroll
-            for (int kb = 0; kb < 2; ++kb) {
-#pragma unroll
-                for (int r = 0; r < 16; ++r) rs += cur[kb][r];
-            }
-            l_run += rs;
-            mloc = local_max(nxt);
-            __builtin_amdgcn_s_setprio(0);
-        } else {
-            load_k(j + 2, par);
-            load_v(j + 1, PN{});
-        }
-        wait_vmem();
-        __syncthreads();
-    };
+            wait_vmem();
+            __syncthreads();
+        };
 
-    int j = 0;
-    for (; j + 1 < nt; j += 2) {
-        step(j, P0{}, sa, sb);
-        step(j + 1, P1{}, sb, sa);
-    }
-    if (j < nt) step(j, P0{}, sa, sb);
-
-    // epilogue: O = acc / l (bf16, nearest even), lse = m*scale + ln(l)
-    const float l_tot = l_run + __shfl_xor(l_run, 32);
-    if (qrow < N) {
-        const float inv = (l_tot > 0.f) ? 1.f / l_tot : 0.f;
-        bf16 *orow = O + hoff + (size_t)qrow * D;
-#pragma unroll
-        for (int db = 0; db < NDB; ++db) {
-#pragma unroll
-            for (int g = 0; g < 4; ++g) {
-                bf16x4 ov;
-#pragma unroll
-                for (int i = 0; i < 4; ++i) ov[i] = (bf16)(oacc[db][4 * g + i] * inv);
-                *(bf16x4 *)(orow + 32 * db + 8 * g + 4 * h) = ov;
-            }
+        int j = 0;
+        for (; j + 1 < nt; j += 2) {
+            step(j, P0{}, sa, sb);
+            step(j + 1, P1{}, sb, sa);
         }
-        if (h == 0)
-            LSE[(size_t)head * N + qrow] = (l_tot > 0.f) ? fmaf(m_run, scale, __logf(l_tot)) : -__builtin_inff();
+        if (j < nt) step(j, P0{}, sa, sb);
+
+        // epilogue: O = acc / l (bf16, nearest even), lse = m*scale + ln(l)
+        const float l_tot = l_run + __shfl_xor(l_run, 32);
+        if (qrow < N) {
+            const float inv = (l_tot > 0.f) ? 1.f / l_tot : 0.f;
+            bf16 *orow = O + hoff + (size_t)qrow * D;
+#pragma unroll
+            for (int db = 0; db < NDB; ++db) {
+#pragma unroll
+                for (int g = 0; g < 4; ++g) {
+                    bf16x4 ov;
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) ov[i] = (bf16)(oacc[db][4 * g + i] * inv);
+                    *(bf16x4 *)(orow + 32 * db + 8 * g + 4 * h) = ov;
+                }
+            }
+            if (h == 0)
+                LSE[(size_t)head * N + qrow] = (l_tot > 0.f) ? fmaf(m_run, scale, __logf(l_tot)) : -__builtin_inff();
+        }
     }
 }
 
@@ -266,7 +277,7 @@ hipError_t launch_fwd_t(const FwdArgs &a)
     constexpr int kFwdBM = fwd_bm<D>();
     constexpr int kThreads = 64 * fwd_waves<D>();
     const int n_qtiles = (a.N + kFwdBM - 1) / kFwdBM;
-    const long long G = (long long)a.B * a.H * n_qtiles;
+    const long long G = (long long)a.B * a.H * (CAUSAL ? (n_qtiles + 1) / 2 : n_qtiles);
     const float c_log2 = a.scale * kLog2e;
     hipLaunchKernelGGL((fwd_kernel<D, CAUSAL>), dim3((unsigned)G), dim3(kThreads), 0, (hipStream_t)a.stream,
                        (const bf16 *)a.q, (const bf16 *)a.k, (const bf16 *)a.v, (bf16 *)a.o, a.lse, a.N, n_qtiles,
