@@ -197,43 +197,80 @@ __global__ __launch_bounds__(64 * fwd_waves<D>(), 8 / fwd_waves<D>()) void fwd_k
                         for (int r = 0; r < 16; ++r) oacc[db][r] *= alpha;
                     }
                 }
-                // scores of block j+1 on the matrix cores, probabilities of block j on the vector units
+                // One step is NC chunks, each one matrix instruction plus a slice of vector work:
+                //   S1: first half of the score MFMAs of block j+1   | exponentials of keys 0..31 of block j
+                //   V1: first half of the P V MFMAs (keys 0..31)     | exponentials of keys 32..63
+                //   S2: second half of the score MFMAs               | exp-sum of block j
+                //   V2: second half of the P V MFMAs (keys 32..63)   | maximum of block j+1
+                // LDS fragments are fetched 2 chunks ahead; scheduling barriers keep each chunk whole.
                 __builtin_amdgcn_s_setprio(1);
-                scores(PN{}, nxt);  // past the last block: garbage scores that are never used
-                // K of block j+2 replaces K of block j (last read one step ago), V of block j+1
-                // replaces V of block j-1: both stages are free since the previous barrier.  The
-                // loads are issued every step (past the last block they fetch zeros that are never
-                // read), after the score MFMAs so that their issue overlaps matrix work.
-                load_k(j + 2, par);
-                load_v(j + 1, PN{});
-                bf16x8 pb[kFwdBN / 16];
-#pragma unroll
-                for (int kb = 0; kb < 2; ++kb) {
-#pragma unroll
-                    for (int r = 0; r < 16; ++r) {
-                        cur[kb][r] = fast_exp2(fmaf(cur[kb][r], c_log2, -msc));
-                        pb[2 * kb + (r >> 3)][r & 7] = (bf16)cur[kb][r];
-                    }
-                }
-                // O^T += V^T P^T over 4 groups of 16 keys
+                constexpr int NS = 2 * NKS, NPV = (kFwdBN / 16) * NDB, NC = NS + NPV;
+                const lds_char *ks = kstage(PN{});
                 const lds_char *vs = vstage(par);
-#pragma unroll
-                for (int t = 0; t < kFwdBN / 16; ++t) {
-#pragma unroll
-                    for (int db = 0; db < NDB; ++db) {
-                        const bf16x8 a = lds_read_tr_rows_swz<D>(vs, 16 * t, 32 * db, lane);
-                        oacc[db] = mfma(a, pb[t], oacc[db]);
+                auto fetch = [&](int c) __attribute__((always_inline)) {
+                    bf16x8 f;
+                    if (c < NS / 2 || (c >= NS / 2 + NPV / 2 && c < NS + NPV / 2)) {
+                        const int s = c < NS / 2 ? c : c - NPV / 2;
+                        f = lds_read16(ks, swz_off<D>(32 * (s & 1) + c32, 2 * (s >> 1) + h));
+                    } else {
+                        const int p = c < NS / 2 + NPV / 2 ? c - NS / 2 : c - NS;
+                        f = lds_read_tr_rows_swz<D>(vs, 16 * (p / NDB), 32 * (p % NDB), lane);
                     }
-                }
-                // while the P V products run: this half's exp-sum of block j and its maximum of block j+1
-                float rs = 0.f;
+                    return f;
+                };
+                nxt[0] = zero16();
+                nxt[1] = zero16();
+                bf16x8 pb[kFwdBN / 16];
+                float rs = 0.f, mx = -__builtin_inff();
+                bf16x8 fr[2 + 1];
 #pragma unroll
-                for (int kb = 0; kb < 2; ++kb) {
+                for (int c = 0; c < 2; ++c) fr[c] = fetch(c);
 #pragma unroll
-                    for (int r = 0; r < 16; ++r) rs += cur[kb][r];
+                for (int c = 0; c < NC; ++c) {
+                    if (c + 2 < NC) fr[(c + 2) % (2 + 1)] = fetch(c + 2);
+                    const bf16x8 fc = fr[c % (2 + 1)];
+                    if (c < NS / 2 || (c >= NS / 2 + NPV / 2 && c < NS + NPV / 2)) {
+                        const int s = c < NS / 2 ? c : c - NPV / 2;
+                        nxt[s & 1] = mfma(fc, qf[s >> 1], nxt[s & 1]);
+                    } else {
+                        const int p = c < NS / 2 + NPV / 2 ? c - NS / 2 : c - NS;
+                        oacc[p % NDB] = mfma(fc, pb[p / NDB], oacc[p % NDB]);
+                    }
+                    if (c == 1) load_k(j + 2, par);
+                    if (c == 3) load_v(j + 1, PN{});
+                    if (c < NS / 2 + NPV / 2) {
+                        // exponentials: keys 0..31 during S1, 32..63 during V1
+                        const int kb = c < NS / 2 ? 0 : 1;
+                        const int i = c < NS / 2 ? c : c - NS / 2;
+                        constexpr int E = 16 / (NS / 2);
+                        static_assert(NS / 2 == NPV / 2, "phases S1 and V1 must have equal length");
+#pragma unroll
+                        for (int e = 0; e < E; ++e) {
+                            const int r = i * E + e;
+                            cur[kb][r] = fast_exp2(fmaf(cur[kb][r], c_log2, -msc));
+                            pb[2 * kb + (r >> 3)][r & 7] = (bf16)cur[kb][r];
+                        }
+                    } else if (c < NS + NPV / 2) {
+                        const int i = c - NS / 2 - NPV / 2;
+                        constexpr int E = 32 / (NS / 2);
+#pragma unroll
+                        for (int e = 0; e < E; ++e) {
+                            const int r = i * E + e;
+                            rs += cur[r >> 4][r & 15];
+                        }
+                    } else {
+                        const int i = c - NS - NPV / 2;
+                        constexpr int E = 32 / (NPV / 2);
+#pragma unroll
+                        for (int e = 0; e < E; ++e) {
+                            const int r = i * E + e;
+                            mx = fmaxf(mx, nxt[r >> 4][r & 15]);
+                        }
+                    }
+                    __builtin_amdgcn_sched_barrier(0);
                 }
                 l_run += rs;
-                mloc = local_max(nxt);
+                mloc = mx;
                 __builtin_amdgcn_s_setprio(0);
             } else {
                 load_k(j + 2, par);
