@@ -137,47 +137,79 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(
         const int qs = q_start + i * kKvBM;
         // some query of this block sees some key of this wave
         if ((kw0 < N) && (!CAUSAL || qs + kKvBM - 1 >= kw0)) {
-            // S = Q K^T and dP = dO V^T, two 32-query blocks
-            f32x16 s[2] = {zero16(), zero16()};
-            f32x16 dp[2] = {zero16(), zero16()};
-#pragma unroll
-            for (int kst = 0; kst < NKS; ++kst) {
-#pragma unroll
-                for (int qb = 0; qb < 2; ++qb) {
-                    const int off = swz_off<D>(32 * qb + c32, 2 * kst + h);
-                    s[qb] = mfma(lds_read16(q_l, off), kf[kst], s[qb]);
-                    dp[qb] = mfma(lds_read16(g_l, off), vf[kst], dp[qb]);
-                }
-            }
+            // The step is NC chunks of one matrix instruction each, in four phases:
+            //   A: S and dP of queries 0..31      B: S and dP of queries 32..63
+            //   C: dV and dK over queries 0..31   D: dV and dK over queries 32..63
+            // P and dS of queries 0..31 are computed on the vector units during B, those of
+            // queries 32..63 during C.  LDS fragments are fetched PF chunks ahead; scheduling
+            // barriers keep each chunk whole.
             const bool need_mask = CAUSAL && (qs < kw0 + 31);
+            constexpr int PH = 2 * NKS;  // chunks per phase
+            constexpr int NC = 4 * PH;
+            static_assert(4 * NDB == PH, "a dV/dK phase has as many MFMAs as an S/dP phase");
+            constexpr int PF = 3;
+            f32x16 s[2], dp[2];
             bf16x8 pb[4], sb[4];
+            f32x4 l4[2][4], d4[2][4];  // lse and D of the lane's query rows, per half and row group
 #pragma unroll
-            for (int qb = 0; qb < 2; ++qb) {
-#pragma unroll
-                for (int g = 0; g < 4; ++g) {
+            for (int qb = 0; qb < 2; ++qb) s[qb] = dp[qb] = zero16();
+            auto fetch = [&](auto C) __attribute__((always_inline)) {
+                constexpr int c = decltype(C)::value;
+                if constexpr (c < 2 * PH) {
+                    constexpr int qb = c / PH, m = c % PH, kst = m / 2;
+                    return lds_read16((m & 1) ? g_l : q_l, swz_off<D>(32 * qb + c32, 2 * kst + h));
+                } else {
+                    constexpr int qb = (c - 2 * PH) / PH, n = (c - 2 * PH) % PH;
+                    constexpr int t = 2 * qb + n / (2 * NDB), db = (n / 2) % NDB;
+                    // dV takes dO^T, dK takes Q^T
+                    return lds_read_tr_rows_swz<D>((n & 1) ? q_l : g_l, 16 * t, 32 * db, lane);
+                }
+            };
+            bf16x8 fr[PF + 1];
+            static_for<0, PF>([&](auto F) __attribute__((always_inline)) { fr[decltype(F)::value] = fetch(F); });
+            static_for<0, NC>([&](auto C) __attribute__((always_inline)) {
+                constexpr int c = decltype(C)::value;
+                if constexpr (c + PF < NC) fr[(c + PF) % (PF + 1)] = fetch(std::integral_constant<int, c + PF>{});
+                // lse and D of a half's rows, read one phase before they are needed
+                if constexpr (c % PH < 8 && c < 2 * PH) {
+                    constexpr int qb = c / PH, g = (c % PH) / 2;
                     const int qloc = 32 * qb + 8 * g + 4 * h;  // first of 4 consecutive queries
-                    const f32x4 l4 = *(const __attribute__((address_space(3))) f32x4 *)(st_l + 4 * qloc);
-                    const f32x4 d4 = *(const __attribute__((address_space(3))) f32x4 *)(st_l + 4 * (kKvBM + qloc));
+                    if constexpr ((c % PH) % 2 == 0)
+                        l4[qb][g] = *(const __attribute__((address_space(3))) f32x4 *)(st_l + 4 * qloc);
+                    else
+                        d4[qb][g] = *(const __attribute__((address_space(3))) f32x4 *)(st_l + 4 * (kKvBM + qloc));
+                }
+                const bf16x8 fc = fr[c % (PF + 1)];
+                if constexpr (c < 2 * PH) {
+                    constexpr int qb = c / PH, m = c % PH, kst = m / 2;
+                    if constexpr (m & 1)
+                        dp[qb] = mfma(fc, vf[kst], dp[qb]);
+                    else
+                        s[qb] = mfma(fc, kf[kst], s[qb]);
+                } else {
+                    constexpr int qb = (c - 2 * PH) / PH, n = (c - 2 * PH) % PH;
+                    constexpr int t = 2 * qb + n / (2 * NDB), db = (n / 2) % NDB;
+                    if constexpr (n & 1)
+                        dk[db] = mfma(fc, sb[t], dk[db]);
+                    else
+                        dv[db] = mfma(fc, pb[t], dv[db]);
+                }
+                if constexpr (c >= PH && c < 3 * PH) {
+                    // P = exp2(S scale log2e - lse log2e), dS = P (dP - D) for half qb
+                    constexpr int qb = (c - PH) / PH, i = (c - PH) % PH;
+                    constexpr int E = 16 / PH;
 #pragma unroll
-                    for (int u = 0; u < 4; ++u) {
-                        const int r = 4 * g + u;
-                        float p = fast_exp2(fmaf(s[qb][r], c_log2, -l4[u] * kLog2e));
-                        if (need_mask && (qs + qloc + u < key)) p = 0.f;
-                        const float ds = p * (dp[qb][r] - d4[u]);
+                    for (int e = 0; e < E; ++e) {
+                        const int r = i * E + e, g = r >> 2, u = r & 3;
+                        float p = fast_exp2(fmaf(s[qb][r], c_log2, -l4[qb][g][u] * kLog2e));
+                        if (need_mask && (qs + 32 * qb + 8 * g + 4 * h + u < key)) p = 0.f;
+                        const float ds = p * (dp[qb][r] - d4[qb][g][u]);
                         pb[2 * qb + (r >> 3)][r & 7] = (bf16)p;
                         sb[2 * qb + (r >> 3)][r & 7] = (bf16)ds;
                     }
                 }
-            }
-            // dV^T += dO^T P and dK^T += Q^T dS over 4 groups of 16 queries
-#pragma unroll
-            for (int t = 0; t < kKvBM / 16; ++t) {
-#pragma unroll
-                for (int db = 0; db < NDB; ++db) {
-                    dv[db] = mfma(lds_read_tr_rows_swz<D>(g_l, 16 * t, 32 * db, lane), pb[t], dv[db]);
-                    dk[db] = mfma(lds_read_tr_rows_swz<D>(q_l, 16 * t, 32 * db, lane), sb[t], dk[db]);
-                }
-            }
+                __builtin_amdgcn_sched_barrier(0);
+            });
         }
         wait_vmem();
         __syncthreads();

@@ -17,6 +17,7 @@
 #pragma once
 
 #include <hip/hip_runtime.h>
+#include <type_traits>
 #include <stdint.h>
 
 namespace attn {
@@ -91,6 +92,17 @@ __device__ __forceinline__ bf16x8 pack_bf16(const f32x16 &acc, int half)
 #pragma unroll
     for (int e = 0; e < 8; ++e) r[e] = (bf16)acc[8 * half + e];
     return r;
+}
+
+// Calls f(std::integral_constant<int, I>{}) for I = B .. E-1 in order: loop bodies whose
+// register indices must be compile-time constants.
+template <int B, int E, class F>
+__device__ __forceinline__ void static_for(F &&f)
+{
+    if constexpr (B < E) {
+        f(std::integral_constant<int, B>{});
+        static_for<B + 1, E>(f);
+    }
 }
 
 // Workgroups are dispatched round-robin over the 8 XCDs of the chip, each with
@@ -190,24 +202,32 @@ __device__ __forceinline__ void barrier_wait_vmem_upto()
     asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(N) : "memory");
 }
 
-// Load rows [row0, row0 + ROWS) of a row-major [*, D] bf16 matrix into a swizzled
-// LDS tile with direct loads; all NW waves of the workgroup take part.
-// Each wave instruction covers 1 KB = 1024 / (2 D) whole rows.
+// Instruction i of the NI = ROWS / (1024 / (2 D)) / NW direct loads that wave `wave` issues
+// to fill rows [row0, row0 + ROWS) of a row-major [*, D] bf16 matrix into a swizzled LDS
+// tile (each wave instruction covers 1 KB = 1024 / (2 D) whole rows).
 template <int D, int NW, int ROWS = 64>
-__device__ __forceinline__ void load_tile_lds(__amdgpu_buffer_rsrc_t r, lds_char *tile, int row0, int wave, int lane)
+__device__ __forceinline__ void load_tile_lds_part(__amdgpu_buffer_rsrc_t r, lds_char *tile, int row0, int wave,
+                                                   int lane, int i)
 {
     constexpr int RB = 2 * D;            // bytes per row
     constexpr int RPI = 1024 / RB;       // rows per wave instruction
     constexpr int NI = ROWS / RPI / NW;  // instructions per wave for the tile
     static_assert(NI >= 1 && NI * RPI * NW == ROWS, "tile must split evenly over the waves");
     const int lr = lane / (RB / 16), p = lane % (RB / 16);
+    const int r0 = (wave * NI + i) * RPI;  // first tile row of this instruction
+    const int row = r0 + lr;
+    const int chunk = p ^ lds_swz<D>(row);
+    buffer_load_lds16(r, tile + r0 * RB, (uint32_t)((row0 + row) * RB + 16 * chunk));
+}
+
+// Load rows [row0, row0 + ROWS) of a row-major [*, D] bf16 matrix into a swizzled
+// LDS tile with direct loads; all NW waves of the workgroup take part.
+template <int D, int NW, int ROWS = 64>
+__device__ __forceinline__ void load_tile_lds(__amdgpu_buffer_rsrc_t r, lds_char *tile, int row0, int wave, int lane)
+{
+    constexpr int NI = ROWS / (1024 / (2 * D)) / NW;
 #pragma unroll
-    for (int i = 0; i < NI; ++i) {
-        const int r0 = (wave * NI + i) * RPI;  // first tile row of this instruction
-        const int row = r0 + lr;
-        const int chunk = p ^ lds_swz<D>(row);
-        buffer_load_lds16(r, tile + r0 * RB, (uint32_t)((row0 + row) * RB + 16 * chunk));
-    }
+    for (int i = 0; i < NI; ++i) load_tile_lds_part<D, NW, ROWS>(r, tile, row0, wave, lane, i);
 }
 
 // lds_read_tr_rows for a swizzled tile.
