@@ -6,6 +6,10 @@ forward kernel, then the backward preprocess, dK/dV and dQ kernels (the same fou
 launches attn_bwd makes).  The default workload is the forward+backward causal case
 B=2, H=16, N=4096, d=128; ``--workload c2|c3|c4`` times forward-only workloads.
 
+Before the W warmup steps the step runs untimed for --ramp-seconds (1 s by default): an
+idle MI355X needs a fraction of a second under load before its clocks settle, and the timed
+K steps are meant to measure the steady state.
+
 FLOP convention: 4*B*H*N^2*d for the forward, halved when causal; the backward counts
 2.5x the forward.  Printed: one JSON line with the whole-job TFLOP/s, the dominant
 kernel's roofline (achieved algorithmic TFLOP/s against the bf16 dense MFMA peak,
@@ -106,6 +110,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="c5", choices=["c2", "c3", "c4", "c5"])
     ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle work for the CPU baseline")
+    ap.add_argument("--ramp-seconds", type=float, default=1.0,
+                    help="untimed steps for this long before the warmup steps, so that the GPU clocks "
+                         "have left their idle state when timing starts")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     args = ap.parse_args()
 
@@ -164,6 +171,11 @@ def main():
             for i, kname in enumerate(kernels):
                 ev[kname].append((e[i], e[i + 1]))
 
+    t_ramp = time.perf_counter()
+    while time.perf_counter() - t_ramp < args.ramp_seconds:
+        for _ in range(10):
+            step(False)
+        torch.cuda.synchronize()
     for _ in range(args.warmup):
         step(False)
     torch.cuda.synchronize()
