@@ -151,8 +151,17 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(
             f32x16 s[2], dp[2];
             bf16x8 pb[4], sb[4];
             f32x4 l4[2][4], d4[2][4];  // lse and D of the lane's query rows, per half and row group
+            // The causal mask enters through the accumulator: S starts at -inf for queries before
+            // this lane's key, so that P = 0 there, and the chunks carry no per-element mask work.
 #pragma unroll
-            for (int qb = 0; qb < 2; ++qb) s[qb] = dp[qb] = zero16();
+            for (int qb = 0; qb < 2; ++qb) {
+                s[qb] = dp[qb] = zero16();
+                if (need_mask) {
+#pragma unroll
+                    for (int r = 0; r < 16; ++r)
+                        if (qs + 32 * qb + 8 * (r >> 2) + 4 * h + (r & 3) < key) s[qb][r] = -__builtin_inff();
+                }
+            }
             auto fetch = [&](auto C) __attribute__((always_inline)) {
                 constexpr int c = decltype(C)::value;
                 if constexpr (c < 2 * PH) {
@@ -202,7 +211,6 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(
                     for (int e = 0; e < E; ++e) {
                         const int r = i * E + e, g = r >> 2, u = r & 3;
                         float p = fast_exp2(fmaf(s[qb][r], c_log2, -l4[qb][g][u] * kLog2e));
-                        if (need_mask && (qs + 32 * qb + 8 * g + 4 * h + u < key)) p = 0.f;
                         const float ds = p * (dp[qb][r] - d4[qb][g][u]);
                         pb[2 * qb + (r >> 3)][r & 7] = (bf16)p;
                         sb[2 * qb + (r >> 3)][r & 7] = (bf16)ds;
@@ -313,8 +321,21 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(
         const lds_char *vs = vst_l(par);
         const int k0 = j * kQBN;
         if ((qw0 < N) && (!CAUSAL || k0 <= qw0 + 31)) {
+            const bool need_mask = (CAUSAL && (k0 + kQBN - 1 > qw0)) || (k0 + kQBN > N);
+            // Masked scores start at -inf in the accumulator, so that P = 0 there without
+            // per-element mask work after the products.
             f32x16 s[2] = {zero16(), zero16()};
             f32x16 dp[2] = {zero16(), zero16()};
+            if (need_mask) {
+#pragma unroll
+                for (int kb = 0; kb < 2; ++kb) {
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) {
+                        const int kk = k0 + 32 * kb + 8 * (r >> 2) + 4 * h + (r & 3);
+                        if ((CAUSAL && kk > qrow) || kk >= N) s[kb][r] = -__builtin_inff();
+                    }
+                }
+            }
 #pragma unroll
             for (int kst = 0; kst < NKS; ++kst) {
 #pragma unroll
@@ -324,17 +345,12 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(
                     dp[kb] = mfma(lds_read16(vs, off), gf[kst], dp[kb]);
                 }
             }
-            const bool need_mask = (CAUSAL && (k0 + kQBN - 1 > qw0)) || (k0 + kQBN > N);
             bf16x8 sb[4];
 #pragma unroll
             for (int kb = 0; kb < 2; ++kb) {
 #pragma unroll
                 for (int r = 0; r < 16; ++r) {
-                    float p = fast_exp2(fmaf(s[kb][r], c_log2, -lse2));
-                    if (need_mask) {
-                        const int kk = k0 + 32 * kb + 8 * (r >> 2) + 4 * h + (r & 3);
-                        if ((CAUSAL && kk > qrow) || kk >= N) p = 0.f;
-                    }
+                    const float p = fast_exp2(fmaf(s[kb][r], c_log2, -lse2));
                     sb[2 * kb + (r >> 3)][r & 7] = (bf16)(p * (dp[kb][r] - dval));
                 }
             }
