@@ -151,17 +151,8 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(
             f32x16 s[2], dp[2];
             bf16x8 pb[4], sb[4];
             f32x4 l4[2][4], d4[2][4];  // lse and D of the lane's query rows, per half and row group
-            // The causal mask enters through the accumulator: S starts at -inf for queries before
-            // this lane's key, so that P = 0 there, and the chunks carry no per-element mask work.
 #pragma unroll
-            for (int qb = 0; qb < 2; ++qb) {
-                s[qb] = dp[qb] = zero16();
-                if (need_mask) {
-#pragma unroll
-                    for (int r = 0; r < 16; ++r)
-                        if (qs + 32 * qb + 8 * (r >> 2) + 4 * h + (r & 3) < key) s[qb][r] = -__builtin_inff();
-                }
-            }
+            for (int qb = 0; qb < 2; ++qb) s[qb] = dp[qb] = zero16();
             auto fetch = [&](auto C) __attribute__((always_inline)) {
                 constexpr int c = decltype(C)::value;
                 if constexpr (c < 2 * PH) {
@@ -202,6 +193,16 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(
                         dk[db] = mfma(fc, sb[t], dk[db]);
                     else
                         dv[db] = mfma(fc, pb[t], dv[db]);
+                }
+                if constexpr (c == PH || c == 2 * PH) {
+                    // On blocks that cross the diagonal, scores of queries before this lane's key
+                    // become -inf (P = 0) before their half is exponentiated; other blocks skip this.
+                    constexpr int qb = c / PH - 1;
+                    if (need_mask) {
+#pragma unroll
+                        for (int r = 0; r < 16; ++r)
+                            if (qs + 32 * qb + 8 * (r >> 2) + 4 * h + (r & 3) < key) s[qb][r] = -__builtin_inff();
+                    }
                 }
                 if constexpr (c >= PH && c < 3 * PH) {
                     // P = exp2(S scale log2e - lse log2e), dS = P (dP - D) for half qb
@@ -321,11 +322,20 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(
         const lds_char *vs = vst_l(par);
         const int k0 = j * kQBN;
         if ((qw0 < N) && (!CAUSAL || k0 <= qw0 + 31)) {
-            const bool need_mask = (CAUSAL && (k0 + kQBN - 1 > qw0)) || (k0 + kQBN > N);
-            // Masked scores start at -inf in the accumulator, so that P = 0 there without
-            // per-element mask work after the products.
             f32x16 s[2] = {zero16(), zero16()};
             f32x16 dp[2] = {zero16(), zero16()};
+#pragma unroll
+            for (int kst = 0; kst < NKS; ++kst) {
+#pragma unroll
+                for (int kb = 0; kb < 2; ++kb) {
+                    const int off = swz_off<D>(32 * kb + c32, 2 * kst + h);
+                    s[kb] = mfma(lds_read16(ks, off), qf[kst], s[kb]);
+                    dp[kb] = mfma(lds_read16(vs, off), gf[kst], dp[kb]);
+                }
+            }
+            // Only blocks that cross the diagonal or the end of the keys are masked: their masked
+            // scores become -inf (P = 0) in a branch that the other blocks skip.
+            const bool need_mask = (CAUSAL && (k0 + kQBN - 1 > qw0)) || (k0 + kQBN > N);
             if (need_mask) {
 #pragma unroll
                 for (int kb = 0; kb < 2; ++kb) {
@@ -334,15 +344,6 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(
                         const int kk = k0 + 32 * kb + 8 * (r >> 2) + 4 * h + (r & 3);
                         if ((CAUSAL && kk > qrow) || kk >= N) s[kb][r] = -__builtin_inff();
                     }
-                }
-            }
-#pragma unroll
-            for (int kst = 0; kst < NKS; ++kst) {
-#pragma unroll
-                for (int kb = 0; kb < 2; ++kb) {
-                    const int off = swz_off<D>(32 * kb + c32, 2 * kst + h);
-                    s[kb] = mfma(lds_read16(ks, off), qf[kst], s[kb]);
-                    dp[kb] = mfma(lds_read16(vs, off), gf[kst], dp[kb]);
                 }
             }
             bf16x8 sb[4];
