@@ -14,12 +14,19 @@
  *
  * Conventions shared by every entry point
  * ---------------------------------------
- * Tensors are device pointers to dense row-major arrays:
- *   q, k, v, o, dout, dq, dk, dv : bfloat16 (raw 16-bit patterns), [B, H, N, d]
- *   lse, delta                   : float32, [B, H, N]
+ * Tensors are device pointers to dense row-major arrays.  With Nq query rows
+ * and Nk key rows per head (Nq = Nk = N for the entry points that take one N):
+ *   q, o, dout, dq : bfloat16 (raw 16-bit patterns), [B, H, Nq, d]
+ *   k, v, dk, dv   : bfloat16, [B, H, Nk, d]
+ *   lse, delta     : float32, [B, H, Nq]
  * lse is the natural log of sum_j exp(scale * <q_i, k_j>) over the keys j that
  * query i sees; delta is D_i = sum_c dout[i][c] * o[i][c].
- * Causal masking (causal = 1) hides key j from query i when j > i.
+ * Causal masking (causal = 1) hides key j from query i when j > i + (Nk - Nq),
+ * i.e. the mask is aligned to the bottom-right corner of the Nq x Nk score
+ * matrix ("GPU Programming and Kernel Optimization", item 59),
+ * which is the plain j > i when Nq = Nk.  A query that sees no key at all
+ * (causal with Nq > Nk, rows i < Nq - Nk, or Nk = 0) gets o = 0, lse = -inf,
+ * and dq = 0; it adds nothing to dk and dv.
  * scale is the factor applied to the dot products (usually 1/sqrt(d)).
  *
  * Ownership: the caller owns every buffer.  The library neither allocates,
@@ -33,9 +40,10 @@
  * Errors: every entry point checks its arguments on the host before any HIP
  * call.  On a nonzero status nothing was enqueued and no output was touched.
  * The library never aborts or prints.  An empty problem (B, H or N equal to 0)
- * is valid, enqueues nothing and returns ATTN_OK (its pointers may be NULL).
- * Sizes: B, H, N >= 0; d in {64, 128}; B*H*N*d < 2^62; (N + 256)*d*2 < 2^32.
- * Pointers must be 16-byte aligned.
+ * is valid, enqueues nothing and returns ATTN_OK; more generally a pointer to a
+ * buffer of zero bytes may be NULL.
+ * Sizes: B, H, N (Nq, Nk) >= 0; d in {64, 128}; B*H*N*d < 2^62;
+ * (N + 256)*d*2 < 2^32 for N = Nq and N = Nk.  Pointers must be 16-byte aligned.
  */
 #ifndef ATTN_H_
 #define ATTN_H_
@@ -61,6 +69,12 @@ enum attn_status {
 int attn_fwd(const void *q, const void *k, const void *v, void *o, float *lse,
              int B, int H, int N, int d, int causal, float scale, void *stream);
 
+/* Forward pass with Nq query rows and Nk key/value rows per head (see the
+ * conventions above for the causal alignment and for rows that see no key).
+ * attn_fwd(..., N, ...) is attn_fwd_qk(..., N, N, ...). */
+int attn_fwd_qk(const void *q, const void *k, const void *v, void *o, float *lse,
+                int B, int H, int Nq, int Nk, int d, int causal, float scale, void *stream);
+
 /* Backward pass: enqueues attn_bwd_preprocess, attn_bwd_dkdv and attn_bwd_dq
  * in that order on `stream`.  Reads q, k, v, o, dout and the lse written by
  * attn_fwd with the same q, k, v, causal and scale; writes dq, dk, dv
@@ -69,6 +83,16 @@ int attn_fwd(const void *q, const void *k, const void *v, void *o, float *lse,
 int attn_bwd(const void *q, const void *k, const void *v, const void *o, const void *dout,
              const float *lse, void *dq, void *dk, void *dv, float *delta,
              int B, int H, int N, int d, int causal, float scale, void *stream);
+
+/* Backward pass with Nq query rows and Nk key/value rows per head; the same
+ * three kernels as attn_bwd.  delta is [B, H, Nq].  With Nq = 0 it writes
+ * dk = dv = 0; with Nk = 0 it writes dq = 0. */
+int attn_bwd_qk(const void *q, const void *k, const void *v, const void *o, const void *dout,
+                const float *lse, void *dq, void *dk, void *dv, float *delta,
+                int B, int H, int Nq, int Nk, int d, int causal, float scale, void *stream);
+
+/* The three backward steps below take one length N (Nq = Nk = N); they exist
+ * so that each kernel can be enqueued and timed on its own. */
 
 /* Backward step 1: delta[i] = sum_c dout[i][c] * o[i][c] (fp32 products and
  * sums of the bf16 inputs).  Memory-bound; one kernel launch. */

@@ -33,8 +33,8 @@ def declared_functions():
 
 def test_header_declares_the_expected_entry_points():
     assert declared_functions() == sorted([
-        "attn_fwd", "attn_bwd", "attn_bwd_preprocess", "attn_bwd_dkdv", "attn_bwd_dq",
-        "attn_status_string", "attn_last_hip_error"])
+        "attn_fwd", "attn_fwd_qk", "attn_bwd", "attn_bwd_qk", "attn_bwd_preprocess", "attn_bwd_dkdv",
+        "attn_bwd_dq", "attn_status_string", "attn_last_hip_error"])
 
 
 def test_library_exports_every_declared_symbol(lib):
@@ -125,3 +125,48 @@ def test_python_binding_raises_with_status(lib):
     with pytest.raises(A.AttnError) as e:
         A.attn_fwd(P[0], P[1], P[2], P[3], P[4], 1, 1, 64, 64, False, -1.0)
     assert e.value.status == A.ATTN_ERR_BAD_SCALE
+
+
+def fwd_qk(lib, q=P[0], k=P[1], v=P[2], o=P[3], lse=P[4], B=1, H=1, Nq=64, Nk=128, d=64, causal=1, scale=0.125):
+    return lib.attn_fwd_qk(q, k, v, o, lse, B, H, Nq, Nk, d, causal, scale, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(Nq=-1), A.ATTN_ERR_BAD_SHAPE),
+    (dict(Nk=-1), A.ATTN_ERR_BAD_SHAPE),
+    (dict(Nk=1 << 24, d=128), A.ATTN_ERR_BAD_SHAPE),    # (Nk+256)*d*2 > 2^32
+    (dict(Nq=1 << 24, d=128), A.ATTN_ERR_BAD_SHAPE),
+    (dict(d=96), A.ATTN_ERR_UNSUPPORTED_D),
+    (dict(causal=3), A.ATTN_ERR_BAD_ARG),
+    (dict(k=None), A.ATTN_ERR_NULLPTR),                 # Nk > 0: k is required
+    (dict(o=None), A.ATTN_ERR_NULLPTR),
+    (dict(v=P[2] + 4), A.ATTN_ERR_MISALIGNED),
+    (dict(o=P[1] + 16384 - 16), A.ATTN_ERR_ALIAS),      # inside k, whose size is Nk*d*2 = 16384
+    (dict(lse=P[0] + 8192 - 16), A.ATTN_ERR_ALIAS),     # inside q, whose size is Nq*d*2 = 8192
+])
+def test_forward_qk_argument_checks(lib, kw, status):
+    assert fwd_qk(lib, **kw) == status
+
+
+def test_qk_empty_problems(lib):
+    # no query rows: the forward has nothing to write and accepts NULL everywhere
+    assert fwd_qk(lib, q=None, k=None, v=None, o=None, lse=None, Nq=0, Nk=64) == A.ATTN_OK
+    # the backward with Nq = Nk = 0 is empty
+    assert lib.attn_bwd_qk(*([None] * 10), 1, 1, 0, 0, 64, 1, 0.125, None) == A.ATTN_OK
+
+
+def test_backward_qk_argument_checks(lib):
+    args = [P[0], P[1], P[2], P[3], P[4], P[5], P[6], P[7], P[8], P[9]]
+
+    def bwd(Nq=64, Nk=96, **kw):
+        a = list(args)
+        for i, val in kw.get("ptr", {}).items():
+            a[i] = val
+        return lib.attn_bwd_qk(*a, 1, 2, Nq, Nk, 64, 1, 0.125, None)
+
+    assert bwd(Nq=-2) == A.ATTN_ERR_BAD_SHAPE
+    assert bwd(ptr={9: None}) == A.ATTN_ERR_NULLPTR     # delta
+    assert bwd(ptr={1: None}) == A.ATTN_ERR_NULLPTR     # k with Nk > 0
+    assert bwd(ptr={7: P[1]}) == A.ATTN_ERR_ALIAS       # dk == k
+    assert bwd(ptr={6: P[3] + 16384 - 16}) == A.ATTN_ERR_ALIAS  # dq inside o (Nq rows: 2*64*64*2 B)
+    assert bwd(ptr={8: P[2] + 24576 - 16}) == A.ATTN_ERR_ALIAS  # dv inside v (Nk rows: 2*96*64*2 B)

@@ -1,15 +1,17 @@
 """Python binding of libattn.so, the gfx950 attention library (C ABI in include/attn.h).
 
-The functions named like the C entry points (``attn_fwd``, ``attn_bwd``,
-``attn_bwd_preprocess``, ``attn_bwd_dkdv``, ``attn_bwd_dq``,
-``attn_status_string``) only marshal arguments: tensors become device
+The functions named like the C entry points (``attn_fwd``, ``attn_fwd_qk``,
+``attn_bwd``, ``attn_bwd_qk``, ``attn_bwd_preprocess``, ``attn_bwd_dkdv``,
+``attn_bwd_dq``, ``attn_status_string``) only marshal arguments: tensors become device
 pointers, ``stream=None`` becomes the current PyTorch stream of the tensors'
 device, and a nonzero status becomes :class:`AttnError`.  Every step of the
 computation runs in the library's HIP kernels; there is no fallback.  If the
 library has not been built the first call raises.
 
 ``fwd`` and ``bwd`` are conveniences that check dtypes, devices and
-contiguity and allocate the outputs with ``torch.empty``.
+contiguity and allocate the outputs with ``torch.empty``; q may have a
+different number of rows than k and v (causal masks then align to the
+bottom-right corner).
 """
 from __future__ import annotations
 
@@ -41,6 +43,8 @@ _F = ctypes.c_float
 
 _SIGNATURES = {
     "attn_fwd": [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _F, _P],
+    "attn_fwd_qk": [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _F, _P],
+    "attn_bwd_qk": [_P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _F, _P],
     "attn_bwd": [_P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _F, _P],
     "attn_bwd_preprocess": [_P, _P, _P, _I, _I, _I, _I, _P],
     "attn_bwd_dkdv": [_P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _F, _P],
@@ -110,6 +114,16 @@ def attn_fwd(q, k, v, o, lse, B, H, N, d, causal, scale, stream=None) -> None:
           _stream(stream, q, o))
 
 
+def attn_fwd_qk(q, k, v, o, lse, B, H, Nq, Nk, d, causal, scale, stream=None) -> None:
+    _call("attn_fwd_qk", _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, H, Nq, Nk, d, int(causal), float(scale),
+          _stream(stream, q, o))
+
+
+def attn_bwd_qk(q, k, v, o, dout, lse, dq, dk, dv, delta, B, H, Nq, Nk, d, causal, scale, stream=None) -> None:
+    _call("attn_bwd_qk", _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(dout), _ptr(lse), _ptr(dq), _ptr(dk), _ptr(dv),
+          _ptr(delta), B, H, Nq, Nk, d, int(causal), float(scale), _stream(stream, q, dq, dk))
+
+
 def attn_bwd(q, k, v, o, dout, lse, dq, dk, dv, delta, B, H, N, d, causal, scale, stream=None) -> None:
     _call("attn_bwd", _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(dout), _ptr(lse), _ptr(dq), _ptr(dk), _ptr(dv),
           _ptr(delta), B, H, N, d, int(causal), float(scale), _stream(stream, q, dq))
@@ -129,19 +143,23 @@ def attn_bwd_dq(q, k, v, dout, lse, delta, dq, B, H, N, d, causal, scale, stream
           int(causal), float(scale), _stream(stream, q, dq))
 
 
-def _check_inputs(*ts):
-    ref = ts[0]
-    if ref.dim() != 4:
+def _check_inputs(q, k, v, *q_like):
+    """q (and o, dO) are [B, H, Nq, d]; k and v are [B, H, Nk, d]."""
+    if q.dim() != 4 or k.dim() != 4 or v.dim() != 4:
         raise ValueError("expected [B, H, N, d] tensors")
-    for t in ts:
+    for t in (q, k, v, *q_like):
         if t.dtype != torch.bfloat16:
             raise TypeError("tensors must be bfloat16")
-        if not t.is_cuda or t.device != ref.device:
+        if not t.is_cuda or t.device != q.device:
             raise ValueError("tensors must be on the same GPU")
         if not t.is_contiguous():
             raise ValueError("tensors must be contiguous")
-        if t.shape != ref.shape:
-            raise ValueError("q, k, v (and o, dO) must have the same shape [B, H, N, d]")
+    B, H, _, d = q.shape
+    if k.shape[:2] != (B, H) or k.shape[3] != d or v.shape != k.shape:
+        raise ValueError("k and v must be [B, H, Nk, d] with the B, H and d of q")
+    for t in q_like:
+        if t.shape != q.shape:
+            raise ValueError("o and dO must have the shape of q")
 
 
 def default_scale(d: int) -> float:
@@ -150,24 +168,32 @@ def default_scale(d: int) -> float:
 
 
 def fwd(q, k, v, causal: bool = False, scale: float | None = None, stream=None):
-    """Forward pass; returns (o bf16 [B,H,N,d], lse fp32 [B,H,N])."""
+    """Forward pass; returns (o bf16 [B,H,Nq,d], lse fp32 [B,H,Nq])."""
     _check_inputs(q, k, v)
-    B, H, N, d = q.shape
+    B, H, Nq, d = q.shape
+    Nk = k.shape[2]
     scale = default_scale(d) if scale is None else scale
     o = torch.empty_like(q)
-    lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
-    attn_fwd(q, k, v, o, lse, B, H, N, d, causal, scale, stream)
+    lse = torch.empty((B, H, Nq), dtype=torch.float32, device=q.device)
+    if Nq == Nk:
+        attn_fwd(q, k, v, o, lse, B, H, Nq, d, causal, scale, stream)
+    else:
+        attn_fwd_qk(q, k, v, o, lse, B, H, Nq, Nk, d, causal, scale, stream)
     return o, lse
 
 
 def bwd(q, k, v, o, dout, lse, causal: bool = False, scale: float | None = None, stream=None):
-    """Backward pass; returns (dq, dk, dv) bf16 [B,H,N,d]."""
+    """Backward pass; returns (dq [B,H,Nq,d], dk, dv [B,H,Nk,d]), bf16."""
     _check_inputs(q, k, v, o, dout)
-    B, H, N, d = q.shape
-    if lse.dtype != torch.float32 or tuple(lse.shape) != (B, H, N) or not lse.is_contiguous():
-        raise ValueError("lse must be a contiguous float32 [B, H, N] tensor")
+    B, H, Nq, d = q.shape
+    Nk = k.shape[2]
+    if lse.dtype != torch.float32 or tuple(lse.shape) != (B, H, Nq) or not lse.is_contiguous():
+        raise ValueError("lse must be a contiguous float32 [B, H, Nq] tensor")
     scale = default_scale(d) if scale is None else scale
     dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
-    delta = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
-    attn_bwd(q, k, v, o, dout, lse, dq, dk, dv, delta, B, H, N, d, causal, scale, stream)
+    delta = torch.empty((B, H, Nq), dtype=torch.float32, device=q.device)
+    if Nq == Nk:
+        attn_bwd(q, k, v, o, dout, lse, dq, dk, dv, delta, B, H, Nq, d, causal, scale, stream)
+    else:
+        attn_bwd_qk(q, k, v, o, dout, lse, dq, dk, dv, delta, B, H, Nq, Nk, d, causal, scale, stream)
     return dq, dk, dv

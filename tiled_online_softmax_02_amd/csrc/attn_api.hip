@@ -17,24 +17,26 @@ struct Range {
 
 Range range_of(const void *p, long long bytes) { return Range{(uintptr_t)p, (uintptr_t)p + (uintptr_t)bytes}; }
 
-bool overlap(Range a, Range b) { return a.lo < b.hi && b.lo < a.hi; }
+bool overlap(Range a, Range b) { return a.lo < b.hi && b.lo < a.hi; }  // empty ranges never overlap
 
 bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
 
-// Shape rules shared by every entry point.  Sets *empty when there is nothing to compute.
-int check_shape(int B, int H, int N, int d, bool *empty)
+// Shape rules shared by every entry point (Nq query rows and Nk key rows per head).
+// Sets *empty when there is nothing to compute.
+int check_shape(int B, int H, int Nq, int Nk, int d, bool *empty)
 {
-    if (B < 0 || H < 0 || N < 0) return ATTN_ERR_BAD_SHAPE;
+    if (B < 0 || H < 0 || Nq < 0 || Nk < 0) return ATTN_ERR_BAD_SHAPE;
     if (d != 64 && d != 128) return ATTN_ERR_UNSUPPORTED_D;
-    const long long rows = (long long)B * H * N;
-    if (rows > ((1LL << 62) / d)) return ATTN_ERR_BAD_SHAPE;
+    const long long rows_q = (long long)B * H * Nq, rows_k = (long long)B * H * Nk;
+    if (rows_q > ((1LL << 62) / d) || rows_k > ((1LL << 62) / d)) return ATTN_ERR_BAD_SHAPE;
     // per-head byte offsets, including the padding rows of the last tile, are 32-bit
-    if ((long long)(N + 256) * d * 2 > 0xFFFFFFFFLL) return ATTN_ERR_BAD_SHAPE;
-    // work-group counts of the launches must fit a 32-bit grid
-    if (attn::fwd_grid_size(B, H, N) >= (1LL << 31) || attn::bwd_dkdv_grid_size(B, H, N) >= (1LL << 31) ||
-        attn::bwd_dq_grid_size(B, H, N) >= (1LL << 31) || rows / 16 >= (1LL << 31))
+    if ((long long)(Nq + 256) * d * 2 > 0xFFFFFFFFLL || (long long)(Nk + 256) * d * 2 > 0xFFFFFFFFLL)
         return ATTN_ERR_BAD_SHAPE;
-    *empty = (rows == 0);
+    // work-group counts of the launches must fit a 32-bit grid
+    if (attn::fwd_grid_size(B, H, Nq) >= (1LL << 31) || attn::bwd_dkdv_grid_size(B, H, Nk) >= (1LL << 31) ||
+        attn::bwd_dq_grid_size(B, H, Nq) >= (1LL << 31) || rows_q / 16 >= (1LL << 31))
+        return ATTN_ERR_BAD_SHAPE;
+    *empty = (rows_q == 0 && rows_k == 0);
     return ATTN_OK;
 }
 
@@ -42,11 +44,11 @@ int check_scale(float scale) { return (isfinite(scale) && scale > 0.f) ? ATTN_OK
 
 int check_causal(int causal) { return (causal == 0 || causal == 1) ? ATTN_OK : ATTN_ERR_BAD_ARG; }
 
-// Pointers: non-null and 16-byte aligned.
-int check_ptrs(const void *const *ptrs, int n)
+// Pointers: non-null and 16-byte aligned, except that a buffer of zero bytes may be NULL.
+int check_ptrs(const void *const *ptrs, const long long *bytes, int n)
 {
     for (int i = 0; i < n; ++i)
-        if (!ptrs[i]) return ATTN_ERR_NULLPTR;
+        if (!ptrs[i] && bytes[i] > 0) return ATTN_ERR_NULLPTR;
     for (int i = 0; i < n; ++i)
         if (!aligned16(ptrs[i])) return ATTN_ERR_MISALIGNED;
     return ATTN_OK;
@@ -77,12 +79,54 @@ int hip_status(hipError_t e)
         if (rc_ != ATTN_OK) return rc_; \
     } while (0)
 
-int validate_common(int B, int H, int N, int d, int causal, float scale, bool *empty)
+int validate_common(int B, int H, int Nq, int Nk, int d, int causal, float scale, bool *empty)
 {
-    RETURN_IF(check_shape(B, H, N, d, empty));
+    RETURN_IF(check_shape(B, H, Nq, Nk, d, empty));
     RETURN_IF(check_causal(causal));
     RETURN_IF(check_scale(scale));
     return ATTN_OK;
+}
+
+// Byte sizes of one [B, H, rows, d] bf16 tensor and of one [B, H, rows] fp32 vector.
+long long tensor_bytes(int B, int H, int rows, int d) { return (long long)B * H * rows * d * 2; }
+long long vector_bytes(int B, int H, int rows) { return (long long)B * H * rows * 4; }
+
+int fwd_impl(const void *q, const void *k, const void *v, void *o, float *lse, int B, int H, int Nq, int Nk, int d,
+             int causal, float scale, void *stream)
+{
+    bool empty = false;
+    RETURN_IF(validate_common(B, H, Nq, Nk, d, causal, scale, &empty));
+    const long long qb = tensor_bytes(B, H, Nq, d), kb = tensor_bytes(B, H, Nk, d), lb = vector_bytes(B, H, Nq);
+    if (qb == 0) return ATTN_OK;  // no query rows: nothing to write
+    const void *ptrs[] = {q, k, v, o, lse};
+    const long long sizes[] = {qb, kb, kb, qb, lb};
+    RETURN_IF(check_ptrs(ptrs, sizes, 5));
+    const Range in[] = {range_of(q, qb), range_of(k, kb), range_of(v, kb)};
+    const Range out[] = {range_of(o, qb), range_of(lse, lb)};
+    RETURN_IF(check_alias(in, 3, out, 2));
+    attn::FwdArgs a{q, k, v, o, lse, B, H, Nq, Nk, d, causal, scale, stream};
+    return hip_status(attn::launch_fwd(a));
+}
+
+int bwd_impl(const void *q, const void *k, const void *v, const void *o, const void *dout, const float *lse, void *dq,
+             void *dk, void *dv, float *delta, int B, int H, int Nq, int Nk, int d, int causal, float scale,
+             void *stream)
+{
+    bool empty = false;
+    RETURN_IF(validate_common(B, H, Nq, Nk, d, causal, scale, &empty));
+    if (empty) return ATTN_OK;
+    const long long qb = tensor_bytes(B, H, Nq, d), kb = tensor_bytes(B, H, Nk, d), lb = vector_bytes(B, H, Nq);
+    const void *ptrs[] = {q, k, v, o, dout, lse, dq, dk, dv, delta};
+    const long long sizes[] = {qb, kb, kb, qb, qb, lb, qb, kb, kb, lb};
+    RETURN_IF(check_ptrs(ptrs, sizes, 10));
+    const Range in[] = {range_of(q, qb), range_of(k, kb),    range_of(v, kb),
+                        range_of(o, qb), range_of(dout, qb), range_of(lse, lb)};
+    const Range out[] = {range_of(dq, qb), range_of(dk, kb), range_of(dv, kb), range_of(delta, lb)};
+    RETURN_IF(check_alias(in, 6, out, 4));
+    attn::BwdArgs a{q, k, v, o, dout, lse, dq, dk, dv, delta, B, H, Nq, Nk, d, causal, scale, stream};
+    RETURN_IF(hip_status(attn::launch_bwd_preprocess(a)));
+    RETURN_IF(hip_status(attn::launch_bwd_dkdv(a)));
+    return hip_status(attn::launch_bwd_dq(a));
 }
 
 }  // namespace
@@ -92,27 +136,24 @@ extern "C" {
 int attn_fwd(const void *q, const void *k, const void *v, void *o, float *lse, int B, int H, int N, int d, int causal,
              float scale, void *stream)
 {
-    bool empty = false;
-    RETURN_IF(validate_common(B, H, N, d, causal, scale, &empty));
-    if (empty) return ATTN_OK;
-    const void *ptrs[] = {q, k, v, o, lse};
-    RETURN_IF(check_ptrs(ptrs, 5));
-    const long long tb = (long long)B * H * N * d * 2, lb = (long long)B * H * N * 4;
-    const Range in[] = {range_of(q, tb), range_of(k, tb), range_of(v, tb)};
-    const Range out[] = {range_of(o, tb), range_of(lse, lb)};
-    RETURN_IF(check_alias(in, 3, out, 2));
-    attn::FwdArgs a{q, k, v, o, lse, B, H, N, d, causal, scale, stream};
-    return hip_status(attn::launch_fwd(a));
+    return fwd_impl(q, k, v, o, lse, B, H, N, N, d, causal, scale, stream);
+}
+
+int attn_fwd_qk(const void *q, const void *k, const void *v, void *o, float *lse, int B, int H, int Nq, int Nk, int d,
+                int causal, float scale, void *stream)
+{
+    return fwd_impl(q, k, v, o, lse, B, H, Nq, Nk, d, causal, scale, stream);
 }
 
 int attn_bwd_preprocess(const void *o, const void *dout, float *delta, int B, int H, int N, int d, void *stream)
 {
     bool empty = false;
-    RETURN_IF(check_shape(B, H, N, d, &empty));
+    RETURN_IF(check_shape(B, H, N, N, d, &empty));
     if (empty) return ATTN_OK;
+    const long long tb = tensor_bytes(B, H, N, d), lb = vector_bytes(B, H, N);
     const void *ptrs[] = {o, dout, delta};
-    RETURN_IF(check_ptrs(ptrs, 3));
-    const long long tb = (long long)B * H * N * d * 2, lb = (long long)B * H * N * 4;
+    const long long sizes[] = {tb, tb, lb};
+    RETURN_IF(check_ptrs(ptrs, sizes, 3));
     const Range in[] = {range_of(o, tb), range_of(dout, tb)};
     const Range out[] = {range_of(delta, lb)};
     RETURN_IF(check_alias(in, 2, out, 1));
@@ -122,7 +163,7 @@ int attn_bwd_preprocess(const void *o, const void *dout, float *delta, int B, in
     a.delta = delta;
     a.B = B;
     a.H = H;
-    a.N = N;
+    a.Nq = a.Nk = N;
     a.d = d;
     a.stream = stream;
     return hip_status(attn::launch_bwd_preprocess(a));
@@ -132,11 +173,12 @@ int attn_bwd_dkdv(const void *q, const void *k, const void *v, const void *dout,
                   void *dk, void *dv, int B, int H, int N, int d, int causal, float scale, void *stream)
 {
     bool empty = false;
-    RETURN_IF(validate_common(B, H, N, d, causal, scale, &empty));
+    RETURN_IF(validate_common(B, H, N, N, d, causal, scale, &empty));
     if (empty) return ATTN_OK;
+    const long long tb = tensor_bytes(B, H, N, d), lb = vector_bytes(B, H, N);
     const void *ptrs[] = {q, k, v, dout, lse, delta, dk, dv};
-    RETURN_IF(check_ptrs(ptrs, 8));
-    const long long tb = (long long)B * H * N * d * 2, lb = (long long)B * H * N * 4;
+    const long long sizes[] = {tb, tb, tb, tb, lb, lb, tb, tb};
+    RETURN_IF(check_ptrs(ptrs, sizes, 8));
     const Range in[] = {range_of(q, tb),    range_of(k, tb),     range_of(v, tb),
                         range_of(dout, tb), range_of(lse, lb),   range_of(delta, lb)};
     const Range out[] = {range_of(dk, tb), range_of(dv, tb)};
@@ -152,7 +194,7 @@ int attn_bwd_dkdv(const void *q, const void *k, const void *v, const void *dout,
     a.dv = dv;
     a.B = B;
     a.H = H;
-    a.N = N;
+    a.Nq = a.Nk = N;
     a.d = d;
     a.causal = causal;
     a.scale = scale;
@@ -164,11 +206,12 @@ int attn_bwd_dq(const void *q, const void *k, const void *v, const void *dout, c
                 void *dq, int B, int H, int N, int d, int causal, float scale, void *stream)
 {
     bool empty = false;
-    RETURN_IF(validate_common(B, H, N, d, causal, scale, &empty));
+    RETURN_IF(validate_common(B, H, N, N, d, causal, scale, &empty));
     if (empty) return ATTN_OK;
+    const long long tb = tensor_bytes(B, H, N, d), lb = vector_bytes(B, H, N);
     const void *ptrs[] = {q, k, v, dout, lse, delta, dq};
-    RETURN_IF(check_ptrs(ptrs, 7));
-    const long long tb = (long long)B * H * N * d * 2, lb = (long long)B * H * N * 4;
+    const long long sizes[] = {tb, tb, tb, tb, lb, lb, tb};
+    RETURN_IF(check_ptrs(ptrs, sizes, 7));
     const Range in[] = {range_of(q, tb),    range_of(k, tb),   range_of(v, tb),
                         range_of(dout, tb), range_of(lse, lb), range_of(delta, lb)};
     const Range out[] = {range_of(dq, tb)};
@@ -183,7 +226,7 @@ int attn_bwd_dq(const void *q, const void *k, const void *v, const void *dout, c
     a.dq = dq;
     a.B = B;
     a.H = H;
-    a.N = N;
+    a.Nq = a.Nk = N;
     a.d = d;
     a.causal = causal;
     a.scale = scale;
@@ -194,20 +237,14 @@ int attn_bwd_dq(const void *q, const void *k, const void *v, const void *dout, c
 int attn_bwd(const void *q, const void *k, const void *v, const void *o, const void *dout, const float *lse, void *dq,
              void *dk, void *dv, float *delta, int B, int H, int N, int d, int causal, float scale, void *stream)
 {
-    bool empty = false;
-    RETURN_IF(validate_common(B, H, N, d, causal, scale, &empty));
-    if (empty) return ATTN_OK;
-    const void *ptrs[] = {q, k, v, o, dout, lse, dq, dk, dv, delta};
-    RETURN_IF(check_ptrs(ptrs, 10));
-    const long long tb = (long long)B * H * N * d * 2, lb = (long long)B * H * N * 4;
-    const Range in[] = {range_of(q, tb), range_of(k, tb),    range_of(v, tb),
-                        range_of(o, tb), range_of(dout, tb), range_of(lse, lb)};
-    const Range out[] = {range_of(dq, tb), range_of(dk, tb), range_of(dv, tb), range_of(delta, lb)};
-    RETURN_IF(check_alias(in, 6, out, 4));
-    attn::BwdArgs a{q, k, v, o, dout, lse, dq, dk, dv, delta, B, H, N, d, causal, scale, stream};
-    RETURN_IF(hip_status(attn::launch_bwd_preprocess(a)));
-    RETURN_IF(hip_status(attn::launch_bwd_dkdv(a)));
-    return hip_status(attn::launch_bwd_dq(a));
+    return bwd_impl(q, k, v, o, dout, lse, dq, dk, dv, delta, B, H, N, N, d, causal, scale, stream);
+}
+
+int attn_bwd_qk(const void *q, const void *k, const void *v, const void *o, const void *dout, const float *lse,
+                void *dq, void *dk, void *dv, float *delta, int B, int H, int Nq, int Nk, int d, int causal,
+                float scale, void *stream)
+{
+    return bwd_impl(q, k, v, o, dout, lse, dq, dk, dv, delta, B, H, Nq, Nk, d, causal, scale, stream);
 }
 
 const char *attn_status_string(int status)
@@ -215,7 +252,7 @@ const char *attn_status_string(int status)
     switch (status) {
     case ATTN_OK: return "ok";
     case ATTN_ERR_NULLPTR: return "a required pointer is NULL";
-    case ATTN_ERR_BAD_SHAPE: return "bad shape: B, H, N must be >= 0 and within the size limits";
+    case ATTN_ERR_BAD_SHAPE: return "bad shape: B, H and the lengths must be >= 0 and within the size limits";
     case ATTN_ERR_UNSUPPORTED_D: return "unsupported head dimension: d must be 64 or 128";
     case ATTN_ERR_MISALIGNED: return "a pointer is not 16-byte aligned";
     case ATTN_ERR_BAD_SCALE: return "scale must be finite and > 0";

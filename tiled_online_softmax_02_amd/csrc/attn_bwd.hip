@@ -61,7 +61,7 @@ constexpr int kKvBM = 64;   // queries per streamed block
 template <int D, bool CAUSAL>
 __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(
     const bf16 *__restrict__ Q, const bf16 *__restrict__ K, const bf16 *__restrict__ V, const bf16 *__restrict__ dO,
-    const float *__restrict__ LSE, const float *__restrict__ Dl, bf16 *__restrict__ dK, bf16 *__restrict__ dV, int N,
+    const float *__restrict__ LSE, const float *__restrict__ Dl, bf16 *__restrict__ dK, bf16 *__restrict__ dV, int Nq, int Nk,
     int n_ktiles, float scale, float c_log2)
 {
     constexpr int NKS = D / 16;
@@ -78,20 +78,22 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(
     const int tid = threadIdx.x;
     const int lane = tid & 63, h = lane >> 5, c32 = lane & 31;
     const int w = wave_uniform(tid >> 6);
-    const size_t hoff = (size_t)head * (size_t)N * D;
-    const uint32_t head_bytes = (uint32_t)N * D * 2;
-    const __amdgpu_buffer_rsrc_t rq = make_rsrc(Q + hoff, head_bytes);
-    const __amdgpu_buffer_rsrc_t rk = make_rsrc(K + hoff, head_bytes);
-    const __amdgpu_buffer_rsrc_t rv = make_rsrc(V + hoff, head_bytes);
-    const __amdgpu_buffer_rsrc_t rg = make_rsrc(dO + hoff, head_bytes);
-    const __amdgpu_buffer_rsrc_t rl = make_rsrc(LSE + (size_t)head * N, (uint32_t)N * 4);
-    const __amdgpu_buffer_rsrc_t rd = make_rsrc(Dl + (size_t)head * N, (uint32_t)N * 4);
+    const size_t hoff_q = (size_t)head * (size_t)Nq * D;  // Q and dO of this head
+    const size_t hoff = (size_t)head * (size_t)Nk * D;    // K, V, dK and dV of this head
+    const __amdgpu_buffer_rsrc_t rq = make_rsrc(Q + hoff_q, (uint32_t)Nq * D * 2);
+    const __amdgpu_buffer_rsrc_t rk = make_rsrc(K + hoff, (uint32_t)Nk * D * 2);
+    const __amdgpu_buffer_rsrc_t rv = make_rsrc(V + hoff, (uint32_t)Nk * D * 2);
+    const __amdgpu_buffer_rsrc_t rg = make_rsrc(dO + hoff_q, (uint32_t)Nq * D * 2);
+    const __amdgpu_buffer_rsrc_t rl = make_rsrc(LSE + (size_t)head * Nq, (uint32_t)Nq * 4);
+    const __amdgpu_buffer_rsrc_t rd = make_rsrc(Dl + (size_t)head * Nq, (uint32_t)Nq * 4);
+    // Causal mask with bottom-right alignment: query i sees keys j <= i + off.
+    const int off = Nk - Nq;
 
     const int k0 = ktile * kKvBN;
     const int kw0 = k0 + 32 * w;  // wave-uniform
     const int key = kw0 + c32;
 
-    // K and V fragments (B operands of S = Q K^T and dP = dO V^T): lane holds row `key` (zeros past N).
+    // K and V fragments (B operands of S = Q K^T and dP = dO V^T): lane holds row `key` (zeros past Nk).
     bf16x8 kf[NKS], vf[NKS];
 #pragma unroll
     for (int ks = 0; ks < NKS; ++ks) {
@@ -106,13 +108,14 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(
         dv[i] = zero16();
     }
 
-    const int q_start = CAUSAL ? (k0 / kKvBM) * kKvBM : 0;
-    const int nsteps = (N > q_start) ? (N - q_start + kKvBM - 1) / kKvBM : 0;
+    // causal: the first query that sees key k0 is k0 - off
+    const int q_start = CAUSAL ? (max(0, k0 - off) / kKvBM) * kKvBM : 0;
+    const int nsteps = (Nq > q_start) ? (Nq - q_start + kKvBM - 1) / kKvBM : 0;
 
     auto qst = [&](auto par) __attribute__((always_inline)) { return (lds_char *)(decltype(par)::value ? q1_raw : q0_raw); };
     auto gst = [&](auto par) __attribute__((always_inline)) { return (lds_char *)(decltype(par)::value ? g1_raw : g0_raw); };
     auto sst = [&](auto par) __attribute__((always_inline)) { return (lds_char *)(decltype(par)::value ? s1_raw : s0_raw); };
-    // Q, dO, lse and D of query block i.  Rows past N read as zeros: such a row has Q = dO = 0,
+    // Q, dO, lse and D of query block i.  Rows past Nq read as zeros: such a row has Q = dO = 0,
     // so its P = exp2(0 - 0) = 1 meets zero operands in every product and contributes nothing.
     auto load_blk = [&](int i, auto par) __attribute__((always_inline)) {
         const int qs = q_start + i * kKvBM;
@@ -136,14 +139,14 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(
         const lds_char *st_l = sst(par);
         const int qs = q_start + i * kKvBM;
         // some query of this block sees some key of this wave
-        if ((kw0 < N) && (!CAUSAL || qs + kKvBM - 1 >= kw0)) {
+        if ((kw0 < Nk) && (!CAUSAL || qs + kKvBM - 1 + off >= kw0)) {
             // The step is NC chunks of one matrix instruction each, in four phases:
             //   A: S and dP of queries 0..31      B: S and dP of queries 32..63
             //   C: dV and dK over queries 0..31   D: dV and dK over queries 32..63
             // P and dS of queries 0..31 are computed on the vector units during B, those of
             // queries 32..63 during C.  LDS fragments are fetched PF chunks ahead; scheduling
             // barriers keep each chunk whole.
-            const bool need_mask = CAUSAL && (qs < kw0 + 31);
+            const bool need_mask = CAUSAL && (qs + off < kw0 + 31);
             constexpr int PH = 2 * NKS;  // chunks per phase
             constexpr int NC = 4 * PH;
             static_assert(4 * NDB == PH, "a dV/dK phase has as many MFMAs as an S/dP phase");
@@ -201,7 +204,14 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(
                     if (need_mask) {
 #pragma unroll
                         for (int r = 0; r < 16; ++r)
-                            if (qs + 32 * qb + 8 * (r >> 2) + 4 * h + (r & 3) < key) s[qb][r] = -__builtin_inff();
+                            if (qs + 32 * qb + 8 * (r >> 2) + 4 * h + (r & 3) + off < key) s[qb][r] = -__builtin_inff();
+                        // a query that sees no key at all has lse = -inf: a finite stand-in keeps
+                        // its P at exp2(-inf) = 0 instead of exp2(-inf + inf)
+#pragma unroll
+                        for (int g = 0; g < 4; ++g) {
+#pragma unroll
+                            for (int u = 0; u < 4; ++u) l4[qb][g][u] = fmaxf(l4[qb][g][u], -1e30f);
+                        }
                     }
                 }
                 if constexpr (c >= PH && c < 3 * PH) {
@@ -231,7 +241,7 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(
     }
     if (i < nsteps) step(i, P0{});
 
-    if (key < N) {
+    if (key < Nk) {
         bf16 *dkrow = dK + hoff + (size_t)key * D;
         bf16 *dvrow = dV + hoff + (size_t)key * D;
 #pragma unroll
@@ -259,7 +269,7 @@ constexpr int kQBN = 64;   // keys per streamed block
 template <int D, bool CAUSAL>
 __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(
     const bf16 *__restrict__ Q, const bf16 *__restrict__ K, const bf16 *__restrict__ V, const bf16 *__restrict__ dO,
-    const float *__restrict__ LSE, const float *__restrict__ Dl, bf16 *__restrict__ dQ, int N, int n_qtiles,
+    const float *__restrict__ LSE, const float *__restrict__ Dl, bf16 *__restrict__ dQ, int Nq, int Nk, int n_qtiles,
     float scale, float c_log2)
 {
     constexpr int NKS = D / 16;
@@ -274,17 +284,19 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(
     const int tid = threadIdx.x;
     const int lane = tid & 63, h = lane >> 5, c32 = lane & 31;
     const int w = wave_uniform(tid >> 6);
-    const size_t hoff = (size_t)head * (size_t)N * D;
-    const uint32_t head_bytes = (uint32_t)N * D * 2;
-    const __amdgpu_buffer_rsrc_t rq = make_rsrc(Q + hoff, head_bytes);
-    const __amdgpu_buffer_rsrc_t rk = make_rsrc(K + hoff, head_bytes);
-    const __amdgpu_buffer_rsrc_t rv = make_rsrc(V + hoff, head_bytes);
-    const __amdgpu_buffer_rsrc_t rg = make_rsrc(dO + hoff, head_bytes);
+    const size_t hoff = (size_t)head * (size_t)Nq * D;    // Q, dO and dQ of this head
+    const size_t hoff_k = (size_t)head * (size_t)Nk * D;  // K and V of this head
+    const __amdgpu_buffer_rsrc_t rq = make_rsrc(Q + hoff, (uint32_t)Nq * D * 2);
+    const __amdgpu_buffer_rsrc_t rk = make_rsrc(K + hoff_k, (uint32_t)Nk * D * 2);
+    const __amdgpu_buffer_rsrc_t rv = make_rsrc(V + hoff_k, (uint32_t)Nk * D * 2);
+    const __amdgpu_buffer_rsrc_t rg = make_rsrc(dO + hoff, (uint32_t)Nq * D * 2);
+    // Causal mask with bottom-right alignment: query i sees keys j <= i + off.
+    const int off = Nk - Nq;
 
     const int q0 = qtile * kQBM;
     const int qw0 = q0 + 32 * w;  // wave-uniform
     const int qrow = qw0 + c32;
-    const bool row_ok = qrow < N;
+    const bool row_ok = qrow < Nq;
 
     bf16x8 qf[NKS], gf[NKS];
 #pragma unroll
@@ -292,14 +304,16 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(
         qf[ks] = __builtin_bit_cast(bf16x8, buffer_load16(rq, (uint32_t)(qrow * D + 16 * ks + 8 * h) * 2u));
         gf[ks] = __builtin_bit_cast(bf16x8, buffer_load16(rg, (uint32_t)(qrow * D + 16 * ks + 8 * h) * 2u));
     }
-    const float lse2 = row_ok ? LSE[(size_t)head * N + qrow] * kLog2e : __builtin_inff();
-    const float dval = row_ok ? Dl[(size_t)head * N + qrow] : 0.f;
+    // a row past Nq, or a query that sees no key (lse = -inf), gets lse2 = +inf and so P = 0
+    const float lse_row = row_ok ? LSE[(size_t)head * Nq + qrow] : -__builtin_inff();
+    const float lse2 = (lse_row == -__builtin_inff()) ? __builtin_inff() : lse_row * kLog2e;
+    const float dval = row_ok ? Dl[(size_t)head * Nq + qrow] : 0.f;
 
     f32x16 dq[NDB];
 #pragma unroll
     for (int i = 0; i < NDB; ++i) dq[i] = zero16();
 
-    const int kv_end = CAUSAL ? min(N, q0 + kQBM) : N;
+    const int kv_end = CAUSAL ? min(Nk, max(0, q0 + kQBM + off)) : Nk;
     const int nt = (kv_end + kQBN - 1) / kQBN;
 
     auto kst_l = [&](auto par) __attribute__((always_inline)) { return (lds_char *)(decltype(par)::value ? k1_raw : k0_raw); };
@@ -321,7 +335,7 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(
         const lds_char *ks = kst_l(par);
         const lds_char *vs = vst_l(par);
         const int k0 = j * kQBN;
-        if ((qw0 < N) && (!CAUSAL || k0 <= qw0 + 31)) {
+        if ((qw0 < Nq) && (!CAUSAL || k0 <= qw0 + 31 + off)) {
             f32x16 s[2] = {zero16(), zero16()};
             f32x16 dp[2] = {zero16(), zero16()};
 #pragma unroll
@@ -335,14 +349,14 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(
             }
             // Only blocks that cross the diagonal or the end of the keys are masked: their masked
             // scores become -inf (P = 0) in a branch that the other blocks skip.
-            const bool need_mask = (CAUSAL && (k0 + kQBN - 1 > qw0)) || (k0 + kQBN > N);
+            const bool need_mask = (CAUSAL && (k0 + kQBN - 1 > qw0 + off)) || (k0 + kQBN > Nk);
             if (need_mask) {
 #pragma unroll
                 for (int kb = 0; kb < 2; ++kb) {
 #pragma unroll
                     for (int r = 0; r < 16; ++r) {
                         const int kk = k0 + 32 * kb + 8 * (r >> 2) + 4 * h + (r & 3);
-                        if ((CAUSAL && kk > qrow) || kk >= N) s[kb][r] = -__builtin_inff();
+                        if ((CAUSAL && kk > qrow + off) || kk >= Nk) s[kb][r] = -__builtin_inff();
                     }
                 }
             }
@@ -393,8 +407,9 @@ template <int D>
 hipError_t launch_pre_t(const BwdArgs &a)
 {
     constexpr int RPB = kThreads / (D / 8);
-    const long long rows = (long long)a.B * a.H * a.N;
+    const long long rows = (long long)a.B * a.H * a.Nq;
     const long long G = (rows + RPB - 1) / RPB;
+    if (G == 0) return hipSuccess;
     hipLaunchKernelGGL((bwd_preprocess_kernel<D>), dim3((unsigned)G), dim3(kThreads), 0, (hipStream_t)a.stream,
                        (const bf16 *)a.o, (const bf16 *)a.dout, a.delta, rows);
     return hipGetLastError();
@@ -403,22 +418,24 @@ hipError_t launch_pre_t(const BwdArgs &a)
 template <int D, bool CAUSAL>
 hipError_t launch_dkdv_t(const BwdArgs &a)
 {
-    const int n_ktiles = (a.N + kKvBN - 1) / kKvBN;
+    const int n_ktiles = (a.Nk + kKvBN - 1) / kKvBN;
     const long long G = (long long)a.B * a.H * n_ktiles;
+    if (G == 0) return hipSuccess;
     hipLaunchKernelGGL((bwd_dkdv_kernel<D, CAUSAL>), dim3((unsigned)G), dim3(kThreads), 0, (hipStream_t)a.stream,
                        (const bf16 *)a.q, (const bf16 *)a.k, (const bf16 *)a.v, (const bf16 *)a.dout, a.lse,
-                       (const float *)a.delta, (bf16 *)a.dk, (bf16 *)a.dv, a.N, n_ktiles, a.scale, a.scale * kLog2e);
+                       (const float *)a.delta, (bf16 *)a.dk, (bf16 *)a.dv, a.Nq, a.Nk, n_ktiles, a.scale, a.scale * kLog2e);
     return hipGetLastError();
 }
 
 template <int D, bool CAUSAL>
 hipError_t launch_dq_t(const BwdArgs &a)
 {
-    const int n_qtiles = (a.N + kQBM - 1) / kQBM;
+    const int n_qtiles = (a.Nq + kQBM - 1) / kQBM;
     const long long G = (long long)a.B * a.H * n_qtiles;
+    if (G == 0) return hipSuccess;
     hipLaunchKernelGGL((bwd_dq_kernel<D, CAUSAL>), dim3((unsigned)G), dim3(kThreads), 0, (hipStream_t)a.stream,
                        (const bf16 *)a.q, (const bf16 *)a.k, (const bf16 *)a.v, (const bf16 *)a.dout, a.lse,
-                       (const float *)a.delta, (bf16 *)a.dq, a.N, n_qtiles, a.scale, a.scale * kLog2e);
+                       (const float *)a.delta, (bf16 *)a.dq, a.Nq, a.Nk, n_qtiles, a.scale, a.scale * kLog2e);
     return hipGetLastError();
 }
 
@@ -441,7 +458,7 @@ hipError_t launch_bwd_dq(const BwdArgs &a)
     return a.causal ? launch_dq_t<128, true>(a) : launch_dq_t<128, false>(a);
 }
 
-long long bwd_dkdv_grid_size(int B, int H, int N) { return (long long)B * H * ((N + kKvBN - 1) / kKvBN); }
-long long bwd_dq_grid_size(int B, int H, int N) { return (long long)B * H * ((N + kQBM - 1) / kQBM); }
+long long bwd_dkdv_grid_size(int B, int H, int Nk) { return (long long)B * H * ((Nk + kKvBN - 1) / kKvBN); }
+long long bwd_dq_grid_size(int B, int H, int Nq) { return (long long)B * H * ((Nq + kQBM - 1) / kQBM); }
 
 }  // namespace attn

@@ -13,7 +13,7 @@
 //     rows; each wave owns 32 rows and holds their Q fragments in VGPRs for the
 //     whole loop;
 //   * key/value blocks of 64 rows are double-buffered through swizzled LDS tiles
-//     filled by direct global->LDS buffer loads (rows past N read as zeros, no
+//     filled by direct global->LDS buffer loads (rows past the end read as zeros, no
 //     staging registers, no LDS store instructions); K runs one block ahead of V, so
 //     the scores of block j+1 are computed on the matrix cores while the
 //     vector units exponentiate block j;
@@ -59,7 +59,7 @@ struct FwdSmem {
 template <int D, bool CAUSAL>
 __global__ __launch_bounds__(64 * fwd_waves<D>(), 8 / fwd_waves<D>()) void fwd_kernel(const bf16 *__restrict__ Q, const bf16 *__restrict__ K,
                                                           const bf16 *__restrict__ V, bf16 *__restrict__ O,
-                                                          float *__restrict__ LSE, int N, int n_qtiles, float scale,
+                                                          float *__restrict__ LSE, int Nq, int Nk, int n_qtiles, float scale,
                                                           float c_log2)
 {
     using L = FwdSmem<D>;
@@ -81,11 +81,13 @@ __global__ __launch_bounds__(64 * fwd_waves<D>(), 8 / fwd_waves<D>()) void fwd_k
     const int tid = threadIdx.x;
     const int lane = tid & 63, h = lane >> 5, c32 = lane & 31;
     const int w = wave_uniform(tid >> 6);
-    const size_t hoff = (size_t)head * (size_t)N * D;
-    const uint32_t head_bytes = (uint32_t)N * D * 2;
-    const __amdgpu_buffer_rsrc_t rq = make_rsrc(Q + hoff, head_bytes);
-    const __amdgpu_buffer_rsrc_t rk = make_rsrc(K + hoff, head_bytes);
-    const __amdgpu_buffer_rsrc_t rv = make_rsrc(V + hoff, head_bytes);
+    const size_t hoff = (size_t)head * (size_t)Nq * D;    // Q and O of this head
+    const size_t hoff_k = (size_t)head * (size_t)Nk * D;  // K and V of this head
+    const __amdgpu_buffer_rsrc_t rq = make_rsrc(Q + hoff, (uint32_t)Nq * D * 2);
+    const __amdgpu_buffer_rsrc_t rk = make_rsrc(K + hoff_k, (uint32_t)Nk * D * 2);
+    const __amdgpu_buffer_rsrc_t rv = make_rsrc(V + hoff_k, (uint32_t)Nk * D * 2);
+    // Causal mask with bottom-right alignment: query i sees keys j <= i + off.
+    const int off = Nk - Nq;
 
     for (int pass = 0; pass < (CAUSAL ? 2 : 1); ++pass) {
         const int qtile = pass == 0 ? (CAUSAL ? n_qtiles - 1 - pos : pos) : pos;
@@ -94,7 +96,7 @@ __global__ __launch_bounds__(64 * fwd_waves<D>(), 8 / fwd_waves<D>()) void fwd_k
         const int qw0 = q0 + 32 * w;  // wave-uniform
         const int qrow = qw0 + c32;
 
-        // Q fragments: B operand of S^T = K Q^T, lane holds Q[qrow][16ks + 8h .. +7] (zeros past N).
+        // Q fragments: B operand of S^T = K Q^T, lane holds Q[qrow][16ks + 8h .. +7] (zeros past Nq).
         bf16x8 qf[NKS];
 #pragma unroll
         for (int ks = 0; ks < NKS; ++ks)
@@ -108,7 +110,8 @@ __global__ __launch_bounds__(64 * fwd_waves<D>(), 8 / fwd_waves<D>()) void fwd_k
         float l_run = 0.f;
         const float grow_thr = kRescaleLog2 / c_log2;
 
-        const int kv_end = CAUSAL ? min(N, q0 + kFwdBM) : N;
+        // keys that some row of this block sees (none for rows that see no key at all)
+        const int kv_end = CAUSAL ? min(Nk, max(0, q0 + kFwdBM + off)) : Nk;
         const int nt = (kv_end + kFwdBN - 1) / kFwdBN;
 
         // Key / value blocks go straight from global memory into swizzled LDS tiles.
@@ -144,7 +147,7 @@ __global__ __launch_bounds__(64 * fwd_waves<D>(), 8 / fwd_waves<D>()) void fwd_k
         };
         float mloc = -__builtin_inff();  // local maximum of the block whose scores are current
 
-        auto active = [&](int j) __attribute__((always_inline)) { return (qw0 < N) && (!CAUSAL || j * kFwdBN <= qw0 + 31); };
+        auto active = [&](int j) __attribute__((always_inline)) { return (qw0 < Nq) && (!CAUSAL || j * kFwdBN <= qw0 + 31 + off); };
 
         // prologue: K0, V0 and K1 in LDS, scores of block 0 in registers
         using P0 = std::integral_constant<int, 0>;
@@ -160,7 +163,7 @@ __global__ __launch_bounds__(64 * fwd_waves<D>(), 8 / fwd_waves<D>()) void fwd_k
             mloc = local_max(sa);
         }
         // the first step loads K of block 2 into the stage of K0: every wave must be done
-        // reading K0 first (rows past N come back as zeros almost at once)
+        // reading K0 first (rows past the end come back as zeros almost at once)
         __syncthreads();
 
         // One pipeline step on key block j: scores of j are in `cur`, scores of j+1 go to `nxt`.
@@ -169,13 +172,13 @@ __global__ __launch_bounds__(64 * fwd_waves<D>(), 8 / fwd_waves<D>()) void fwd_k
             const bool more = j + 1 < nt;
             if (active(j)) {
                 const int k0 = j * kFwdBN;
-                if ((CAUSAL && (k0 + kFwdBN - 1 > qw0)) || (k0 + kFwdBN > N)) {
+                if ((CAUSAL && (k0 + kFwdBN - 1 > qw0 + off)) || (k0 + kFwdBN > Nk)) {
 #pragma unroll
                     for (int kb = 0; kb < 2; ++kb) {
 #pragma unroll
                         for (int r = 0; r < 16; ++r) {
                             const int key = k0 + 32 * kb + 8 * (r >> 2) + 4 * h + (r & 3);
-                            if ((CAUSAL && key > qrow) || key >= N) cur[kb][r] = -__builtin_inff();
+                            if ((CAUSAL && key > qrow + off) || key >= Nk) cur[kb][r] = -__builtin_inff();
                         }
                     }
                     mloc = local_max(cur);
@@ -289,7 +292,7 @@ __global__ __launch_bounds__(64 * fwd_waves<D>(), 8 / fwd_waves<D>()) void fwd_k
 
         // epilogue: O = acc / l (bf16, nearest even), lse = m*scale + ln(l)
         const float l_tot = l_run + __shfl_xor(l_run, 32);
-        if (qrow < N) {
+        if (qrow < Nq) {
             const float inv = (l_tot > 0.f) ? 1.f / l_tot : 0.f;
             bf16 *orow = O + hoff + (size_t)qrow * D;
 #pragma unroll
@@ -303,7 +306,7 @@ __global__ __launch_bounds__(64 * fwd_waves<D>(), 8 / fwd_waves<D>()) void fwd_k
                 }
             }
             if (h == 0)
-                LSE[(size_t)head * N + qrow] = (l_tot > 0.f) ? fmaf(m_run, scale, __logf(l_tot)) : -__builtin_inff();
+                LSE[(size_t)head * Nq + qrow] = (l_tot > 0.f) ? fmaf(m_run, scale, __logf(l_tot)) : -__builtin_inff();
         }
     }
 }
@@ -313,12 +316,13 @@ hipError_t launch_fwd_t(const FwdArgs &a)
 {
     constexpr int kFwdBM = fwd_bm<D>();
     constexpr int kThreads = 64 * fwd_waves<D>();
-    const int n_qtiles = (a.N + kFwdBM - 1) / kFwdBM;
+    const int n_qtiles = (a.Nq + kFwdBM - 1) / kFwdBM;
     const long long G = (long long)a.B * a.H * (CAUSAL ? (n_qtiles + 1) / 2 : n_qtiles);
+    if (G == 0) return hipSuccess;
     const float c_log2 = a.scale * kLog2e;
     hipLaunchKernelGGL((fwd_kernel<D, CAUSAL>), dim3((unsigned)G), dim3(kThreads), 0, (hipStream_t)a.stream,
-                       (const bf16 *)a.q, (const bf16 *)a.k, (const bf16 *)a.v, (bf16 *)a.o, a.lse, a.N, n_qtiles,
-                       a.scale, c_log2);
+                       (const bf16 *)a.q, (const bf16 *)a.k, (const bf16 *)a.v, (bf16 *)a.o, a.lse, a.Nq, a.Nk,
+                       n_qtiles, a.scale, c_log2);
     return hipGetLastError();
 }
 
@@ -330,6 +334,6 @@ hipError_t launch_fwd(const FwdArgs &a)
     return a.causal ? launch_fwd_t<128, true>(a) : launch_fwd_t<128, false>(a);
 }
 
-long long fwd_grid_size(int B, int H, int N) { return (long long)B * H * ((N + fwd_bm<64>() - 1) / fwd_bm<64>()); }
+long long fwd_grid_size(int B, int H, int Nq) { return (long long)B * H * ((Nq + fwd_bm<64>() - 1) / fwd_bm<64>()); }
 
 }  // namespace attn

@@ -10,7 +10,7 @@ struct FwdArgs {
     const void *q, *k, *v;
     void *o;
     float *lse;
-    int B, H, N, d, causal;
+    int B, H, Nq, Nk, d, causal;  // Nq query rows, Nk key rows per head
     float scale;
     void *stream;
 };
@@ -20,7 +20,7 @@ struct BwdArgs {
     const float *lse;
     void *dq, *dk, *dv;
     float *delta;
-    int B, H, N, d, causal;
+    int B, H, Nq, Nk, d, causal;  // Nq query rows, Nk key rows per head
     float scale;
     void *stream;
 };
@@ -30,8 +30,8 @@ hipError_t launch_bwd_preprocess(const BwdArgs &a);
 hipError_t launch_bwd_dkdv(const BwdArgs &a);
 hipError_t launch_bwd_dq(const BwdArgs &a);
 
-long long fwd_grid_size(int B, int H, int N);
-long long bwd_dkdv_grid_size(int B, int H, int N);
-long long bwd_dq_grid_size(int B, int H, int N);
+long long fwd_grid_size(int B, int H, int Nq);
+long long bwd_dkdv_grid_size(int B, int H, int Nk);
+long long bwd_dq_grid_size(int B, int H, int Nq);
 
 }  // namespace attn
