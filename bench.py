@@ -42,6 +42,21 @@ def step_flop(B, H, N, d, causal, backward) -> float:
     return fwd_flop(B, H, N, d, causal) * (3.5 if backward else 1.0)
 
 
+def visible_pairs(Nq, Nk, causal) -> int:
+    """(query, key) pairs that the mask keeps; causal masks align to the bottom-right corner."""
+    if not causal:
+        return Nq * Nk
+    off = Nk - Nq
+    return sum(min(Nk, max(0, i + off + 1)) for i in range(Nq))
+
+
+def workload_flop(w) -> float:
+    """Forward FLOP of a workload: the convention for equal lengths, 4*d per visible pair otherwise."""
+    if w.nq == w.nk:
+        return step_flop(w.B, w.H, w.N, w.d, w.causal, w.backward)
+    return 4.0 * w.B * w.H * w.d * visible_pairs(w.nq, w.nk, w.causal)
+
+
 def kernel_algorithmic_flop(kernel, B, H, N, d, causal) -> float:
     """Algorithmic FLOP one launch performs, in units of one N x N x d product (the
     forward is two of them): fwd 2 (QK^T, PV); dkdv 4 (the recomputed S, dP, dV, dK);
@@ -52,7 +67,11 @@ def kernel_algorithmic_flop(kernel, B, H, N, d, causal) -> float:
 
 def stored_traffic(kernel: str, workload: str):
     """HBM bytes per launch from committed rocprofv3 counter summaries, or None when the
-    kernel sources changed since the counters were taken."""
+    kernel sources changed since the counters were taken.  The split-key forward is two
+    launches (pieces, then their merge): its traffic is their sum."""
+    if kernel == "fwd_splitkv":
+        parts = [stored_traffic("fwd", workload), stored_traffic("combine", workload)]
+        return None if None in parts else sum(parts)
     path = os.path.join(ROOT, "profiles", "hbm_traffic_%s_%s.txt" % (kernel, workload))
     if not os.path.exists(path):
         return None
@@ -73,7 +92,7 @@ def cpu_baseline(w, budget_s: float):
     from tiled_online_softmax_02_amd.inputs import make_inputs
 
     threads = max(1, min(len(os.sched_getaffinity(0)), 16))
-    inp = make_inputs(1, 1, w.N, w.d, seed=w.seed + 1000, backward=w.backward,
+    inp = make_inputs(1, 1, w.N, w.d, nk=w.nk, seed=w.seed + 1000, backward=w.backward,
                       boost_every=w.boost_every, boost=w.boost)
     f64 = {k: t.to(dtype=__import__("torch").float64).numpy() for k, t in inp.items()}
     # one head first, to size the sample
@@ -83,7 +102,7 @@ def cpu_baseline(w, budget_s: float):
         oracle.attn_bwd_matmul(f64["q"], f64["k"], f64["v"], f64["do"], w.causal, w.scale)
     one = time.perf_counter() - t0
     heads = int(max(1, min(w.B * w.H, threads, budget_s // max(one, 1e-3))))
-    inp = make_inputs(1, heads, w.N, w.d, seed=w.seed + 1001, backward=w.backward,
+    inp = make_inputs(1, heads, w.N, w.d, nk=w.nk, seed=w.seed + 1001, backward=w.backward,
                       boost_every=w.boost_every, boost=w.boost)
     f64 = {k: t.to(dtype=__import__("torch").float64).numpy() for k, t in inp.items()}
     t0 = time.perf_counter()
@@ -91,7 +110,7 @@ def cpu_baseline(w, budget_s: float):
     if w.backward:
         oracle.attn_bwd_matmul(f64["q"], f64["k"], f64["v"], f64["do"], w.causal, w.scale)
     dt = time.perf_counter() - t0
-    flop = step_flop(1, heads, w.N, w.d, w.causal, w.backward)
+    flop = workload_flop(w) / (w.B * w.H) * heads
     return {
         "value": flop / dt / 1e12,
         "unit": "TFLOP/s",
@@ -99,7 +118,7 @@ def cpu_baseline(w, budget_s: float):
         "kind": "oracle",
         "sample": "%d of %d heads (%s per head), same FLOP convention, %.1f s wall; forward by the plain "
                   "fp64 C definition (one thread per head), backward by fp64 numpy matmuls"
-                  % (heads, w.B * w.H, "N=%d d=%d" % (w.N, w.d), dt),
+                  % (heads, w.B * w.H, "Nq=%d Nk=%d d=%d" % (w.nq, w.nk, w.d), dt),
     }
 
 
@@ -108,7 +127,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--workload", default="c5", choices=["c2", "c3", "c4", "c5"])
+    ap.add_argument("--workload", default="c5", choices=["c2", "c3", "c4", "c5", "dec"])
     ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle work for the CPU baseline")
     ap.add_argument("--ramp-seconds", type=float, default=1.0,
                     help="untimed steps for this long before the warmup steps, so that the GPU clocks "
@@ -131,6 +150,12 @@ def main():
     inp = workload_inputs(w)
     q, k, v = (inp[n].to(dev) for n in ("q", "k", "v"))
     B, H, N, d = q.shape
+    Nk = k.shape[2]
+    split = w.name == "dec"  # decoding: the split-key forward (partial pieces, then their merge)
+    if split:
+        ns = A.attn_fwd_splitkv_default_splits(B, H, N, Nk, d)
+        ws_bytes = A.attn_fwd_splitkv_workspace_size(B, H, N, d, ns)
+        ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
     causal, scale = w.causal, w.scale
     o = torch.empty_like(q)
     lse = torch.empty((B, H, N), dtype=torch.float32, device=dev)
@@ -147,14 +172,17 @@ def main():
     torch.cuda.synchronize()
     del cal_src, cal_dst
 
-    kernels = ["fwd"] + (["preprocess", "dkdv", "dq"] if w.backward else [])
+    kernels = (["fwd_splitkv"] if split else ["fwd"]) + (["preprocess", "dkdv", "dq"] if w.backward else [])
     ev = {kname: [] for kname in kernels}
 
     def step(record):
         e = [torch.cuda.Event(enable_timing=True) for _ in range(len(kernels) + 1)] if record else None
         if record:
             e[0].record()
-        A.attn_fwd(q, k, v, o, lse, B, H, N, d, causal, scale)
+        if split:
+            A.attn_fwd_splitkv(q, k, v, o, lse, B, H, N, Nk, d, causal, scale, ns, ws, ws_bytes)
+        else:
+            A.attn_fwd(q, k, v, o, lse, B, H, N, d, causal, scale)
         if record:
             e[1].record()
         if w.backward:
@@ -187,12 +215,27 @@ def main():
     ms_per_step = dt * 1e3 / args.steps
 
     kernel_ms = {kname: sum(a.elapsed_time(b) for a, b in pairs) / len(pairs) for kname, pairs in ev.items()}
-    flop = step_flop(B, H, N, d, causal, w.backward)
+    flop = workload_flop(w)
     value = flop / (ms_per_step * 1e-3) / 1e12
     dom = max(kernels, key=lambda kname: kernel_ms[kname])
-    achieved = kernel_algorithmic_flop(dom, B, H, N, d, causal) / (kernel_ms[dom] * 1e-3) / 1e12
-
-    fwd_t = fwd_flop(B, H, N, d, causal) / (kernel_ms["fwd"] * 1e-3) / 1e12
+    if split:
+        # decoding reads every key and value once and does 4*d FLOP per key: the HBM roof bounds it
+        fwd_t = flop / (kernel_ms["fwd_splitkv"] * 1e-3) / 1e12
+        alg_bytes = 2 * (2 * B * H * N * d) + 2 * (2 * B * H * Nk * d) + 4 * B * H * N
+        achieved = alg_bytes / (kernel_ms[dom] * 1e-3) / 1e9
+        roof = {"kernel": dom, "bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": stored_traffic(dom, w.name),
+                "algorithmic_bytes": alg_bytes, "num_splits": ns}
+    else:
+        fwd_t = fwd_flop(B, H, N, d, causal) / (kernel_ms["fwd"] * 1e-3) / 1e12
+        achieved = kernel_algorithmic_flop(dom, B, H, N, d, causal) / (kernel_ms[dom] * 1e-3) / 1e12
+        roof = {"kernel": dom, "bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
+                "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+                "traffic": stored_traffic(dom, w.name)}
+    config = {"workload": w.describe(), "B": B, "H": H, "N": N, "d": d, "causal": causal,
+              "scale": scale, "global_batch": B, "seq_len": N, "parallelism": "single GPU"}
+    if Nk != N:
+        config["Nk"] = Nk
     out = {
         "metric": METRIC,
         "value": round(value, 2),
@@ -206,14 +249,11 @@ def main():
         "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic",
-        "config": {"workload": w.describe(), "B": B, "H": H, "N": N, "d": d, "causal": causal,
-                   "scale": scale, "global_batch": B, "seq_len": N, "parallelism": "single GPU"},
+        "config": config,
         "pct_of_peak": round(100.0 * value / PEAK_BF16_TFLOPS, 2),
         "fwd_tflops": round(fwd_t, 2),
         "kernel_ms": {kname: round(t, 4) for kname, t in kernel_ms.items()},
-        "roofline": {"kernel": dom, "bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
-                     "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
-                     "traffic": stored_traffic(dom, w.name)},
+        "roofline": roof,
     }
     if w.backward:
         out["bwd_tflops"] = round(2.5 * fwd_flop(B, H, N, d, causal)

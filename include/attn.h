@@ -59,9 +59,10 @@ enum attn_status {
     ATTN_ERR_UNSUPPORTED_D = 3,  /* head dimension d is not 64 or 128 */
     ATTN_ERR_MISALIGNED = 4,     /* a pointer is not 16-byte aligned */
     ATTN_ERR_BAD_SCALE = 5,      /* scale is not finite or not > 0 */
-    ATTN_ERR_BAD_ARG = 6,        /* causal is not 0 or 1 */
+    ATTN_ERR_BAD_ARG = 6,        /* causal is not 0 or 1, or num_splits is not in 1..256 */
     ATTN_ERR_ALIAS = 7,          /* an output overlaps an input or another output */
-    ATTN_ERR_HIP = 8             /* the HIP runtime reported an error at launch */
+    ATTN_ERR_HIP = 8,            /* the HIP runtime reported an error at launch */
+    ATTN_ERR_WORKSPACE = 9       /* a workspace is smaller than the call needs */
 };
 
 /* Forward pass.  Reads q, k, v; writes o [B,H,N,d] (bf16, rounded to nearest
@@ -74,6 +75,32 @@ int attn_fwd(const void *q, const void *k, const void *v, void *o, float *lse,
  * attn_fwd(..., N, ...) is attn_fwd_qk(..., N, N, ...). */
 int attn_fwd_qk(const void *q, const void *k, const void *v, void *o, float *lse,
                 int B, int H, int Nq, int Nk, int d, int causal, float scale, void *stream);
+
+/* Split-key forward pass, for few query rows and many keys (decoding): the
+ * key range is cut into num_splits pieces ("GPU Programming and Kernel
+ * Optimization", item 59: small-query attention split across thread blocks
+ * with a separate combining kernel).  One launch computes, for every query
+ * block and piece, the piece's normalised output O_s (fp32) and its lse_s into
+ * `workspace`; a second launch merges the pieces of each row with the merge
+ * rule of the running maxima and sums: lse = log sum_s exp(lse_s),
+ * O = sum_s exp(lse_s - lse) O_s.  Results equal attn_fwd_qk's up to rounding.
+ * workspace: caller-owned device memory of at least
+ * attn_fwd_splitkv_workspace_size(B, H, Nq, d, num_splits) bytes, 16-byte
+ * aligned, not overlapping any input or output; its contents on entry do not
+ * matter.  num_splits in 1..256 (attn_fwd_splitkv_default_splits suggests one);
+ * pieces past the last key a row sees hold no key and drop out of the merge. */
+int attn_fwd_splitkv(const void *q, const void *k, const void *v, void *o, float *lse,
+                     int B, int H, int Nq, int Nk, int d, int causal, float scale,
+                     int num_splits, void *workspace, long long workspace_bytes, void *stream);
+
+/* Bytes of workspace attn_fwd_splitkv needs: num_splits * B * H * Nq * (d + 1) * 4;
+ * -1 for invalid arguments. */
+long long attn_fwd_splitkv_workspace_size(int B, int H, int Nq, int d, int num_splits);
+
+/* A number of pieces that gives the GPU about one workgroup per compute unit
+ * while keeping at least two 64-key blocks per piece; 1 when splitting does
+ * not help or the arguments are invalid. */
+int attn_fwd_splitkv_default_splits(int B, int H, int Nq, int Nk, int d);
 
 /* Backward pass: enqueues attn_bwd_preprocess, attn_bwd_dkdv and attn_bwd_dq
  * in that order on `stream`.  Reads q, k, v, o, dout and the lse written by

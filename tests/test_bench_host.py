@@ -33,3 +33,25 @@ def test_more_than_one_gpu_is_refused_with_a_message():
     r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"], capture_output=True,
                        text=True, timeout=120)
     assert r.returncode == 2 and "one GPU" in r.stderr
+
+
+def test_visible_pairs_bottom_right_alignment():
+    # non-causal: every pair; causal with equal lengths: the lower triangle with its diagonal
+    assert bench.visible_pairs(7, 5, False) == 35
+    assert bench.visible_pairs(6, 6, True) == 21
+    # five queries, two keys: the first three queries see nothing, then 1 and 2 keys
+    assert bench.visible_pairs(5, 2, True) == 3
+    # one query against many keys sees all of them
+    assert bench.visible_pairs(1, 16384, True) == 16384
+    # more keys than queries: query i sees i + (Nk - Nq) + 1 keys
+    assert bench.visible_pairs(3, 10, True) == 8 + 9 + 10
+
+
+def test_decoding_workload_flop():
+    from tiled_online_softmax_02_amd.inputs import WORKLOADS
+    w = WORKLOADS["dec"]
+    assert (w.nq, w.nk) == (1, 65536)
+    assert bench.workload_flop(w) == 4.0 * w.B * w.H * w.d * 65536
+    # the equal-length workloads keep the convention
+    c5 = WORKLOADS["c5"]
+    assert bench.workload_flop(c5) == bench.step_flop(2, 16, 4096, 128, True, True)

@@ -28,12 +28,14 @@ def lib():
 
 def declared_functions():
     text = open(HEADER).read()
-    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(attn_\w+)\s*\(", text, re.M)))
+    # declarations start at column 0 with their return type; comment lines start with "/*" or " *"
+    return sorted(set(re.findall(r"^[a-z][\w ]*?[\s*](attn_\w+)\s*\(", text, re.M)))
 
 
 def test_header_declares_the_expected_entry_points():
     assert declared_functions() == sorted([
-        "attn_fwd", "attn_fwd_qk", "attn_bwd", "attn_bwd_qk", "attn_bwd_preprocess", "attn_bwd_dkdv",
+        "attn_fwd", "attn_fwd_qk", "attn_fwd_splitkv", "attn_fwd_splitkv_workspace_size",
+        "attn_fwd_splitkv_default_splits", "attn_bwd", "attn_bwd_qk", "attn_bwd_preprocess", "attn_bwd_dkdv",
         "attn_bwd_dq", "attn_status_string", "attn_last_hip_error"])
 
 
@@ -43,7 +45,7 @@ def test_library_exports_every_declared_symbol(lib):
 
 
 def test_status_strings(lib):
-    for code in range(0, 9):
+    for code in range(0, 10):
         s = A.attn_status_string(code)
         assert s and s != "unknown status"
     assert A.attn_status_string(99) == "unknown status"
@@ -170,3 +172,46 @@ def test_backward_qk_argument_checks(lib):
     assert bwd(ptr={7: P[1]}) == A.ATTN_ERR_ALIAS       # dk == k
     assert bwd(ptr={6: P[3] + 16384 - 16}) == A.ATTN_ERR_ALIAS  # dq inside o (Nq rows: 2*64*64*2 B)
     assert bwd(ptr={8: P[2] + 24576 - 16}) == A.ATTN_ERR_ALIAS  # dv inside v (Nk rows: 2*96*64*2 B)
+
+
+def test_splitkv_workspace_size_and_default_splits(lib):
+    assert A.attn_fwd_splitkv_workspace_size(2, 3, 5, 128, 4) == 4 * 2 * 3 * 5 * 129 * 4
+    assert A.attn_fwd_splitkv_workspace_size(1, 1, 1, 64, 1) == 65 * 4
+    assert A.attn_fwd_splitkv_workspace_size(1, 1, 1, 96, 1) == -1
+    assert A.attn_fwd_splitkv_workspace_size(1, 1, 1, 64, 0) == -1
+    assert A.attn_fwd_splitkv_workspace_size(1, 1, -1, 64, 2) == -1
+    # decoding: 1 query row per head, 64 heads, 16384 keys -> enough pieces for ~256 workgroups
+    assert A.attn_fwd_splitkv_default_splits(4, 16, 1, 16384, 128) == 4
+    assert A.attn_fwd_splitkv_default_splits(2, 16, 1, 65536, 128) == 8
+    # few keys: at least two 64-key blocks per piece
+    assert A.attn_fwd_splitkv_default_splits(1, 1, 1, 256, 128) == 2
+    assert A.attn_fwd_splitkv_default_splits(1, 1, 1, 64, 128) == 1
+    # many heads and query blocks already fill the GPU
+    assert A.attn_fwd_splitkv_default_splits(8, 64, 4096, 4096, 128) == 1
+
+
+def splitkv(lib, q=P[0], k=P[1], v=P[2], o=P[3], lse=P[4], ws=P[5], wsb=None, B=1, H=2, Nq=4, Nk=512, d=64,
+            causal=0, scale=0.125, ns=4):
+    if wsb is None:
+        wsb = ns * B * H * Nq * (d + 1) * 4
+    return lib.attn_fwd_splitkv(q, k, v, o, lse, B, H, Nq, Nk, d, causal, scale, ns, ws, wsb, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(ns=0), A.ATTN_ERR_BAD_ARG),
+    (dict(ns=257), A.ATTN_ERR_BAD_ARG),
+    (dict(ws=None), A.ATTN_ERR_NULLPTR),
+    (dict(ws=P[5] + 8), A.ATTN_ERR_MISALIGNED),
+    (dict(wsb=4 * 2 * 4 * 65 * 4 - 1), A.ATTN_ERR_WORKSPACE),
+    (dict(ws=P[3]), A.ATTN_ERR_ALIAS),                 # workspace over o
+    (dict(ws=P[1] + 64), A.ATTN_ERR_ALIAS),            # workspace inside k
+    (dict(Nk=-5), A.ATTN_ERR_BAD_SHAPE),
+    (dict(d=80), A.ATTN_ERR_UNSUPPORTED_D),
+    (dict(scale=0.0), A.ATTN_ERR_BAD_SCALE),
+])
+def test_splitkv_argument_checks(lib, kw, status):
+    assert splitkv(lib, **kw) == status
+
+
+def test_splitkv_empty_is_a_no_op(lib):
+    assert splitkv(lib, q=None, k=None, v=None, o=None, lse=None, ws=None, Nq=0) == A.ATTN_OK

@@ -1,8 +1,9 @@
 """Python binding of libattn.so, the gfx950 attention library (C ABI in include/attn.h).
 
 The functions named like the C entry points (``attn_fwd``, ``attn_fwd_qk``,
-``attn_bwd``, ``attn_bwd_qk``, ``attn_bwd_preprocess``, ``attn_bwd_dkdv``,
-``attn_bwd_dq``, ``attn_status_string``) only marshal arguments: tensors become device
+``attn_fwd_splitkv`` and its two size helpers, ``attn_bwd``, ``attn_bwd_qk``,
+``attn_bwd_preprocess``, ``attn_bwd_dkdv``, ``attn_bwd_dq``,
+``attn_status_string``) only marshal arguments: tensors become device
 pointers, ``stream=None`` becomes the current PyTorch stream of the tensors'
 device, and a nonzero status becomes :class:`AttnError`.  Every step of the
 computation runs in the library's HIP kernels; there is no fallback.  If the
@@ -33,6 +34,7 @@ ATTN_ERR_BAD_SCALE = 5
 ATTN_ERR_BAD_ARG = 6
 ATTN_ERR_ALIAS = 7
 ATTN_ERR_HIP = 8
+ATTN_ERR_WORKSPACE = 9
 
 _lock = threading.Lock()
 _lib = None
@@ -45,6 +47,7 @@ _SIGNATURES = {
     "attn_fwd": [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _F, _P],
     "attn_fwd_qk": [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _F, _P],
     "attn_bwd_qk": [_P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _F, _P],
+    "attn_fwd_splitkv": [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _F, _I, _P, ctypes.c_longlong, _P],
     "attn_bwd": [_P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _F, _P],
     "attn_bwd_preprocess": [_P, _P, _P, _I, _I, _I, _I, _P],
     "attn_bwd_dkdv": [_P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _F, _P],
@@ -78,6 +81,10 @@ def library() -> ctypes.CDLL:
             lib.attn_status_string.restype = ctypes.c_char_p
             lib.attn_last_hip_error.argtypes = []
             lib.attn_last_hip_error.restype = _I
+            lib.attn_fwd_splitkv_workspace_size.argtypes = [_I, _I, _I, _I, _I]
+            lib.attn_fwd_splitkv_workspace_size.restype = ctypes.c_longlong
+            lib.attn_fwd_splitkv_default_splits.argtypes = [_I, _I, _I, _I, _I]
+            lib.attn_fwd_splitkv_default_splits.restype = _I
             _lib = lib
     return _lib
 
@@ -117,6 +124,20 @@ def attn_fwd(q, k, v, o, lse, B, H, N, d, causal, scale, stream=None) -> None:
 def attn_fwd_qk(q, k, v, o, lse, B, H, Nq, Nk, d, causal, scale, stream=None) -> None:
     _call("attn_fwd_qk", _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, H, Nq, Nk, d, int(causal), float(scale),
           _stream(stream, q, o))
+
+
+def attn_fwd_splitkv(q, k, v, o, lse, B, H, Nq, Nk, d, causal, scale, num_splits, workspace, workspace_bytes,
+                     stream=None) -> None:
+    _call("attn_fwd_splitkv", _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, H, Nq, Nk, d, int(causal),
+          float(scale), int(num_splits), _ptr(workspace), int(workspace_bytes), _stream(stream, q, o))
+
+
+def attn_fwd_splitkv_workspace_size(B, H, Nq, d, num_splits) -> int:
+    return int(library().attn_fwd_splitkv_workspace_size(B, H, Nq, d, num_splits))
+
+
+def attn_fwd_splitkv_default_splits(B, H, Nq, Nk, d) -> int:
+    return int(library().attn_fwd_splitkv_default_splits(B, H, Nq, Nk, d))
 
 
 def attn_bwd_qk(q, k, v, o, dout, lse, dq, dk, dv, delta, B, H, Nq, Nk, d, causal, scale, stream=None) -> None:
@@ -179,6 +200,26 @@ def fwd(q, k, v, causal: bool = False, scale: float | None = None, stream=None):
         attn_fwd(q, k, v, o, lse, B, H, Nq, d, causal, scale, stream)
     else:
         attn_fwd_qk(q, k, v, o, lse, B, H, Nq, Nk, d, causal, scale, stream)
+    return o, lse
+
+
+def fwd_splitkv(q, k, v, causal: bool = False, scale: float | None = None, num_splits: int | None = None,
+                stream=None):
+    """Split-key forward (few query rows, many keys); returns (o, lse) like ``fwd``.  The
+    workspace for the pieces is a ``torch.empty`` uint8 buffer of the size the library asks for."""
+    _check_inputs(q, k, v)
+    B, H, Nq, d = q.shape
+    Nk = k.shape[2]
+    scale = default_scale(d) if scale is None else scale
+    if num_splits is None:
+        num_splits = attn_fwd_splitkv_default_splits(B, H, Nq, Nk, d)
+    o = torch.empty_like(q)
+    lse = torch.empty((B, H, Nq), dtype=torch.float32, device=q.device)
+    nbytes = attn_fwd_splitkv_workspace_size(B, H, Nq, d, num_splits)
+    if nbytes < 0:
+        raise ValueError("invalid arguments for the split-key forward")
+    ws = torch.empty(max(nbytes, 16), dtype=torch.uint8, device=q.device)
+    attn_fwd_splitkv(q, k, v, o, lse, B, H, Nq, Nk, d, causal, scale, num_splits, ws, nbytes, stream)
     return o, lse
 
 

@@ -108,6 +108,28 @@ int fwd_impl(const void *q, const void *k, const void *v, void *o, float *lse, i
     return hip_status(attn::launch_fwd(a));
 }
 
+int fwd_split_impl(const void *q, const void *k, const void *v, void *o, float *lse, int B, int H, int Nq, int Nk,
+                   int d, int causal, float scale, int num_splits, void *workspace, long long workspace_bytes,
+                   void *stream)
+{
+    bool empty = false;
+    RETURN_IF(validate_common(B, H, Nq, Nk, d, causal, scale, &empty));
+    if (num_splits < 1 || num_splits > 256) return ATTN_ERR_BAD_ARG;
+    const long long qb = tensor_bytes(B, H, Nq, d), kb = tensor_bytes(B, H, Nk, d), lb = vector_bytes(B, H, Nq);
+    if (qb == 0) return ATTN_OK;  // no query rows: nothing to write
+    if (attn::fwd_split_grid_size(B, H, Nq, num_splits) >= (1LL << 31)) return ATTN_ERR_BAD_SHAPE;
+    const long long wb = attn::fwd_split_workspace_bytes(B, H, Nq, d, num_splits);
+    const void *ptrs[] = {q, k, v, o, lse, workspace};
+    const long long sizes[] = {qb, kb, kb, qb, lb, wb};
+    RETURN_IF(check_ptrs(ptrs, sizes, 6));
+    if (workspace_bytes < wb) return ATTN_ERR_WORKSPACE;
+    const Range in[] = {range_of(q, qb), range_of(k, kb), range_of(v, kb)};
+    const Range out[] = {range_of(o, qb), range_of(lse, lb), range_of(workspace, wb)};
+    RETURN_IF(check_alias(in, 3, out, 3));
+    attn::FwdArgs a{q, k, v, o, lse, B, H, Nq, Nk, d, causal, scale, stream};
+    return hip_status(attn::launch_fwd_split(a, num_splits, workspace));
+}
+
 int bwd_impl(const void *q, const void *k, const void *v, const void *o, const void *dout, const float *lse, void *dq,
              void *dk, void *dv, float *delta, int B, int H, int Nq, int Nk, int d, int causal, float scale,
              void *stream)
@@ -143,6 +165,28 @@ int attn_fwd_qk(const void *q, const void *k, const void *v, void *o, float *lse
                 int causal, float scale, void *stream)
 {
     return fwd_impl(q, k, v, o, lse, B, H, Nq, Nk, d, causal, scale, stream);
+}
+
+int attn_fwd_splitkv(const void *q, const void *k, const void *v, void *o, float *lse, int B, int H, int Nq, int Nk,
+                     int d, int causal, float scale, int num_splits, void *workspace, long long workspace_bytes,
+                     void *stream)
+{
+    return fwd_split_impl(q, k, v, o, lse, B, H, Nq, Nk, d, causal, scale, num_splits, workspace, workspace_bytes,
+                          stream);
+}
+
+long long attn_fwd_splitkv_workspace_size(int B, int H, int Nq, int d, int num_splits)
+{
+    bool empty = false;
+    if (check_shape(B, H, Nq, 0, d, &empty) != ATTN_OK || num_splits < 1 || num_splits > 256) return -1;
+    return attn::fwd_split_workspace_bytes(B, H, Nq, d, num_splits);
+}
+
+int attn_fwd_splitkv_default_splits(int B, int H, int Nq, int Nk, int d)
+{
+    bool empty = false;
+    if (check_shape(B, H, Nq, Nk, d, &empty) != ATTN_OK) return 1;
+    return attn::fwd_split_default(B, H, Nq, Nk, d);
 }
 
 int attn_bwd_preprocess(const void *o, const void *dout, float *delta, int B, int H, int N, int d, void *stream)
@@ -256,9 +300,10 @@ const char *attn_status_string(int status)
     case ATTN_ERR_UNSUPPORTED_D: return "unsupported head dimension: d must be 64 or 128";
     case ATTN_ERR_MISALIGNED: return "a pointer is not 16-byte aligned";
     case ATTN_ERR_BAD_SCALE: return "scale must be finite and > 0";
-    case ATTN_ERR_BAD_ARG: return "causal must be 0 or 1";
+    case ATTN_ERR_BAD_ARG: return "causal must be 0 or 1 and num_splits in 1..256";
     case ATTN_ERR_ALIAS: return "an output overlaps an input or another output";
     case ATTN_ERR_HIP: return "the HIP runtime reported an error at launch";
+    case ATTN_ERR_WORKSPACE: return "the workspace is smaller than the size the call needs";
     default: return "unknown status";
     }
 }

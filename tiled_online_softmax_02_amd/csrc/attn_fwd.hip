@@ -56,11 +56,15 @@ struct FwdSmem {
     static constexpr int TOTAL = 4 * TILE;
 };
 
-template <int D, bool CAUSAL>
+// SPLIT: the key range is cut into n_splits pieces of split_blocks key blocks; workgroup
+// (query block, piece) writes the piece's normalised partial output (fp32) to OP and its
+// log-sum-exp to LP, and fwd_combine_kernel merges the pieces.
+template <int D, bool CAUSAL, bool SPLIT>
 __global__ __launch_bounds__(64 * fwd_waves<D>(), 8 / fwd_waves<D>()) void fwd_kernel(const bf16 *__restrict__ Q, const bf16 *__restrict__ K,
                                                           const bf16 *__restrict__ V, bf16 *__restrict__ O,
                                                           float *__restrict__ LSE, int Nq, int Nk, int n_qtiles, float scale,
-                                                          float c_log2)
+                                                          float c_log2, int n_splits, int split_blocks,
+                                                          float *__restrict__ OP, float *__restrict__ LP)
 {
     using L = FwdSmem<D>;
     constexpr int kFwdWaves = fwd_waves<D>();
@@ -74,9 +78,11 @@ __global__ __launch_bounds__(64 * fwd_waves<D>(), 8 / fwd_waves<D>()) void fwd_k
     // Causal: workgroup `pos` of a head takes query blocks T-1-pos and then pos (T = n_qtiles),
     // so every workgroup but a middle one does the same T+1 blocks' worth of work and the
     // grid needs no longest-first balancing.  Non-causal: one query block per workgroup.
-    const int n_pos = CAUSAL ? (n_qtiles + 1) / 2 : n_qtiles;
+    // Split: one (query block, key piece) per workgroup.
+    const int n_pos = SPLIT ? n_qtiles * n_splits : (CAUSAL ? (n_qtiles + 1) / 2 : n_qtiles);
     int head, pos;
     work_item(blockIdx.x, n_pos, head, pos);
+    const int split = SPLIT ? pos % n_splits : 0;
 
     const int tid = threadIdx.x;
     const int lane = tid & 63, h = lane >> 5, c32 = lane & 31;
@@ -89,8 +95,8 @@ __global__ __launch_bounds__(64 * fwd_waves<D>(), 8 / fwd_waves<D>()) void fwd_k
     // Causal mask with bottom-right alignment: query i sees keys j <= i + off.
     const int off = Nk - Nq;
 
-    for (int pass = 0; pass < (CAUSAL ? 2 : 1); ++pass) {
-        const int qtile = pass == 0 ? (CAUSAL ? n_qtiles - 1 - pos : pos) : pos;
+    for (int pass = 0; pass < ((CAUSAL && !SPLIT) ? 2 : 1); ++pass) {
+        const int qtile = SPLIT ? pos / n_splits : (pass == 0 ? (CAUSAL ? n_qtiles - 1 - pos : pos) : pos);
         if (pass == 1 && qtile == n_qtiles - 1 - pos) break;  // odd T: the middle block is alone
         const int q0 = qtile * kFwdBM;
         const int qw0 = q0 + 32 * w;  // wave-uniform
@@ -112,7 +118,9 @@ __global__ __launch_bounds__(64 * fwd_waves<D>(), 8 / fwd_waves<D>()) void fwd_k
 
         // keys that some row of this block sees (none for rows that see no key at all)
         const int kv_end = CAUSAL ? min(Nk, max(0, q0 + kFwdBM + off)) : Nk;
-        const int nt = (kv_end + kFwdBN - 1) / kFwdBN;
+        // key blocks [jb, je) of this workgroup: all of them, or one piece of the split range
+        const int jb = SPLIT ? split * split_blocks : 0;
+        const int je = SPLIT ? min((kv_end + kFwdBN - 1) / kFwdBN, jb + split_blocks) : (kv_end + kFwdBN - 1) / kFwdBN;
 
         // Key / value blocks go straight from global memory into swizzled LDS tiles.
         // stage of block j is j & 1; callers pass the parity as a compile-time constant
@@ -152,13 +160,13 @@ __global__ __launch_bounds__(64 * fwd_waves<D>(), 8 / fwd_waves<D>()) void fwd_k
         // prologue: K0, V0 and K1 in LDS, scores of block 0 in registers
         using P0 = std::integral_constant<int, 0>;
         using P1 = std::integral_constant<int, 1>;
-        load_k(0, P0{});
-        load_v(0, P0{});
-        load_k(1, P1{});
+        load_k(jb, P0{});
+        load_v(jb, P0{});
+        load_k(jb + 1, P1{});
         wait_vmem();
         __syncthreads();
         f32x16 sa[2], sb[2];
-        if (active(0)) {
+        if (active(jb)) {  // (an empty piece computes these and never uses them)
             scores(P0{}, sa);
             mloc = local_max(sa);
         }
@@ -169,7 +177,6 @@ __global__ __launch_bounds__(64 * fwd_waves<D>(), 8 / fwd_waves<D>()) void fwd_k
         // One pipeline step on key block j: scores of j are in `cur`, scores of j+1 go to `nxt`.
         auto step = [&](int j, auto par, f32x16 *cur, f32x16 *nxt) __attribute__((always_inline)) {
             using PN = std::integral_constant<int, 1 - decltype(par)::value>;  // parity of j + 1
-            const bool more = j + 1 < nt;
             if (active(j)) {
                 const int k0 = j * kFwdBN;
                 if ((CAUSAL && (k0 + kFwdBN - 1 > qw0 + off)) || (k0 + kFwdBN > Nk)) {
@@ -283,16 +290,33 @@ __global__ __launch_bounds__(64 * fwd_waves<D>(), 8 / fwd_waves<D>()) void fwd_k
             __syncthreads();
         };
 
-        int j = 0;
-        for (; j + 1 < nt; j += 2) {
+        int j = jb;
+        for (; j + 1 < je; j += 2) {
             step(j, P0{}, sa, sb);
             step(j + 1, P1{}, sb, sa);
         }
-        if (j < nt) step(j, P0{}, sa, sb);
+        if (j < je) step(j, P0{}, sa, sb);
 
         // epilogue: O = acc / l (bf16, nearest even), lse = m*scale + ln(l)
         const float l_tot = l_run + __shfl_xor(l_run, 32);
-        if (qrow < Nq) {
+        if (SPLIT && qrow < Nq) {
+            // this piece's O = acc / l in fp32 and its lse (-inf when it holds no visible key)
+            const float inv = (l_tot > 0.f) ? 1.f / l_tot : 0.f;
+            const int n_heads = (int)gridDim.x / n_pos;  // B * H
+            const size_t prow = ((size_t)split * n_heads + head) * Nq + qrow;
+            float *orow = OP + prow * D;
+#pragma unroll
+            for (int db = 0; db < NDB; ++db) {
+#pragma unroll
+                for (int g = 0; g < 4; ++g) {
+                    f32x4 ov;
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) ov[i] = oacc[db][4 * g + i] * inv;
+                    *(f32x4 *)(orow + 32 * db + 8 * g + 4 * h) = ov;
+                }
+            }
+            if (h == 0) LP[prow] = (l_tot > 0.f) ? fmaf(m_run, scale, __logf(l_tot)) : -__builtin_inff();
+        } else if (qrow < Nq) {
             const float inv = (l_tot > 0.f) ? 1.f / l_tot : 0.f;
             bf16 *orow = O + hoff + (size_t)qrow * D;
 #pragma unroll
@@ -320,9 +344,64 @@ hipError_t launch_fwd_t(const FwdArgs &a)
     const long long G = (long long)a.B * a.H * (CAUSAL ? (n_qtiles + 1) / 2 : n_qtiles);
     if (G == 0) return hipSuccess;
     const float c_log2 = a.scale * kLog2e;
-    hipLaunchKernelGGL((fwd_kernel<D, CAUSAL>), dim3((unsigned)G), dim3(kThreads), 0, (hipStream_t)a.stream,
+    hipLaunchKernelGGL((fwd_kernel<D, CAUSAL, false>), dim3((unsigned)G), dim3(kThreads), 0, (hipStream_t)a.stream,
                        (const bf16 *)a.q, (const bf16 *)a.k, (const bf16 *)a.v, (bf16 *)a.o, a.lse, a.Nq, a.Nk,
-                       n_qtiles, a.scale, c_log2);
+                       n_qtiles, a.scale, c_log2, 1, 0, (float *)nullptr, (float *)nullptr);
+    return hipGetLastError();
+}
+
+// Merge of the split pieces of one row: lse = log sum_s exp(lse_s), O = sum_s exp(lse_s - lse) O_s
+// (the merge rule of the running maxima and sums, applied to normalised pieces).  One wave per
+// row; lane c holds columns c*D/64 .. c*D/64 + D/64 - 1.
+template <int D>
+__global__ __launch_bounds__(256) void fwd_combine_kernel(const float *__restrict__ OP, const float *__restrict__ LP,
+                                                          bf16 *__restrict__ O, float *__restrict__ LSE, long long rows,
+                                                          int n_splits)
+{
+    constexpr int E = D / 64;
+    const long long row = (long long)blockIdx.x * 4 + (threadIdx.x >> 6);
+    const int lane = threadIdx.x & 63;
+    if (row >= rows) return;
+    float m = -__builtin_inff();
+    for (int s = 0; s < n_splits; ++s) m = fmaxf(m, LP[(size_t)s * rows + row]);
+    float acc[E] = {};
+    float wsum = 0.f;
+    if (m != -__builtin_inff()) {
+        for (int s = 0; s < n_splits; ++s) {
+            const float ls = LP[(size_t)s * rows + row];
+            if (ls == -__builtin_inff()) continue;
+            const float wgt = expf(ls - m);
+            wsum += wgt;
+            const float *op = OP + ((size_t)s * rows + row) * D + lane * E;
+#pragma unroll
+            for (int e = 0; e < E; ++e) acc[e] = fmaf(wgt, op[e], acc[e]);
+        }
+    }
+    const float inv = wsum > 0.f ? 1.f / wsum : 0.f;
+#pragma unroll
+    for (int e = 0; e < E; ++e) O[row * D + lane * E + e] = (bf16)(acc[e] * inv);
+    if (lane == 0) LSE[row] = wsum > 0.f ? m + logf(wsum) : -__builtin_inff();
+}
+
+template <int D, bool CAUSAL>
+hipError_t launch_fwd_split_t(const FwdArgs &a, int n_splits, float *op, float *lp)
+{
+    constexpr int kFwdBM = fwd_bm<D>();
+    constexpr int kThreads = 64 * fwd_waves<D>();
+    const int n_qtiles = (a.Nq + kFwdBM - 1) / kFwdBM;
+    const long long G = (long long)a.B * a.H * n_qtiles * n_splits;
+    if (G == 0) return hipSuccess;
+    const int blocks = (a.Nk + kFwdBN - 1) / kFwdBN;
+    const int split_blocks = (blocks + n_splits - 1) / n_splits;
+    const float c_log2 = a.scale * kLog2e;
+    hipLaunchKernelGGL((fwd_kernel<D, CAUSAL, true>), dim3((unsigned)G), dim3(kThreads), 0, (hipStream_t)a.stream,
+                       (const bf16 *)a.q, (const bf16 *)a.k, (const bf16 *)a.v, (bf16 *)a.o, a.lse, a.Nq, a.Nk,
+                       n_qtiles, a.scale, c_log2, n_splits, split_blocks, op, lp);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    const long long rows = (long long)a.B * a.H * a.Nq;
+    hipLaunchKernelGGL((fwd_combine_kernel<D>), dim3((unsigned)((rows + 3) / 4)), dim3(256), 0, (hipStream_t)a.stream,
+                       (const float *)op, (const float *)lp, (bf16 *)a.o, a.lse, rows, n_splits);
     return hipGetLastError();
 }
 
@@ -332,6 +411,38 @@ hipError_t launch_fwd(const FwdArgs &a)
 {
     if (a.d == 64) return a.causal ? launch_fwd_t<64, true>(a) : launch_fwd_t<64, false>(a);
     return a.causal ? launch_fwd_t<128, true>(a) : launch_fwd_t<128, false>(a);
+}
+
+hipError_t launch_fwd_split(const FwdArgs &a, int n_splits, void *workspace)
+{
+    float *op = (float *)workspace;
+    float *lp = op + (size_t)n_splits * a.B * a.H * a.Nq * a.d;
+    if (a.d == 64)
+        return a.causal ? launch_fwd_split_t<64, true>(a, n_splits, op, lp) : launch_fwd_split_t<64, false>(a, n_splits, op, lp);
+    return a.causal ? launch_fwd_split_t<128, true>(a, n_splits, op, lp) : launch_fwd_split_t<128, false>(a, n_splits, op, lp);
+}
+
+long long fwd_split_workspace_bytes(int B, int H, int Nq, int d, int n_splits)
+{
+    return (long long)n_splits * B * H * Nq * (d + 1) * 4;
+}
+
+long long fwd_split_grid_size(int B, int H, int Nq, int n_splits)
+{
+    return (long long)B * H * ((Nq + fwd_bm<64>() - 1) / fwd_bm<64>()) * n_splits;
+}
+
+int fwd_split_default(int B, int H, int Nq, int Nk, int d)
+{
+    // about one workgroup per compute unit (measured best for decoding shapes: one 8-wave
+    // workgroup already fills a compute unit), at least two key blocks per piece
+    const long long base = (long long)B * H * ((Nq + (d == 128 ? fwd_bm<128>() : fwd_bm<64>()) - 1) /
+                                               (d == 128 ? fwd_bm<128>() : fwd_bm<64>()));
+    const int blocks = (Nk + kFwdBN - 1) / kFwdBN;
+    long long s = base > 0 ? (256 + base - 1) / base : 1;
+    s = s < blocks / 2 ? s : blocks / 2;
+    s = s < 128 ? s : 128;
+    return s < 1 ? 1 : (int)s;
 }
 
 long long fwd_grid_size(int B, int H, int Nq) { return (long long)B * H * ((Nq + fwd_bm<64>() - 1) / fwd_bm<64>()); }

@@ -26,11 +26,16 @@ struct BwdArgs {
 };
 
 hipError_t launch_fwd(const FwdArgs &a);
+// Split-key forward: partial pieces into `workspace` (fwd_split_workspace_bytes), then the merge.
+hipError_t launch_fwd_split(const FwdArgs &a, int n_splits, void *workspace);
 hipError_t launch_bwd_preprocess(const BwdArgs &a);
 hipError_t launch_bwd_dkdv(const BwdArgs &a);
 hipError_t launch_bwd_dq(const BwdArgs &a);
 
 long long fwd_grid_size(int B, int H, int Nq);
+long long fwd_split_grid_size(int B, int H, int Nq, int n_splits);
+long long fwd_split_workspace_bytes(int B, int H, int Nq, int d, int n_splits);
+int fwd_split_default(int B, int H, int Nq, int Nk, int d);
 long long bwd_dkdv_grid_size(int B, int H, int Nk);
 long long bwd_dq_grid_size(int B, int H, int Nq);
 

@@ -66,6 +66,10 @@ WORKLOADS = {
     "c3": Workload("c3", 2, 32, 4096, 128, True),
     "c4": Workload("c4", 1, 16, 16384, 128, True, boost_every=64),
     "c5": Workload("c5", 2, 16, 4096, 128, True, backward=True),
+    # decoding (widening beyond the five configurations): one query row per head against a
+    # long key/value cache of 1 GiB; causal with bottom-right alignment, so the row sees every
+    # key.  32 heads alone would occupy 32 of the 256 compute units without splitting.
+    "dec": Workload("dec", 2, 16, 1, 128, True, Nk=65536, note="decoding, split-key forward"),
 }
 
 

@@ -23,7 +23,7 @@ from collections import defaultdict
 PKG = os.path.dirname(os.path.abspath(__file__))
 KERNEL_SOURCES = ["attn_device.h", "attn_fwd.hip", "attn_bwd.hip"]
 CALIBRATION_BYTES = 256 << 20   # bench.py copies 64 Mi int32 values before timing
-SHORT = {"fwd_kernel": "fwd", "bwd_dkdv_kernel": "dkdv", "bwd_dq_kernel": "dq",
+SHORT = {"fwd_kernel": "fwd", "fwd_combine_kernel": "combine", "bwd_dkdv_kernel": "dkdv", "bwd_dq_kernel": "dq",
          "bwd_preprocess_kernel": "preprocess"}
 
 
@@ -58,7 +58,8 @@ def stats_summary(stats_csv: str, command: str) -> str:
 
 
 def counter_per_kernel(path: str, counter: str):
-    """Average counter value (KiB) per dispatch for each attention kernel, plus the copy kernel."""
+    """Average counter value (KiB) per dispatch for each attention kernel, and for "copy" the
+    largest copy dispatch (the calibration copy; the runtime may add small copies of its own)."""
     vals = defaultdict(list)
     for r in csv.DictReader(open(path)):
         if r["Counter_Name"] != counter:
@@ -67,7 +68,7 @@ def counter_per_kernel(path: str, counter: str):
         key = short_name(name) or ("copy" if "copyBuffer" in name else None)
         if key:
             vals[key].append(float(r["Counter_Value"]))
-    return {k: sum(v) / len(v) for k, v in vals.items()}
+    return {k: (max(v) if k == "copy" else sum(v) / len(v)) for k, v in vals.items()}
 
 
 def traffic_summaries(fetch_csv: str, write_csv: str, workload: str, out_dir: str, commands: str) -> list[str]:
