@@ -180,7 +180,7 @@ def main():
         if record:
             e[0].record()
         if split:
-            A.attn_fwd_splitkv(q, k, v, o, lse, B, H, N, Nk, d, causal, scale, ns, ws, ws_bytes)
+            A.attn_fwd_splitkv(q, k, v, o, lse, B, H, H, N, Nk, d, causal, scale, ns, ws, ws_bytes)
         else:
             A.attn_fwd(q, k, v, o, lse, B, H, N, d, causal, scale)
         if record:

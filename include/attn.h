@@ -14,11 +14,17 @@
  *
  * Conventions shared by every entry point
  * ---------------------------------------
- * Tensors are device pointers to dense row-major arrays.  With Nq query rows
- * and Nk key rows per head (Nq = Nk = N for the entry points that take one N):
+ * Tensors are device pointers to dense row-major arrays.  With H query heads,
+ * Hk key/value heads, Nq query rows and Nk key rows per head (Hk = H and
+ * Nq = Nk = N for the entry points that take one H and one N):
  *   q, o, dout, dq : bfloat16 (raw 16-bit patterns), [B, H, Nq, d]
- *   k, v, dk, dv   : bfloat16, [B, H, Nk, d]
+ *   k, v, dk, dv   : bfloat16, [B, Hk, Nk, d]
  *   lse, delta     : float32, [B, H, Nq]
+ * Grouped-query attention: H is a multiple of Hk and query head h uses K/V
+ * head h / (H / Hk) (the kernel wiki's "FlashAttention v3 (Tri Dao et al.)"
+ * page, sections "What it is" and "Runtime parameters": separate counts of
+ * query heads and K/V heads); dk and dv of a K/V head sum over its query
+ * heads.  Hk = 1 is multi-query attention.
  * lse is the natural log of sum_j exp(scale * <q_i, k_j>) over the keys j that
  * query i sees; delta is D_i = sum_c dout[i][c] * o[i][c].
  * Causal masking (causal = 1) hides key j from query i when j > i + (Nk - Nq),
@@ -42,7 +48,7 @@
  * The library never aborts or prints.  An empty problem (B, H or N equal to 0)
  * is valid, enqueues nothing and returns ATTN_OK; more generally a pointer to a
  * buffer of zero bytes may be NULL.
- * Sizes: B, H, N (Nq, Nk) >= 0; d in {64, 128}; B*H*N*d < 2^62;
+ * Sizes: B, H, Hk, N (Nq, Nk) >= 0; d in {64, 128}; B*H*N*d < 2^62;
  * (N + 256)*d*2 < 2^32 for N = Nq and N = Nk.  Pointers must be 16-byte aligned.
  */
 #ifndef ATTN_H_
@@ -55,7 +61,7 @@ extern "C" {
 enum attn_status {
     ATTN_OK = 0,
     ATTN_ERR_NULLPTR = 1,        /* a required pointer is NULL (non-empty problem) */
-    ATTN_ERR_BAD_SHAPE = 2,      /* B, H or N negative, or a size limit exceeded */
+    ATTN_ERR_BAD_SHAPE = 2,      /* a size negative, H not a multiple of Hk, or a limit exceeded */
     ATTN_ERR_UNSUPPORTED_D = 3,  /* head dimension d is not 64 or 128 */
     ATTN_ERR_MISALIGNED = 4,     /* a pointer is not 16-byte aligned */
     ATTN_ERR_BAD_SCALE = 5,      /* scale is not finite or not > 0 */
@@ -70,11 +76,12 @@ enum attn_status {
 int attn_fwd(const void *q, const void *k, const void *v, void *o, float *lse,
              int B, int H, int N, int d, int causal, float scale, void *stream);
 
-/* Forward pass with Nq query rows and Nk key/value rows per head (see the
- * conventions above for the causal alignment and for rows that see no key).
- * attn_fwd(..., N, ...) is attn_fwd_qk(..., N, N, ...). */
+/* Forward pass with H query heads and Hk K/V heads, Nq query rows and Nk
+ * key/value rows per head (see the conventions above for grouped heads, the
+ * causal alignment and rows that see no key).
+ * attn_fwd(..., H, N, ...) is attn_fwd_qk(..., H, H, N, N, ...). */
 int attn_fwd_qk(const void *q, const void *k, const void *v, void *o, float *lse,
-                int B, int H, int Nq, int Nk, int d, int causal, float scale, void *stream);
+                int B, int H, int Hk, int Nq, int Nk, int d, int causal, float scale, void *stream);
 
 /* Split-key forward pass, for few query rows and many keys (decoding): the
  * key range is cut into num_splits pieces ("GPU Programming and Kernel
@@ -90,7 +97,7 @@ int attn_fwd_qk(const void *q, const void *k, const void *v, void *o, float *lse
  * matter.  num_splits in 1..256 (attn_fwd_splitkv_default_splits suggests one);
  * pieces past the last key a row sees hold no key and drop out of the merge. */
 int attn_fwd_splitkv(const void *q, const void *k, const void *v, void *o, float *lse,
-                     int B, int H, int Nq, int Nk, int d, int causal, float scale,
+                     int B, int H, int Hk, int Nq, int Nk, int d, int causal, float scale,
                      int num_splits, void *workspace, long long workspace_bytes, void *stream);
 
 /* Bytes of workspace attn_fwd_splitkv needs: num_splits * B * H * Nq * (d + 1) * 4;
@@ -111,12 +118,13 @@ int attn_bwd(const void *q, const void *k, const void *v, const void *o, const v
              const float *lse, void *dq, void *dk, void *dv, float *delta,
              int B, int H, int N, int d, int causal, float scale, void *stream);
 
-/* Backward pass with Nq query rows and Nk key/value rows per head; the same
- * three kernels as attn_bwd.  delta is [B, H, Nq].  With Nq = 0 it writes
- * dk = dv = 0; with Nk = 0 it writes dq = 0. */
+/* Backward pass with H query heads and Hk K/V heads, Nq query rows and Nk
+ * key/value rows per head; the same three kernels as attn_bwd (the dK/dV
+ * kernel loops over the H / Hk query heads of each K/V head).  delta is
+ * [B, H, Nq].  With Nq = 0 it writes dk = dv = 0; with Nk = 0 it writes dq = 0. */
 int attn_bwd_qk(const void *q, const void *k, const void *v, const void *o, const void *dout,
                 const float *lse, void *dq, void *dk, void *dv, float *delta,
-                int B, int H, int Nq, int Nk, int d, int causal, float scale, void *stream);
+                int B, int H, int Hk, int Nq, int Nk, int d, int causal, float scale, void *stream);
 
 /* The three backward steps below take one length N (Nq = Nk = N); they exist
  * so that each kernel can be enqueued and timed on its own. */

@@ -129,8 +129,9 @@ def test_python_binding_raises_with_status(lib):
     assert e.value.status == A.ATTN_ERR_BAD_SCALE
 
 
-def fwd_qk(lib, q=P[0], k=P[1], v=P[2], o=P[3], lse=P[4], B=1, H=1, Nq=64, Nk=128, d=64, causal=1, scale=0.125):
-    return lib.attn_fwd_qk(q, k, v, o, lse, B, H, Nq, Nk, d, causal, scale, None)
+def fwd_qk(lib, q=P[0], k=P[1], v=P[2], o=P[3], lse=P[4], B=1, H=1, Hk=None, Nq=64, Nk=128, d=64, causal=1,
+           scale=0.125):
+    return lib.attn_fwd_qk(q, k, v, o, lse, B, H, H if Hk is None else Hk, Nq, Nk, d, causal, scale, None)
 
 
 @pytest.mark.parametrize("kw,status", [
@@ -145,6 +146,11 @@ def fwd_qk(lib, q=P[0], k=P[1], v=P[2], o=P[3], lse=P[4], B=1, H=1, Nq=64, Nk=12
     (dict(v=P[2] + 4), A.ATTN_ERR_MISALIGNED),
     (dict(o=P[1] + 16384 - 16), A.ATTN_ERR_ALIAS),      # inside k, whose size is Nk*d*2 = 16384
     (dict(lse=P[0] + 8192 - 16), A.ATTN_ERR_ALIAS),     # inside q, whose size is Nq*d*2 = 8192
+    (dict(H=4, Hk=3), A.ATTN_ERR_BAD_SHAPE),             # H must be a multiple of Hk
+    (dict(H=4, Hk=0), A.ATTN_ERR_BAD_SHAPE),
+    (dict(H=4, Hk=-1), A.ATTN_ERR_BAD_SHAPE),
+    (dict(H=4, Hk=8), A.ATTN_ERR_BAD_SHAPE),
+    (dict(H=4, Hk=2, o=P[1] + 2 * 16384 - 16), A.ATTN_ERR_ALIAS),   # k holds Hk = 2 heads of 16384 B
 ])
 def test_forward_qk_argument_checks(lib, kw, status):
     assert fwd_qk(lib, **kw) == status
@@ -154,7 +160,7 @@ def test_qk_empty_problems(lib):
     # no query rows: the forward has nothing to write and accepts NULL everywhere
     assert fwd_qk(lib, q=None, k=None, v=None, o=None, lse=None, Nq=0, Nk=64) == A.ATTN_OK
     # the backward with Nq = Nk = 0 is empty
-    assert lib.attn_bwd_qk(*([None] * 10), 1, 1, 0, 0, 64, 1, 0.125, None) == A.ATTN_OK
+    assert lib.attn_bwd_qk(*([None] * 10), 1, 1, 1, 0, 0, 64, 1, 0.125, None) == A.ATTN_OK
 
 
 def test_backward_qk_argument_checks(lib):
@@ -164,7 +170,7 @@ def test_backward_qk_argument_checks(lib):
         a = list(args)
         for i, val in kw.get("ptr", {}).items():
             a[i] = val
-        return lib.attn_bwd_qk(*a, 1, 2, Nq, Nk, 64, 1, 0.125, None)
+        return lib.attn_bwd_qk(*a, 1, 2, kw.get("Hk", 2), Nq, Nk, 64, 1, 0.125, None)
 
     assert bwd(Nq=-2) == A.ATTN_ERR_BAD_SHAPE
     assert bwd(ptr={9: None}) == A.ATTN_ERR_NULLPTR     # delta
@@ -172,6 +178,7 @@ def test_backward_qk_argument_checks(lib):
     assert bwd(ptr={7: P[1]}) == A.ATTN_ERR_ALIAS       # dk == k
     assert bwd(ptr={6: P[3] + 16384 - 16}) == A.ATTN_ERR_ALIAS  # dq inside o (Nq rows: 2*64*64*2 B)
     assert bwd(ptr={8: P[2] + 24576 - 16}) == A.ATTN_ERR_ALIAS  # dv inside v (Nk rows: 2*96*64*2 B)
+    assert bwd(Hk=3) == A.ATTN_ERR_BAD_SHAPE                   # 2 query heads over 3 K/V heads
 
 
 def test_splitkv_workspace_size_and_default_splits(lib):
@@ -194,7 +201,7 @@ def splitkv(lib, q=P[0], k=P[1], v=P[2], o=P[3], lse=P[4], ws=P[5], wsb=None, B=
             causal=0, scale=0.125, ns=4):
     if wsb is None:
         wsb = ns * B * H * Nq * (d + 1) * 4
-    return lib.attn_fwd_splitkv(q, k, v, o, lse, B, H, Nq, Nk, d, causal, scale, ns, ws, wsb, None)
+    return lib.attn_fwd_splitkv(q, k, v, o, lse, B, H, H, Nq, Nk, d, causal, scale, ns, ws, wsb, None)
 
 
 @pytest.mark.parametrize("kw,status", [

@@ -91,5 +91,5 @@ def test_splitkv_workspace_too_small_is_rejected():
     need = A.attn_fwd_splitkv_workspace_size(1, 1, 2, 64, 4)
     ws = torch.empty(need, dtype=torch.uint8, device=DEV)
     with pytest.raises(A.AttnError) as e:
-        A.attn_fwd_splitkv(q, k, v, o, lse, 1, 1, 2, 256, 64, False, 0.125, 4, ws, need - 16)
+        A.attn_fwd_splitkv(q, k, v, o, lse, 1, 1, 1, 2, 256, 64, False, 0.125, 4, ws, need - 16)
     assert e.value.status == A.ATTN_ERR_WORKSPACE

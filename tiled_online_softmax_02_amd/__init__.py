@@ -12,7 +12,8 @@ library has not been built the first call raises.
 ``fwd`` and ``bwd`` are conveniences that check dtypes, devices and
 contiguity and allocate the outputs with ``torch.empty``; q may have a
 different number of rows than k and v (causal masks then align to the
-bottom-right corner).
+bottom-right corner) and a multiple of their number of heads (grouped-query
+attention).
 """
 from __future__ import annotations
 
@@ -45,9 +46,9 @@ _F = ctypes.c_float
 
 _SIGNATURES = {
     "attn_fwd": [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _F, _P],
-    "attn_fwd_qk": [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _F, _P],
-    "attn_bwd_qk": [_P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _F, _P],
-    "attn_fwd_splitkv": [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _F, _I, _P, ctypes.c_longlong, _P],
+    "attn_fwd_qk": [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _F, _P],
+    "attn_bwd_qk": [_P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _F, _P],
+    "attn_fwd_splitkv": [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _F, _I, _P, ctypes.c_longlong, _P],
     "attn_bwd": [_P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _F, _P],
     "attn_bwd_preprocess": [_P, _P, _P, _I, _I, _I, _I, _P],
     "attn_bwd_dkdv": [_P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _F, _P],
@@ -121,14 +122,14 @@ def attn_fwd(q, k, v, o, lse, B, H, N, d, causal, scale, stream=None) -> None:
           _stream(stream, q, o))
 
 
-def attn_fwd_qk(q, k, v, o, lse, B, H, Nq, Nk, d, causal, scale, stream=None) -> None:
-    _call("attn_fwd_qk", _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, H, Nq, Nk, d, int(causal), float(scale),
-          _stream(stream, q, o))
+def attn_fwd_qk(q, k, v, o, lse, B, H, Hk, Nq, Nk, d, causal, scale, stream=None) -> None:
+    _call("attn_fwd_qk", _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, H, Hk, Nq, Nk, d, int(causal),
+          float(scale), _stream(stream, q, o))
 
 
-def attn_fwd_splitkv(q, k, v, o, lse, B, H, Nq, Nk, d, causal, scale, num_splits, workspace, workspace_bytes,
+def attn_fwd_splitkv(q, k, v, o, lse, B, H, Hk, Nq, Nk, d, causal, scale, num_splits, workspace, workspace_bytes,
                      stream=None) -> None:
-    _call("attn_fwd_splitkv", _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, H, Nq, Nk, d, int(causal),
+    _call("attn_fwd_splitkv", _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, H, Hk, Nq, Nk, d, int(causal),
           float(scale), int(num_splits), _ptr(workspace), int(workspace_bytes), _stream(stream, q, o))
 
 
@@ -140,9 +141,9 @@ def attn_fwd_splitkv_default_splits(B, H, Nq, Nk, d) -> int:
     return int(library().attn_fwd_splitkv_default_splits(B, H, Nq, Nk, d))
 
 
-def attn_bwd_qk(q, k, v, o, dout, lse, dq, dk, dv, delta, B, H, Nq, Nk, d, causal, scale, stream=None) -> None:
+def attn_bwd_qk(q, k, v, o, dout, lse, dq, dk, dv, delta, B, H, Hk, Nq, Nk, d, causal, scale, stream=None) -> None:
     _call("attn_bwd_qk", _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(dout), _ptr(lse), _ptr(dq), _ptr(dk), _ptr(dv),
-          _ptr(delta), B, H, Nq, Nk, d, int(causal), float(scale), _stream(stream, q, dq, dk))
+          _ptr(delta), B, H, Hk, Nq, Nk, d, int(causal), float(scale), _stream(stream, q, dq, dk))
 
 
 def attn_bwd(q, k, v, o, dout, lse, dq, dk, dv, delta, B, H, N, d, causal, scale, stream=None) -> None:
@@ -165,7 +166,7 @@ def attn_bwd_dq(q, k, v, dout, lse, delta, dq, B, H, N, d, causal, scale, stream
 
 
 def _check_inputs(q, k, v, *q_like):
-    """q (and o, dO) are [B, H, Nq, d]; k and v are [B, H, Nk, d]."""
+    """q (and o, dO) are [B, H, Nq, d]; k and v are [B, Hk, Nk, d] with H a multiple of Hk."""
     if q.dim() != 4 or k.dim() != 4 or v.dim() != 4:
         raise ValueError("expected [B, H, N, d] tensors")
     for t in (q, k, v, *q_like):
@@ -176,8 +177,9 @@ def _check_inputs(q, k, v, *q_like):
         if not t.is_contiguous():
             raise ValueError("tensors must be contiguous")
     B, H, _, d = q.shape
-    if k.shape[:2] != (B, H) or k.shape[3] != d or v.shape != k.shape:
-        raise ValueError("k and v must be [B, H, Nk, d] with the B, H and d of q")
+    Hk = k.shape[1]
+    if k.shape[0] != B or k.shape[3] != d or v.shape != k.shape or Hk < 1 or H % Hk:
+        raise ValueError("k and v must be [B, Hk, Nk, d] with the B and d of q and H a multiple of Hk")
     for t in q_like:
         if t.shape != q.shape:
             raise ValueError("o and dO must have the shape of q")
@@ -192,14 +194,14 @@ def fwd(q, k, v, causal: bool = False, scale: float | None = None, stream=None):
     """Forward pass; returns (o bf16 [B,H,Nq,d], lse fp32 [B,H,Nq])."""
     _check_inputs(q, k, v)
     B, H, Nq, d = q.shape
-    Nk = k.shape[2]
+    Hk, Nk = k.shape[1], k.shape[2]
     scale = default_scale(d) if scale is None else scale
     o = torch.empty_like(q)
     lse = torch.empty((B, H, Nq), dtype=torch.float32, device=q.device)
-    if Nq == Nk:
+    if Nq == Nk and H == Hk:
         attn_fwd(q, k, v, o, lse, B, H, Nq, d, causal, scale, stream)
     else:
-        attn_fwd_qk(q, k, v, o, lse, B, H, Nq, Nk, d, causal, scale, stream)
+        attn_fwd_qk(q, k, v, o, lse, B, H, Hk, Nq, Nk, d, causal, scale, stream)
     return o, lse
 
 
@@ -209,7 +211,7 @@ def fwd_splitkv(q, k, v, causal: bool = False, scale: float | None = None, num_s
     workspace for the pieces is a ``torch.empty`` uint8 buffer of the size the library asks for."""
     _check_inputs(q, k, v)
     B, H, Nq, d = q.shape
-    Nk = k.shape[2]
+    Hk, Nk = k.shape[1], k.shape[2]
     scale = default_scale(d) if scale is None else scale
     if num_splits is None:
         num_splits = attn_fwd_splitkv_default_splits(B, H, Nq, Nk, d)
@@ -219,22 +221,22 @@ def fwd_splitkv(q, k, v, causal: bool = False, scale: float | None = None, num_s
     if nbytes < 0:
         raise ValueError("invalid arguments for the split-key forward")
     ws = torch.empty(max(nbytes, 16), dtype=torch.uint8, device=q.device)
-    attn_fwd_splitkv(q, k, v, o, lse, B, H, Nq, Nk, d, causal, scale, num_splits, ws, nbytes, stream)
+    attn_fwd_splitkv(q, k, v, o, lse, B, H, Hk, Nq, Nk, d, causal, scale, num_splits, ws, nbytes, stream)
     return o, lse
 
 
 def bwd(q, k, v, o, dout, lse, causal: bool = False, scale: float | None = None, stream=None):
-    """Backward pass; returns (dq [B,H,Nq,d], dk, dv [B,H,Nk,d]), bf16."""
+    """Backward pass; returns (dq [B,H,Nq,d], dk, dv [B,Hk,Nk,d]), bf16."""
     _check_inputs(q, k, v, o, dout)
     B, H, Nq, d = q.shape
-    Nk = k.shape[2]
+    Hk, Nk = k.shape[1], k.shape[2]
     if lse.dtype != torch.float32 or tuple(lse.shape) != (B, H, Nq) or not lse.is_contiguous():
         raise ValueError("lse must be a contiguous float32 [B, H, Nq] tensor")
     scale = default_scale(d) if scale is None else scale
     dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
     delta = torch.empty((B, H, Nq), dtype=torch.float32, device=q.device)
-    if Nq == Nk:
+    if Nq == Nk and H == Hk:
         attn_bwd(q, k, v, o, dout, lse, dq, dk, dv, delta, B, H, Nq, d, causal, scale, stream)
     else:
-        attn_bwd_qk(q, k, v, o, dout, lse, dq, dk, dv, delta, B, H, Nq, Nk, d, causal, scale, stream)
+        attn_bwd_qk(q, k, v, o, dout, lse, dq, dk, dv, delta, B, H, Hk, Nq, Nk, d, causal, scale, stream)
     return dq, dk, dv

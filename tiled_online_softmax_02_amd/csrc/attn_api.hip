@@ -21,19 +21,20 @@ bool overlap(Range a, Range b) { return a.lo < b.hi && b.lo < a.hi; }  // empty 
 
 bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
 
-// Shape rules shared by every entry point (Nq query rows and Nk key rows per head).
-// Sets *empty when there is nothing to compute.
-int check_shape(int B, int H, int Nq, int Nk, int d, bool *empty)
+// Shape rules shared by every entry point: H query heads and Hk K/V heads (H a multiple of
+// Hk), Nq query rows and Nk key rows per head.  Sets *empty when there is nothing to compute.
+int check_shape(int B, int H, int Hk, int Nq, int Nk, int d, bool *empty)
 {
-    if (B < 0 || H < 0 || Nq < 0 || Nk < 0) return ATTN_ERR_BAD_SHAPE;
+    if (B < 0 || H < 0 || Hk < 0 || Nq < 0 || Nk < 0) return ATTN_ERR_BAD_SHAPE;
+    if (H > 0 && (Hk < 1 || H % Hk != 0)) return ATTN_ERR_BAD_SHAPE;
     if (d != 64 && d != 128) return ATTN_ERR_UNSUPPORTED_D;
-    const long long rows_q = (long long)B * H * Nq, rows_k = (long long)B * H * Nk;
+    const long long rows_q = (long long)B * H * Nq, rows_k = (long long)B * Hk * Nk;
     if (rows_q > ((1LL << 62) / d) || rows_k > ((1LL << 62) / d)) return ATTN_ERR_BAD_SHAPE;
     // per-head byte offsets, including the padding rows of the last tile, are 32-bit
     if ((long long)(Nq + 256) * d * 2 > 0xFFFFFFFFLL || (long long)(Nk + 256) * d * 2 > 0xFFFFFFFFLL)
         return ATTN_ERR_BAD_SHAPE;
     // work-group counts of the launches must fit a 32-bit grid
-    if (attn::fwd_grid_size(B, H, Nq) >= (1LL << 31) || attn::bwd_dkdv_grid_size(B, H, Nk) >= (1LL << 31) ||
+    if (attn::fwd_grid_size(B, H, Nq) >= (1LL << 31) || attn::bwd_dkdv_grid_size(B, Hk, Nk) >= (1LL << 31) ||
         attn::bwd_dq_grid_size(B, H, Nq) >= (1LL << 31) || rows_q / 16 >= (1LL << 31))
         return ATTN_ERR_BAD_SHAPE;
     *empty = (rows_q == 0 && rows_k == 0);
@@ -79,9 +80,9 @@ int hip_status(hipError_t e)
         if (rc_ != ATTN_OK) return rc_; \
     } while (0)
 
-int validate_common(int B, int H, int Nq, int Nk, int d, int causal, float scale, bool *empty)
+int validate_common(int B, int H, int Hk, int Nq, int Nk, int d, int causal, float scale, bool *empty)
 {
-    RETURN_IF(check_shape(B, H, Nq, Nk, d, empty));
+    RETURN_IF(check_shape(B, H, Hk, Nq, Nk, d, empty));
     RETURN_IF(check_causal(causal));
     RETURN_IF(check_scale(scale));
     return ATTN_OK;
@@ -91,12 +92,12 @@ int validate_common(int B, int H, int Nq, int Nk, int d, int causal, float scale
 long long tensor_bytes(int B, int H, int rows, int d) { return (long long)B * H * rows * d * 2; }
 long long vector_bytes(int B, int H, int rows) { return (long long)B * H * rows * 4; }
 
-int fwd_impl(const void *q, const void *k, const void *v, void *o, float *lse, int B, int H, int Nq, int Nk, int d,
-             int causal, float scale, void *stream)
+int fwd_impl(const void *q, const void *k, const void *v, void *o, float *lse, int B, int H, int Hk, int Nq, int Nk,
+             int d, int causal, float scale, void *stream)
 {
     bool empty = false;
-    RETURN_IF(validate_common(B, H, Nq, Nk, d, causal, scale, &empty));
-    const long long qb = tensor_bytes(B, H, Nq, d), kb = tensor_bytes(B, H, Nk, d), lb = vector_bytes(B, H, Nq);
+    RETURN_IF(validate_common(B, H, Hk, Nq, Nk, d, causal, scale, &empty));
+    const long long qb = tensor_bytes(B, H, Nq, d), kb = tensor_bytes(B, Hk, Nk, d), lb = vector_bytes(B, H, Nq);
     if (qb == 0) return ATTN_OK;  // no query rows: nothing to write
     const void *ptrs[] = {q, k, v, o, lse};
     const long long sizes[] = {qb, kb, kb, qb, lb};
@@ -104,18 +105,18 @@ int fwd_impl(const void *q, const void *k, const void *v, void *o, float *lse, i
     const Range in[] = {range_of(q, qb), range_of(k, kb), range_of(v, kb)};
     const Range out[] = {range_of(o, qb), range_of(lse, lb)};
     RETURN_IF(check_alias(in, 3, out, 2));
-    attn::FwdArgs a{q, k, v, o, lse, B, H, Nq, Nk, d, causal, scale, stream};
+    attn::FwdArgs a{q, k, v, o, lse, B, H, Hk, Nq, Nk, d, causal, scale, stream};
     return hip_status(attn::launch_fwd(a));
 }
 
-int fwd_split_impl(const void *q, const void *k, const void *v, void *o, float *lse, int B, int H, int Nq, int Nk,
-                   int d, int causal, float scale, int num_splits, void *workspace, long long workspace_bytes,
-                   void *stream)
+int fwd_split_impl(const void *q, const void *k, const void *v, void *o, float *lse, int B, int H, int Hk, int Nq,
+                   int Nk, int d, int causal, float scale, int num_splits, void *workspace,
+                   long long workspace_bytes, void *stream)
 {
     bool empty = false;
-    RETURN_IF(validate_common(B, H, Nq, Nk, d, causal, scale, &empty));
+    RETURN_IF(validate_common(B, H, Hk, Nq, Nk, d, causal, scale, &empty));
     if (num_splits < 1 || num_splits > 256) return ATTN_ERR_BAD_ARG;
-    const long long qb = tensor_bytes(B, H, Nq, d), kb = tensor_bytes(B, H, Nk, d), lb = vector_bytes(B, H, Nq);
+    const long long qb = tensor_bytes(B, H, Nq, d), kb = tensor_bytes(B, Hk, Nk, d), lb = vector_bytes(B, H, Nq);
     if (qb == 0) return ATTN_OK;  // no query rows: nothing to write
     if (attn::fwd_split_grid_size(B, H, Nq, num_splits) >= (1LL << 31)) return ATTN_ERR_BAD_SHAPE;
     const long long wb = attn::fwd_split_workspace_bytes(B, H, Nq, d, num_splits);
@@ -126,18 +127,18 @@ int fwd_split_impl(const void *q, const void *k, const void *v, void *o, float *
     const Range in[] = {range_of(q, qb), range_of(k, kb), range_of(v, kb)};
     const Range out[] = {range_of(o, qb), range_of(lse, lb), range_of(workspace, wb)};
     RETURN_IF(check_alias(in, 3, out, 3));
-    attn::FwdArgs a{q, k, v, o, lse, B, H, Nq, Nk, d, causal, scale, stream};
+    attn::FwdArgs a{q, k, v, o, lse, B, H, Hk, Nq, Nk, d, causal, scale, stream};
     return hip_status(attn::launch_fwd_split(a, num_splits, workspace));
 }
 
 int bwd_impl(const void *q, const void *k, const void *v, const void *o, const void *dout, const float *lse, void *dq,
-             void *dk, void *dv, float *delta, int B, int H, int Nq, int Nk, int d, int causal, float scale,
+             void *dk, void *dv, float *delta, int B, int H, int Hk, int Nq, int Nk, int d, int causal, float scale,
              void *stream)
 {
     bool empty = false;
-    RETURN_IF(validate_common(B, H, Nq, Nk, d, causal, scale, &empty));
+    RETURN_IF(validate_common(B, H, Hk, Nq, Nk, d, causal, scale, &empty));
     if (empty) return ATTN_OK;
-    const long long qb = tensor_bytes(B, H, Nq, d), kb = tensor_bytes(B, H, Nk, d), lb = vector_bytes(B, H, Nq);
+    const long long qb = tensor_bytes(B, H, Nq, d), kb = tensor_bytes(B, Hk, Nk, d), lb = vector_bytes(B, H, Nq);
     const void *ptrs[] = {q, k, v, o, dout, lse, dq, dk, dv, delta};
     const long long sizes[] = {qb, kb, kb, qb, qb, lb, qb, kb, kb, lb};
     RETURN_IF(check_ptrs(ptrs, sizes, 10));
@@ -145,7 +146,7 @@ int bwd_impl(const void *q, const void *k, const void *v, const void *o, const v
                         range_of(o, qb), range_of(dout, qb), range_of(lse, lb)};
     const Range out[] = {range_of(dq, qb), range_of(dk, kb), range_of(dv, kb), range_of(delta, lb)};
     RETURN_IF(check_alias(in, 6, out, 4));
-    attn::BwdArgs a{q, k, v, o, dout, lse, dq, dk, dv, delta, B, H, Nq, Nk, d, causal, scale, stream};
+    attn::BwdArgs a{q, k, v, o, dout, lse, dq, dk, dv, delta, B, H, Hk, Nq, Nk, d, causal, scale, stream};
     RETURN_IF(hip_status(attn::launch_bwd_preprocess(a)));
     RETURN_IF(hip_status(attn::launch_bwd_dkdv(a)));
     return hip_status(attn::launch_bwd_dq(a));
@@ -158,41 +159,41 @@ extern "C" {
 int attn_fwd(const void *q, const void *k, const void *v, void *o, float *lse, int B, int H, int N, int d, int causal,
              float scale, void *stream)
 {
-    return fwd_impl(q, k, v, o, lse, B, H, N, N, d, causal, scale, stream);
+    return fwd_impl(q, k, v, o, lse, B, H, H, N, N, d, causal, scale, stream);
 }
 
-int attn_fwd_qk(const void *q, const void *k, const void *v, void *o, float *lse, int B, int H, int Nq, int Nk, int d,
-                int causal, float scale, void *stream)
+int attn_fwd_qk(const void *q, const void *k, const void *v, void *o, float *lse, int B, int H, int Hk, int Nq, int Nk,
+                int d, int causal, float scale, void *stream)
 {
-    return fwd_impl(q, k, v, o, lse, B, H, Nq, Nk, d, causal, scale, stream);
+    return fwd_impl(q, k, v, o, lse, B, H, Hk, Nq, Nk, d, causal, scale, stream);
 }
 
-int attn_fwd_splitkv(const void *q, const void *k, const void *v, void *o, float *lse, int B, int H, int Nq, int Nk,
-                     int d, int causal, float scale, int num_splits, void *workspace, long long workspace_bytes,
-                     void *stream)
+int attn_fwd_splitkv(const void *q, const void *k, const void *v, void *o, float *lse, int B, int H, int Hk, int Nq,
+                     int Nk, int d, int causal, float scale, int num_splits, void *workspace,
+                     long long workspace_bytes, void *stream)
 {
-    return fwd_split_impl(q, k, v, o, lse, B, H, Nq, Nk, d, causal, scale, num_splits, workspace, workspace_bytes,
-                          stream);
+    return fwd_split_impl(q, k, v, o, lse, B, H, Hk, Nq, Nk, d, causal, scale, num_splits, workspace,
+                          workspace_bytes, stream);
 }
 
 long long attn_fwd_splitkv_workspace_size(int B, int H, int Nq, int d, int num_splits)
 {
     bool empty = false;
-    if (check_shape(B, H, Nq, 0, d, &empty) != ATTN_OK || num_splits < 1 || num_splits > 256) return -1;
+    if (check_shape(B, H, H > 0 ? 1 : 0, Nq, 0, d, &empty) != ATTN_OK || num_splits < 1 || num_splits > 256) return -1;
     return attn::fwd_split_workspace_bytes(B, H, Nq, d, num_splits);
 }
 
 int attn_fwd_splitkv_default_splits(int B, int H, int Nq, int Nk, int d)
 {
     bool empty = false;
-    if (check_shape(B, H, Nq, Nk, d, &empty) != ATTN_OK) return 1;
+    if (check_shape(B, H, H, Nq, Nk, d, &empty) != ATTN_OK) return 1;
     return attn::fwd_split_default(B, H, Nq, Nk, d);
 }
 
 int attn_bwd_preprocess(const void *o, const void *dout, float *delta, int B, int H, int N, int d, void *stream)
 {
     bool empty = false;
-    RETURN_IF(check_shape(B, H, N, N, d, &empty));
+    RETURN_IF(check_shape(B, H, H, N, N, d, &empty));
     if (empty) return ATTN_OK;
     const long long tb = tensor_bytes(B, H, N, d), lb = vector_bytes(B, H, N);
     const void *ptrs[] = {o, dout, delta};
@@ -207,6 +208,7 @@ int attn_bwd_preprocess(const void *o, const void *dout, float *delta, int B, in
     a.delta = delta;
     a.B = B;
     a.H = H;
+    a.Hk = H;
     a.Nq = a.Nk = N;
     a.d = d;
     a.stream = stream;
@@ -217,7 +219,7 @@ int attn_bwd_dkdv(const void *q, const void *k, const void *v, const void *dout,
                   void *dk, void *dv, int B, int H, int N, int d, int causal, float scale, void *stream)
 {
     bool empty = false;
-    RETURN_IF(validate_common(B, H, N, N, d, causal, scale, &empty));
+    RETURN_IF(validate_common(B, H, H, N, N, d, causal, scale, &empty));
     if (empty) return ATTN_OK;
     const long long tb = tensor_bytes(B, H, N, d), lb = vector_bytes(B, H, N);
     const void *ptrs[] = {q, k, v, dout, lse, delta, dk, dv};
@@ -238,6 +240,7 @@ int attn_bwd_dkdv(const void *q, const void *k, const void *v, const void *dout,
     a.dv = dv;
     a.B = B;
     a.H = H;
+    a.Hk = H;
     a.Nq = a.Nk = N;
     a.d = d;
     a.causal = causal;
@@ -250,7 +253,7 @@ int attn_bwd_dq(const void *q, const void *k, const void *v, const void *dout, c
                 void *dq, int B, int H, int N, int d, int causal, float scale, void *stream)
 {
     bool empty = false;
-    RETURN_IF(validate_common(B, H, N, N, d, causal, scale, &empty));
+    RETURN_IF(validate_common(B, H, H, N, N, d, causal, scale, &empty));
     if (empty) return ATTN_OK;
     const long long tb = tensor_bytes(B, H, N, d), lb = vector_bytes(B, H, N);
     const void *ptrs[] = {q, k, v, dout, lse, delta, dq};
@@ -270,6 +273,7 @@ int attn_bwd_dq(const void *q, const void *k, const void *v, const void *dout, c
     a.dq = dq;
     a.B = B;
     a.H = H;
+    a.Hk = H;
     a.Nq = a.Nk = N;
     a.d = d;
     a.causal = causal;
@@ -281,14 +285,14 @@ int attn_bwd_dq(const void *q, const void *k, const void *v, const void *dout, c
 int attn_bwd(const void *q, const void *k, const void *v, const void *o, const void *dout, const float *lse, void *dq,
              void *dk, void *dv, float *delta, int B, int H, int N, int d, int causal, float scale, void *stream)
 {
-    return bwd_impl(q, k, v, o, dout, lse, dq, dk, dv, delta, B, H, N, N, d, causal, scale, stream);
+    return bwd_impl(q, k, v, o, dout, lse, dq, dk, dv, delta, B, H, H, N, N, d, causal, scale, stream);
 }
 
 int attn_bwd_qk(const void *q, const void *k, const void *v, const void *o, const void *dout, const float *lse,
-                void *dq, void *dk, void *dv, float *delta, int B, int H, int Nq, int Nk, int d, int causal,
+                void *dq, void *dk, void *dv, float *delta, int B, int H, int Hk, int Nq, int Nk, int d, int causal,
                 float scale, void *stream)
 {
-    return bwd_impl(q, k, v, o, dout, lse, dq, dk, dv, delta, B, H, Nq, Nk, d, causal, scale, stream);
+    return bwd_impl(q, k, v, o, dout, lse, dq, dk, dv, delta, B, H, Hk, Nq, Nk, d, causal, scale, stream);
 }
 
 const char *attn_status_string(int status)
@@ -296,7 +300,8 @@ const char *attn_status_string(int status)
     switch (status) {
     case ATTN_OK: return "ok";
     case ATTN_ERR_NULLPTR: return "a required pointer is NULL";
-    case ATTN_ERR_BAD_SHAPE: return "bad shape: B, H and the lengths must be >= 0 and within the size limits";
+    case ATTN_ERR_BAD_SHAPE:
+        return "bad shape: B, H, Hk and the lengths must be >= 0 and within the size limits, H a multiple of Hk";
     case ATTN_ERR_UNSUPPORTED_D: return "unsupported head dimension: d must be 64 or 128";
     case ATTN_ERR_MISALIGNED: return "a pointer is not 16-byte aligned";
     case ATTN_ERR_BAD_SCALE: return "scale must be finite and > 0";

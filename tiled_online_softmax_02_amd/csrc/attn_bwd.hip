@@ -62,7 +62,7 @@ template <int D, bool CAUSAL>
 __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(
     const bf16 *__restrict__ Q, const bf16 *__restrict__ K, const bf16 *__restrict__ V, const bf16 *__restrict__ dO,
     const float *__restrict__ LSE, const float *__restrict__ Dl, bf16 *__restrict__ dK, bf16 *__restrict__ dV, int Nq, int Nk,
-    int n_ktiles, float scale, float c_log2)
+    int H, int G, int n_ktiles, float scale, float c_log2)
 {
     constexpr int NKS = D / 16;
     constexpr int NDB = D / 32;
@@ -72,20 +72,28 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(
     __shared__ __attribute__((aligned(16))) char q0_raw[TILE], q1_raw[TILE], g0_raw[TILE], g1_raw[TILE];
     __shared__ __attribute__((aligned(16))) float s0_raw[2 * kKvBM], s1_raw[2 * kKvBM];  // lse, then D
 
+    // `head` is a K/V head (one of B * H/G); its G query heads (grouped-query attention; G = 1
+    // for multi-head attention) all add to its dK and dV.
     int head, ktile;
     work_item(blockIdx.x, n_ktiles, head, ktile);  // causal: key block 0 sees the most queries and goes first
+    const int Hk = H / G;
+    const int qh0 = (head / Hk) * H + (head % Hk) * G;  // first query head of the group
 
     const int tid = threadIdx.x;
     const int lane = tid & 63, h = lane >> 5, c32 = lane & 31;
     const int w = wave_uniform(tid >> 6);
-    const size_t hoff_q = (size_t)head * (size_t)Nq * D;  // Q and dO of this head
     const size_t hoff = (size_t)head * (size_t)Nk * D;    // K, V, dK and dV of this head
-    const __amdgpu_buffer_rsrc_t rq = make_rsrc(Q + hoff_q, (uint32_t)Nq * D * 2);
     const __amdgpu_buffer_rsrc_t rk = make_rsrc(K + hoff, (uint32_t)Nk * D * 2);
     const __amdgpu_buffer_rsrc_t rv = make_rsrc(V + hoff, (uint32_t)Nk * D * 2);
-    const __amdgpu_buffer_rsrc_t rg = make_rsrc(dO + hoff_q, (uint32_t)Nq * D * 2);
-    const __amdgpu_buffer_rsrc_t rl = make_rsrc(LSE + (size_t)head * Nq, (uint32_t)Nq * 4);
-    const __amdgpu_buffer_rsrc_t rd = make_rsrc(Dl + (size_t)head * Nq, (uint32_t)Nq * 4);
+    // Q, dO, lse and D of the query head being worked on
+    __amdgpu_buffer_rsrc_t rq, rg, rl, rd;
+    auto bind_query_head = [&](int qh) __attribute__((always_inline)) {
+        const size_t hoff_q = (size_t)qh * (size_t)Nq * D;
+        rq = make_rsrc(Q + hoff_q, (uint32_t)Nq * D * 2);
+        rg = make_rsrc(dO + hoff_q, (uint32_t)Nq * D * 2);
+        rl = make_rsrc(LSE + (size_t)qh * Nq, (uint32_t)Nq * 4);
+        rd = make_rsrc(Dl + (size_t)qh * Nq, (uint32_t)Nq * 4);
+    };
     // Causal mask with bottom-right alignment: query i sees keys j <= i + off.
     const int off = Nk - Nq;
 
@@ -127,9 +135,6 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(
 
     using P0 = std::integral_constant<int, 0>;
     using P1 = std::integral_constant<int, 1>;
-    load_blk(0, P0{});
-    wait_vmem();
-    __syncthreads();
 
     auto step = [&](int i, auto par) __attribute__((always_inline)) {
         using PN = std::integral_constant<int, 1 - decltype(par)::value>;
@@ -234,12 +239,18 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(
         __syncthreads();
     };
 
-    int i = 0;
-    for (; i + 1 < nsteps; i += 2) {
-        step(i, P0{});
-        step(i + 1, P1{});
+    for (int gq = 0; gq < G; ++gq) {
+        bind_query_head(qh0 + gq);
+        load_blk(0, P0{});  // the previous query head's last step ended with a barrier
+        wait_vmem();
+        __syncthreads();
+        int i = 0;
+        for (; i + 1 < nsteps; i += 2) {
+            step(i, P0{});
+            step(i + 1, P1{});
+        }
+        if (i < nsteps) step(i, P0{});
     }
-    if (i < nsteps) step(i, P0{});
 
     if (key < Nk) {
         bf16 *dkrow = dK + hoff + (size_t)key * D;
@@ -269,8 +280,8 @@ constexpr int kQBN = 64;   // keys per streamed block
 template <int D, bool CAUSAL>
 __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(
     const bf16 *__restrict__ Q, const bf16 *__restrict__ K, const bf16 *__restrict__ V, const bf16 *__restrict__ dO,
-    const float *__restrict__ LSE, const float *__restrict__ Dl, bf16 *__restrict__ dQ, int Nq, int Nk, int n_qtiles,
-    float scale, float c_log2)
+    const float *__restrict__ LSE, const float *__restrict__ Dl, bf16 *__restrict__ dQ, int Nq, int Nk, int H, int G,
+    int n_qtiles, float scale, float c_log2)
 {
     constexpr int NKS = D / 16;
     constexpr int NDB = D / 32;
@@ -285,7 +296,9 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(
     const int lane = tid & 63, h = lane >> 5, c32 = lane & 31;
     const int w = wave_uniform(tid >> 6);
     const size_t hoff = (size_t)head * (size_t)Nq * D;    // Q, dO and dQ of this head
-    const size_t hoff_k = (size_t)head * (size_t)Nk * D;  // K and V of this head
+    // K and V of the query head's K/V head (grouped-query attention: G query heads per K/V head)
+    const int kvh = (head / H) * (H / G) + (head % H) / G;
+    const size_t hoff_k = (size_t)kvh * (size_t)Nk * D;
     const __amdgpu_buffer_rsrc_t rq = make_rsrc(Q + hoff, (uint32_t)Nq * D * 2);
     const __amdgpu_buffer_rsrc_t rk = make_rsrc(K + hoff_k, (uint32_t)Nk * D * 2);
     const __amdgpu_buffer_rsrc_t rv = make_rsrc(V + hoff_k, (uint32_t)Nk * D * 2);
@@ -419,11 +432,11 @@ template <int D, bool CAUSAL>
 hipError_t launch_dkdv_t(const BwdArgs &a)
 {
     const int n_ktiles = (a.Nk + kKvBN - 1) / kKvBN;
-    const long long G = (long long)a.B * a.H * n_ktiles;
+    const long long G = (long long)a.B * a.Hk * n_ktiles;
     if (G == 0) return hipSuccess;
     hipLaunchKernelGGL((bwd_dkdv_kernel<D, CAUSAL>), dim3((unsigned)G), dim3(kThreads), 0, (hipStream_t)a.stream,
                        (const bf16 *)a.q, (const bf16 *)a.k, (const bf16 *)a.v, (const bf16 *)a.dout, a.lse,
-                       (const float *)a.delta, (bf16 *)a.dk, (bf16 *)a.dv, a.Nq, a.Nk, n_ktiles, a.scale, a.scale * kLog2e);
+                       (const float *)a.delta, (bf16 *)a.dk, (bf16 *)a.dv, a.Nq, a.Nk, a.H, a.H / a.Hk, n_ktiles, a.scale, a.scale * kLog2e);
     return hipGetLastError();
 }
 
@@ -435,7 +448,7 @@ hipError_t launch_dq_t(const BwdArgs &a)
     if (G == 0) return hipSuccess;
     hipLaunchKernelGGL((bwd_dq_kernel<D, CAUSAL>), dim3((unsigned)G), dim3(kThreads), 0, (hipStream_t)a.stream,
                        (const bf16 *)a.q, (const bf16 *)a.k, (const bf16 *)a.v, (const bf16 *)a.dout, a.lse,
-                       (const float *)a.delta, (bf16 *)a.dq, a.Nq, a.Nk, n_qtiles, a.scale, a.scale * kLog2e);
+                       (const float *)a.delta, (bf16 *)a.dq, a.Nq, a.Nk, a.H, a.H / a.Hk, n_qtiles, a.scale, a.scale * kLog2e);
     return hipGetLastError();
 }
 
@@ -458,7 +471,7 @@ hipError_t launch_bwd_dq(const BwdArgs &a)
     return a.causal ? launch_dq_t<128, true>(a) : launch_dq_t<128, false>(a);
 }
 
-long long bwd_dkdv_grid_size(int B, int H, int Nk) { return (long long)B * H * ((Nk + kKvBN - 1) / kKvBN); }
+long long bwd_dkdv_grid_size(int B, int Hk, int Nk) { return (long long)B * Hk * ((Nk + kKvBN - 1) / kKvBN); }
 long long bwd_dq_grid_size(int B, int H, int Nq) { return (long long)B * H * ((Nq + kQBM - 1) / kQBM); }
 
 }  // namespace attn

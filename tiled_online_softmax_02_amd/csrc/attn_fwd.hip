@@ -62,8 +62,8 @@ struct FwdSmem {
 template <int D, bool CAUSAL, bool SPLIT>
 __global__ __launch_bounds__(64 * fwd_waves<D>(), 8 / fwd_waves<D>()) void fwd_kernel(const bf16 *__restrict__ Q, const bf16 *__restrict__ K,
                                                           const bf16 *__restrict__ V, bf16 *__restrict__ O,
-                                                          float *__restrict__ LSE, int Nq, int Nk, int n_qtiles, float scale,
-                                                          float c_log2, int n_splits, int split_blocks,
+                                                          float *__restrict__ LSE, int Nq, int Nk, int H, int G, int n_qtiles,
+                                                          float scale, float c_log2, int n_splits, int split_blocks,
                                                           float *__restrict__ OP, float *__restrict__ LP)
 {
     using L = FwdSmem<D>;
@@ -88,7 +88,9 @@ __global__ __launch_bounds__(64 * fwd_waves<D>(), 8 / fwd_waves<D>()) void fwd_k
     const int lane = tid & 63, h = lane >> 5, c32 = lane & 31;
     const int w = wave_uniform(tid >> 6);
     const size_t hoff = (size_t)head * (size_t)Nq * D;    // Q and O of this head
-    const size_t hoff_k = (size_t)head * (size_t)Nk * D;  // K and V of this head
+    // K and V of the query head's K/V head (grouped-query attention: G query heads per K/V head)
+    const int kvh = (head / H) * (H / G) + (head % H) / G;
+    const size_t hoff_k = (size_t)kvh * (size_t)Nk * D;
     const __amdgpu_buffer_rsrc_t rq = make_rsrc(Q + hoff, (uint32_t)Nq * D * 2);
     const __amdgpu_buffer_rsrc_t rk = make_rsrc(K + hoff_k, (uint32_t)Nk * D * 2);
     const __amdgpu_buffer_rsrc_t rv = make_rsrc(V + hoff_k, (uint32_t)Nk * D * 2);
@@ -346,7 +348,7 @@ hipError_t launch_fwd_t(const FwdArgs &a)
     const float c_log2 = a.scale * kLog2e;
     hipLaunchKernelGGL((fwd_kernel<D, CAUSAL, false>), dim3((unsigned)G), dim3(kThreads), 0, (hipStream_t)a.stream,
                        (const bf16 *)a.q, (const bf16 *)a.k, (const bf16 *)a.v, (bf16 *)a.o, a.lse, a.Nq, a.Nk,
-                       n_qtiles, a.scale, c_log2, 1, 0, (float *)nullptr, (float *)nullptr);
+                       a.H, a.H / a.Hk, n_qtiles, a.scale, c_log2, 1, 0, (float *)nullptr, (float *)nullptr);
     return hipGetLastError();
 }
 
@@ -396,7 +398,7 @@ hipError_t launch_fwd_split_t(const FwdArgs &a, int n_splits, float *op, float *
     const float c_log2 = a.scale * kLog2e;
     hipLaunchKernelGGL((fwd_kernel<D, CAUSAL, true>), dim3((unsigned)G), dim3(kThreads), 0, (hipStream_t)a.stream,
                        (const bf16 *)a.q, (const bf16 *)a.k, (const bf16 *)a.v, (bf16 *)a.o, a.lse, a.Nq, a.Nk,
-                       n_qtiles, a.scale, c_log2, n_splits, split_blocks, op, lp);
+                       a.H, a.H / a.Hk, n_qtiles, a.scale, c_log2, n_splits, split_blocks, op, lp);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     const long long rows = (long long)a.B * a.H * a.Nq;

@@ -10,7 +10,7 @@ struct FwdArgs {
     const void *q, *k, *v;
     void *o;
     float *lse;
-    int B, H, Nq, Nk, d, causal;  // Nq query rows, Nk key rows per head
+    int B, H, Hk, Nq, Nk, d, causal;  // H query heads, Hk K/V heads; Nq query rows, Nk key rows per head
     float scale;
     void *stream;
 };
@@ -20,7 +20,7 @@ struct BwdArgs {
     const float *lse;
     void *dq, *dk, *dv;
     float *delta;
-    int B, H, Nq, Nk, d, causal;  // Nq query rows, Nk key rows per head
+    int B, H, Hk, Nq, Nk, d, causal;  // H query heads, Hk K/V heads; Nq query rows, Nk key rows per head
     float scale;
     void *stream;
 };
@@ -36,7 +36,7 @@ long long fwd_grid_size(int B, int H, int Nq);
 long long fwd_split_grid_size(int B, int H, int Nq, int n_splits);
 long long fwd_split_workspace_bytes(int B, int H, int Nq, int d, int n_splits);
 int fwd_split_default(int B, int H, int Nq, int Nk, int d);
-long long bwd_dkdv_grid_size(int B, int H, int Nk);
+long long bwd_dkdv_grid_size(int B, int Hk, int Nk);
 long long bwd_dq_grid_size(int B, int H, int Nq);
 
 }  // namespace attn
