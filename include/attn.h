@@ -48,7 +48,7 @@
  * The library never aborts or prints.  An empty problem (B, H or N equal to 0)
  * is valid, enqueues nothing and returns ATTN_OK; more generally a pointer to a
  * buffer of zero bytes may be NULL.
- * Sizes: B, H, Hk, N (Nq, Nk) >= 0; d in {64, 128}; B*H*N*d < 2^62;
+ * Sizes: B, H, Hk, N (Nq, Nk) >= 0; d in {64, 128, 192, 256}; B*H*N*d < 2^62;
  * (N + 256)*d*2 < 2^32 for N = Nq and N = Nk.  Pointers must be 16-byte aligned.
  */
 #ifndef ATTN_H_
@@ -62,7 +62,7 @@ enum attn_status {
     ATTN_OK = 0,
     ATTN_ERR_NULLPTR = 1,        /* a required pointer is NULL (non-empty problem) */
     ATTN_ERR_BAD_SHAPE = 2,      /* a size negative, H not a multiple of Hk, or a limit exceeded */
-    ATTN_ERR_UNSUPPORTED_D = 3,  /* head dimension d is not 64 or 128 */
+    ATTN_ERR_UNSUPPORTED_D = 3,  /* head dimension d is not 64, 128, 192 or 256 */
     ATTN_ERR_MISALIGNED = 4,     /* a pointer is not 16-byte aligned */
     ATTN_ERR_BAD_SCALE = 5,      /* scale is not finite or not > 0 */
     ATTN_ERR_BAD_ARG = 6,        /* causal is not 0 or 1, or num_splits is not in 1..256 */

@@ -62,7 +62,8 @@ def fwd(lib, q=P[0], k=P[1], v=P[2], o=P[3], lse=P[4], B=1, H=1, N=64, d=64, cau
     (dict(N=-1), A.ATTN_ERR_BAD_SHAPE),
     (dict(d=96), A.ATTN_ERR_UNSUPPORTED_D),
     (dict(d=0), A.ATTN_ERR_UNSUPPORTED_D),
-    (dict(d=256), A.ATTN_ERR_UNSUPPORTED_D),
+    (dict(d=320), A.ATTN_ERR_UNSUPPORTED_D),
+    (dict(d=160), A.ATTN_ERR_UNSUPPORTED_D),
     (dict(N=1 << 24, d=128), A.ATTN_ERR_BAD_SHAPE),   # (N+256)*d*2 > 2^32
     (dict(N=(1 << 24) - 200, d=128), A.ATTN_ERR_BAD_SHAPE),  # (N+256)*d*2 just above 2^32
     (dict(causal=2), A.ATTN_ERR_BAD_ARG),

@@ -27,7 +27,7 @@ int check_shape(int B, int H, int Hk, int Nq, int Nk, int d, bool *empty)
 {
     if (B < 0 || H < 0 || Hk < 0 || Nq < 0 || Nk < 0) return ATTN_ERR_BAD_SHAPE;
     if (H > 0 && (Hk < 1 || H % Hk != 0)) return ATTN_ERR_BAD_SHAPE;
-    if (d != 64 && d != 128) return ATTN_ERR_UNSUPPORTED_D;
+    if (d != 64 && d != 128 && d != 192 && d != 256) return ATTN_ERR_UNSUPPORTED_D;
     const long long rows_q = (long long)B * H * Nq, rows_k = (long long)B * Hk * Nk;
     if (rows_q > ((1LL << 62) / d) || rows_k > ((1LL << 62) / d)) return ATTN_ERR_BAD_SHAPE;
     // per-head byte offsets, including the padding rows of the last tile, are 32-bit
@@ -302,7 +302,7 @@ const char *attn_status_string(int status)
     case ATTN_ERR_NULLPTR: return "a required pointer is NULL";
     case ATTN_ERR_BAD_SHAPE:
         return "bad shape: B, H, Hk and the lengths must be >= 0 and within the size limits, H a multiple of Hk";
-    case ATTN_ERR_UNSUPPORTED_D: return "unsupported head dimension: d must be 64 or 128";
+    case ATTN_ERR_UNSUPPORTED_D: return "unsupported head dimension: d must be 64, 128, 192 or 256";
     case ATTN_ERR_MISALIGNED: return "a pointer is not 16-byte aligned";
     case ATTN_ERR_BAD_SCALE: return "scale must be finite and > 0";
     case ATTN_ERR_BAD_ARG: return "causal must be 0 or 1 and num_splits in 1..256";

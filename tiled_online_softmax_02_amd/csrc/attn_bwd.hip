@@ -37,25 +37,33 @@ __global__ __launch_bounds__(kThreads) void bwd_preprocess_kernel(const bf16 *__
                                                                   const bf16 *__restrict__ dO,
                                                                   float *__restrict__ Dl, long long rows)
 {
-    constexpr int CPR = D / 8;            // lanes per row, 8 elements each
-    constexpr int RPB = kThreads / CPR;   // rows per workgroup
-    const long long row = (long long)blockIdx.x * RPB + threadIdx.x / CPR;
-    const int c = threadIdx.x % CPR;
+    constexpr int CPR = D / 8;                              // 8-element chunks per row
+    constexpr int LPR = CPR <= 8 ? 8 : CPR <= 16 ? 16 : 32;  // lanes per row (a power of two)
+    constexpr int RPB = kThreads / LPR;                     // rows per workgroup
+    const long long row = (long long)blockIdx.x * RPB + threadIdx.x / LPR;
+    const int c = threadIdx.x % LPR;
     float acc = 0.f;
-    if (row < rows) {
+    if (row < rows && c < CPR) {
         const bf16x8 o = *(const bf16x8 *)(O + row * D + 8 * c);
         const bf16x8 g = *(const bf16x8 *)(dO + row * D + 8 * c);
 #pragma unroll
         for (int e = 0; e < 8; ++e) acc = fmaf((float)o[e], (float)g[e], acc);
     }
 #pragma unroll
-    for (int off = CPR / 2; off > 0; off >>= 1) acc += __shfl_xor(acc, off);
+    for (int off = LPR / 2; off > 0; off >>= 1) acc += __shfl_xor(acc, off);
     if (row < rows && c == 0) Dl[row] = acc;
 }
 
 // ------------------------------------------------------------ dK / dV
 
-constexpr int kKvBN = 128;  // keys per workgroup (32 per wave)
+// d <= 128: each of the 4 waves owns 32 keys (128 keys per workgroup) and all of d.  d = 192
+// and 256: the dK/dV accumulators of 32 keys over all of d do not fit next to the K and V
+// fragments, so waves w and w + 2 share 32 keys and take one half of the columns of dK and dV
+// each (64 keys per workgroup); both compute the same S and dP.
+template <int D>
+constexpr bool kv_dsplit() { return D >= 192; }
+template <int D>
+constexpr int kv_bn() { return kv_dsplit<D>() ? 64 : 128; }
 constexpr int kKvBM = 64;   // queries per streamed block
 
 template <int D, bool CAUSAL>
@@ -97,8 +105,11 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(
     // Causal mask with bottom-right alignment: query i sees keys j <= i + off.
     const int off = Nk - Nq;
 
+    constexpr int kKvBN = kv_bn<D>();
+    constexpr int NDBH = kv_dsplit<D>() ? NDB / 2 : NDB;  // 32-column blocks of dK, dV per wave
+    const int db0 = kv_dsplit<D>() ? (w >> 1) * NDBH : 0;  // first of them
     const int k0 = ktile * kKvBN;
-    const int kw0 = k0 + 32 * w;  // wave-uniform
+    const int kw0 = k0 + 32 * (kv_dsplit<D>() ? (w & 1) : w);  // wave-uniform
     const int key = kw0 + c32;
 
     // K and V fragments (B operands of S = Q K^T and dP = dO V^T): lane holds row `key` (zeros past Nk).
@@ -109,9 +120,9 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(
         vf[ks] = __builtin_bit_cast(bf16x8, buffer_load16(rv, (uint32_t)(key * D + 16 * ks + 8 * h) * 2u));
     }
 
-    f32x16 dk[NDB], dv[NDB];
+    f32x16 dk[NDBH], dv[NDBH];
 #pragma unroll
-    for (int i = 0; i < NDB; ++i) {
+    for (int i = 0; i < NDBH; ++i) {
         dk[i] = zero16();
         dv[i] = zero16();
     }
@@ -152,9 +163,9 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(
             // queries 32..63 during C.  LDS fragments are fetched PF chunks ahead; scheduling
             // barriers keep each chunk whole.
             const bool need_mask = CAUSAL && (qs + off < kw0 + 31);
-            constexpr int PH = 2 * NKS;  // chunks per phase
-            constexpr int NC = 4 * PH;
-            static_assert(4 * NDB == PH, "a dV/dK phase has as many MFMAs as an S/dP phase");
+            constexpr int PA = 2 * NKS;   // chunks of an S/dP phase (A, B)
+            constexpr int PC = 4 * NDBH;  // chunks of a dV/dK phase (C, D): 2 groups of 16 queries x NDBH x 2
+            constexpr int NC = 2 * PA + 2 * PC;
             constexpr int PF = 3;
             f32x16 s[2], dp[2];
             bf16x8 pb[4], sb[4];
@@ -163,14 +174,14 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(
             for (int qb = 0; qb < 2; ++qb) s[qb] = dp[qb] = zero16();
             auto fetch = [&](auto C) __attribute__((always_inline)) {
                 constexpr int c = decltype(C)::value;
-                if constexpr (c < 2 * PH) {
-                    constexpr int qb = c / PH, m = c % PH, kst = m / 2;
+                if constexpr (c < 2 * PA) {
+                    constexpr int qb = c / PA, m = c % PA, kst = m / 2;
                     return lds_read16((m & 1) ? g_l : q_l, swz_off<D>(32 * qb + c32, 2 * kst + h));
                 } else {
-                    constexpr int qb = (c - 2 * PH) / PH, n = (c - 2 * PH) % PH;
-                    constexpr int t = 2 * qb + n / (2 * NDB), db = (n / 2) % NDB;
-                    // dV takes dO^T, dK takes Q^T
-                    return lds_read_tr_rows_swz<D>((n & 1) ? q_l : g_l, 16 * t, 32 * db, lane);
+                    constexpr int qb = (c - 2 * PA) / PC, n = (c - 2 * PA) % PC;
+                    constexpr int t = 2 * qb + n / (2 * NDBH), db = (n / 2) % NDBH;
+                    // dV takes dO^T, dK takes Q^T (columns of this wave's part of d)
+                    return lds_read_tr_rows_swz<D>((n & 1) ? q_l : g_l, 16 * t, 32 * (db0 + db), lane);
                 }
             };
             bf16x8 fr[PF + 1];
@@ -179,33 +190,33 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(
                 constexpr int c = decltype(C)::value;
                 if constexpr (c + PF < NC) fr[(c + PF) % (PF + 1)] = fetch(std::integral_constant<int, c + PF>{});
                 // lse and D of a half's rows, read one phase before they are needed
-                if constexpr (c % PH < 8 && c < 2 * PH) {
-                    constexpr int qb = c / PH, g = (c % PH) / 2;
+                if constexpr (c % PA < 8 && c < 2 * PA) {
+                    constexpr int qb = c / PA, g = (c % PA) / 2;
                     const int qloc = 32 * qb + 8 * g + 4 * h;  // first of 4 consecutive queries
-                    if constexpr ((c % PH) % 2 == 0)
+                    if constexpr ((c % PA) % 2 == 0)
                         l4[qb][g] = *(const __attribute__((address_space(3))) f32x4 *)(st_l + 4 * qloc);
                     else
                         d4[qb][g] = *(const __attribute__((address_space(3))) f32x4 *)(st_l + 4 * (kKvBM + qloc));
                 }
                 const bf16x8 fc = fr[c % (PF + 1)];
-                if constexpr (c < 2 * PH) {
-                    constexpr int qb = c / PH, m = c % PH, kst = m / 2;
+                if constexpr (c < 2 * PA) {
+                    constexpr int qb = c / PA, m = c % PA, kst = m / 2;
                     if constexpr (m & 1)
                         dp[qb] = mfma(fc, vf[kst], dp[qb]);
                     else
                         s[qb] = mfma(fc, kf[kst], s[qb]);
                 } else {
-                    constexpr int qb = (c - 2 * PH) / PH, n = (c - 2 * PH) % PH;
-                    constexpr int t = 2 * qb + n / (2 * NDB), db = (n / 2) % NDB;
+                    constexpr int qb = (c - 2 * PA) / PC, n = (c - 2 * PA) % PC;
+                    constexpr int t = 2 * qb + n / (2 * NDBH), db = (n / 2) % NDBH;
                     if constexpr (n & 1)
                         dk[db] = mfma(fc, sb[t], dk[db]);
                     else
                         dv[db] = mfma(fc, pb[t], dv[db]);
                 }
-                if constexpr (c == PH || c == 2 * PH) {
+                if constexpr (c == PA || c == 2 * PA) {
                     // On blocks that cross the diagonal, scores of queries before this lane's key
                     // become -inf (P = 0) before their half is exponentiated; other blocks skip this.
-                    constexpr int qb = c / PH - 1;
+                    constexpr int qb = c / PA - 1;
                     if (need_mask) {
 #pragma unroll
                         for (int r = 0; r < 16; ++r)
@@ -219,18 +230,20 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(
                         }
                     }
                 }
-                if constexpr (c >= PH && c < 3 * PH) {
-                    // P = exp2(S scale log2e - lse log2e), dS = P (dP - D) for half qb
-                    constexpr int qb = (c - PH) / PH, i = (c - PH) % PH;
-                    constexpr int E = 16 / PH;
-#pragma unroll
-                    for (int e = 0; e < E; ++e) {
-                        const int r = i * E + e, g = r >> 2, u = r & 3;
-                        float p = fast_exp2(fmaf(s[qb][r], c_log2, -l4[qb][g][u] * kLog2e));
+                if constexpr (c >= PA && c < 2 * PA + PC) {
+                    // P = exp2(S scale log2e - lse log2e), dS = P (dP - D) for half qb: the
+                    // first half during phase B, the second during phase C; chunk i of a phase of
+                    // L chunks takes elements [16 i / L, 16 (i + 1) / L)
+                    constexpr int qb = c < 2 * PA ? 0 : 1;
+                    constexpr int L = c < 2 * PA ? PA : PC;
+                    constexpr int i = c < 2 * PA ? c - PA : c - 2 * PA;
+                    static_for<i * 16 / L, (i + 1) * 16 / L>([&](auto RR) __attribute__((always_inline)) {
+                        constexpr int r = decltype(RR)::value, g = r >> 2, u = r & 3;
+                        const float p = fast_exp2(fmaf(s[qb][r], c_log2, -l4[qb][g][u] * kLog2e));
                         const float ds = p * (dp[qb][r] - d4[qb][g][u]);
                         pb[2 * qb + (r >> 3)][r & 7] = (bf16)p;
                         sb[2 * qb + (r >> 3)][r & 7] = (bf16)ds;
-                    }
+                    });
                 }
                 __builtin_amdgcn_sched_barrier(0);
             });
@@ -256,7 +269,7 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(
         bf16 *dkrow = dK + hoff + (size_t)key * D;
         bf16 *dvrow = dV + hoff + (size_t)key * D;
 #pragma unroll
-        for (int db = 0; db < NDB; ++db) {
+        for (int db = 0; db < NDBH; ++db) {
 #pragma unroll
             for (int g = 0; g < 4; ++g) {
                 bf16x4 kv4, vv4;
@@ -265,8 +278,8 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(
                     kv4[u] = (bf16)(dk[db][4 * g + u] * scale);
                     vv4[u] = (bf16)dv[db][4 * g + u];
                 }
-                *(bf16x4 *)(dkrow + 32 * db + 8 * g + 4 * h) = kv4;
-                *(bf16x4 *)(dvrow + 32 * db + 8 * g + 4 * h) = vv4;
+                *(bf16x4 *)(dkrow + 32 * (db0 + db) + 8 * g + 4 * h) = kv4;
+                *(bf16x4 *)(dvrow + 32 * (db0 + db) + 8 * g + 4 * h) = vv4;
             }
         }
     }
@@ -278,7 +291,7 @@ constexpr int kQBM = 128;  // queries per workgroup (32 per wave)
 constexpr int kQBN = 64;   // keys per streamed block
 
 template <int D, bool CAUSAL>
-__global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(
+__global__ __launch_bounds__(kThreads, D >= 192 ? 1 : 2) void bwd_dq_kernel(
     const bf16 *__restrict__ Q, const bf16 *__restrict__ K, const bf16 *__restrict__ V, const bf16 *__restrict__ dO,
     const float *__restrict__ LSE, const float *__restrict__ Dl, bf16 *__restrict__ dQ, int Nq, int Nk, int H, int G,
     int n_qtiles, float scale, float c_log2)
@@ -419,7 +432,7 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(
 template <int D>
 hipError_t launch_pre_t(const BwdArgs &a)
 {
-    constexpr int RPB = kThreads / (D / 8);
+    constexpr int RPB = kThreads / (D / 8 <= 8 ? 8 : D / 8 <= 16 ? 16 : 32);
     const long long rows = (long long)a.B * a.H * a.Nq;
     const long long G = (rows + RPB - 1) / RPB;
     if (G == 0) return hipSuccess;
@@ -431,7 +444,7 @@ hipError_t launch_pre_t(const BwdArgs &a)
 template <int D, bool CAUSAL>
 hipError_t launch_dkdv_t(const BwdArgs &a)
 {
-    const int n_ktiles = (a.Nk + kKvBN - 1) / kKvBN;
+    const int n_ktiles = (a.Nk + kv_bn<D>() - 1) / kv_bn<D>();
     const long long G = (long long)a.B * a.Hk * n_ktiles;
     if (G == 0) return hipSuccess;
     hipLaunchKernelGGL((bwd_dkdv_kernel<D, CAUSAL>), dim3((unsigned)G), dim3(kThreads), 0, (hipStream_t)a.stream,
@@ -456,22 +469,35 @@ hipError_t launch_dq_t(const BwdArgs &a)
 
 hipError_t launch_bwd_preprocess(const BwdArgs &a)
 {
-    return a.d == 64 ? launch_pre_t<64>(a) : launch_pre_t<128>(a);
+    switch (a.d) {
+    case 64: return launch_pre_t<64>(a);
+    case 128: return launch_pre_t<128>(a);
+    case 192: return launch_pre_t<192>(a);
+    default: return launch_pre_t<256>(a);
+    }
 }
 
 hipError_t launch_bwd_dkdv(const BwdArgs &a)
 {
-    if (a.d == 64) return a.causal ? launch_dkdv_t<64, true>(a) : launch_dkdv_t<64, false>(a);
-    return a.causal ? launch_dkdv_t<128, true>(a) : launch_dkdv_t<128, false>(a);
+    switch (a.d) {
+    case 64: return a.causal ? launch_dkdv_t<64, true>(a) : launch_dkdv_t<64, false>(a);
+    case 128: return a.causal ? launch_dkdv_t<128, true>(a) : launch_dkdv_t<128, false>(a);
+    case 192: return a.causal ? launch_dkdv_t<192, true>(a) : launch_dkdv_t<192, false>(a);
+    default: return a.causal ? launch_dkdv_t<256, true>(a) : launch_dkdv_t<256, false>(a);
+    }
 }
 
 hipError_t launch_bwd_dq(const BwdArgs &a)
 {
-    if (a.d == 64) return a.causal ? launch_dq_t<64, true>(a) : launch_dq_t<64, false>(a);
-    return a.causal ? launch_dq_t<128, true>(a) : launch_dq_t<128, false>(a);
+    switch (a.d) {
+    case 64: return a.causal ? launch_dq_t<64, true>(a) : launch_dq_t<64, false>(a);
+    case 128: return a.causal ? launch_dq_t<128, true>(a) : launch_dq_t<128, false>(a);
+    case 192: return a.causal ? launch_dq_t<192, true>(a) : launch_dq_t<192, false>(a);
+    default: return a.causal ? launch_dq_t<256, true>(a) : launch_dq_t<256, false>(a);
+    }
 }
 
-long long bwd_dkdv_grid_size(int B, int Hk, int Nk) { return (long long)B * Hk * ((Nk + kKvBN - 1) / kKvBN); }
+long long bwd_dkdv_grid_size(int B, int Hk, int Nk) { return (long long)B * Hk * ((Nk + kv_bn<256>() - 1) / kv_bn<256>()); }
 long long bwd_dq_grid_size(int B, int H, int Nq) { return (long long)B * H * ((Nq + kQBM - 1) / kQBM); }
 
 }  // namespace attn

@@ -161,14 +161,19 @@ namespace attn {
 // Swizzled LDS tiles: rows of D bf16 (2*D bytes, no padding) whose 16-byte
 // chunks are permuted per row, physical chunk = logical chunk ^ lds_swz<D>(row).
 // The map XORs fixed chunk masks selected by the low four row bits; it keeps both
-// access patterns of the kernels free of bank conflicts: 16-byte reads of one
-// chunk column by 16 consecutive rows, and the transposing 8-byte reads of
-// 4 consecutive rows x 4 consecutive chunks.  Only bits 0..3 of the row matter,
-// so the map is linear over row blocks aligned to 16.
+// access patterns of the kernels free of bank conflicts (64 banks of 4 bytes):
+// 16-byte reads of one chunk column by 16 consecutive rows, and the transposing
+// 8-byte reads of 4 consecutive rows x 4 consecutive chunks.  Only bits 0..3 of
+// the row matter, so the map is linear over row blocks aligned to 16.  The masks
+// stay below the number of chunks per row (for D = 192, 24 chunks, below 8, so
+// that a chunk never leaves its group of 8).
 template <int D>
 __device__ __forceinline__ int lds_swz(int r)
 {
-    constexpr int m0 = D == 128 ? 4 : 2, m1 = D == 128 ? 10 : 4, m2 = 1, m3 = 2;
+    static_assert(D == 64 || D == 128 || D == 192 || D == 256, "head dimension");
+    constexpr int m0 = D == 64 ? 2 : D == 128 ? 4 : D == 192 ? 0 : 4;
+    constexpr int m1 = D == 64 ? 4 : D == 128 ? 10 : D == 192 ? 4 : 8;
+    constexpr int m2 = 1, m3 = 2;
     return ((r & 1) ? m0 : 0) ^ ((r & 2) ? m1 : 0) ^ ((r & 4) ? m2 : 0) ^ ((r & 8) ? m3 : 0);
 }
 
@@ -202,22 +207,24 @@ __device__ __forceinline__ void barrier_wait_vmem_upto()
     asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(N) : "memory");
 }
 
-// Instruction i of the NI = ROWS / (1024 / (2 D)) / NW direct loads that wave `wave` issues
-// to fill rows [row0, row0 + ROWS) of a row-major [*, D] bf16 matrix into a swizzled LDS
-// tile (each wave instruction covers 1 KB = 1024 / (2 D) whole rows).
+// Instruction i of the NI direct loads that wave `wave` issues to fill rows
+// [row0, row0 + ROWS) of a row-major [*, D] bf16 matrix into a swizzled LDS tile.  The
+// tile holds ROWS * D / 8 physical 16-byte chunks; wave instruction n = wave * NI + i
+// writes physical chunks 64 n .. 64 n + 63 (1 KB, lane l at chunk 64 n + l), and each lane
+// fetches the logical chunk that the swizzle puts there.
 template <int D, int NW, int ROWS = 64>
 __device__ __forceinline__ void load_tile_lds_part(__amdgpu_buffer_rsrc_t r, lds_char *tile, int row0, int wave,
                                                    int lane, int i)
 {
-    constexpr int RB = 2 * D;            // bytes per row
-    constexpr int RPI = 1024 / RB;       // rows per wave instruction
-    constexpr int NI = ROWS / RPI / NW;  // instructions per wave for the tile
-    static_assert(NI >= 1 && NI * RPI * NW == ROWS, "tile must split evenly over the waves");
-    const int lr = lane / (RB / 16), p = lane % (RB / 16);
-    const int r0 = (wave * NI + i) * RPI;  // first tile row of this instruction
-    const int row = r0 + lr;
-    const int chunk = p ^ lds_swz<D>(row);
-    buffer_load_lds16(r, tile + r0 * RB, (uint32_t)((row0 + row) * RB + 16 * chunk));
+    constexpr int RB = 2 * D;                   // bytes per row
+    constexpr int CPR = D / 8;                  // 16-byte chunks per row
+    constexpr int NI = ROWS * CPR / 64 / NW;    // instructions per wave for the tile
+    static_assert(NI >= 1 && NI * 64 * NW == ROWS * CPR, "tile must split evenly over the waves");
+    const int n = wave * NI + i;
+    const int pchunk = 64 * n + lane;           // physical chunk of this lane
+    const int row = pchunk / CPR;
+    const int chunk = (pchunk - row * CPR) ^ lds_swz<D>(row);
+    buffer_load_lds16(r, tile + 1024 * n, (uint32_t)((row0 + row) * RB + 16 * chunk));
 }
 
 // Load rows [row0, row0 + ROWS) of a row-major [*, D] bf16 matrix into a swizzled
@@ -225,7 +232,7 @@ __device__ __forceinline__ void load_tile_lds_part(__amdgpu_buffer_rsrc_t r, lds
 template <int D, int NW, int ROWS = 64>
 __device__ __forceinline__ void load_tile_lds(__amdgpu_buffer_rsrc_t r, lds_char *tile, int row0, int wave, int lane)
 {
-    constexpr int NI = ROWS / (1024 / (2 * D)) / NW;
+    constexpr int NI = ROWS * (D / 8) / 64 / NW;
 #pragma unroll
     for (int i = 0; i < NI; ++i) load_tile_lds_part<D, NW, ROWS>(r, tile, row0, wave, lane, i);
 }

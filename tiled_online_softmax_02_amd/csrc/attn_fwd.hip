@@ -41,9 +41,13 @@ namespace attn {
 namespace {
 
 // Waves per workgroup (32 query rows each): 8 at d = 128, where two waves per SIMD come from
-// the same workgroup and share each K/V block loaded into LDS; 4 at d = 64.
+// the same workgroup and share each K/V block loaded into LDS; 4 otherwise.
 template <int D>
 constexpr int fwd_waves() { return D == 128 ? 8 : 4; }
+// Workgroups per CU the launch bounds ask for: two waves per SIMD for d <= 128; one for
+// d = 192 and 256, whose accumulators need more than 256 registers per wave.
+template <int D>
+constexpr int fwd_min_blocks() { return D >= 192 ? 1 : 8 / fwd_waves<D>(); }
 template <int D>
 constexpr int fwd_bm() { return 32 * fwd_waves<D>(); }
 constexpr int kFwdBN = 64;                 // keys per streamed block
@@ -60,7 +64,7 @@ struct FwdSmem {
 // (query block, piece) writes the piece's normalised partial output (fp32) to OP and its
 // log-sum-exp to LP, and fwd_combine_kernel merges the pieces.
 template <int D, bool CAUSAL, bool SPLIT>
-__global__ __launch_bounds__(64 * fwd_waves<D>(), 8 / fwd_waves<D>()) void fwd_kernel(const bf16 *__restrict__ Q, const bf16 *__restrict__ K,
+__global__ __launch_bounds__(64 * fwd_waves<D>(), fwd_min_blocks<D>()) void fwd_kernel(const bf16 *__restrict__ Q, const bf16 *__restrict__ K,
                                                           const bf16 *__restrict__ V, bf16 *__restrict__ O,
                                                           float *__restrict__ LSE, int Nq, int Nk, int H, int G, int n_qtiles,
                                                           float scale, float c_log2, int n_splits, int split_blocks,
@@ -219,68 +223,64 @@ __global__ __launch_bounds__(64 * fwd_waves<D>(), 8 / fwd_waves<D>()) void fwd_k
                 constexpr int NS = 2 * NKS, NPV = (kFwdBN / 16) * NDB, NC = NS + NPV;
                 const lds_char *ks = kstage(PN{});
                 const lds_char *vs = vstage(par);
-                auto fetch = [&](int c) __attribute__((always_inline)) {
-                    bf16x8 f;
-                    if (c < NS / 2 || (c >= NS / 2 + NPV / 2 && c < NS + NPV / 2)) {
-                        const int s = c < NS / 2 ? c : c - NPV / 2;
-                        f = lds_read16(ks, swz_off<D>(32 * (s & 1) + c32, 2 * (s >> 1) + h));
+                constexpr auto is_s = [](int c) { return c < NS / 2 || (c >= NS / 2 + NPV / 2 && c < NS + NPV / 2); };
+                auto fetch = [&](auto C) __attribute__((always_inline)) {
+                    constexpr int c = decltype(C)::value;
+                    if constexpr (is_s(c)) {
+                        constexpr int s = c < NS / 2 ? c : c - NPV / 2;
+                        return lds_read16(ks, swz_off<D>(32 * (s & 1) + c32, 2 * (s >> 1) + h));
                     } else {
-                        const int p = c < NS / 2 + NPV / 2 ? c - NS / 2 : c - NS;
-                        f = lds_read_tr_rows_swz<D>(vs, 16 * (p / NDB), 32 * (p % NDB), lane);
+                        constexpr int p = c < NS / 2 + NPV / 2 ? c - NS / 2 : c - NS;
+                        return lds_read_tr_rows_swz<D>(vs, 16 * (p / NDB), 32 * (p % NDB), lane);
                     }
-                    return f;
                 };
                 nxt[0] = zero16();
                 nxt[1] = zero16();
                 bf16x8 pb[kFwdBN / 16];
                 float rs = 0.f, mx = -__builtin_inff();
-                bf16x8 fr[2 + 1];
-#pragma unroll
-                for (int c = 0; c < 2; ++c) fr[c] = fetch(c);
-#pragma unroll
-                for (int c = 0; c < NC; ++c) {
-                    if (c + 2 < NC) fr[(c + 2) % (2 + 1)] = fetch(c + 2);
-                    const bf16x8 fc = fr[c % (2 + 1)];
-                    if (c < NS / 2 || (c >= NS / 2 + NPV / 2 && c < NS + NPV / 2)) {
-                        const int s = c < NS / 2 ? c : c - NPV / 2;
+                constexpr int PF = 2;
+                bf16x8 fr[PF + 1];
+                static_for<0, PF>([&](auto F) __attribute__((always_inline)) { fr[decltype(F)::value] = fetch(F); });
+                static_assert(NS / 2 == NPV / 2, "phases S1 and V1 must have equal length");
+                constexpr int PH = NS / 2;  // chunks per phase
+                static_for<0, NC>([&](auto C) __attribute__((always_inline)) {
+                    constexpr int c = decltype(C)::value;
+                    if constexpr (c + PF < NC) fr[(c + PF) % (PF + 1)] = fetch(std::integral_constant<int, c + PF>{});
+                    const bf16x8 fc = fr[c % (PF + 1)];
+                    if constexpr (is_s(c)) {
+                        constexpr int s = c < NS / 2 ? c : c - NPV / 2;
                         nxt[s & 1] = mfma(fc, qf[s >> 1], nxt[s & 1]);
                     } else {
-                        const int p = c < NS / 2 + NPV / 2 ? c - NS / 2 : c - NS;
+                        constexpr int p = c < NS / 2 + NPV / 2 ? c - NS / 2 : c - NS;
                         oacc[p % NDB] = mfma(fc, pb[p / NDB], oacc[p % NDB]);
                     }
-                    if (c == 1) load_k(j + 2, par);
-                    if (c == 3) load_v(j + 1, PN{});
-                    if (c < NS / 2 + NPV / 2) {
-                        // exponentials: keys 0..31 during S1, 32..63 during V1
-                        const int kb = c < NS / 2 ? 0 : 1;
-                        const int i = c < NS / 2 ? c : c - NS / 2;
-                        constexpr int E = 16 / (NS / 2);
-                        static_assert(NS / 2 == NPV / 2, "phases S1 and V1 must have equal length");
-#pragma unroll
-                        for (int e = 0; e < E; ++e) {
-                            const int r = i * E + e;
+                    if constexpr (c == 1) load_k(j + 2, par);
+                    if constexpr (c == 3) load_v(j + 1, PN{});
+                    if constexpr (c < 2 * PH) {
+                        // exponentials: keys 0..31 during S1, 32..63 during V1; chunk i of the phase
+                        // takes elements [16 i / PH, 16 (i + 1) / PH)
+                        constexpr int kb = c < PH ? 0 : 1;
+                        constexpr int i = c < PH ? c : c - PH;
+                        static_for<i * 16 / PH, (i + 1) * 16 / PH>([&](auto RR) __attribute__((always_inline)) {
+                            constexpr int r = decltype(RR)::value;
                             cur[kb][r] = fast_exp2(fmaf(cur[kb][r], c_log2, -msc));
                             pb[2 * kb + (r >> 3)][r & 7] = (bf16)cur[kb][r];
-                        }
-                    } else if (c < NS + NPV / 2) {
-                        const int i = c - NS / 2 - NPV / 2;
-                        constexpr int E = 32 / (NS / 2);
-#pragma unroll
-                        for (int e = 0; e < E; ++e) {
-                            const int r = i * E + e;
+                        });
+                    } else if constexpr (c < 3 * PH) {
+                        constexpr int i = c - 2 * PH;
+                        static_for<i * 32 / PH, (i + 1) * 32 / PH>([&](auto RR) __attribute__((always_inline)) {
+                            constexpr int r = decltype(RR)::value;
                             rs += cur[r >> 4][r & 15];
-                        }
+                        });
                     } else {
-                        const int i = c - NS - NPV / 2;
-                        constexpr int E = 32 / (NPV / 2);
-#pragma unroll
-                        for (int e = 0; e < E; ++e) {
-                            const int r = i * E + e;
+                        constexpr int i = c - 3 * PH;
+                        static_for<i * 32 / PH, (i + 1) * 32 / PH>([&](auto RR) __attribute__((always_inline)) {
+                            constexpr int r = decltype(RR)::value;
                             mx = fmaxf(mx, nxt[r >> 4][r & 15]);
-                        }
+                        });
                     }
                     __builtin_amdgcn_sched_barrier(0);
-                }
+                });
                 l_run += rs;
                 mloc = mx;
                 __builtin_amdgcn_s_setprio(0);
@@ -411,17 +411,28 @@ hipError_t launch_fwd_split_t(const FwdArgs &a, int n_splits, float *op, float *
 
 hipError_t launch_fwd(const FwdArgs &a)
 {
-    if (a.d == 64) return a.causal ? launch_fwd_t<64, true>(a) : launch_fwd_t<64, false>(a);
-    return a.causal ? launch_fwd_t<128, true>(a) : launch_fwd_t<128, false>(a);
+    switch (a.d) {
+    case 64: return a.causal ? launch_fwd_t<64, true>(a) : launch_fwd_t<64, false>(a);
+    case 128: return a.causal ? launch_fwd_t<128, true>(a) : launch_fwd_t<128, false>(a);
+    case 192: return a.causal ? launch_fwd_t<192, true>(a) : launch_fwd_t<192, false>(a);
+    default: return a.causal ? launch_fwd_t<256, true>(a) : launch_fwd_t<256, false>(a);
+    }
 }
 
 hipError_t launch_fwd_split(const FwdArgs &a, int n_splits, void *workspace)
 {
     float *op = (float *)workspace;
     float *lp = op + (size_t)n_splits * a.B * a.H * a.Nq * a.d;
-    if (a.d == 64)
+    switch (a.d) {
+    case 64:
         return a.causal ? launch_fwd_split_t<64, true>(a, n_splits, op, lp) : launch_fwd_split_t<64, false>(a, n_splits, op, lp);
-    return a.causal ? launch_fwd_split_t<128, true>(a, n_splits, op, lp) : launch_fwd_split_t<128, false>(a, n_splits, op, lp);
+    case 128:
+        return a.causal ? launch_fwd_split_t<128, true>(a, n_splits, op, lp) : launch_fwd_split_t<128, false>(a, n_splits, op, lp);
+    case 192:
+        return a.causal ? launch_fwd_split_t<192, true>(a, n_splits, op, lp) : launch_fwd_split_t<192, false>(a, n_splits, op, lp);
+    default:
+        return a.causal ? launch_fwd_split_t<256, true>(a, n_splits, op, lp) : launch_fwd_split_t<256, false>(a, n_splits, op, lp);
+    }
 }
 
 long long fwd_split_workspace_bytes(int B, int H, int Nq, int d, int n_splits)
@@ -438,8 +449,8 @@ int fwd_split_default(int B, int H, int Nq, int Nk, int d)
 {
     // about one workgroup per compute unit (measured best for decoding shapes: one 8-wave
     // workgroup already fills a compute unit), at least two key blocks per piece
-    const long long base = (long long)B * H * ((Nq + (d == 128 ? fwd_bm<128>() : fwd_bm<64>()) - 1) /
-                                               (d == 128 ? fwd_bm<128>() : fwd_bm<64>()));
+    const int bm = d == 128 ? fwd_bm<128>() : fwd_bm<64>();  // 128 rows for d = 64, 192 and 256
+    const long long base = (long long)B * H * ((Nq + bm - 1) / bm);
     const int blocks = (Nk + kFwdBN - 1) / kFwdBN;
     long long s = base > 0 ? (256 + base - 1) / base : 1;
     s = s < blocks / 2 ? s : blocks / 2;
