@@ -18,6 +18,11 @@ The functions follow these pages (cited by title and section):
   59 and 60: row softmax, the online normaliser, blockwise rescaling of the
   outputs, bottom-right causal alignment with zero output for fully masked
   rows, and the -inf guards.
+* 8-bit inputs: "FlashAttention v3 (Tri Dao et al.)", section "What it is" (FP8
+  input types); "CUTLASS WGMMA Atom Skeleton", table "Atom Family Names Seen In
+  CUTLASS" (FP8 products take e4m3 or e5m2); [gpko] item 33 (affine
+  quantisation, real value = scale * (code - zero point)).  The e4m3 code itself
+  is decoded by its OCP definition, written out in ``attn_oracle.c``.
 """
 from __future__ import annotations
 
@@ -68,9 +73,10 @@ def _load():
             lib.oracle_attn_bwd.argtypes = [_D, _D, _D, _D, _D, _D, _D, _D, ctypes.c_long, ctypes.c_long,
                                             ctypes.c_long, ctypes.c_long, ctypes.c_long, ctypes.c_int,
                                             ctypes.c_double, ctypes.c_int]
+            lib.oracle_fp8_e4m3_decode.argtypes = [ctypes.POINTER(ctypes.c_ubyte), ctypes.c_long, _D]
             for name in ("oracle_softmax_rows", "oracle_online_merge", "oracle_online_normalizer",
                          "oracle_attn_fwd", "oracle_attn_fwd_rows", "oracle_attn_fwd_blockwise",
-                         "oracle_attn_bwd"):
+                         "oracle_attn_bwd", "oracle_fp8_e4m3_decode"):
                 getattr(lib, name).restype = ctypes.c_int
             _lib = lib
     return _lib
@@ -208,3 +214,26 @@ def attn_bwd_matmul(q, k, v, dout, causal: bool, scale: float, nthreads: int | N
             dk[b, h] = scale * (ds.T @ q[b, h])
             dvec[b, h] = D
     return dq, dk, dv, dvec
+
+
+def fp8_e4m3_decode(codes) -> np.ndarray:
+    """Exact values of e4m3 codes (any integer array of bytes, same shape out, float64)."""
+    c = np.ascontiguousarray(np.asarray(codes, dtype=np.uint8))
+    out = np.empty(c.shape, dtype=np.float64)
+    _check(_load().oracle_fp8_e4m3_decode(c.ctypes.data_as(ctypes.POINTER(ctypes.c_ubyte)), c.size, _p(out)),
+           "fp8_e4m3_decode")
+    return out
+
+
+def attn_fwd_fp8(q8, k8, v8, descale_q, descale_k, descale_v, causal: bool, scale: float, nthreads: int | None = None):
+    """Forward pass on 8-bit inputs by the definition.
+
+    q8 ``[B, H, nq, d]``, k8 and v8 ``[B, H, nk, d]`` are e4m3 codes (uint8); descale_q, descale_k and
+    descale_v ``[B, H]`` are the per-head scales.  The real inputs are descale * decoded code; S and P
+    follow from them exactly as in :func:`attn_fwd` (with the same softmax ``scale``).
+    Returns (O, lse) in float64."""
+    dq, dk, dv = (np.asarray(x, dtype=np.float64) for x in (descale_q, descale_k, descale_v))
+    q = fp8_e4m3_decode(q8) * dq[:, :, None, None]
+    k = fp8_e4m3_decode(k8) * dk[:, :, None, None]
+    v = fp8_e4m3_decode(v8) * dv[:, :, None, None]
+    return attn_fwd(q, k, v, causal, scale, nthreads=nthreads)

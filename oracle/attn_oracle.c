@@ -505,3 +505,41 @@ int oracle_attn_bwd(const double *q, const double *k, const double *v, const dou
         return 0;
     return run_threads(&jb, nthreads, bwd_worker);
 }
+
+/* ---------------------------------------------------------------------------
+ * 8-bit floating-point inputs.
+ *
+ * FlashAttention v3 takes FP8 inputs ("FlashAttention v3 (Tri Dao et al.)",
+ * section "What it is"); products of FP8 operands with fp32 results take the
+ * e4m3 or e5m2 element type ("CUTLASS WGMMA Atom Skeleton", table "Atom
+ * Family Names Seen In CUTLASS").  The codes here are e4m3 in the OCP 8-bit
+ * floating-point definition (the form this GPU's matrix cores take): one sign
+ * bit s, four exponent bits e with bias 7, three fraction bits f;
+ *   e = 0:          (-1)^s * 2^-6 * f/8        (zero and subnormals)
+ *   e = 1 .. 15:    (-1)^s * 2^(e-7) * (1 + f/8)
+ * except e = 15, f = 7, which is NaN; there is no infinity (largest 448).
+ * Each tensor of codes carries a per-head scale, and the real value is scale *
+ * decoded code: the affine map r = S (q - Z) of "Quantization and Training of
+ * Neural Networks for Efficient Integer-Arithmetic-Only Inference" ([gpko]
+ * item 33) with zero point Z = 0.
+ * ------------------------------------------------------------------------- */
+
+/* Decode n e4m3 codes into doubles (exact). */
+int oracle_fp8_e4m3_decode(const unsigned char *x, long n, double *out)
+{
+    long i;
+    if ((!x || !out) && n > 0)
+        return -1;
+    for (i = 0; i < n; ++i) {
+        const int s = x[i] >> 7, e = (x[i] >> 3) & 15, f = x[i] & 7;
+        double mag;
+        if (e == 15 && f == 7)
+            mag = NAN;
+        else if (e == 0)
+            mag = ldexp((double)f / 8.0, -6);
+        else
+            mag = ldexp(1.0 + (double)f / 8.0, e - 7);
+        out[i] = s ? -mag : mag;
+    }
+    return 0;
+}

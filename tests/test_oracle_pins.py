@@ -337,3 +337,74 @@ def test_matmul_backward_matches_loops_on_a_multi_head_case():
         got = oracle.attn_bwd_matmul(q, k, v, dout, causal, 0.25)
         for a, b in zip(got, ref):
             np.testing.assert_allclose(a, b, rtol=1e-11, atol=1e-12)
+
+
+# ---------------------------------------------------------------- 8-bit inputs
+
+def test_fp8_decode_matches_torch_e4m3fn_for_all_codes():
+    """Every e4m3 code decodes to PyTorch's float8_e4m3fn value (an independent library
+    implementation of the OCP format); the NaN codes are exactly 0x7f and 0xff."""
+    codes = np.arange(256, dtype=np.uint8)
+    mine = oracle.fp8_e4m3_decode(codes)
+    ref = torch.from_numpy(codes.copy()).view(torch.float8_e4m3fn).to(torch.float64).numpy()
+    nan = np.isnan(mine)
+    assert np.array_equal(nan, np.isnan(ref))
+    assert sorted(np.nonzero(nan)[0].tolist()) == [0x7F, 0xFF]
+    assert np.array_equal(mine[~nan], ref[~nan])
+    assert np.array_equal(np.signbit(mine[~nan]), np.signbit(ref[~nan]))
+
+
+def test_fp8_decode_closed_form_values():
+    """Values that follow from the format's fields alone: 1.0 (exponent field 7), the largest
+    finite value 1.75 * 2^8 = 448, the smallest subnormal 2^-9, the largest subnormal 7 * 2^-9,
+    the smallest normal 2^-6, and the sign bit."""
+    got = oracle.fp8_e4m3_decode(np.array([0x38, 0x7E, 0x01, 0x07, 0x08, 0xB8, 0x00, 0x80], np.uint8))
+    assert got.tolist() == [1.0, 448.0, 2.0**-9, 7 * 2.0**-9, 2.0**-6, -1.0, 0.0, -0.0]
+
+
+def _fp8_case(B=2, H=3, nq=13, nk=21, d=16, seed=5):
+    rng = np.random.default_rng(seed)
+    finite = np.array([c for c in range(256) if (c & 0x7F) != 0x7F], np.uint8)
+    q8 = rng.choice(finite, size=(B, H, nq, d))
+    k8 = rng.choice(finite, size=(B, H, nk, d))
+    v8 = rng.choice(finite, size=(B, H, nk, d))
+    ds = [np.exp2(rng.integers(-9, -5, size=(B, H))).astype(np.float64) * rng.uniform(0.5, 1.0, size=(B, H))
+          for _ in range(3)]
+    return q8, k8, v8, ds
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_fp8_attention_is_attention_of_the_scaled_decoded_inputs(causal):
+    """Per head (b, h) the real inputs are descale[b, h] * value(code): PyTorch's e4m3 decode,
+    scaled head by head, fed to PyTorch's own fp64 softmax attention, gives the same O and lse.
+    A descale applied to the wrong tensor or the wrong head fails this."""
+    q8, k8, v8, (dq, dk, dv) = _fp8_case()
+    scale = 0.25
+    o, lse = oracle.attn_fwd_fp8(q8, k8, v8, dq, dk, dv, causal, scale)
+    dec = lambda c: torch.from_numpy(c.copy()).view(torch.float8_e4m3fn).to(torch.float64).numpy()
+    q = dec(q8) * dq[:, :, None, None]
+    k = dec(k8) * dk[:, :, None, None]
+    v = dec(v8) * dv[:, :, None, None]
+    s = torch_attention(q, k, v, causal, scale)
+    ref_lse = torch.logsumexp(s, dim=-1).numpy()
+    ref_o = torch.matmul(torch.softmax(s, dim=-1), torch.from_numpy(v)).numpy()
+    np.testing.assert_allclose(o, ref_o, rtol=1e-10, atol=1e-12)
+    np.testing.assert_allclose(lse, ref_lse, rtol=1e-12, atol=1e-12)
+
+
+def test_fp8_attention_scale_invariances():
+    """Doubling the value scale doubles O and leaves lse; moving a factor 2 from the key scale to
+    the query scale changes nothing (the scores are bilinear in the two scales); a value tensor
+    whose rows all hold the same codes returns those values for every query."""
+    q8, k8, v8, (dq, dk, dv) = _fp8_case(seed=6)
+    o, lse = oracle.attn_fwd_fp8(q8, k8, v8, dq, dk, dv, True, 0.5)
+    o2, lse2 = oracle.attn_fwd_fp8(q8, k8, v8, dq, dk, 2 * dv, True, 0.5)
+    np.testing.assert_allclose(o2, 2 * o, rtol=1e-14, atol=0)
+    np.testing.assert_array_equal(lse2, lse)
+    o3, lse3 = oracle.attn_fwd_fp8(q8, k8, v8, 2 * dq, dk / 2, dv, True, 0.5)
+    np.testing.assert_allclose(o3, o, rtol=1e-12, atol=1e-14)
+    np.testing.assert_allclose(lse3, lse, rtol=1e-12, atol=1e-14)
+    vconst = np.broadcast_to(v8[:, :, :1, :], v8.shape).copy()
+    o4, _ = oracle.attn_fwd_fp8(q8, k8, vconst, dq, dk, dv, False, 0.5)
+    row = oracle.fp8_e4m3_decode(v8[:, :, :1, :]) * dv[:, :, None, None]
+    np.testing.assert_allclose(o4, np.broadcast_to(row, o4.shape), rtol=1e-12, atol=0)
