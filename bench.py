@@ -4,7 +4,9 @@
 One step is one pass of the whole path over resident synthetic inputs: the fused
 forward kernel, then the backward preprocess, dK/dV and dQ kernels (the same four
 launches attn_bwd makes).  The default workload is the forward+backward causal case
-B=2, H=16, N=4096, d=128; ``--workload c2|c3|c4`` times forward-only workloads.
+B=2, H=16, N=4096, d=128; ``--workload c2|c3|c4`` times forward-only workloads, ``dec`` the
+split-key forward of a decoding shape, and ``c3f8|c4f8`` the 8-bit forward on the shapes of
+c3 and c4.
 
 Before the W warmup steps the step runs untimed for --ramp-seconds (1 s by default): an
 idle MI355X needs a fraction of a second under load before its clocks settle, and the timed
@@ -12,7 +14,7 @@ K steps are meant to measure the steady state.
 
 FLOP convention: 4*B*H*N^2*d for the forward, halved when causal; the backward counts
 2.5x the forward.  Printed: one JSON line with the whole-job TFLOP/s, the dominant
-kernel's roofline (achieved algorithmic TFLOP/s against the bf16 dense MFMA peak,
+kernel's roofline (achieved algorithmic TFLOP/s against the dense MFMA peak of its dtype,
 measured with HIP events on the launch stream) and the fp64 CPU oracle timed on a
 bounded sample of the same workload on the host cores.
 """
@@ -30,6 +32,7 @@ if ROOT not in sys.path:
 
 METRIC = "attention fwd/bwd TFLOP/s on 1 MI355X and % of bf16 MFMA peak"
 PEAK_BF16_TFLOPS = 2516.6   # 256 CUs x 2.4 GHz x 4096 dense bf16 FLOP/clk/CU
+PEAK_FP8_TFLOPS = 5033.2    # twice the bf16 rate (MI355X dense fp8: 5.0 PFLOP/s)
 PEAK_HBM_GBS = 8000.0
 
 
@@ -62,7 +65,7 @@ def kernel_algorithmic_flop(kernel, B, H, N, d, causal) -> float:
     forward is two of them): fwd 2 (QK^T, PV); dkdv 4 (the recomputed S, dP, dV, dK);
     dq 1 (dQ; its recomputed S and dP are counted in dkdv); preprocess 0."""
     unit = fwd_flop(B, H, N, d, causal) / 2.0
-    return unit * {"fwd": 2, "dkdv": 4, "dq": 1, "preprocess": 0}[kernel]
+    return unit * {"fwd": 2, "fwd_fp8": 2, "dkdv": 4, "dq": 1, "preprocess": 0}[kernel]
 
 
 def stored_traffic(kernel: str, workload: str):
@@ -92,6 +95,8 @@ def cpu_baseline(w, budget_s: float):
     from tiled_online_softmax_02_amd.inputs import make_inputs
 
     threads = max(1, min(len(os.sched_getaffinity(0)), 16))
+    if w.fp8:
+        return cpu_baseline_fp8(w, budget_s, threads)
     inp = make_inputs(1, 1, w.N, w.d, nk=w.nk, seed=w.seed + 1000, backward=w.backward,
                       boost_every=w.boost_every, boost=w.boost)
     f64 = {k: t.to(dtype=__import__("torch").float64).numpy() for k, t in inp.items()}
@@ -122,12 +127,40 @@ def cpu_baseline(w, budget_s: float):
     }
 
 
+def cpu_baseline_fp8(w, budget_s: float, threads: int):
+    """The oracle's 8-bit forward (decode, scale, fp64 attention) on whole heads."""
+    import oracle
+    from tiled_online_softmax_02_amd.inputs import make_fp8_inputs
+
+    def run(heads, seed, nthreads):
+        x = make_fp8_inputs(1, heads, w.N, w.d, nk=w.nk, seed=seed, boost_every=w.boost_every, boost=w.boost)
+        c = {n: x[n + "8"].view(__import__("torch").uint8).numpy() for n in "qkv"}
+        ds = [x["descale_" + n].double().numpy() for n in "qkv"]
+        t0 = time.perf_counter()
+        oracle.attn_fwd_fp8(c["q"], c["k"], c["v"], *ds, w.causal, w.scale, nthreads=nthreads)
+        return time.perf_counter() - t0
+
+    one = run(1, w.seed + 1000, 1)
+    heads = int(max(1, min(w.B * w.H, threads, budget_s // max(one, 1e-3))))
+    dt = run(heads, w.seed + 1001, min(threads, heads))
+    flop = workload_flop(w) / (w.B * w.H) * heads
+    return {
+        "value": flop / dt / 1e12,
+        "unit": "TFLOP/s",
+        "cores": min(threads, heads),
+        "kind": "oracle",
+        "sample": "%d of %d heads (Nq=%d Nk=%d d=%d per head), same FLOP convention, %.1f s wall; e4m3 codes "
+                  "decoded and scaled, then the plain fp64 C definition (one thread per head)"
+                  % (heads, w.B * w.H, w.nq, w.nk, w.d, dt),
+    }
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--workload", default="c5", choices=["c2", "c3", "c4", "c5", "dec"])
+    ap.add_argument("--workload", default="c5", choices=["c2", "c3", "c4", "c5", "dec", "c3f8", "c4f8"])
     ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle work for the CPU baseline")
     ap.add_argument("--ramp-seconds", type=float, default=1.0,
                     help="untimed steps for this long before the warmup steps, so that the GPU clocks "
@@ -148,7 +181,12 @@ def main():
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     inp = workload_inputs(w)
-    q, k, v = (inp[n].to(dev) for n in ("q", "k", "v"))
+    fp8 = w.fp8
+    if fp8:
+        q, k, v = (inp[n + "8"].to(dev) for n in ("q", "k", "v"))
+        dsq, dsk, dsv = (inp["descale_" + n].to(dev) for n in ("q", "k", "v"))
+    else:
+        q, k, v = (inp[n].to(dev) for n in ("q", "k", "v"))
     B, H, N, d = q.shape
     Nk = k.shape[2]
     split = w.name == "dec"  # decoding: the split-key forward (partial pieces, then their merge)
@@ -157,7 +195,7 @@ def main():
         ws_bytes = A.attn_fwd_splitkv_workspace_size(B, H, N, d, ns)
         ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
     causal, scale = w.causal, w.scale
-    o = torch.empty_like(q)
+    o = torch.empty((B, H, N, d), dtype=torch.bfloat16, device=dev)
     lse = torch.empty((B, H, N), dtype=torch.float32, device=dev)
     if w.backward:
         do = inp["do"].to(dev)
@@ -172,7 +210,8 @@ def main():
     torch.cuda.synchronize()
     del cal_src, cal_dst
 
-    kernels = (["fwd_splitkv"] if split else ["fwd"]) + (["preprocess", "dkdv", "dq"] if w.backward else [])
+    kernels = (["fwd_splitkv"] if split else ["fwd_fp8"] if fp8 else ["fwd"]) + (
+        ["preprocess", "dkdv", "dq"] if w.backward else [])
     ev = {kname: [] for kname in kernels}
 
     def step(record):
@@ -181,6 +220,8 @@ def main():
             e[0].record()
         if split:
             A.attn_fwd_splitkv(q, k, v, o, lse, B, H, H, N, Nk, d, causal, scale, ns, ws, ws_bytes)
+        elif fp8:
+            A.attn_fwd_fp8(q, k, v, dsq, dsk, dsv, o, lse, B, H, H, N, Nk, d, causal, scale)
         else:
             A.attn_fwd(q, k, v, o, lse, B, H, N, d, causal, scale)
         if record:
@@ -217,6 +258,7 @@ def main():
     kernel_ms = {kname: sum(a.elapsed_time(b) for a, b in pairs) / len(pairs) for kname, pairs in ev.items()}
     flop = workload_flop(w)
     value = flop / (ms_per_step * 1e-3) / 1e12
+    peak = PEAK_FP8_TFLOPS if fp8 else PEAK_BF16_TFLOPS  # the products' own dtype
     dom = max(kernels, key=lambda kname: kernel_ms[kname])
     if split:
         # decoding reads every key and value once and does 4*d FLOP per key: the HBM roof bounds it
@@ -227,10 +269,10 @@ def main():
                 "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": stored_traffic(dom, w.name),
                 "algorithmic_bytes": alg_bytes, "num_splits": ns}
     else:
-        fwd_t = fwd_flop(B, H, N, d, causal) / (kernel_ms["fwd"] * 1e-3) / 1e12
+        fwd_t = fwd_flop(B, H, N, d, causal) / (kernel_ms[kernels[0]] * 1e-3) / 1e12
         achieved = kernel_algorithmic_flop(dom, B, H, N, d, causal) / (kernel_ms[dom] * 1e-3) / 1e12
-        roof = {"kernel": dom, "bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
-                "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+        roof = {"kernel": dom, "bound": "mfma", "achieved": round(achieved, 2), "peak": peak,
+                "unit": "TFLOP/s", "frac": round(achieved / peak, 4),
                 "traffic": stored_traffic(dom, w.name)}
     config = {"workload": w.describe(), "B": B, "H": H, "N": N, "d": d, "causal": causal,
               "scale": scale, "global_batch": B, "seq_len": N, "parallelism": "single GPU"}
@@ -247,10 +289,11 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16",
+        "dtype": "fp8_e4m3" if fp8 else "bf16",
         "data": "synthetic",
         "config": config,
-        "pct_of_peak": round(100.0 * value / PEAK_BF16_TFLOPS, 2),
+        "pct_of_peak": round(100.0 * value / peak, 2),
+        "peak_tflops": peak,
         "fwd_tflops": round(fwd_t, 2),
         "kernel_ms": {kname: round(t, 4) for kname, t in kernel_ms.items()},
         "roofline": roof,

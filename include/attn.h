@@ -49,7 +49,8 @@
  * is valid, enqueues nothing and returns ATTN_OK; more generally a pointer to a
  * buffer of zero bytes may be NULL.
  * Sizes: B, H, Hk, N (Nq, Nk) >= 0; d in {64, 128, 192, 256}; B*H*N*d < 2^62;
- * (N + 256)*d*2 < 2^32 for N = Nq and N = Nk.  Pointers must be 16-byte aligned.
+ * (N + 256)*d*2 < 2^32 for N = Nq and N = Nk.  Pointers must be 16-byte aligned
+ * (the per-head scale arrays of attn_fwd_fp8: 4-byte aligned).
  */
 #ifndef ATTN_H_
 #define ATTN_H_
@@ -108,6 +109,27 @@ long long attn_fwd_splitkv_workspace_size(int B, int H, int Nq, int d, int num_s
  * while keeping at least two 64-key blocks per piece; 1 when splitting does
  * not help or the arguments are invalid. */
 int attn_fwd_splitkv_default_splits(int B, int H, int Nq, int Nk, int d);
+
+/* Forward pass on 8-bit inputs ("FlashAttention v3 (Tri Dao et al.)",
+ * section "What it is": FP8 input types; the "CUTLASS WGMMA Atom Skeleton"
+ * page, table "Atom Family Names Seen In CUTLASS": FP8 products take e4m3).
+ * q [B,H,Nq,d], k and v [B,Hk,Nk,d] hold e4m3 codes (OCP form: bias 7, no
+ * infinity, largest 448), one byte each, 16-byte aligned.  descale_q [B*H],
+ * descale_k and descale_v [B*Hk] are fp32 device arrays (4-byte aligned) of
+ * per-head scales: the real input of head (b, h) is descale[b*H + h] times the
+ * code's value ("GPU Programming and Kernel Optimization", item 33: affine
+ * quantisation with zero point 0).  The scales must be finite and > 0.
+ * Computes the same O and lse as attn_fwd_qk on those real inputs: o is bf16
+ * [B,H,Nq,d], lse fp32 [B,H,Nq] (natural log, with `scale` as there).  Both
+ * products run on 8-bit operands with fp32 accumulation; the probabilities
+ * are rounded to e4m3 before the product with V, which makes O less exact
+ * than the 16-bit path (each probability carries up to 2^-4 relative
+ * rounding).  d in {64, 128} (else ATTN_ERR_UNSUPPORTED_D); causal alignment,
+ * grouped heads and empty rows as in the conventions above. */
+int attn_fwd_fp8(const void *q, const void *k, const void *v,
+                 const float *descale_q, const float *descale_k, const float *descale_v,
+                 void *o, float *lse, int B, int H, int Hk, int Nq, int Nk, int d, int causal,
+                 float scale, void *stream);
 
 /* Backward pass: enqueues attn_bwd_preprocess, attn_bwd_dkdv and attn_bwd_dq
  * in that order on `stream`.  Reads q, k, v, o, dout and the lse written by

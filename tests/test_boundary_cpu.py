@@ -35,7 +35,7 @@ def declared_functions():
 def test_header_declares_the_expected_entry_points():
     assert declared_functions() == sorted([
         "attn_fwd", "attn_fwd_qk", "attn_fwd_splitkv", "attn_fwd_splitkv_workspace_size",
-        "attn_fwd_splitkv_default_splits", "attn_bwd", "attn_bwd_qk", "attn_bwd_preprocess", "attn_bwd_dkdv",
+        "attn_fwd_splitkv_default_splits", "attn_fwd_fp8", "attn_bwd", "attn_bwd_qk", "attn_bwd_preprocess", "attn_bwd_dkdv",
         "attn_bwd_dq", "attn_status_string", "attn_last_hip_error"])
 
 
@@ -223,3 +223,34 @@ def test_splitkv_argument_checks(lib, kw, status):
 
 def test_splitkv_empty_is_a_no_op(lib):
     assert splitkv(lib, q=None, k=None, v=None, o=None, lse=None, ws=None, Nq=0) == A.ATTN_OK
+
+
+def fwd8(lib, q=P[0], k=P[1], v=P[2], dq=P[5], dk=P[6], dv=P[7], o=P[3], lse=P[4], B=1, H=2, Hk=1, Nq=64, Nk=80,
+         d=128, causal=1, scale=0.125):
+    return lib.attn_fwd_fp8(q, k, v, dq, dk, dv, o, lse, B, H, Hk, Nq, Nk, d, causal, scale, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(d=192), A.ATTN_ERR_UNSUPPORTED_D),
+    (dict(d=256), A.ATTN_ERR_UNSUPPORTED_D),
+    (dict(d=32), A.ATTN_ERR_UNSUPPORTED_D),
+    (dict(H=3, Hk=2), A.ATTN_ERR_BAD_SHAPE),
+    (dict(Nk=-1), A.ATTN_ERR_BAD_SHAPE),
+    (dict(causal=2), A.ATTN_ERR_BAD_ARG),
+    (dict(scale=0.0), A.ATTN_ERR_BAD_SCALE),
+    (dict(q=0), A.ATTN_ERR_NULLPTR),
+    (dict(dq=0), A.ATTN_ERR_NULLPTR),
+    (dict(dv=0), A.ATTN_ERR_NULLPTR),
+    (dict(k=P[1] + 8), A.ATTN_ERR_MISALIGNED),
+    (dict(dk=P[6] + 2), A.ATTN_ERR_MISALIGNED),
+    (dict(o=P[0]), A.ATTN_ERR_ALIAS),
+    (dict(lse=P[5]), A.ATTN_ERR_ALIAS),           # lse on top of the query scales
+    (dict(o=P[7] - 64), A.ATTN_ERR_ALIAS),        # o runs into the value scales
+])
+def test_fp8_forward_argument_checks(lib, kw, status):
+    assert fwd8(lib, **kw) == status
+
+
+def test_fp8_forward_empty_is_a_no_op(lib):
+    assert fwd8(lib, q=0, o=0, lse=0, Nq=0) == A.ATTN_OK
+    assert fwd8(lib, B=0, q=0, k=0, v=0, dq=0, dk=0, dv=0, o=0, lse=0) == A.ATTN_OK

@@ -1,0 +1,186 @@
+"""8-bit (e4m3) forward on the GPU against the fp64 oracle, through the C ABI.
+
+The oracle computes exact attention of the real inputs the codes stand for (descale * code
+value).  The GPU rounds every probability to e4m3 before the product with V, so its O is
+compared with a bound derived from that rounding rather than with the 16-bit path's fixed
+2e-2 (derivation in the design notes; the exp-sum l is taken from the unrounded fp32
+probabilities, so lse carries only the score error):
+
+* per element, rigorous:  |O - O_ref|[i,c] <= sum_j (max(2^-4 P_ij, 2^-10 Pmax_i)
+  + (eps_i + 2^-9) P_ij) |V_jc| + 2^-8 |O_ref[i,c]| + 1e-6.
+  2^-4 is e4m3's relative half-spacing; 2^-10 its absolute half-spacing below 2^-6 in the
+  kernel's units, where the largest probability of a row is at least 1 (so l >= 1/Pmax);
+  eps_i = 2 * 2^-10 * max_j scale * sum_k |q_ik k_jk| bounds the scores' summation error
+  (the 8-bit products of the matrix cores were measured to sum with at most 2^-12.3 of
+  sum |products|; 2^-10 leaves margin); 2^-9 P covers the fp32 accumulation of P V and
+  2^-8 |O| the bf16 rounding of the output.
+* overall, statistical: rms(O - O_ref) <= 1.5 * rms of the predicted error, whose variance
+  per element is sum_j (2^-4 P_ij)^2 / 3 * V_jc^2 + (2^-9 O_ref)^2 / 3 (rounding errors
+  uniform within half a spacing).  This is what catches a wrong result in rows whose
+  softmax is flat, where the rigorous bound exceeds |O| itself.
+* lse: |lse - lse_ref| <= eps_i + 1e-5 max(1, |lse_ref|); rows with no visible key must
+  give lse = -inf and O = 0.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import tiled_online_softmax_02_amd as A
+from tiled_online_softmax_02_amd.inputs import WORKLOADS, make_fp8_inputs, softmax_scale, workload_inputs
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda:0"
+
+
+def note(msg):
+    print("[fp8] " + msg, flush=True)
+
+
+def codes(t):
+    return t.contiguous().view(torch.uint8).numpy()
+
+
+def real(inp, name):
+    """Real fp64 values of a code tensor: decoded by the oracle, times its per-head scale."""
+    ds = inp["descale_" + name].double().numpy()
+    return oracle.fp8_e4m3_decode(codes(inp[name + "8"])) * ds[:, :, None, None]
+
+
+def gpu_fwd8(inp, causal, scale):
+    dev = {k: v.to(DEV) for k, v in inp.items()}
+    o, lse = A.fwd_fp8(dev["q8"], dev["k8"], dev["v8"], dev["descale_q"], dev["descale_k"], dev["descale_v"],
+                       causal=causal, scale=scale)
+    torch.cuda.synchronize()
+    return o.double().cpu().numpy(), lse.double().cpu().numpy()
+
+
+def bound_rows(q_rows, rows, k, v, nq, causal, scale, o_ref):
+    """Rigorous bound, predicted variance and eps for query rows `rows` of one head.
+    q_rows [R, d]; k, v [nk, d] (real values); o_ref [R, d]."""
+    nk = k.shape[0]
+    s = (q_rows @ k.T) * scale
+    sabs = (np.abs(q_rows) @ np.abs(k).T) * scale
+    if causal:
+        vis = np.arange(nk)[None, :] <= (np.asarray(rows)[:, None] + (nk - nq))
+    else:
+        vis = np.ones(s.shape, bool)
+    s = np.where(vis, s, -np.inf)
+    m = s.max(axis=1, keepdims=True)
+    live = np.isfinite(m[:, 0])
+    p = np.zeros_like(s)
+    p[live] = np.exp(s[live] - m[live])
+    p[live] /= p[live].sum(axis=1, keepdims=True)
+    pmax = p.max(axis=1, keepdims=True)
+    eps = 2 * 2.0**-10 * np.where(vis, sabs, 0).max(axis=1, initial=0.0)
+    w = np.maximum(2.0**-4 * p, 2.0**-10 * pmax) + (eps[:, None] + 2.0**-9) * p
+    bound = w @ np.abs(v) + 2.0**-8 * np.abs(o_ref) + 1e-6
+    var = ((2.0**-4 * p) ** 2 / 3) @ (v ** 2) + (2.0**-9 * o_ref) ** 2 / 3
+    return bound, var, eps, live
+
+
+class Acc:
+    """Collects the statistical check over several heads."""
+
+    def __init__(self):
+        self.err2, self.var, self.n = 0.0, 0.0, 0
+
+    def add(self, err, var):
+        self.err2 += float((err ** 2).sum())
+        self.var += float(var.sum())
+        self.n += err.size
+
+    def check(self, what):
+        rms_e, rms_p = np.sqrt(self.err2 / self.n), np.sqrt(self.var / self.n)
+        note("  %s: rms err %.3e, predicted %.3e (ratio %.2f)" % (what, rms_e, rms_p, rms_e / rms_p))
+        assert rms_e <= 1.5 * rms_p, (what, rms_e, rms_p)
+
+
+def check_rows(o, lse, o_ref, lse_ref, bound, eps, live, what):
+    err = np.abs(o - o_ref)
+    assert np.all(np.isfinite(o)), what
+    ratio = (err / bound).max() if err.size else 0.0
+    assert np.all(np.isneginf(lse[~live])) and np.all(o[~live] == 0), what
+    dl = np.abs(lse[live] - lse_ref[live])
+    tol = eps[live] + 1e-5 * np.maximum(1.0, np.abs(lse_ref[live]))
+    assert np.all(dl <= tol), (what, (dl - tol).max())
+    assert ratio <= 1.0, (what, ratio)
+    return ratio
+
+
+CASES = [
+    # B, H, Hk, Nq, Nk, d, causal
+    (1, 2, 2, 300, 300, 128, True),
+    (2, 1, 1, 257, 257, 64, False),
+    (1, 4, 2, 200, 333, 128, True),     # grouped heads, more keys than queries
+    (1, 2, 2, 65, 17, 64, True),        # rows that see no key
+    (1, 1, 1, 1024, 1024, 128, True),   # several query and key blocks
+    (1, 2, 1, 130, 700, 64, False),     # multi-query, ragged
+    (1, 1, 1, 1, 1, 128, False),
+]
+
+
+@pytest.mark.parametrize("B,H,Hk,Nq,Nk,d,causal", CASES)
+def test_fp8_forward_against_oracle(B, H, Hk, Nq, Nk, d, causal):
+    note("B=%d H=%d Hk=%d Nq=%d Nk=%d d=%d causal=%d seed=61" % (B, H, Hk, Nq, Nk, d, causal))
+    scale = softmax_scale(d)
+    inp = make_fp8_inputs(B, H, Nq, d, nk=Nk, Hk=Hk, seed=61)
+    o, lse = gpu_fwd8(inp, causal, scale)
+    G = H // Hk
+    q, k, v = real(inp, "q"), real(inp, "k"), real(inp, "v")
+    k_rep, v_rep = np.repeat(k, G, axis=1), np.repeat(v, G, axis=1)
+    o_ref, lse_ref = oracle.attn_fwd(q, k_rep, v_rep, causal, scale)
+    acc = Acc()
+    worst = 0.0
+    for b in range(B):
+        for h in range(H):
+            rows = np.arange(Nq)
+            bound, var, eps, live = bound_rows(q[b, h], rows, k_rep[b, h], v_rep[b, h], Nq, causal, scale,
+                                               o_ref[b, h])
+            worst = max(worst, check_rows(o[b, h], lse[b, h], o_ref[b, h], lse_ref[b, h], bound, eps, live,
+                                          "head (%d,%d)" % (b, h)))
+            acc.add(o[b, h][live] - o_ref[b, h][live], var[live])
+    note("  max err / bound %.3f, max|err| %.3e" % (worst, np.abs(o - o_ref).max()))
+    if acc.n:
+        acc.check("B=%d H=%d Nq=%d d=%d" % (B, H, Nq, d))
+
+
+@pytest.mark.parametrize("wname", ["c3f8", "c4f8"])
+def test_fp8_workload_sampled(wname):
+    """The 8-bit workloads at full size, in the launch configuration the benchmark times: every
+    head checked on sampled rows (first, last, block edges and random ones)."""
+    w = WORKLOADS[wname]
+    note(wname + " " + w.describe())
+    inp = workload_inputs(w)
+    o, lse = gpu_fwd8(inp, w.causal, w.scale)
+    q, k, v = real(inp, "q"), real(inp, "k"), real(inp, "v")
+    rng = np.random.default_rng(71)
+    acc = Acc()
+    worst = 0.0
+    for b in range(w.B):
+        for h in range(w.H):
+            rows = {0, 1, 63, 64, 255, 256, w.N // 2, w.N - 257, w.N - 1}
+            rows |= set(rng.integers(0, w.N, size=6).tolist())
+            rows = np.array(sorted(rows))
+            o_ref, lse_ref = oracle.attn_fwd_rows(q[b, h, rows], rows, k[b, h], v[b, h], w.N, w.causal, w.scale)
+            bound, var, eps, live = bound_rows(q[b, h, rows], rows, k[b, h], v[b, h], w.N, w.causal, w.scale, o_ref)
+            worst = max(worst, check_rows(o[b, h, rows], lse[b, h, rows], o_ref, lse_ref, bound, eps, live,
+                                          "%s head (%d,%d)" % (wname, b, h)))
+            acc.add(o[b, h, rows][live] - o_ref[live], var[live])
+    note("  max err / bound %.3f" % worst)
+    acc.check(wname)
+
+
+def test_fp8_scales_enter_as_stated():
+    """Doubling descale_v doubles O exactly (a power of two), and moving a factor 2 from the key
+    scale to the query scale leaves O and lse unchanged bit for bit."""
+    B, H, N, d = 1, 2, 200, 128
+    note("scale invariances N=%d d=%d" % (N, d))
+    inp = make_fp8_inputs(B, H, N, d, seed=62)
+    o1, l1 = gpu_fwd8(inp, True, softmax_scale(d))
+    inp2 = dict(inp, descale_v=inp["descale_v"] * 2)
+    o2, l2 = gpu_fwd8(inp2, True, softmax_scale(d))
+    assert np.array_equal(o2, 2 * o1) and np.array_equal(l2, l1)
+    inp3 = dict(inp, descale_q=inp["descale_q"] * 2, descale_k=inp["descale_k"] / 2)
+    o3, l3 = gpu_fwd8(inp3, True, softmax_scale(d))
+    assert np.array_equal(o3, o1) and np.array_equal(l3, l1)

@@ -1,7 +1,7 @@
 """Python binding of libattn.so, the gfx950 attention library (C ABI in include/attn.h).
 
 The functions named like the C entry points (``attn_fwd``, ``attn_fwd_qk``,
-``attn_fwd_splitkv`` and its two size helpers, ``attn_bwd``, ``attn_bwd_qk``,
+``attn_fwd_splitkv`` and its two size helpers, ``attn_fwd_fp8``, ``attn_bwd``, ``attn_bwd_qk``,
 ``attn_bwd_preprocess``, ``attn_bwd_dkdv``, ``attn_bwd_dq``,
 ``attn_status_string``) only marshal arguments: tensors become device
 pointers, ``stream=None`` becomes the current PyTorch stream of the tensors'
@@ -13,7 +13,8 @@ library has not been built the first call raises.
 contiguity and allocate the outputs with ``torch.empty``; q may have a
 different number of rows than k and v (causal masks then align to the
 bottom-right corner) and a multiple of their number of heads (grouped-query
-attention).
+attention).  ``fwd_fp8`` does the same for 8-bit (e4m3) inputs with per-head
+scales.
 """
 from __future__ import annotations
 
@@ -49,6 +50,7 @@ _SIGNATURES = {
     "attn_fwd_qk": [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _F, _P],
     "attn_bwd_qk": [_P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _F, _P],
     "attn_fwd_splitkv": [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _F, _I, _P, ctypes.c_longlong, _P],
+    "attn_fwd_fp8": [_P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _F, _P],
     "attn_bwd": [_P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _F, _P],
     "attn_bwd_preprocess": [_P, _P, _P, _I, _I, _I, _I, _P],
     "attn_bwd_dkdv": [_P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _F, _P],
@@ -139,6 +141,12 @@ def attn_fwd_splitkv_workspace_size(B, H, Nq, d, num_splits) -> int:
 
 def attn_fwd_splitkv_default_splits(B, H, Nq, Nk, d) -> int:
     return int(library().attn_fwd_splitkv_default_splits(B, H, Nq, Nk, d))
+
+
+def attn_fwd_fp8(q, k, v, descale_q, descale_k, descale_v, o, lse, B, H, Hk, Nq, Nk, d, causal, scale,
+                 stream=None) -> None:
+    _call("attn_fwd_fp8", _ptr(q), _ptr(k), _ptr(v), _ptr(descale_q), _ptr(descale_k), _ptr(descale_v), _ptr(o),
+          _ptr(lse), B, H, Hk, Nq, Nk, d, int(causal), float(scale), _stream(stream, q, o))
 
 
 def attn_bwd_qk(q, k, v, o, dout, lse, dq, dk, dv, delta, B, H, Hk, Nq, Nk, d, causal, scale, stream=None) -> None:
@@ -240,3 +248,32 @@ def bwd(q, k, v, o, dout, lse, causal: bool = False, scale: float | None = None,
     else:
         attn_bwd_qk(q, k, v, o, dout, lse, dq, dk, dv, delta, B, H, Hk, Nq, Nk, d, causal, scale, stream)
     return dq, dk, dv
+
+
+def fwd_fp8(q8, k8, v8, descale_q, descale_k, descale_v, causal: bool = False, scale: float | None = None,
+            stream=None):
+    """Forward pass on e4m3 inputs: q8 [B,H,Nq,d], k8 and v8 [B,Hk,Nk,d] (torch.float8_e4m3fn or uint8
+    codes), descale_q [B,H], descale_k and descale_v [B,Hk] (float32, the per-head scales).
+    Returns (o bf16 [B,H,Nq,d], lse fp32 [B,H,Nq])."""
+    if q8.dim() != 4 or k8.dim() != 4 or v8.dim() != 4:
+        raise ValueError("expected [B, H, N, d] tensors")
+    for t in (q8, k8, v8):
+        if t.dtype not in (torch.float8_e4m3fn, torch.uint8):
+            raise TypeError("8-bit inputs must be float8_e4m3fn (or their uint8 codes)")
+    for t in (q8, k8, v8, descale_q, descale_k, descale_v):
+        if not t.is_cuda or t.device != q8.device:
+            raise ValueError("tensors must be on the same GPU")
+        if not t.is_contiguous():
+            raise ValueError("tensors must be contiguous")
+    B, H, Nq, d = q8.shape
+    Hk, Nk = k8.shape[1], k8.shape[2]
+    if k8.shape[0] != B or k8.shape[3] != d or v8.shape != k8.shape or Hk < 1 or H % Hk:
+        raise ValueError("k8 and v8 must be [B, Hk, Nk, d] with the B and d of q8 and H a multiple of Hk")
+    for t, heads in ((descale_q, H), (descale_k, Hk), (descale_v, Hk)):
+        if t.dtype != torch.float32 or tuple(t.shape) != (B, heads):
+            raise ValueError("descale_q must be float32 [B, H], descale_k and descale_v float32 [B, Hk]")
+    scale = default_scale(d) if scale is None else scale
+    o = torch.empty((B, H, Nq, d), dtype=torch.bfloat16, device=q8.device)
+    lse = torch.empty((B, H, Nq), dtype=torch.float32, device=q8.device)
+    attn_fwd_fp8(q8, k8, v8, descale_q, descale_k, descale_v, o, lse, B, H, Hk, Nq, Nk, d, causal, scale, stream)
+    return o, lse

@@ -15,7 +15,7 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libattn.so")
-SOURCES = ["attn_api.hip", "attn_fwd.hip", "attn_bwd.hip"]
+SOURCES = ["attn_api.hip", "attn_fwd.hip", "attn_bwd.hip", "attn_fwd_fp8.hip"]
 ARCH = "gfx950"
 
 # Packed fp32 instructions are disabled for all device code.

@@ -131,6 +131,42 @@ int fwd_split_impl(const void *q, const void *k, const void *v, void *o, float *
     return hip_status(attn::launch_fwd_split(a, num_splits, workspace));
 }
 
+// Per-head scale arrays of the 8-bit forward: non-null (unless empty) and 4-byte aligned.
+int check_scale_ptrs(const float *const *ptrs, const long long *bytes, int n)
+{
+    for (int i = 0; i < n; ++i)
+        if (!ptrs[i] && bytes[i] > 0) return ATTN_ERR_NULLPTR;
+    for (int i = 0; i < n; ++i)
+        if (((uintptr_t)ptrs[i] & 3u) != 0) return ATTN_ERR_MISALIGNED;
+    return ATTN_OK;
+}
+
+int fwd_fp8_impl(const void *q, const void *k, const void *v, const float *descale_q, const float *descale_k,
+                 const float *descale_v, void *o, float *lse, int B, int H, int Hk, int Nq, int Nk, int d, int causal,
+                 float scale, void *stream)
+{
+    bool empty = false;
+    RETURN_IF(validate_common(B, H, Hk, Nq, Nk, d, causal, scale, &empty));
+    if (d != 64 && d != 128) return ATTN_ERR_UNSUPPORTED_D;
+    const long long qb = tensor_bytes(B, H, Nq, d), kb = tensor_bytes(B, Hk, Nk, d), lb = vector_bytes(B, H, Nq);
+    if (qb == 0) return ATTN_OK;  // no query rows: nothing to write
+    // 8-bit inputs take half the bytes of the bf16 output
+    const long long q8 = qb / 2, k8 = kb / 2;
+    const long long sqb = (long long)B * H * 4, skb = (long long)B * Hk * 4;
+    const void *ptrs[] = {q, k, v, o, lse};
+    const long long sizes[] = {q8, k8, k8, qb, lb};
+    RETURN_IF(check_ptrs(ptrs, sizes, 5));
+    const float *sptrs[] = {descale_q, descale_k, descale_v};
+    const long long ssizes[] = {sqb, skb, skb};
+    RETURN_IF(check_scale_ptrs(sptrs, ssizes, 3));
+    const Range in[] = {range_of(q, q8), range_of(k, k8), range_of(v, k8),
+                        range_of(descale_q, sqb), range_of(descale_k, skb), range_of(descale_v, skb)};
+    const Range out[] = {range_of(o, qb), range_of(lse, lb)};
+    RETURN_IF(check_alias(in, 6, out, 2));
+    attn::Fp8FwdArgs a{q, k, v, descale_q, descale_k, descale_v, o, lse, B, H, Hk, Nq, Nk, d, causal, scale, stream};
+    return hip_status(attn::launch_fwd_fp8(a));
+}
+
 int bwd_impl(const void *q, const void *k, const void *v, const void *o, const void *dout, const float *lse, void *dq,
              void *dk, void *dv, float *delta, int B, int H, int Hk, int Nq, int Nk, int d, int causal, float scale,
              void *stream)
@@ -174,6 +210,13 @@ int attn_fwd_splitkv(const void *q, const void *k, const void *v, void *o, float
 {
     return fwd_split_impl(q, k, v, o, lse, B, H, Hk, Nq, Nk, d, causal, scale, num_splits, workspace,
                           workspace_bytes, stream);
+}
+
+int attn_fwd_fp8(const void *q, const void *k, const void *v, const float *descale_q, const float *descale_k,
+                 const float *descale_v, void *o, float *lse, int B, int H, int Hk, int Nq, int Nk, int d, int causal,
+                 float scale, void *stream)
+{
+    return fwd_fp8_impl(q, k, v, descale_q, descale_k, descale_v, o, lse, B, H, Hk, Nq, Nk, d, causal, scale, stream);
 }
 
 long long attn_fwd_splitkv_workspace_size(int B, int H, int Nq, int d, int num_splits)

@@ -25,7 +25,19 @@ struct BwdArgs {
     void *stream;
 };
 
+// Forward pass on e4m3 inputs with per-head scales (d = 64 or 128).
+struct Fp8FwdArgs {
+    const void *q, *k, *v;                                 // e4m3 codes
+    const float *descale_q, *descale_k, *descale_v;        // [B*H], [B*Hk], [B*Hk]
+    void *o;                                               // bf16
+    float *lse;
+    int B, H, Hk, Nq, Nk, d, causal;
+    float scale;
+    void *stream;
+};
+
 hipError_t launch_fwd(const FwdArgs &a);
+hipError_t launch_fwd_fp8(const Fp8FwdArgs &a);
 // Split-key forward: partial pieces into `workspace` (fwd_split_workspace_bytes), then the merge.
 hipError_t launch_fwd_split(const FwdArgs &a, int n_splits, void *workspace);
 hipError_t launch_bwd_preprocess(const BwdArgs &a);

@@ -11,6 +11,12 @@ long-sequence workload every query row whose 0-based index is a multiple of 64
 is multiplied by 8 after rounding (exact in bfloat16), which makes the running
 row maximum jump and forces rescaling of the accumulators.  The softmax scale is
 1/sqrt(d) rounded to float32.
+
+8-bit workloads draw the same float32 numbers (same generator, same order, the
+boost applied in float32) and store each (batch, head) slice of Q, K and V as
+e4m3 codes with its own scale: scale = max|x| / 448 over the slice (448 being the
+largest e4m3 value), codes = e4m3(x / scale), rounded to nearest even.  The
+scales are float32.
 """
 from __future__ import annotations
 
@@ -35,6 +41,7 @@ class Workload:
     boost: float = 8.0
     seed: int = 0
     Nk: int | None = None     # key length when it differs from the query length
+    fp8: bool = False         # Q, K, V as e4m3 codes with per-head scales
     note: str = field(default="", compare=False)
 
     @property
@@ -50,7 +57,7 @@ class Workload:
         return softmax_scale(self.d)
 
     def describe(self) -> str:
-        kind = "fwd+bwd" if self.backward else "fwd"
+        kind = ("fwd+bwd" if self.backward else "fwd") + (" e4m3" if self.fp8 else "")
         mask = "causal" if self.causal else "non-causal"
         s = "%s %s B=%d H=%d N=%d d=%d" % (kind, mask, self.B, self.H, self.N, self.d)
         if self.Nk is not None:
@@ -70,6 +77,9 @@ WORKLOADS = {
     # long key/value cache of 1 GiB; causal with bottom-right alignment, so the row sees every
     # key.  32 heads alone would occupy 32 of the 256 compute units without splitting.
     "dec": Workload("dec", 2, 16, 1, 128, True, Nk=65536, note="decoding, split-key forward"),
+    # 8-bit forward (widening): the shapes of c3 and c4 with e4m3 inputs
+    "c3f8": Workload("c3f8", 2, 32, 4096, 128, True, fp8=True, note="8-bit forward"),
+    "c4f8": Workload("c4f8", 1, 16, 16384, 128, True, boost_every=64, fp8=True, note="8-bit forward"),
 }
 
 
@@ -96,7 +106,34 @@ def make_inputs(B: int, H: int, nq: int, d: int, *, nk: int | None = None, seed:
     return out
 
 
+def make_fp8_inputs(B: int, H: int, nq: int, d: int, *, nk: int | None = None, Hk: int | None = None,
+                    seed: int = 0, boost_every: int = 0, boost: float = 8.0) -> dict:
+    """Draw Q, K, V in float32 and store them as per-head scaled e4m3 codes.
+
+    Returns q8 ``[B, H, nq, d]``, k8 and v8 ``[B, Hk, nk, d]`` (torch.float8_e4m3fn CPU tensors) and
+    descale_q ``[B, H]``, descale_k and descale_v ``[B, Hk]`` (float32): the real input is
+    descale * code value."""
+    nk = nq if nk is None else nk
+    Hk = H if Hk is None else Hk
+    g = torch.Generator().manual_seed(seed)
+    q = torch.randn(B, H, nq, d, generator=g, dtype=torch.float32)
+    k = torch.randn(B, Hk, nk, d, generator=g, dtype=torch.float32)
+    v = torch.randn(B, Hk, nk, d, generator=g, dtype=torch.float32)
+    if boost_every:
+        q[:, :, ::boost_every, :] *= boost
+    out = {}
+    for name, x in (("q", q), ("k", k), ("v", v)):
+        amax = x.abs().amax(dim=(2, 3)) if x.numel() else torch.zeros(x.shape[:2])
+        ds = torch.where(amax > 0, amax / 448.0, torch.ones_like(amax)).to(torch.float32)
+        codes = (x / ds[:, :, None, None]).clamp(-448.0, 448.0).to(torch.float8_e4m3fn)
+        out[name + "8"] = codes
+        out["descale_" + name] = ds
+    return out
+
+
 def workload_inputs(w: Workload) -> dict:
+    if w.fp8:
+        return make_fp8_inputs(w.B, w.H, w.nq, w.d, nk=w.nk, seed=w.seed, boost_every=w.boost_every, boost=w.boost)
     return make_inputs(w.B, w.H, w.nq, w.d, nk=w.nk, seed=w.seed, backward=w.backward,
                        boost_every=w.boost_every, boost=w.boost)
 
@@ -104,7 +141,8 @@ def workload_inputs(w: Workload) -> dict:
 def inputs_sha256(tensors: dict) -> str:
     """SHA-256 over the raw bytes of the tensors, in key order q, k, v, do."""
     h = hashlib.sha256()
-    for key in ("q", "k", "v", "do"):
+    for key in ("q", "k", "v", "do", "q8", "k8", "v8", "descale_q", "descale_k", "descale_v"):
         if key in tensors:
-            h.update(tensors[key].contiguous().view(torch.int16).numpy().tobytes())
+            t = tensors[key].contiguous()
+            h.update(t.view(torch.uint8).numpy().tobytes())
     return h.hexdigest()

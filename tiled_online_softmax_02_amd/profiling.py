@@ -21,9 +21,9 @@ import sys
 from collections import defaultdict
 
 PKG = os.path.dirname(os.path.abspath(__file__))
-KERNEL_SOURCES = ["attn_device.h", "attn_fwd.hip", "attn_bwd.hip"]
+KERNEL_SOURCES = ["attn_device.h", "attn_fwd.hip", "attn_bwd.hip", "attn_fwd_fp8.hip"]
 CALIBRATION_BYTES = 256 << 20   # bench.py copies 64 Mi int32 values before timing
-SHORT = {"fwd_kernel": "fwd", "fwd_combine_kernel": "combine", "bwd_dkdv_kernel": "dkdv", "bwd_dq_kernel": "dq",
+SHORT = {"fwd_kernel": "fwd", "fwd_fp8_kernel": "fwd_fp8", "fwd_combine_kernel": "combine", "bwd_dkdv_kernel": "dkdv", "bwd_dq_kernel": "dq",
          "bwd_preprocess_kernel": "preprocess"}
 
 
@@ -53,7 +53,7 @@ def stats_summary(stats_csv: str, command: str) -> str:
             name, r["Calls"], float(r["AverageNs"]) / 1e3, float(r["MinNs"]) / 1e3, float(r["MaxNs"]) / 1e3,
             100.0 * float(r["TotalDurationNs"]) / total))
     lines.append("")
-    lines.append("kernel source sha (attn_device.h, attn_fwd.hip, attn_bwd.hip): " + kernel_source_sha())
+    lines.append("kernel source sha (%s): %s" % (", ".join(KERNEL_SOURCES), kernel_source_sha()))
     return "\n".join(lines) + "\n"
 
 
