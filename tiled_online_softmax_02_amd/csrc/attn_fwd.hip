@@ -161,7 +161,12 @@ __global__ __launch_bounds__(64 * fwd_waves<D>(), fwd_min_blocks<D>()) void fwd_
         };
         float mloc = -__builtin_inff();  // local maximum of the block whose scores are current
 
-        auto active = [&](int j) __attribute__((always_inline)) { return (qw0 < Nq) && (!CAUSAL || j * kFwdBN <= qw0 + 31 + off); };
+        // The wave works on key blocks [jb, ja) and only loads and waits on [ja, je): under the
+        // causal mask the blocks from ja on lie wholly above its rows.  Two loops with no branch
+        // on the block index inside keep the score registers out of control flow.
+        const int last_key = qw0 + 31 + off;  // last key some row of the wave sees (causal)
+        const int ja = (qw0 >= Nq) ? jb
+                       : (!CAUSAL ? je : (last_key < 0 ? jb : max(jb, min(je, last_key / kFwdBN + 1))));
 
         // prologue: K0, V0 and K1 in LDS, scores of block 0 in registers
         using P0 = std::integral_constant<int, 0>;
@@ -172,7 +177,7 @@ __global__ __launch_bounds__(64 * fwd_waves<D>(), fwd_min_blocks<D>()) void fwd_
         wait_vmem();
         __syncthreads();
         f32x16 sa[2], sb[2];
-        if (active(jb)) {  // (an empty piece computes these and never uses them)
+        if (ja > jb) {
             scores(P0{}, sa);
             mloc = local_max(sa);
         }
@@ -180,10 +185,18 @@ __global__ __launch_bounds__(64 * fwd_waves<D>(), fwd_min_blocks<D>()) void fwd_
         // reading K0 first (rows past the end come back as zeros almost at once)
         __syncthreads();
 
+        // A step on a key block the wave does not see: the loads of the pipeline and the barrier.
+        auto step_idle = [&](int j, auto par) __attribute__((always_inline)) {
+            using PN = std::integral_constant<int, 1 - decltype(par)::value>;
+            load_k(j + 2, par);
+            load_v(j + 1, PN{});
+            wait_vmem();
+            __syncthreads();
+        };
         // One pipeline step on key block j: scores of j are in `cur`, scores of j+1 go to `nxt`.
         auto step = [&](int j, auto par, f32x16 *cur, f32x16 *nxt) __attribute__((always_inline)) {
             using PN = std::integral_constant<int, 1 - decltype(par)::value>;  // parity of j + 1
-            if (active(j)) {
+            {
                 const int k0 = j * kFwdBN;
                 if ((CAUSAL && (k0 + kFwdBN - 1 > qw0 + off)) || (k0 + kFwdBN > Nk)) {
 #pragma unroll
@@ -284,20 +297,24 @@ __global__ __launch_bounds__(64 * fwd_waves<D>(), fwd_min_blocks<D>()) void fwd_
                 l_run += rs;
                 mloc = mx;
                 __builtin_amdgcn_s_setprio(0);
-            } else {
-                load_k(j + 2, par);
-                load_v(j + 1, PN{});
             }
             wait_vmem();
             __syncthreads();
         };
 
+        // stage parity of block j is (j - jb) & 1
         int j = jb;
-        for (; j + 1 < je; j += 2) {
+        for (; j + 1 < ja; j += 2) {
             step(j, P0{}, sa, sb);
             step(j + 1, P1{}, sb, sa);
         }
-        if (j < je) step(j, P0{}, sa, sb);
+        if (j < ja) step(j++, P0{}, sa, sb);
+        if (j < je && ((j - jb) & 1)) step_idle(j++, P1{});
+        for (; j + 1 < je; j += 2) {
+            step_idle(j, P0{});
+            step_idle(j + 1, P1{});
+        }
+        if (j < je) step_idle(j, P0{});
 
         // epilogue: O = acc / l (bf16, nearest even), lse = m*scale + ln(l)
         const float l_tot = l_run + __shfl_xor(l_run, 32);
