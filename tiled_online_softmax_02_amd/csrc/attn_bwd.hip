@@ -355,13 +355,23 @@ __global__ __launch_bounds__(kThreads, D >= 192 ? 1 : 2) void bwd_dq_kernel(
     wait_vmem();
     __syncthreads();
 
+    // The wave works on key blocks [0, ja) and only loads and waits on [ja, nt) (causal: the
+    // blocks wholly above its rows); separate loops keep the block index out of the step.
+    const int last_key = qw0 + 31 + off;
+    const int ja = (qw0 >= Nq) ? 0 : (!CAUSAL ? nt : (last_key < 0 ? 0 : min(nt, last_key / kQBN + 1)));
+    auto step_idle = [&](int j, auto par) __attribute__((always_inline)) {
+        using PN = std::integral_constant<int, 1 - decltype(par)::value>;
+        load_blk(j + 1, PN{});
+        wait_vmem();
+        __syncthreads();
+    };
     auto step = [&](int j, auto par) __attribute__((always_inline)) {
         using PN = std::integral_constant<int, 1 - decltype(par)::value>;
         load_blk(j + 1, PN{});  // past the last block: zeros into the free stage, never read
         const lds_char *ks = kst_l(par);
         const lds_char *vs = vst_l(par);
         const int k0 = j * kQBN;
-        if ((qw0 < Nq) && (!CAUSAL || k0 <= qw0 + 31 + off)) {
+        {
             f32x16 s[2] = {zero16(), zero16()};
             f32x16 dp[2] = {zero16(), zero16()};
 #pragma unroll
@@ -407,12 +417,19 @@ __global__ __launch_bounds__(kThreads, D >= 192 ? 1 : 2) void bwd_dq_kernel(
         __syncthreads();
     };
 
+    // stage parity of key block j is j & 1
     int j = 0;
-    for (; j + 1 < nt; j += 2) {
+    for (; j + 1 < ja; j += 2) {
         step(j, P0{});
         step(j + 1, P1{});
     }
-    if (j < nt) step(j, P0{});
+    if (j < ja) step(j++, P0{});
+    if (j < nt && (j & 1)) step_idle(j++, P1{});
+    for (; j + 1 < nt; j += 2) {
+        step_idle(j, P0{});
+        step_idle(j + 1, P1{});
+    }
+    if (j < nt) step_idle(j, P0{});
 
     if (row_ok) {
         bf16 *qrow_p = dQ + hoff + (size_t)qrow * D;
