@@ -53,19 +53,26 @@ def visible_pairs(Nq, Nk, causal) -> int:
     return sum(min(Nk, max(0, i + off + 1)) for i in range(Nq))
 
 
-def workload_flop(w) -> float:
-    """Forward FLOP of a workload: the convention for equal lengths, 4*d per visible pair otherwise."""
+def workload_fwd_flop(w) -> float:
+    """Forward FLOP of a workload: the convention for equal lengths, 4*d per visible pair otherwise
+    (both count query heads, so grouped K/V heads change nothing)."""
     if w.nq == w.nk:
-        return step_flop(w.B, w.H, w.N, w.d, w.causal, w.backward)
+        return fwd_flop(w.B, w.H, w.N, w.d, w.causal)
     return 4.0 * w.B * w.H * w.d * visible_pairs(w.nq, w.nk, w.causal)
 
 
-def kernel_algorithmic_flop(kernel, B, H, N, d, causal) -> float:
-    """Algorithmic FLOP one launch performs, in units of one N x N x d product (the
+def workload_flop(w) -> float:
+    """FLOP of one step: the forward, times 3.5 with the backward (which counts 2.5x)."""
+    return workload_fwd_flop(w) * (3.5 if w.backward else 1.0)
+
+
+def kernel_algorithmic_flop(kernel, w) -> float:
+    """Algorithmic FLOP one launch performs, in units of one Nq x Nk x d product (the
     forward is two of them): fwd 2 (QK^T, PV); dkdv 4 (the recomputed S, dP, dV, dK);
-    dq 1 (dQ; its recomputed S and dP are counted in dkdv); preprocess 0."""
-    unit = fwd_flop(B, H, N, d, causal) / 2.0
-    return unit * {"fwd": 2, "fwd_fp8": 2, "dkdv": 4, "dq": 1, "preprocess": 0}[kernel]
+    dq 1 (dQ; its recomputed S and dP are counted in dkdv); preprocess 0; bwd 5 (the three
+    backward kernels of one attn_bwd_qk call, timed together)."""
+    unit = workload_fwd_flop(w) / 2.0
+    return unit * {"fwd": 2, "fwd_fp8": 2, "dkdv": 4, "dq": 1, "preprocess": 0, "bwd": 5}[kernel]
 
 
 def stored_traffic(kernel: str, workload: str):
@@ -160,7 +167,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--workload", default="c5", choices=["c2", "c3", "c4", "c5", "dec", "c3f8", "c4f8"])
+    ap.add_argument("--workload", default="c5", choices=["c2", "c3", "c4", "c5", "dec", "c3f8", "c4f8", "c5g", "c5d256", "c5u"])
     ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle work for the CPU baseline")
     ap.add_argument("--ramp-seconds", type=float, default=1.0,
                     help="untimed steps for this long before the warmup steps, so that the GPU clocks "
@@ -188,7 +195,10 @@ def main():
     else:
         q, k, v = (inp[n].to(dev) for n in ("q", "k", "v"))
     B, H, N, d = q.shape
-    Nk = k.shape[2]
+    Hk, Nk = k.shape[1], k.shape[2]
+    # grouped heads or unequal lengths: the _qk entry points (the backward's three kernels are
+    # then one call and are timed together)
+    qk = Hk != H or Nk != N
     split = w.name == "dec"  # decoding: the split-key forward (partial pieces, then their merge)
     if split:
         ns = A.attn_fwd_splitkv_default_splits(B, H, N, Nk, d)
@@ -211,7 +221,7 @@ def main():
     del cal_src, cal_dst
 
     kernels = (["fwd_splitkv"] if split else ["fwd_fp8"] if fp8 else ["fwd"]) + (
-        ["preprocess", "dkdv", "dq"] if w.backward else [])
+        (["bwd"] if qk else ["preprocess", "dkdv", "dq"]) if w.backward else [])
     ev = {kname: [] for kname in kernels}
 
     def step(record):
@@ -222,11 +232,17 @@ def main():
             A.attn_fwd_splitkv(q, k, v, o, lse, B, H, H, N, Nk, d, causal, scale, ns, ws, ws_bytes)
         elif fp8:
             A.attn_fwd_fp8(q, k, v, dsq, dsk, dsv, o, lse, B, H, H, N, Nk, d, causal, scale)
+        elif qk:
+            A.attn_fwd_qk(q, k, v, o, lse, B, H, Hk, N, Nk, d, causal, scale)
         else:
             A.attn_fwd(q, k, v, o, lse, B, H, N, d, causal, scale)
         if record:
             e[1].record()
-        if w.backward:
+        if w.backward and qk:
+            A.attn_bwd_qk(q, k, v, o, do, lse, dq, dk, dv, delta, B, H, Hk, N, Nk, d, causal, scale)
+            if record:
+                e[2].record()
+        elif w.backward:
             A.attn_bwd_preprocess(o, do, delta, B, H, N, d)
             if record:
                 e[2].record()
@@ -269,8 +285,8 @@ def main():
                 "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": stored_traffic(dom, w.name),
                 "algorithmic_bytes": alg_bytes, "num_splits": ns}
     else:
-        fwd_t = fwd_flop(B, H, N, d, causal) / (kernel_ms[kernels[0]] * 1e-3) / 1e12
-        achieved = kernel_algorithmic_flop(dom, B, H, N, d, causal) / (kernel_ms[dom] * 1e-3) / 1e12
+        fwd_t = workload_fwd_flop(w) / (kernel_ms[kernels[0]] * 1e-3) / 1e12
+        achieved = kernel_algorithmic_flop(dom, w) / (kernel_ms[dom] * 1e-3) / 1e12
         roof = {"kernel": dom, "bound": "mfma", "achieved": round(achieved, 2), "peak": peak,
                 "unit": "TFLOP/s", "frac": round(achieved / peak, 4),
                 "traffic": stored_traffic(dom, w.name)}
@@ -278,6 +294,8 @@ def main():
               "scale": scale, "global_batch": B, "seq_len": N, "parallelism": "single GPU"}
     if Nk != N:
         config["Nk"] = Nk
+    if Hk != H:
+        config["Hk"] = Hk
     out = {
         "metric": METRIC,
         "value": round(value, 2),
@@ -299,8 +317,8 @@ def main():
         "roofline": roof,
     }
     if w.backward:
-        out["bwd_tflops"] = round(2.5 * fwd_flop(B, H, N, d, causal)
-                                  / (sum(kernel_ms[x] for x in ("preprocess", "dkdv", "dq")) * 1e-3) / 1e12, 2)
+        bwd_ms = kernel_ms["bwd"] if qk else sum(kernel_ms[x] for x in ("preprocess", "dkdv", "dq"))
+        out["bwd_tflops"] = round(2.5 * workload_fwd_flop(w) / (bwd_ms * 1e-3) / 1e12, 2)
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(w, args.cpu_budget)
     else:

@@ -24,9 +24,12 @@ def test_causal_halves_and_backward_is_two_and_a_half_forwards():
     f = bench.fwd_flop(2, 16, 4096, 128, False)
     assert bench.fwd_flop(2, 16, 4096, 128, True) == f / 2
     assert bench.step_flop(2, 16, 4096, 128, True, True) == pytest.approx(3.5 * f / 2)
-    # per-kernel algorithmic counts add up to the whole step
-    parts = sum(bench.kernel_algorithmic_flop(k, 2, 16, 4096, 128, True) for k in ("fwd", "preprocess", "dkdv", "dq"))
+    # per-kernel algorithmic counts add up to the whole step, and so does the backward timed as one
+    from tiled_online_softmax_02_amd.inputs import WORKLOADS
+    c5 = WORKLOADS["c5"]
+    parts = sum(bench.kernel_algorithmic_flop(k, c5) for k in ("fwd", "preprocess", "dkdv", "dq"))
     assert parts == pytest.approx(bench.step_flop(2, 16, 4096, 128, True, True))
+    assert bench.kernel_algorithmic_flop("fwd", c5) + bench.kernel_algorithmic_flop("bwd", c5) == pytest.approx(parts)
 
 
 def test_more_than_one_gpu_is_refused_with_a_message():
@@ -55,3 +58,14 @@ def test_decoding_workload_flop():
     # the equal-length workloads keep the convention
     c5 = WORKLOADS["c5"]
     assert bench.workload_flop(c5) == bench.step_flop(2, 16, 4096, 128, True, True)
+
+
+def test_widened_workloads_flop():
+    from tiled_online_softmax_02_amd.inputs import WORKLOADS
+    # grouped heads: FLOP count query heads, the same as c5
+    assert bench.workload_flop(WORKLOADS["c5g"]) == bench.workload_flop(WORKLOADS["c5"])
+    # 2048 queries against 4096 keys, causal bottom-right: query i sees 2048 + i + 1 keys
+    w = WORKLOADS["c5u"]
+    pairs = sum(2048 + i + 1 for i in range(2048))
+    assert bench.workload_flop(w) == pytest.approx(3.5 * 4.0 * 2 * 16 * 128 * pairs)
+    assert bench.workload_flop(WORKLOADS["c5d256"]) == bench.step_flop(2, 16, 4096, 256, True, True)

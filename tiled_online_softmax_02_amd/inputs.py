@@ -42,6 +42,7 @@ class Workload:
     seed: int = 0
     Nk: int | None = None     # key length when it differs from the query length
     fp8: bool = False         # Q, K, V as e4m3 codes with per-head scales
+    Hk: int | None = None     # K/V heads when fewer than the query heads (grouped-query attention)
     note: str = field(default="", compare=False)
 
     @property
@@ -53,6 +54,10 @@ class Workload:
         return self.N if self.Nk is None else self.Nk
 
     @property
+    def hk(self) -> int:
+        return self.H if self.Hk is None else self.Hk
+
+    @property
     def scale(self) -> float:
         return softmax_scale(self.d)
 
@@ -60,6 +65,8 @@ class Workload:
         kind = ("fwd+bwd" if self.backward else "fwd") + (" e4m3" if self.fp8 else "")
         mask = "causal" if self.causal else "non-causal"
         s = "%s %s B=%d H=%d N=%d d=%d" % (kind, mask, self.B, self.H, self.N, self.d)
+        if self.Hk is not None:
+            s += " Hk=%d" % self.Hk
         if self.Nk is not None:
             s += " Nk=%d" % self.Nk
         if self.boost_every:
@@ -80,6 +87,11 @@ WORKLOADS = {
     # 8-bit forward (widening): the shapes of c3 and c4 with e4m3 inputs
     "c3f8": Workload("c3f8", 2, 32, 4096, 128, True, fp8=True, note="8-bit forward"),
     "c4f8": Workload("c4f8", 1, 16, 16384, 128, True, boost_every=64, fp8=True, note="8-bit forward"),
+    # the other widened rows at the size of c5: grouped heads (4 query heads per K/V head),
+    # head dimension 256, and half as many queries as keys (bottom-right causal alignment)
+    "c5g": Workload("c5g", 2, 16, 4096, 128, True, backward=True, Hk=4, note="grouped-query attention"),
+    "c5d256": Workload("c5d256", 2, 16, 4096, 256, True, backward=True, note="head dimension 256"),
+    "c5u": Workload("c5u", 2, 16, 2048, 128, True, backward=True, Nk=4096, note="unequal lengths"),
 }
 
 
@@ -89,15 +101,16 @@ def softmax_scale(d: int) -> float:
 
 
 def make_inputs(B: int, H: int, nq: int, d: int, *, nk: int | None = None, seed: int = 0,
-                backward: bool = False, boost_every: int = 0, boost: float = 8.0) -> dict:
+                backward: bool = False, boost_every: int = 0, boost: float = 8.0, Hk: int | None = None) -> dict:
     """Draw Q, K, V (and dO when ``backward``) as bfloat16 CPU tensors.
 
-    Shapes: q and do ``[B, H, nq, d]``; k and v ``[B, H, nk, d]``."""
+    Shapes: q and do ``[B, H, nq, d]``; k and v ``[B, Hk, nk, d]`` (Hk = H unless given)."""
     nk = nq if nk is None else nk
+    Hk = H if Hk is None else Hk
     g = torch.Generator().manual_seed(seed)
     q = torch.randn(B, H, nq, d, generator=g, dtype=torch.float32).to(torch.bfloat16)
-    k = torch.randn(B, H, nk, d, generator=g, dtype=torch.float32).to(torch.bfloat16)
-    v = torch.randn(B, H, nk, d, generator=g, dtype=torch.float32).to(torch.bfloat16)
+    k = torch.randn(B, Hk, nk, d, generator=g, dtype=torch.float32).to(torch.bfloat16)
+    v = torch.randn(B, Hk, nk, d, generator=g, dtype=torch.float32).to(torch.bfloat16)
     out = {"q": q, "k": k, "v": v}
     if backward:
         out["do"] = torch.randn(B, H, nq, d, generator=g, dtype=torch.float32).to(torch.bfloat16)
@@ -135,7 +148,7 @@ def workload_inputs(w: Workload) -> dict:
     if w.fp8:
         return make_fp8_inputs(w.B, w.H, w.nq, w.d, nk=w.nk, seed=w.seed, boost_every=w.boost_every, boost=w.boost)
     return make_inputs(w.B, w.H, w.nq, w.d, nk=w.nk, seed=w.seed, backward=w.backward,
-                       boost_every=w.boost_every, boost=w.boost)
+                       boost_every=w.boost_every, boost=w.boost, Hk=w.Hk)
 
 
 def inputs_sha256(tensors: dict) -> str:
