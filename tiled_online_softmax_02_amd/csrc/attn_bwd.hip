@@ -13,7 +13,11 @@
 // Splitting dQ into its own kernel keeps every sum in registers of a single
 // workgroup: no atomics, bitwise reproducible results.
 //
-// MFMA layouts follow attn_device.h.  In the dK/dV kernel the scores are
+// Two dK/dV kernels: bwd_dkdv2_kernel (d <= 128) splits each key block's work between the
+// two waves of a SIMD (one computes P and dV, the other dS and dK); bwd_dkdv_kernel
+// (d = 192, 256) has one wave per SIMD doing all four products.
+//
+// MFMA layouts follow attn_device.h.  In the dK/dV kernels the scores are
 // computed as S = Q K^T (each lane: one key, 16 queries of a 32-query block),
 // so P and dS feed dV^T += dO^T P and dK^T += Q^T dS from registers, with dO^T
 // and Q^T read from LDS by transposing reads.  In the dQ kernel the scores are
@@ -56,10 +60,12 @@ __global__ __launch_bounds__(kThreads) void bwd_preprocess_kernel(const bf16 *__
 
 // ------------------------------------------------------------ dK / dV
 
-// d <= 128: each of the 4 waves owns 32 keys (128 keys per workgroup) and all of d.  d = 192
-// and 256: the dK/dV accumulators of 32 keys over all of d do not fit next to the K and V
-// fragments, so waves w and w + 2 share 32 keys and take one half of the columns of dK and dV
-// each (64 keys per workgroup); both compute the same S and dP.
+// One wave per SIMD; launched for d = 192 and 256 (d <= 128 launches the paired-wave kernel
+// below; the code here is written for every width).  d <= 128: each of the 4 waves owns 32 keys
+// (128 keys per workgroup) and all of d.  d = 192 and 256: the dK/dV accumulators
+// of 32 keys over all of d do not fit next to the K and V fragments, so waves w and w + 2 share
+// 32 keys and take one half of the columns of dK and dV each (64 keys per workgroup); both
+// compute the same S and dP.
 template <int D>
 constexpr bool kv_dsplit() { return D >= 192; }
 template <int D>
