@@ -95,6 +95,19 @@ def stored_traffic(kernel: str, workload: str):
     return rec.get("hbm_bytes_per_launch")
 
 
+def host_cpu() -> dict:
+    """CPU model and logical core count of the host the oracle runs on."""
+    model = "unknown"
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                model = line.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
+    return {"cpu_model": model, "nproc": os.cpu_count()}
+
+
 def cpu_baseline(w, budget_s: float):
     """Time the fp64 CPU oracle on whole heads of the workload until ~budget_s of work."""
     import numpy as np
@@ -272,6 +285,10 @@ def main():
     ms_per_step = dt * 1e3 / args.steps
 
     kernel_ms = {kname: sum(a.elapsed_time(b) for a, b in pairs) / len(pairs) for kname, pairs in ev.items()}
+    kernel_stats = {}
+    for kname, pairs in ev.items():
+        ts = sorted(a.elapsed_time(b) for a, b in pairs)
+        kernel_stats[kname] = {"median": round(ts[len(ts) // 2], 4), "min": round(ts[0], 4), "max": round(ts[-1], 4)}
     flop = workload_flop(w)
     value = flop / (ms_per_step * 1e-3) / 1e12
     peak = PEAK_FP8_TFLOPS if fp8 else PEAK_BF16_TFLOPS  # the products' own dtype
@@ -314,6 +331,7 @@ def main():
         "peak_tflops": peak,
         "fwd_tflops": round(fwd_t, 2),
         "kernel_ms": {kname: round(t, 4) for kname, t in kernel_ms.items()},
+        "kernel_ms_stats": kernel_stats,
         "roofline": roof,
     }
     if w.backward:
@@ -321,6 +339,7 @@ def main():
         out["bwd_tflops"] = round(2.5 * workload_fwd_flop(w) / (bwd_ms * 1e-3) / 1e12, 2)
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(w, args.cpu_budget)
+        out["cpu_baseline"].update(host_cpu())
     else:
         out["cpu_baseline"] = None
     print(json.dumps(out), flush=True)

@@ -10,6 +10,10 @@
     size is known: 256 MiB read, 256 MiB written), which calibrates the counter units.
     One file ``hbm_traffic_<kernel>_<workload>.txt`` is written per kernel; bench.py reports it
     as ``roofline.traffic`` while the kernel sources are unchanged.
+
+``python -m tiled_online_softmax_02_amd.profiling sq <out.txt> "<commands>" <pass1.csv> <pass2.csv> ...``
+    averages ``rocprofv3 --pmc`` SQ counters per dispatch for each attention kernel and derives
+    the matrix-core busy fraction and the vector and LDS instruction activity per SIMD.
 """
 from __future__ import annotations
 
@@ -101,10 +105,48 @@ def traffic_summaries(fetch_csv: str, write_csv: str, workload: str, out_dir: st
     return written
 
 
+# MI355X: 256 CUs of 4 SIMDs in 32 shader engines; the SQ cycle counters are summed over the
+# engines, the wave-level activity counters count 4-cycle units summed over waves.
+N_SE, N_SIMD = 32, 1024
+
+
+def sq_summary(csvs: list[str], commands: str) -> str:
+    vals = defaultdict(lambda: defaultdict(list))
+    for path in csvs:
+        for r in csv.DictReader(open(path)):
+            k = short_name(r["Kernel_Name"])
+            if k:
+                vals[k][r["Counter_Name"]].append(float(r["Counter_Value"]))
+    lines = ["rocprofv3 SQ counters, average per dispatch", "commands: " + commands, ""]
+    for k in sorted(vals):
+        c = {n: sum(v) / len(v) for n, v in vals[k].items()}
+        lines.append("== %s" % k)
+        for n in sorted(c):
+            lines.append("  %-28s %16.0f" % (n, c[n]))
+        if "SQ_CYCLES" in c:
+            cyc = c["SQ_CYCLES"] / N_SE  # kernel cycles (per engine)
+            derived = []
+            if "SQ_VALU_MFMA_BUSY_CYCLES" in c:
+                derived.append("matrix cores busy %.1f%% of SIMD cycles" % (100 * c["SQ_VALU_MFMA_BUSY_CYCLES"] / (N_SIMD * cyc)))
+            if "SQ_ACTIVE_INST_VALU" in c:
+                derived.append("vector instructions active %.1f%%" % (100 * 4 * c["SQ_ACTIVE_INST_VALU"] / (N_SIMD * cyc)))
+            if "SQ_ACTIVE_INST_LDS" in c:
+                derived.append("LDS instructions active %.1f%%" % (100 * 4 * c["SQ_ACTIVE_INST_LDS"] / (N_SIMD * cyc)))
+            if "SQ_WAIT_INST_ANY" in c and "SQ_WAVE_CYCLES" in c:
+                derived.append("waves waiting to issue %.1f%% of their cycles" % (100 * c["SQ_WAIT_INST_ANY"] / c["SQ_WAVE_CYCLES"]))
+            lines.append("  derived (kernel %.0f cycles): %s" % (cyc, "; ".join(derived)))
+        lines.append("")
+    lines.append("kernel source sha (%s): %s" % (", ".join(KERNEL_SOURCES), kernel_source_sha()))
+    return "\n".join(lines) + "\n"
+
+
 if __name__ == "__main__":
     if sys.argv[1] == "stats":
         with open(sys.argv[3], "w") as f:
             f.write(stats_summary(sys.argv[2], sys.argv[4]))
+    elif sys.argv[1] == "sq":
+        with open(sys.argv[2], "w") as f:
+            f.write(sq_summary(sys.argv[4:], sys.argv[3]))
     elif sys.argv[1] == "traffic":
         for p in traffic_summaries(sys.argv[2], sys.argv[3], sys.argv[4], sys.argv[5], sys.argv[6]):
             print(p)
