@@ -546,6 +546,226 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv2_kernel(
     }
 }
 
+// ------------------------------------------------------------ dK / dV, paired waves (d = 192, 256)
+
+// The paired-wave scheme of bwd_dkdv2_kernel for the wide heads: eight waves in four SIMD pairs;
+// wave w has role w / 4 (P wave or dS wave), key group w % 2 (32 keys; 64 keys per workgroup)
+// and column half (w / 2) % 2 of dK and dV.  The two waves of a column pair both form S (P
+// waves) or dP (dS waves) over all of d, and each accumulates its half of the columns, which
+// keeps every wave's registers (one key-side operand over d, half an accumulator) under the
+// 256 that two waves per SIMD allow.  Query blocks are 32 rows so that three stages of Q and dO
+// fit in LDS.  The P wave of column half 0 leaves P in LDS for the dS waves, one block behind.
+template <int D, bool CAUSAL>
+__global__ __launch_bounds__(512, 1) void bwd_dkdv3_kernel(
+    const bf16 *__restrict__ Q, const bf16 *__restrict__ K, const bf16 *__restrict__ V, const bf16 *__restrict__ dO,
+    const float *__restrict__ LSE, const float *__restrict__ Dl, bf16 *__restrict__ dK, bf16 *__restrict__ dV, int Nq,
+    int Nk, int H, int G, int n_ktiles, float scale, float c_log2)
+{
+    static_assert(D == 192 || D == 256, "wide-head dK/dV kernel");
+    constexpr int NKS = D / 16;
+    constexpr int NDBH = D / 64;     // 32-column blocks of each half of dK, dV
+    constexpr int BMQ = 32;          // queries per streamed block
+    constexpr int TILE = BMQ * D * 2;
+    constexpr int kBN = 64;
+    constexpr int PBUF = 2 * 2 * 64 * 16;  // P of the two key groups (2 KB each)
+    __shared__ __attribute__((aligned(16))) char q0_raw[TILE], q1_raw[TILE], q2_raw[TILE];
+    __shared__ __attribute__((aligned(16))) char g0_raw[TILE], g1_raw[TILE], g2_raw[TILE];
+    __shared__ __attribute__((aligned(16))) float s0_raw[2 * BMQ], s1_raw[2 * BMQ], s2_raw[2 * BMQ];  // lse, D
+    __shared__ __attribute__((aligned(16))) char p0_raw[PBUF], p1_raw[PBUF];
+
+    int head, ktile;
+    work_item(blockIdx.x, n_ktiles, head, ktile);
+    const int Hk = H / G;
+    const int qh0 = (head / Hk) * H + (head % Hk) * G;
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63, h = lane >> 5, c32 = lane & 31;
+    const int w = wave_uniform(tid >> 6);
+    const int kg = w & 1, ch = (w >> 1) & 1;
+    const bool pwave = w < 4;
+    const int db0 = ch * NDBH;
+    const size_t hoff = (size_t)head * (size_t)Nk * D;
+    __amdgpu_buffer_rsrc_t rq, rg, rl, rd;
+    auto bind_query_head = [&](int qh) __attribute__((always_inline)) {
+        const size_t hoff_q = (size_t)qh * (size_t)Nq * D;
+        rq = make_rsrc(Q + hoff_q, (uint32_t)Nq * D * 2);
+        rg = make_rsrc(dO + hoff_q, (uint32_t)Nq * D * 2);
+        rl = make_rsrc(LSE + (size_t)qh * Nq, (uint32_t)Nq * 4);
+        rd = make_rsrc(Dl + (size_t)qh * Nq, (uint32_t)Nq * 4);
+    };
+    const int off = Nk - Nq;
+    const int k0 = ktile * kBN;
+    const int kw0 = k0 + 32 * kg;
+    const int key = kw0 + c32;
+    const bool keys_ok = kw0 < Nk;
+
+    bf16x8 kvf[NKS];  // K (P wave) or V (dS wave) of the lane's key, over all of d
+    {
+        const __amdgpu_buffer_rsrc_t rkv = make_rsrc((pwave ? K : V) + hoff, (uint32_t)Nk * D * 2);
+#pragma unroll
+        for (int ks = 0; ks < NKS; ++ks)
+            kvf[ks] = __builtin_bit_cast(bf16x8, buffer_load16(rkv, (uint32_t)(key * D + 16 * ks + 8 * h) * 2u));
+    }
+    f32x16 acc[NDBH];  // dV (P wave) or dK (dS wave), columns 32 (db0 + i)
+#pragma unroll
+    for (int i = 0; i < NDBH; ++i) acc[i] = zero16();
+
+    const int q_start = CAUSAL ? (max(0, k0 - off) / BMQ) * BMQ : 0;
+    const int nsteps = (Nq > q_start) ? (Nq - q_start + BMQ - 1) / BMQ : 0;
+
+    auto qst = [&](auto st) __attribute__((always_inline)) {
+        constexpr int v = decltype(st)::value;
+        return (lds_char *)(v == 0 ? q0_raw : v == 1 ? q1_raw : q2_raw);
+    };
+    auto gst = [&](auto st) __attribute__((always_inline)) {
+        constexpr int v = decltype(st)::value;
+        return (lds_char *)(v == 0 ? g0_raw : v == 1 ? g1_raw : g2_raw);
+    };
+    auto sst = [&](auto st) __attribute__((always_inline)) {
+        constexpr int v = decltype(st)::value;
+        return (lds_char *)(v == 0 ? s0_raw : v == 1 ? s1_raw : s2_raw);
+    };
+    auto pst = [&](auto b) __attribute__((always_inline)) {
+        return (lds_char *)(decltype(b)::value ? p1_raw : p0_raw) + kg * (2 * 64 * 16);
+    };
+    // Q by waves 0..3 and dO by waves 4..7 (a tile of 32 rows is 12 or 16 wave loads)
+    auto load_blk = [&](int i, auto st) __attribute__((always_inline)) {
+        const int qs = q_start + i * BMQ;
+        if (w < 4)
+            load_tile_lds<D, 4, BMQ>(rq, qst(st), qs, w & 3, lane);
+        else
+            load_tile_lds<D, 4, BMQ>(rg, gst(st), qs, w & 3, lane);
+        if (w == 0 && lane < 8) buffer_load_lds16(rl, sst(st), (uint32_t)(qs + 4 * lane) * 4u);
+        if (w == 1 && lane < 8) buffer_load_lds16(rd, sst(st) + 4 * BMQ, (uint32_t)(qs + 4 * lane) * 4u);
+    };
+
+    auto run = [&](auto PW) __attribute__((always_inline)) {
+        constexpr bool P_WAVE = decltype(PW)::value;
+        auto step = [&](int i, auto S, auto B, auto FIRST) __attribute__((always_inline)) {
+            constexpr int s_cur = decltype(S)::value;
+            using SN = std::integral_constant<int, (s_cur + 1) % 3>;
+            using SP = std::integral_constant<int, (s_cur + 2) % 3>;
+            using BP = std::integral_constant<int, 1 - decltype(B)::value>;
+            load_blk(i + 1, SN{});  // past the last block: zeros into a free stage, never read
+            if constexpr (P_WAVE || !decltype(FIRST)::value) {
+                if (keys_ok) {
+                    using SB = std::conditional_t<P_WAVE, decltype(S), SP>;
+                    const lds_char *a_l = P_WAVE ? qst(SB{}) : gst(SB{});
+                    const lds_char *t_l = P_WAVE ? gst(SB{}) : qst(SB{});
+                    const lds_char *st_l = sst(SB{});
+                    lds_char *p_l = P_WAVE ? pst(B) : pst(BP{});
+                    const int qs = q_start + (P_WAVE ? i : i - 1) * BMQ;
+                    // first product: S = Q K^T (P wave) or dP = dO V^T (dS wave) over all of d
+                    f32x16 sc = zero16();
+                    constexpr int PF = 2;
+                    bf16x8 fr[PF + 1];
+                    static_for<0, PF>([&](auto F) __attribute__((always_inline)) {
+                        constexpr int f = decltype(F)::value;
+                        fr[f] = lds_read16(a_l, swz_off<D>(c32, 2 * f + h));
+                    });
+                    static_for<0, NKS>([&](auto C) __attribute__((always_inline)) {
+                        constexpr int c = decltype(C)::value;
+                        if constexpr (c + PF < NKS) fr[(c + PF) % (PF + 1)] = lds_read16(a_l, swz_off<D>(c32, 2 * (c + PF) + h));
+                        sc = mfma(fr[c % (PF + 1)], kvf[c], sc);
+                        __builtin_amdgcn_sched_barrier(0);
+                    });
+                    f32x4 v4[4];  // lse (P wave) or D (dS wave) of the lane's queries 8g + 4h + u
+#pragma unroll
+                    for (int g = 0; g < 4; ++g)
+                        v4[g] = *(const __attribute__((address_space(3))) f32x4 *)(st_l + 4 * ((P_WAVE ? 0 : BMQ) + 8 * g + 4 * h));
+                    bf16x8 pb[2];  // P (P wave) or dS (dS wave), two groups of 16 queries
+                    if constexpr (P_WAVE) {
+                        if (CAUSAL && (qs + off < kw0 + 31)) {
+                            // scores of queries before this lane's key -> -inf (P = 0); a query that
+                            // sees no key has lse = -inf: keep exp2 away from -inf + inf
+#pragma unroll
+                            for (int g = 0; g < 4; ++g) {
+#pragma unroll
+                                for (int u = 0; u < 4; ++u) {
+                                    v4[g][u] = fmaxf(v4[g][u], -1e30f);
+                                    if (qs + 8 * g + 4 * h + u + off < key) sc[4 * g + u] = -__builtin_inff();
+                                }
+                            }
+                        }
+#pragma unroll
+                        for (int r = 0; r < 16; ++r)
+                            pb[r >> 3][r & 7] = (bf16)fast_exp2(fmaf(sc[r], c_log2, -v4[r >> 2][r & 3] * kLog2e));
+                        if (ch == 0) {
+#pragma unroll
+                            for (int t = 0; t < 2; ++t) lds_write16(p_l, (t * 64 + lane) * 16, __builtin_bit_cast(u32x4, pb[t]));
+                        }
+                    } else {
+#pragma unroll
+                        for (int t = 0; t < 2; ++t) {
+                            const bf16x8 pv = __builtin_bit_cast(bf16x8, *(const __attribute__((address_space(3))) u32x4 *)(p_l + (t * 64 + lane) * 16));
+#pragma unroll
+                            for (int e = 0; e < 8; ++e) {
+                                const int r = 8 * t + e;
+                                pb[t][e] = (bf16)((float)pv[e] * (sc[r] - v4[r >> 2][r & 3]));
+                            }
+                        }
+                    }
+                    // second product: dV^T += dO^T P or dK^T += Q^T dS over this wave's columns
+                    static_for<0, 2 * NDBH>([&](auto C) __attribute__((always_inline)) {
+                        constexpr int c = decltype(C)::value, t = c / NDBH, db = c % NDBH;
+                        acc[db] = mfma(lds_read_tr_rows_swz<D>(t_l, 16 * t, 32 * (db0 + db), lane), pb[t], acc[db]);
+                        __builtin_amdgcn_sched_barrier(0);
+                    });
+                }
+            }
+            wait_vmem();
+            __syncthreads();
+        };
+
+        using I0 = std::integral_constant<int, 0>;
+        using I1 = std::integral_constant<int, 1>;
+        using I2 = std::integral_constant<int, 2>;
+        using F = std::false_type;
+        for (int gq = 0; gq < G; ++gq) {
+            bind_query_head(qh0 + gq);
+            load_blk(0, I0{});  // the previous query head's last step ended with a barrier
+            wait_vmem();
+            __syncthreads();
+            if (nsteps == 0) continue;
+            step(0, I0{}, I0{}, std::true_type{});
+            const int n = nsteps + 1;
+            int i = 1;
+            for (; i + 5 < n; i += 6) {
+                step(i, I1{}, I1{}, F{});
+                step(i + 1, I2{}, I0{}, F{});
+                step(i + 2, I0{}, I1{}, F{});
+                step(i + 3, I1{}, I0{}, F{});
+                step(i + 4, I2{}, I1{}, F{});
+                step(i + 5, I0{}, I0{}, F{});
+            }
+            if (i < n) step(i++, I1{}, I1{}, F{});
+            if (i < n) step(i++, I2{}, I0{}, F{});
+            if (i < n) step(i++, I0{}, I1{}, F{});
+            if (i < n) step(i++, I1{}, I0{}, F{});
+            if (i < n) step(i++, I2{}, I1{}, F{});
+        }
+    };
+    if (pwave)
+        run(std::true_type{});
+    else
+        run(std::false_type{});
+
+    if (key < Nk) {
+        bf16 *row = (pwave ? dV : dK) + hoff + (size_t)key * D;
+        const float f = pwave ? 1.f : scale;
+#pragma unroll
+        for (int db = 0; db < NDBH; ++db) {
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+                bf16x4 v4;
+#pragma unroll
+                for (int u = 0; u < 4; ++u) v4[u] = (bf16)(acc[db][4 * g + u] * f);
+                *(bf16x4 *)(row + 32 * (db0 + db) + 8 * g + 4 * h) = v4;
+            }
+        }
+    }
+}
+
 // ------------------------------------------------------------ dQ
 
 constexpr int kQBM = 128;  // queries per workgroup (32 per wave)
@@ -732,6 +952,18 @@ hipError_t launch_dkdv2_t(const BwdArgs &a)
 }
 
 template <int D, bool CAUSAL>
+hipError_t launch_dkdv3_t(const BwdArgs &a)
+{
+    const int n_ktiles = (a.Nk + 63) / 64;
+    const long long G = (long long)a.B * a.Hk * n_ktiles;
+    if (G == 0) return hipSuccess;
+    hipLaunchKernelGGL((bwd_dkdv3_kernel<D, CAUSAL>), dim3((unsigned)G), dim3(512), 0, (hipStream_t)a.stream,
+                       (const bf16 *)a.q, (const bf16 *)a.k, (const bf16 *)a.v, (const bf16 *)a.dout, a.lse,
+                       (const float *)a.delta, (bf16 *)a.dk, (bf16 *)a.dv, a.Nq, a.Nk, a.H, a.H / a.Hk, n_ktiles, a.scale, a.scale * kLog2e);
+    return hipGetLastError();
+}
+
+template <int D, bool CAUSAL>
 hipError_t launch_dkdv_t(const BwdArgs &a)
 {
     const int n_ktiles = (a.Nk + kv_bn<D>() - 1) / kv_bn<D>();
@@ -772,8 +1004,8 @@ hipError_t launch_bwd_dkdv(const BwdArgs &a)
     switch (a.d) {
     case 64: return a.causal ? launch_dkdv2_t<64, true>(a) : launch_dkdv2_t<64, false>(a);
     case 128: return a.causal ? launch_dkdv2_t<128, true>(a) : launch_dkdv2_t<128, false>(a);
-    case 192: return a.causal ? launch_dkdv_t<192, true>(a) : launch_dkdv_t<192, false>(a);
-    default: return a.causal ? launch_dkdv_t<256, true>(a) : launch_dkdv_t<256, false>(a);
+    case 192: return a.causal ? launch_dkdv3_t<192, true>(a) : launch_dkdv3_t<192, false>(a);
+    default: return a.causal ? launch_dkdv3_t<256, true>(a) : launch_dkdv3_t<256, false>(a);
     }
 }
 
