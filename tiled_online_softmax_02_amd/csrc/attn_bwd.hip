@@ -659,13 +659,20 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv3_kernel(
                     f32x16 sc = zero16();
                     constexpr int PF = 2;
                     bf16x8 fr[PF + 1];
+                    // LDS offsets: at d = 256 each is recomputed where it is used (the opaque copy keeps
+                    // the compiler from holding all of them, which spilled), at d = 192 they are kept
+                    auto a_off = [&](int kst) __attribute__((always_inline)) {
+                        int row = c32;
+                        if constexpr (D == 256) asm volatile("" : "+v"(row));
+                        return swz_off<D>(row, 2 * kst + h);
+                    };
                     static_for<0, PF>([&](auto F) __attribute__((always_inline)) {
                         constexpr int f = decltype(F)::value;
-                        fr[f] = lds_read16(a_l, swz_off<D>(c32, 2 * f + h));
+                        fr[f] = lds_read16(a_l, a_off(f));
                     });
                     static_for<0, NKS>([&](auto C) __attribute__((always_inline)) {
                         constexpr int c = decltype(C)::value;
-                        if constexpr (c + PF < NKS) fr[(c + PF) % (PF + 1)] = lds_read16(a_l, swz_off<D>(c32, 2 * (c + PF) + h));
+                        if constexpr (c + PF < NKS) fr[(c + PF) % (PF + 1)] = lds_read16(a_l, a_off(c + PF));
                         sc = mfma(fr[c % (PF + 1)], kvf[c], sc);
                         __builtin_amdgcn_sched_barrier(0);
                     });
@@ -708,7 +715,9 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv3_kernel(
                     // second product: dV^T += dO^T P or dK^T += Q^T dS over this wave's columns
                     static_for<0, 2 * NDBH>([&](auto C) __attribute__((always_inline)) {
                         constexpr int c = decltype(C)::value, t = c / NDBH, db = c % NDBH;
-                        acc[db] = mfma(lds_read_tr_rows_swz<D>(t_l, 16 * t, 32 * (db0 + db), lane), pb[t], acc[db]);
+                        int ln = lane;
+                        if constexpr (D == 256) asm volatile("" : "+v"(ln));
+                        acc[db] = mfma(lds_read_tr_rows_swz<D>(t_l, 16 * t, 32 * (db0 + db), ln), pb[t], acc[db]);
                         __builtin_amdgcn_sched_barrier(0);
                     });
                 }
