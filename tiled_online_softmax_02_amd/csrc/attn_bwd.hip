@@ -868,7 +868,11 @@ __global__ __launch_bounds__(kThreads, D >= 192 ? 1 : 2) void bwd_dq_kernel(
             for (int kst = 0; kst < NKS; ++kst) {
 #pragma unroll
                 for (int kb = 0; kb < 2; ++kb) {
-                    const int off = swz_off<D>(32 * kb + c32, 2 * kst + h);
+                    // at d = 256 the offsets are recomputed where they are used (an opaque copy of the
+                    // row keeps the compiler from holding all of them, which spilled)
+                    int row = c32;
+                    if constexpr (D == 256) asm volatile("" : "+v"(row));
+                    const int off = swz_off<D>(32 * kb + row, 2 * kst + h);
                     s[kb] = mfma(lds_read16(ks, off), qf[kst], s[kb]);
                     dp[kb] = mfma(lds_read16(vs, off), gf[kst], dp[kb]);
                 }
@@ -899,8 +903,11 @@ __global__ __launch_bounds__(kThreads, D >= 192 ? 1 : 2) void bwd_dq_kernel(
 #pragma unroll
             for (int t = 0; t < kQBN / 16; ++t) {
 #pragma unroll
-                for (int db = 0; db < NDB; ++db)
-                    dq[db] = mfma(lds_read_tr_rows_swz<D>(ks, 16 * t, 32 * db, lane), sb[t], dq[db]);
+                for (int db = 0; db < NDB; ++db) {
+                    int ln = lane;
+                    if constexpr (D == 256) asm volatile("" : "+v"(ln));
+                    dq[db] = mfma(lds_read_tr_rows_swz<D>(ks, 16 * t, 32 * db, ln), sb[t], dq[db]);
+                }
             }
         }
         wait_vmem();

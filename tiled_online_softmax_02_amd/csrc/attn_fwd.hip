@@ -241,10 +241,16 @@ __global__ __launch_bounds__(64 * fwd_waves<D>(), fwd_min_blocks<D>()) void fwd_
                     constexpr int c = decltype(C)::value;
                     if constexpr (is_s(c)) {
                         constexpr int s = c < NS / 2 ? c : c - NPV / 2;
-                        return lds_read16(ks, swz_off<D>(32 * (s & 1) + c32, 2 * (s >> 1) + h));
+                        // at d = 256 the offsets are recomputed where they are used (an opaque copy of
+                        // the row keeps the compiler from holding all of them, which spilled)
+                        int row = c32;
+                        if constexpr (D == 256) asm volatile("" : "+v"(row));
+                        return lds_read16(ks, swz_off<D>(32 * (s & 1) + row, 2 * (s >> 1) + h));
                     } else {
                         constexpr int p = c < NS / 2 + NPV / 2 ? c - NS / 2 : c - NS;
-                        return lds_read_tr_rows_swz<D>(vs, 16 * (p / NDB), 32 * (p % NDB), lane);
+                        int ln = lane;
+                        if constexpr (D == 256) asm volatile("" : "+v"(ln));
+                        return lds_read_tr_rows_swz<D>(vs, 16 * (p / NDB), 32 * (p % NDB), ln);
                     }
                 };
                 nxt[0] = zero16();
