@@ -845,10 +845,13 @@ __global__ __launch_bounds__(kThreads, D >= 192 ? 1 : 2) void bwd_dq_kernel(
     wait_vmem();
     __syncthreads();
 
-    // The wave works on key blocks [0, ja) and only loads and waits on [ja, nt) (causal: the
-    // blocks wholly above its rows); separate loops keep the block index out of the step.
+    // d <= 128: the wave works on key blocks [0, ja) and only loads and waits on [ja, nt) (causal:
+    // the blocks wholly above its rows); separate loops keep the block index out of the step.
+    // d = 192, 256: one loop with the test inside the step, which measured faster there.
+    constexpr bool kSplitLoops = D <= 128;
     const int last_key = qw0 + 31 + off;
-    const int ja = (qw0 >= Nq) ? 0 : (!CAUSAL ? nt : (last_key < 0 ? 0 : min(nt, last_key / kQBN + 1)));
+    const int ja_seen = (qw0 >= Nq) ? 0 : (!CAUSAL ? nt : (last_key < 0 ? 0 : min(nt, last_key / kQBN + 1)));
+    const int ja = kSplitLoops ? ja_seen : nt;
     auto step_idle = [&](int j, auto par) __attribute__((always_inline)) {
         using PN = std::integral_constant<int, 1 - decltype(par)::value>;
         load_blk(j + 1, PN{});
@@ -861,18 +864,14 @@ __global__ __launch_bounds__(kThreads, D >= 192 ? 1 : 2) void bwd_dq_kernel(
         const lds_char *ks = kst_l(par);
         const lds_char *vs = vst_l(par);
         const int k0 = j * kQBN;
-        {
+        if (kSplitLoops || j < ja_seen) {
             f32x16 s[2] = {zero16(), zero16()};
             f32x16 dp[2] = {zero16(), zero16()};
 #pragma unroll
             for (int kst = 0; kst < NKS; ++kst) {
 #pragma unroll
                 for (int kb = 0; kb < 2; ++kb) {
-                    // at d = 256 the offsets are recomputed where they are used (an opaque copy of the
-                    // row keeps the compiler from holding all of them, which spilled)
-                    int row = c32;
-                    if constexpr (D == 256) asm volatile("" : "+v"(row));
-                    const int off = swz_off<D>(32 * kb + row, 2 * kst + h);
+                    const int off = swz_off<D>(32 * kb + c32, 2 * kst + h);
                     s[kb] = mfma(lds_read16(ks, off), qf[kst], s[kb]);
                     dp[kb] = mfma(lds_read16(vs, off), gf[kst], dp[kb]);
                 }
@@ -903,11 +902,8 @@ __global__ __launch_bounds__(kThreads, D >= 192 ? 1 : 2) void bwd_dq_kernel(
 #pragma unroll
             for (int t = 0; t < kQBN / 16; ++t) {
 #pragma unroll
-                for (int db = 0; db < NDB; ++db) {
-                    int ln = lane;
-                    if constexpr (D == 256) asm volatile("" : "+v"(ln));
-                    dq[db] = mfma(lds_read_tr_rows_swz<D>(ks, 16 * t, 32 * db, ln), sb[t], dq[db]);
-                }
+                for (int db = 0; db < NDB; ++db)
+                    dq[db] = mfma(lds_read_tr_rows_swz<D>(ks, 16 * t, 32 * db, lane), sb[t], dq[db]);
             }
         }
         wait_vmem();
