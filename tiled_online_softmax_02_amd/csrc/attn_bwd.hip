@@ -374,12 +374,19 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv2_kernel(
     auto pst = [&](auto b) __attribute__((always_inline)) {
         return (lds_char *)(decltype(b)::value ? p1_raw : p0_raw) + pair * (4 * 64 * 16);
     };
+    // lse of the block being loaded (wave 0, lanes 0..15): it goes to LDS in log2 units at the end
+    // of the step, so that the P waves form each exponent with one fused multiply-add
+    f32x4 lse_ld;
     auto load_blk = [&](int i, auto st) __attribute__((always_inline)) {
         const int qs = q_start + i * kKvBM;
         load_tile_lds<D, 8>(rq, qst(st), qs, w, lane);
         load_tile_lds<D, 8>(rg, gst(st), qs, w, lane);
-        if (w == 0 && lane < 16) buffer_load_lds16(rl, sst(st), (uint32_t)(qs + 4 * lane) * 4u);
+        if (w == 0 && lane < 16) lse_ld = __builtin_bit_cast(f32x4, buffer_load16(rl, (uint32_t)(qs + 4 * lane) * 4u));
         if (w == 1 && lane < 16) buffer_load_lds16(rd, sst(st) + 4 * kKvBM, (uint32_t)(qs + 4 * lane) * 4u);
+    };
+    auto store_lse = [&](auto st) __attribute__((always_inline)) {
+        if (w == 0 && lane < 16)
+            *(__attribute__((address_space(3))) f32x4 *)(sst(st) + 16 * lane) = lse_ld * kLog2e;
     };
     // Every step runs in full: a block that no query of it sees for this pair's keys (causal:
     // the first block for the later pairs) is masked to P = 0 and adds nothing, and the P wave's
@@ -418,7 +425,7 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv2_kernel(
                     const bool need_mask = P_WAVE && CAUSAL && (qs + off < kw0 + 31);
                     f32x16 sc[2] = {zero16(), zero16()};
                     bf16x8 pb[4];     // P (P wave) or dS (dS wave), bf16, groups of 16 queries
-                    f32x4 v4[2][4];   // lse (P wave) or D (dS wave) of the lane's queries, per half
+                    f32x4 v4[2][4];   // lse * log2e (P wave) or D (dS wave) of the lane's queries, per half
                     bf16x8 pv[2][2];  // P of the half read back from LDS (dS wave)
                     auto fetch = [&](auto C) __attribute__((always_inline)) {
                         constexpr int c = decltype(C)::value;
@@ -477,7 +484,7 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv2_kernel(
                             static_for<k * 16 / L, (k + 1) * 16 / L>([&](auto RR) __attribute__((always_inline)) {
                                 constexpr int r = decltype(RR)::value, g = r >> 2, u = r & 3;
                                 if constexpr (P_WAVE)
-                                    pb[2 * qb + (r >> 3)][r & 7] = (bf16)fast_exp2(fmaf(sc[qb][r], c_log2, -v4[qb][g][u] * kLog2e));
+                                    pb[2 * qb + (r >> 3)][r & 7] = (bf16)fast_exp2(fmaf(sc[qb][r], c_log2, -v4[qb][g][u]));
                                 else
                                     pb[2 * qb + (r >> 3)][r & 7] = (bf16)((float)pv[qb][r >> 3][r & 7] * (sc[qb][r] - v4[qb][g][u]));
                             });
@@ -492,6 +499,7 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv2_kernel(
                 }
             }
             wait_vmem();
+            store_lse(SN{});
             __syncthreads();
         };
 
@@ -503,6 +511,7 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv2_kernel(
             bind_query_head(qh0 + gq);
             load_blk(0, I0{});  // the previous query head's last step ended with a barrier
             wait_vmem();
+            store_lse(I0{});
             __syncthreads();
             // steps 0 .. nsteps (the dS wave's last block is nsteps - 1); stage i % 3, P buffer
             // i % 2; in step 0 only the P wave works

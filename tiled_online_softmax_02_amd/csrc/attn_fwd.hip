@@ -291,12 +291,16 @@ __global__ __launch_bounds__(64 * fwd_waves<D>(), fwd_min_blocks<D>()) void fwd_
                             constexpr int r = decltype(RR)::value;
                             rs += cur[r >> 4][r & 15];
                         });
+                        // keep the slice in this chunk: the sum is only read after the step, and
+                        // without a use here the compiler sinks the whole chain past the barrier
+                        asm volatile("" : "+v"(rs));
                     } else {
                         constexpr int i = c - 3 * PH;
                         static_for<i * 32 / PH, (i + 1) * 32 / PH>([&](auto RR) __attribute__((always_inline)) {
                             constexpr int r = decltype(RR)::value;
                             mx = fmaxf(mx, nxt[r >> 4][r & 15]);
                         });
+                        asm volatile("" : "+v"(mx));
                     }
                     __builtin_amdgcn_sched_barrier(0);
                 });

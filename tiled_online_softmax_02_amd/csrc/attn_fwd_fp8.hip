@@ -318,12 +318,16 @@ __global__ __launch_bounds__(64 * f8_waves<D>(), 8 / f8_waves<D>()) void fwd_fp8
                             constexpr int r = decltype(RR)::value;
                             rs += cur[r >> 4][r & 15];
                         });
+                        // keep each slice in its chunk: the sum and the maximum are only read after
+                        // the step, and without a use here the compiler sinks them past the barrier
+                        asm volatile("" : "+v"(rs));
                         if constexpr (i >= 1) {
                             // maximum of block j+1 once its scores are complete
                             static_for<(i - 1) * 32 / (NDB - 1), i * 32 / (NDB - 1)>([&](auto RR) __attribute__((always_inline)) {
                                 constexpr int r = decltype(RR)::value;
                                 mx = fmaxf(mx, nxt[r >> 4][r & 15]);
                             });
+                            asm volatile("" : "+v"(mx));
                         }
                     }
                     __builtin_amdgcn_sched_barrier(0);
