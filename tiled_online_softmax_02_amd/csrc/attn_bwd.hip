@@ -343,13 +343,16 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv2_kernel(
     const int kw0 = k0 + 32 * pair;
     const int key = kw0 + c32;
 
-    // key-side operand: K for the P wave (S = Q K^T), V for the dS wave (dP = dO V^T)
+    // key-side operand: K for the P wave (S = Q K^T), -V for the dS wave, whose product then
+    // starts from D: D - dO V^T = -(dP - D), so that dS needs one multiply per element; its dK
+    // accumulator holds -dK and is negated with the scale at the end
     bf16x8 kvf[NKS];
     {
         const __amdgpu_buffer_rsrc_t rkv = make_rsrc((pwave ? K : V) + hoff, (uint32_t)Nk * D * 2);
+        const unsigned sign = pwave ? 0u : 0x80008000u;
 #pragma unroll
         for (int ks = 0; ks < NKS; ++ks)
-            kvf[ks] = __builtin_bit_cast(bf16x8, buffer_load16(rkv, (uint32_t)(key * D + 16 * ks + 8 * h) * 2u));
+            kvf[ks] = __builtin_bit_cast(bf16x8, buffer_load16(rkv, (uint32_t)(key * D + 16 * ks + 8 * h) * 2u) ^ sign);
     }
 
     f32x16 acc[NDB];  // dV (P wave) or dK (dS wave)
@@ -424,8 +427,21 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv2_kernel(
                     constexpr int HS = NKS, NS = 2 * NKS, NA = 4 * NDB, NC = NS + NA, PF = 2;
                     const bool need_mask = P_WAVE && CAUSAL && (qs + off < kw0 + 31);
                     f32x16 sc[2] = {zero16(), zero16()};
-                    bf16x8 pb[4];     // P (P wave) or dS (dS wave), bf16, groups of 16 queries
-                    f32x4 v4[2][4];   // lse * log2e (P wave) or D (dS wave) of the lane's queries, per half
+                    bf16x8 pb[4];     // P (P wave) or -dS (dS wave), bf16, groups of 16 queries
+                    f32x4 v4[2][4];   // lse * log2e of the lane's queries, per half (P wave)
+                    if constexpr (!P_WAVE) {
+                        // dS wave: the products start from D of the lane's queries 32 qb + 8 g + 4 h + u
+#pragma unroll
+                        for (int qb = 0; qb < 2; ++qb) {
+#pragma unroll
+                            for (int g = 0; g < 4; ++g) {
+                                const f32x4 dv = *(const __attribute__((address_space(3))) f32x4 *)(
+                                    st_l + 4 * (kKvBM + 32 * qb + 8 * g + 4 * h));
+#pragma unroll
+                                for (int u = 0; u < 4; ++u) sc[qb][4 * g + u] = dv[u];
+                            }
+                        }
+                    }
                     bf16x8 pv[2][2];  // P of the half read back from LDS (dS wave)
                     auto fetch = [&](auto C) __attribute__((always_inline)) {
                         constexpr int c = decltype(C)::value;
@@ -457,11 +473,13 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv2_kernel(
                             constexpr int L = qb == 0 ? NS - HS : NA / 2;
                             constexpr int k = c - w0;
                             if constexpr (k == 0) {
-                                // the half's lse or D (and for the dS wave its P) from LDS
+                                // the half's lse (P wave) or P (dS wave) from LDS
+                                if constexpr (P_WAVE) {
 #pragma unroll
-                                for (int g = 0; g < 4; ++g)
-                                    v4[qb][g] = *(const __attribute__((address_space(3))) f32x4 *)(
-                                        st_l + 4 * ((P_WAVE ? 0 : kKvBM) + 32 * qb + 8 * g + 4 * h));
+                                    for (int g = 0; g < 4; ++g)
+                                        v4[qb][g] = *(const __attribute__((address_space(3))) f32x4 *)(
+                                            st_l + 4 * (32 * qb + 8 * g + 4 * h));
+                                }
                                 if constexpr (!P_WAVE) {
 #pragma unroll
                                     for (int tt = 0; tt < 2; ++tt)
@@ -486,7 +504,7 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv2_kernel(
                                 if constexpr (P_WAVE)
                                     pb[2 * qb + (r >> 3)][r & 7] = (bf16)fast_exp2(fmaf(sc[qb][r], c_log2, -v4[qb][g][u]));
                                 else
-                                    pb[2 * qb + (r >> 3)][r & 7] = (bf16)((float)pv[qb][r >> 3][r & 7] * (sc[qb][r] - v4[qb][g][u]));
+                                    pb[2 * qb + (r >> 3)][r & 7] = (bf16)((float)pv[qb][r >> 3][r & 7] * sc[qb][r]);
                             });
                             if constexpr (P_WAVE && k == L - 1) {
 #pragma unroll
@@ -541,7 +559,7 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv2_kernel(
 
     if (key < Nk) {
         bf16 *row = (pwave ? dV : dK) + hoff + (size_t)key * D;
-        const float f = pwave ? 1.f : scale;
+        const float f = pwave ? 1.f : -scale;
 #pragma unroll
         for (int db = 0; db < NDB; ++db) {
 #pragma unroll
