@@ -101,6 +101,41 @@ __global__ __launch_bounds__(64 * fwd_waves<D>(), fwd_min_blocks<D>()) void fwd_
     // Causal mask with bottom-right alignment: query i sees keys j <= i + off.
     const int off = Nk - Nq;
 
+    // d <= 128: the lane's byte offsets inside a swizzled K/V tile are computed once and kept
+    // opaque, so that every LDS read of the loop is one register plus a constant (stage and row
+    // block) in the instruction's offset field, and every direct load one register plus a buffer
+    // base moved by scalar arithmetic; otherwise the compiler rebuilt them with vector adds.
+    constexpr bool kFixedOffsets = D <= 128;
+    constexpr int kLoadNI = kFwdBN * (D / 8) / 64 / kFwdWaves;  // direct loads per wave and tile
+    int ko[NKS];         // K fragment of reduction step kst: row c32, chunk 2 kst + h
+    int vo[NDB][2];      // V^T fragment of column block db: rows r and r + 8 of a 16-row block
+    int go[kLoadNI];     // source of direct load i within a tile
+    if constexpr (kFixedOffsets) {
+#pragma unroll
+        for (int kst = 0; kst < NKS; ++kst) {
+            ko[kst] = swz_off<D>(c32, 2 * kst + h);
+            asm volatile("" : "+v"(ko[kst]));
+        }
+        const int G = lane >> 4, s16 = lane & 15;
+        const int vr = 4 * (G >> 1) + (s16 >> 2);
+#pragma unroll
+        for (int db = 0; db < NDB; ++db) {
+            const int byte = 2 * (32 * db + 16 * (G & 1) + 4 * (s16 & 3));
+            vo[db][0] = swz_off<D>(vr, byte >> 4) + (byte & 15);
+            vo[db][1] = swz_off<D>(vr + 8, byte >> 4) + (byte & 15);
+            asm volatile("" : "+v"(vo[db][0]));
+            asm volatile("" : "+v"(vo[db][1]));
+        }
+#pragma unroll
+        for (int i = 0; i < kLoadNI; ++i) {
+            const int pchunk = 64 * (w * kLoadNI + i) + lane;
+            const int row = pchunk / (D / 8);
+            const int chunk = (pchunk - row * (D / 8)) ^ lds_swz<D>(row);
+            go[i] = row * 2 * D + 16 * chunk;
+            asm volatile("" : "+v"(go[i]));
+        }
+    }
+
     for (int pass = 0; pass < ((CAUSAL && !SPLIT) ? 2 : 1); ++pass) {
         const int qtile = SPLIT ? pos / n_splits : (pass == 0 ? (CAUSAL ? n_qtiles - 1 - pos : pos) : pos);
         if (pass == 1 && qtile == n_qtiles - 1 - pos) break;  // odd T: the middle block is alone
@@ -132,8 +167,19 @@ __global__ __launch_bounds__(64 * fwd_waves<D>(), fwd_min_blocks<D>()) void fwd_
         // stage of block j is j & 1; callers pass the parity as a compile-time constant
         auto kstage = [&](auto par) __attribute__((always_inline)) { return (lds_char *)(decltype(par)::value ? k1_raw : k0_raw); };
         auto vstage = [&](auto par) __attribute__((always_inline)) { return (lds_char *)(decltype(par)::value ? v1_raw : v0_raw); };
-        auto load_k = [&](int j, auto par) __attribute__((always_inline)) { load_tile_lds<D, kFwdWaves>(rk, kstage(par), j * kFwdBN, w, lane); };
-        auto load_v = [&](int j, auto par) __attribute__((always_inline)) { load_tile_lds<D, kFwdWaves>(rv, vstage(par), j * kFwdBN, w, lane); };
+        // key rows [j * BN, j * BN + BN) of K or V into a stage; rows past Nk read as zeros
+        auto load_blk = [&](const bf16 *src, __amdgpu_buffer_rsrc_t r, lds_char *tile, int j) __attribute__((always_inline)) {
+            if constexpr (kFixedOffsets) {
+                const int r0 = min(j * kFwdBN, Nk);
+                const __amdgpu_buffer_rsrc_t rj = make_rsrc(src + hoff_k + (size_t)r0 * D, (uint32_t)(Nk - r0) * D * 2);
+#pragma unroll
+                for (int i = 0; i < kLoadNI; ++i) buffer_load_lds16(rj, tile + 1024 * (w * kLoadNI + i), (uint32_t)go[i]);
+            } else {
+                load_tile_lds<D, kFwdWaves>(r, tile, j * kFwdBN, w, lane);
+            }
+        };
+        auto load_k = [&](int j, auto par) __attribute__((always_inline)) { load_blk(K, rk, kstage(par), j); };
+        auto load_v = [&](int j, auto par) __attribute__((always_inline)) { load_blk(V, rv, vstage(par), j); };
 
         // S^T block (64 keys x 32 queries) of key block j
         auto scores = [&](auto par, f32x16 *s) __attribute__((always_inline)) {
@@ -239,7 +285,16 @@ __global__ __launch_bounds__(64 * fwd_waves<D>(), fwd_min_blocks<D>()) void fwd_
                 constexpr auto is_s = [](int c) { return c < NS / 2 || (c >= NS / 2 + NPV / 2 && c < NS + NPV / 2); };
                 auto fetch = [&](auto C) __attribute__((always_inline)) {
                     constexpr int c = decltype(C)::value;
-                    if constexpr (is_s(c)) {
+                    if constexpr (is_s(c) && kFixedOffsets) {
+                        constexpr int s = c < NS / 2 ? c : c - NPV / 2;
+                        return lds_read16(ks, ko[s >> 1] + 32 * (s & 1) * 2 * D);
+                    } else if constexpr (kFixedOffsets) {
+                        constexpr int p = c < NS / 2 + NPV / 2 ? c - NS / 2 : c - NS;
+                        constexpr int rb = 16 * (p / NDB) * 2 * D;
+                        const bf16x4 lo = lds_read_tr(vs, vo[p % NDB][0] + rb);
+                        const bf16x4 hi = lds_read_tr(vs, vo[p % NDB][1] + rb);
+                        return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+                    } else if constexpr (is_s(c)) {
                         constexpr int s = c < NS / 2 ? c : c - NPV / 2;
                         // at d = 256 the offsets are recomputed where they are used (an opaque copy of
                         // the row keeps the compiler from holding all of them, which spilled)
