@@ -841,11 +841,15 @@ __global__ __launch_bounds__(kThreads, D >= 192 ? 1 : 2) void bwd_dq_kernel(
     const int qrow = qw0 + c32;
     const bool row_ok = qrow < Nq;
 
+    // d <= 128: dO is held negated, so that the dP product starts from D and yields D - dP;
+    // dS = P (dP - D) is then one multiply per element and dQ accumulates with the opposite sign
+    constexpr bool kNegDP = D <= 128;
     bf16x8 qf[NKS], gf[NKS];
 #pragma unroll
     for (int ks = 0; ks < NKS; ++ks) {
         qf[ks] = __builtin_bit_cast(bf16x8, buffer_load16(rq, (uint32_t)(qrow * D + 16 * ks + 8 * h) * 2u));
-        gf[ks] = __builtin_bit_cast(bf16x8, buffer_load16(rg, (uint32_t)(qrow * D + 16 * ks + 8 * h) * 2u));
+        gf[ks] = __builtin_bit_cast(bf16x8, buffer_load16(rg, (uint32_t)(qrow * D + 16 * ks + 8 * h) * 2u) ^
+                                                (kNegDP ? 0x80008000u : 0u));
     }
     // a row past Nq, or a query that sees no key (lse = -inf), gets lse2 = +inf and so P = 0
     const float lse_row = row_ok ? LSE[(size_t)head * Nq + qrow] : -__builtin_inff();
@@ -861,9 +865,52 @@ __global__ __launch_bounds__(kThreads, D >= 192 ? 1 : 2) void bwd_dq_kernel(
 
     auto kst_l = [&](auto par) __attribute__((always_inline)) { return (lds_char *)(decltype(par)::value ? k1_raw : k0_raw); };
     auto vst_l = [&](auto par) __attribute__((always_inline)) { return (lds_char *)(decltype(par)::value ? v1_raw : v0_raw); };
+    // d <= 128: the lane's byte offsets inside a swizzled K/V tile are computed once and kept
+    // opaque, so that every LDS read of the loop is one register plus a constant in the
+    // instruction's offset field, and every direct load one register plus a buffer base moved by
+    // scalar arithmetic.
+    constexpr bool kFixedOffsets = D <= 128;
+    constexpr int kLoadNI = kQBN * (D / 8) / 64 / 4;  // direct loads per wave and tile
+    int ko[NKS], vo[NDB][2], go[kLoadNI];
+    if constexpr (kFixedOffsets) {
+#pragma unroll
+        for (int kst = 0; kst < NKS; ++kst) {
+            ko[kst] = swz_off<D>(c32, 2 * kst + h);
+            asm volatile("" : "+v"(ko[kst]));
+        }
+        const int G4 = lane >> 4, s16 = lane & 15;
+        const int vr = 4 * (G4 >> 1) + (s16 >> 2);
+#pragma unroll
+        for (int db = 0; db < NDB; ++db) {
+            const int byte = 2 * (32 * db + 16 * (G4 & 1) + 4 * (s16 & 3));
+            vo[db][0] = swz_off<D>(vr, byte >> 4) + (byte & 15);
+            vo[db][1] = swz_off<D>(vr + 8, byte >> 4) + (byte & 15);
+            asm volatile("" : "+v"(vo[db][0]));
+            asm volatile("" : "+v"(vo[db][1]));
+        }
+#pragma unroll
+        for (int i = 0; i < kLoadNI; ++i) {
+            const int pchunk = 64 * (w * kLoadNI + i) + lane;
+            const int row = pchunk / (D / 8);
+            const int chunk = (pchunk - row * (D / 8)) ^ lds_swz<D>(row);
+            go[i] = row * 2 * D + 16 * chunk;
+            asm volatile("" : "+v"(go[i]));
+        }
+    }
     auto load_blk = [&](int j, auto par) __attribute__((always_inline)) {
-        load_tile_lds<D, 4>(rk, kst_l(par), j * kQBN, w, lane);
-        load_tile_lds<D, 4>(rv, vst_l(par), j * kQBN, w, lane);
+        if constexpr (kFixedOffsets) {
+            // rows past Nk read as zeros
+            const int r0 = min(j * kQBN, Nk);
+            const __amdgpu_buffer_rsrc_t rkj = make_rsrc(K + hoff_k + (size_t)r0 * D, (uint32_t)(Nk - r0) * D * 2);
+            const __amdgpu_buffer_rsrc_t rvj = make_rsrc(V + hoff_k + (size_t)r0 * D, (uint32_t)(Nk - r0) * D * 2);
+#pragma unroll
+            for (int i = 0; i < kLoadNI; ++i) buffer_load_lds16(rkj, kst_l(par) + 1024 * (w * kLoadNI + i), (uint32_t)go[i]);
+#pragma unroll
+            for (int i = 0; i < kLoadNI; ++i) buffer_load_lds16(rvj, vst_l(par) + 1024 * (w * kLoadNI + i), (uint32_t)go[i]);
+        } else {
+            load_tile_lds<D, 4>(rk, kst_l(par), j * kQBN, w, lane);
+            load_tile_lds<D, 4>(rv, vst_l(par), j * kQBN, w, lane);
+        }
     };
 
     using P0 = std::integral_constant<int, 0>;
@@ -893,12 +940,16 @@ __global__ __launch_bounds__(kThreads, D >= 192 ? 1 : 2) void bwd_dq_kernel(
         const int k0 = j * kQBN;
         if (kSplitLoops || j < ja_seen) {
             f32x16 s[2] = {zero16(), zero16()};
-            f32x16 dp[2] = {zero16(), zero16()};
+            f32x16 dp[2] = {zero16(), zero16()};  // dP, or D - dP (kNegDP)
+            if constexpr (kNegDP) {
+#pragma unroll
+                for (int r = 0; r < 16; ++r) dp[0][r] = dp[1][r] = dval;
+            }
 #pragma unroll
             for (int kst = 0; kst < NKS; ++kst) {
 #pragma unroll
                 for (int kb = 0; kb < 2; ++kb) {
-                    const int off = swz_off<D>(32 * kb + c32, 2 * kst + h);
+                    const int off = kFixedOffsets ? ko[kst] + 32 * kb * 2 * D : swz_off<D>(32 * kb + c32, 2 * kst + h);
                     s[kb] = mfma(lds_read16(ks, off), qf[kst], s[kb]);
                     dp[kb] = mfma(lds_read16(vs, off), gf[kst], dp[kb]);
                 }
@@ -922,15 +973,24 @@ __global__ __launch_bounds__(kThreads, D >= 192 ? 1 : 2) void bwd_dq_kernel(
 #pragma unroll
                 for (int r = 0; r < 16; ++r) {
                     const float p = fast_exp2(fmaf(s[kb][r], c_log2, -lse2));
-                    sb[2 * kb + (r >> 3)][r & 7] = (bf16)(p * (dp[kb][r] - dval));
+                    sb[2 * kb + (r >> 3)][r & 7] = kNegDP ? (bf16)(p * dp[kb][r]) : (bf16)(p * (dp[kb][r] - dval));
                 }
             }
             // dQ^T += K^T dS^T over 4 groups of 16 keys
 #pragma unroll
             for (int t = 0; t < kQBN / 16; ++t) {
 #pragma unroll
-                for (int db = 0; db < NDB; ++db)
-                    dq[db] = mfma(lds_read_tr_rows_swz<D>(ks, 16 * t, 32 * db, lane), sb[t], dq[db]);
+                for (int db = 0; db < NDB; ++db) {
+                    bf16x8 kt;
+                    if constexpr (kFixedOffsets) {
+                        const bf16x4 lo = lds_read_tr(ks, vo[db][0] + 16 * t * 2 * D);
+                        const bf16x4 hi = lds_read_tr(ks, vo[db][1] + 16 * t * 2 * D);
+                        kt = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+                    } else {
+                        kt = lds_read_tr_rows_swz<D>(ks, 16 * t, 32 * db, lane);
+                    }
+                    dq[db] = mfma(kt, sb[t], dq[db]);
+                }
             }
         }
         wait_vmem();
@@ -959,7 +1019,7 @@ __global__ __launch_bounds__(kThreads, D >= 192 ? 1 : 2) void bwd_dq_kernel(
             for (int g = 0; g < 4; ++g) {
                 bf16x4 v4;
 #pragma unroll
-                for (int u = 0; u < 4; ++u) v4[u] = (bf16)(dq[db][4 * g + u] * scale);
+                for (int u = 0; u < 4; ++u) v4[u] = (bf16)(dq[db][4 * g + u] * (kNegDP ? -scale : scale));
                 *(bf16x4 *)(qrow_p + 32 * db + 8 * g + 4 * h) = v4;
             }
         }
