@@ -68,24 +68,6 @@ __device__ __forceinline__ int swz8_off(int row, int chunk)
     return row * D + 16 * (chunk ^ swz8<D>(row));
 }
 
-// Rows [row0, row0 + 64) of a row-major [*, D] byte matrix into a swizzled LDS tile with
-// direct loads; wave instruction n writes physical chunks 64 n .. 64 n + 63.
-template <int D, int NW>
-__device__ __forceinline__ void load_tile8(__amdgpu_buffer_rsrc_t r, lds_char *tile, int row0, int wave, int lane)
-{
-    constexpr int CPR = D / 16;
-    constexpr int NI = kF8BN * CPR / 64 / NW;
-    static_assert(NI >= 1 && NI * 64 * NW == kF8BN * CPR, "tile must split evenly over the waves");
-#pragma unroll
-    for (int i = 0; i < NI; ++i) {
-        const int n = wave * NI + i;
-        const int pchunk = 64 * n + lane;
-        const int row = pchunk / CPR;
-        const int chunk = (pchunk - row * CPR) ^ swz8<D>(row);
-        buffer_load_lds16(r, tile + 1024 * n, (uint32_t)((row0 + row) * D + 16 * chunk));
-    }
-}
-
 __device__ __forceinline__ u32x4 lds_read_b128(const lds_char *base, int off)
 {
     return *(const __attribute__((address_space(3))) u32x4 *)(base + off);
@@ -97,34 +79,6 @@ __device__ __forceinline__ u32x4 lds_read_b128(const lds_char *base, int off)
 __device__ __forceinline__ i32x2 lds_read_tr8(const lds_char *base, int off)
 {
     return __builtin_amdgcn_ds_read_tr8_b64_v2i32((__attribute__((address_space(3))) i32x2 *)(base + off));
-}
-
-// A operand of S^T = K Q^T for key rows 32 kb .. 32 kb + 31 and d bytes 64 kst .. 64 kst + 63:
-// lane (c, h) takes row 32 kb + c, bytes 64 kst + 32 h .. + 31.
-template <int D>
-__device__ __forceinline__ i32x8 k_frag(const lds_char *ks, int kb, int kst, int c32, int h)
-{
-    const u32x4 lo = lds_read_b128(ks, swz8_off<D>(32 * kb + c32, 4 * kst + 2 * h));
-    const u32x4 hi = lds_read_b128(ks, swz8_off<D>(32 * kb + c32, 4 * kst + 2 * h + 1));
-    return __builtin_bit_cast(i32x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-}
-
-// A operand of O^T += V^T P^T for columns 32 db .. 32 db + 31 of O: lane (c, h) takes byte p =
-// V[sigma_h(p)][32 db + c], sigma_h(p) = 32(p/16) + 8((p%16)/4) + 4h + p%4.  Read t (bytes
-// 8t .. 8t+7) is issued by source lane s = 16 g + 2 e + o at key sigma_{g/2}(8 t + e), bytes
-// 32 db + 16 (g%2) + 8 o .. + 7 of that row.
-template <int D>
-__device__ __forceinline__ i32x8 v_frag(const lds_char *vs, int db, int lane)
-{
-    const int g = lane >> 4, e = (lane & 15) >> 1, o = lane & 1;
-    const int klo = 8 * (e >> 2) + 4 * (g >> 1) + (e & 3);  // key within a 16-key group
-    i32x2 r[4];
-#pragma unroll
-    for (int t = 0; t < 4; ++t) {
-        const int key = 16 * t + klo;  // 32 (t/2) + 16 (t%2) + klo
-        r[t] = lds_read_tr8(vs, swz8_off<D>(key, 2 * db + (g & 1)) + 8 * o);
-    }
-    return i32x8{r[0][0], r[0][1], r[1][0], r[1][1], r[2][0], r[2][1], r[3][0], r[3][1]};
 }
 
 template <int D, bool CAUSAL>
@@ -152,9 +106,41 @@ __global__ __launch_bounds__(64 * f8_waves<D>(), 8 / f8_waves<D>()) void fwd_fp8
     const size_t hoff = (size_t)head * (size_t)Nq * D;
     const size_t hoff_k = (size_t)kvh * (size_t)Nk * D;
     const __amdgpu_buffer_rsrc_t rq = make_rsrc(Q + hoff, (uint32_t)Nq * D);
-    const __amdgpu_buffer_rsrc_t rk = make_rsrc(K + hoff_k, (uint32_t)Nk * D);
-    const __amdgpu_buffer_rsrc_t rv = make_rsrc(V + hoff_k, (uint32_t)Nk * D);
     const int off = Nk - Nq;  // bottom-right causal alignment: query i sees keys j <= i + off
+
+    // The lane's byte offsets inside a swizzled K/V tile, computed once and kept opaque: every LDS
+    // read of the loop is one register plus a constant (stage, row block) in the instruction's
+    // offset field, and every direct load one register plus a buffer base moved by scalar
+    // arithmetic, so the step carries no address arithmetic on the vector units.
+    constexpr int kLoadNI = kF8BN * (D / 16) / 64 / NW;  // direct loads per wave and tile
+    int ko[NK8][2];   // K fragment of reduction step kst: row c32, chunks 4 kst + 2 h (+1)
+    int vo[NDB];      // V^T fragment of column block db (key block 0 of each 16-key group)
+    int go[kLoadNI];  // source of direct load i within a tile
+    {
+#pragma unroll
+        for (int kst = 0; kst < NK8; ++kst) {
+#pragma unroll
+            for (int x = 0; x < 2; ++x) {
+                ko[kst][x] = swz8_off<D>(c32, 4 * kst + 2 * h + x);
+                asm volatile("" : "+v"(ko[kst][x]));
+            }
+        }
+        const int g = lane >> 4, e = (lane & 15) >> 1, o = lane & 1;
+        const int klo = 8 * (e >> 2) + 4 * (g >> 1) + (e & 3);
+#pragma unroll
+        for (int db = 0; db < NDB; ++db) {
+            vo[db] = swz8_off<D>(klo, 2 * db + (g & 1)) + 8 * o;
+            asm volatile("" : "+v"(vo[db]));
+        }
+#pragma unroll
+        for (int i = 0; i < kLoadNI; ++i) {
+            const int pchunk = 64 * (w * kLoadNI + i) + lane;
+            const int row = pchunk / (D / 16);
+            const int chunk = (pchunk - row * (D / 16)) ^ swz8<D>(row);
+            go[i] = row * D + 16 * chunk;
+            asm volatile("" : "+v"(go[i]));
+        }
+    }
 
     // real score per unit of the 8-bit dot product, and the exp2 factor
     const float s_raw = scale * DSQ[head] * DSK[kvh];
@@ -195,8 +181,32 @@ __global__ __launch_bounds__(64 * f8_waves<D>(), 8 / f8_waves<D>()) void fwd_fp8
 
         auto kstage = [&](auto par) __attribute__((always_inline)) { return (lds_char *)(decltype(par)::value ? k1_raw : k0_raw); };
         auto vstage = [&](auto par) __attribute__((always_inline)) { return (lds_char *)(decltype(par)::value ? v1_raw : v0_raw); };
-        auto load_k = [&](int j, auto par) __attribute__((always_inline)) { load_tile8<D, NW>(rk, kstage(par), j * kF8BN, w, lane); };
-        auto load_v = [&](int j, auto par) __attribute__((always_inline)) { load_tile8<D, NW>(rv, vstage(par), j * kF8BN, w, lane); };
+        // key rows [j * BN, j * BN + BN) of K or V into a stage; rows past Nk read as zeros
+        auto load_blk = [&](const uint8_t *src, lds_char *tile, int j) __attribute__((always_inline)) {
+            const int r0 = min(j * kF8BN, Nk);
+            const __amdgpu_buffer_rsrc_t rj = make_rsrc(src + hoff_k + (size_t)r0 * D, (uint32_t)(Nk - r0) * D);
+#pragma unroll
+            for (int i = 0; i < kLoadNI; ++i) buffer_load_lds16(rj, tile + 1024 * (w * kLoadNI + i), (uint32_t)go[i]);
+        };
+        auto load_k = [&](int j, auto par) __attribute__((always_inline)) { load_blk(K, kstage(par), j); };
+        auto load_v = [&](int j, auto par) __attribute__((always_inline)) { load_blk(V, vstage(par), j); };
+        // A operand of S^T = K Q^T for key rows 32 kb .. 32 kb + 31 and d bytes 64 kst .. 64 kst + 63:
+        // lane (c, h) takes row 32 kb + c, bytes 64 kst + 32 h .. + 31.
+        auto kfrag = [&](const lds_char *ks, int kb, int kst) __attribute__((always_inline)) {
+            const u32x4 lo = lds_read_b128(ks, ko[kst][0] + 32 * kb * D);
+            const u32x4 hi = lds_read_b128(ks, ko[kst][1] + 32 * kb * D);
+            return __builtin_bit_cast(i32x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+        };
+        // A operand of O^T += V^T P^T for columns 32 db .. 32 db + 31 of O: lane (c, h) takes byte
+        // p = V[sigma_h(p)][32 db + c], sigma_h(p) = 32(p/16) + 8((p%16)/4) + 4h + p%4.  Read t
+        // (bytes 8t .. 8t+7) is issued by source lane s = 16 g + 2 e + o at key 16 t + klo,
+        // klo = 8(e/4) + 4(g/2) + e%4, bytes 32 db + 16 (g%2) + 8 o .. + 7 of that row.
+        auto vfrag = [&](const lds_char *vs, int db) __attribute__((always_inline)) {
+            i32x2 r[4];
+#pragma unroll
+            for (int t = 0; t < 4; ++t) r[t] = lds_read_tr8(vs, vo[db] + 16 * t * D);
+            return i32x8{r[0][0], r[0][1], r[1][0], r[1][1], r[2][0], r[2][1], r[3][0], r[3][1]};
+        };
 
         auto local_max = [&](const f32x16 *sc) __attribute__((always_inline)) {
             float m = fmaxf(sc[0][0], sc[0][1]);
@@ -216,6 +226,10 @@ __global__ __launch_bounds__(64 * f8_waves<D>(), 8 / f8_waves<D>()) void fwd_fp8
         wait_vmem();
         __syncthreads();
         f32x16 sa[2], sb[2];
+        // P as e4m3, byte p = 16 kb + r of the lane's keys; every step rewrites all four bytes of
+        // each word, so the conversions take the previous step's word as their untouched half and
+        // need no cleared register
+        int pw[8] = {0, 0, 0, 0, 0, 0, 0, 0};
         if (ja > 0) {
             const lds_char *ks = kstage(P0{});
             sa[0] = zero16();
@@ -223,7 +237,7 @@ __global__ __launch_bounds__(64 * f8_waves<D>(), 8 / f8_waves<D>()) void fwd_fp8
 #pragma unroll
             for (int kst = 0; kst < NK8; ++kst) {
 #pragma unroll
-                for (int kb = 0; kb < 2; ++kb) sa[kb] = mfma8(k_frag<D>(ks, kb, kst, c32, h), qf[kst], sa[kb]);
+                for (int kb = 0; kb < 2; ++kb) sa[kb] = mfma8(kfrag(ks, kb, kst), qf[kst], sa[kb]);
             }
             mloc = local_max(sa);
         }
@@ -276,12 +290,11 @@ __global__ __launch_bounds__(64 * f8_waves<D>(), 8 / f8_waves<D>()) void fwd_fp8
                 const lds_char *vs = vstage(par);
                 auto fetch = [&](auto C) __attribute__((always_inline)) {
                     constexpr int c = decltype(C)::value;
-                    if constexpr (c < NS) return k_frag<D>(ks, c & 1, c >> 1, c32, h);
-                    else return v_frag<D>(vs, c - NS, lane);
+                    if constexpr (c < NS) return kfrag(ks, c & 1, c >> 1);
+                    else return vfrag(vs, c - NS);
                 };
                 nxt[0] = zero16();
                 nxt[1] = zero16();
-                int pw[8];  // P as e4m3, byte p = 16 kb + r of the lane's keys
                 float rs = 0.f, mx = -__builtin_inff();
                 constexpr int PF = 1;
                 i32x8 fr[PF + 1];
@@ -309,7 +322,7 @@ __global__ __launch_bounds__(64 * f8_waves<D>(), 8 / f8_waves<D>()) void fwd_fp8
                                 p[i] = fast_exp2(fmaf(cur[kb][r0 + i], c_log2, -msc));
                                 cur[kb][r0 + i] = p[i];
                             }
-                            int x = __builtin_amdgcn_cvt_pk_fp8_f32(p[0], p[1], 0, false);
+                            int x = __builtin_amdgcn_cvt_pk_fp8_f32(p[0], p[1], pw[wd], false);
                             pw[wd] = __builtin_amdgcn_cvt_pk_fp8_f32(p[2], p[3], x, true);
                         });
                     } else {
