@@ -2,8 +2,9 @@
 """Benchmark: attention forward + backward throughput on one MI355X.
 
 One step is one pass of the whole path over resident synthetic inputs: the fused
-forward kernel, then the backward preprocess, dK/dV and dQ kernels (the same four
-launches attn_bwd makes).  The default workload is the forward+backward causal case
+forward kernel, then the launches attn_bwd makes (d <= 128: the dQ kernel, which also forms
+D = rowsum(dO o O), then the dK/dV kernel; wider heads: preprocess, dK/dV, dQ).  The default
+workload is the forward+backward causal case
 B=2, H=16, N=4096, d=128; ``--workload c2|c3|c4`` times forward-only workloads, ``dec`` the
 split-key forward of a decoding shape, and ``c3f8|c4f8`` the 8-bit forward on the shapes of
 c3 and c4.
@@ -233,8 +234,11 @@ def main():
     torch.cuda.synchronize()
     del cal_src, cal_dst
 
-    kernels = (["fwd_splitkv"] if split else ["fwd_fp8"] if fp8 else ["fwd"]) + (
-        (["bwd"] if qk else ["preprocess", "dkdv", "dq"]) if w.backward else [])
+    # the backward kernels in attn_bwd's order: d <= 128 runs dQ first, forming D of its rows on
+    # the way (attn_bwd_dq_delta), then dK/dV; wider heads run the preprocess, dK/dV and dQ
+    fused_d = d <= 128
+    bwd_kernels = ["bwd"] if qk else (["dq", "dkdv"] if fused_d else ["preprocess", "dkdv", "dq"])
+    kernels = (["fwd_splitkv"] if split else ["fwd_fp8"] if fp8 else ["fwd"]) + (bwd_kernels if w.backward else [])
     ev = {kname: [] for kname in kernels}
 
     def step(record):
@@ -255,6 +259,13 @@ def main():
             A.attn_bwd_qk(q, k, v, o, do, lse, dq, dk, dv, delta, B, H, Hk, N, Nk, d, causal, scale)
             if record:
                 e[2].record()
+        elif w.backward and fused_d:
+            A.attn_bwd_dq_delta(q, k, v, o, do, lse, delta, dq, B, H, N, d, causal, scale)
+            if record:
+                e[2].record()
+            A.attn_bwd_dkdv(q, k, v, do, lse, delta, dk, dv, B, H, N, d, causal, scale)
+            if record:
+                e[3].record()
         elif w.backward:
             A.attn_bwd_preprocess(o, do, delta, B, H, N, d)
             if record:
@@ -335,7 +346,7 @@ def main():
         "roofline": roof,
     }
     if w.backward:
-        bwd_ms = kernel_ms["bwd"] if qk else sum(kernel_ms[x] for x in ("preprocess", "dkdv", "dq"))
+        bwd_ms = sum(kernel_ms[x] for x in bwd_kernels)
         out["bwd_tflops"] = round(2.5 * workload_fwd_flop(w) / (bwd_ms * 1e-3) / 1e12, 2)
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(w, args.cpu_budget)

@@ -131,25 +131,27 @@ int attn_fwd_fp8(const void *q, const void *k, const void *v,
                  void *o, float *lse, int B, int H, int Hk, int Nq, int Nk, int d, int causal,
                  float scale, void *stream);
 
-/* Backward pass: enqueues attn_bwd_preprocess, attn_bwd_dkdv and attn_bwd_dq
- * in that order on `stream`.  Reads q, k, v, o, dout and the lse written by
- * attn_fwd with the same q, k, v, causal and scale; writes dq, dk, dv
- * [B,H,N,d] (bf16) and delta [B,H,N] (fp32), a caller-owned workspace that
- * holds D on return. */
+/* Backward pass: for d = 64 and 128 enqueues attn_bwd_dq_delta then
+ * attn_bwd_dkdv (two launches); for d = 192 and 256 attn_bwd_preprocess,
+ * attn_bwd_dkdv and attn_bwd_dq, in that order on `stream`.  Reads q, k, v, o,
+ * dout and the lse written by attn_fwd with the same q, k, v, causal and scale;
+ * writes dq, dk, dv [B,H,N,d] (bf16) and delta [B,H,N] (fp32), a caller-owned
+ * workspace that holds D on return.  Both orders give bitwise the same
+ * results. */
 int attn_bwd(const void *q, const void *k, const void *v, const void *o, const void *dout,
              const float *lse, void *dq, void *dk, void *dv, float *delta,
              int B, int H, int N, int d, int causal, float scale, void *stream);
 
 /* Backward pass with H query heads and Hk K/V heads, Nq query rows and Nk
- * key/value rows per head; the same three kernels as attn_bwd (the dK/dV
+ * key/value rows per head; the same kernels as attn_bwd (the dK/dV
  * kernel loops over the H / Hk query heads of each K/V head).  delta is
  * [B, H, Nq].  With Nq = 0 it writes dk = dv = 0; with Nk = 0 it writes dq = 0. */
 int attn_bwd_qk(const void *q, const void *k, const void *v, const void *o, const void *dout,
                 const float *lse, void *dq, void *dk, void *dv, float *delta,
                 int B, int H, int Hk, int Nq, int Nk, int d, int causal, float scale, void *stream);
 
-/* The three backward steps below take one length N (Nq = Nk = N); they exist
- * so that each kernel can be enqueued and timed on its own. */
+/* The backward steps below take one length N (Nq = Nk = N); they exist so
+ * that each kernel can be enqueued and timed on its own. */
 
 /* Backward step 1: delta[i] = sum_c dout[i][c] * o[i][c] (fp32 products and
  * sums of the bf16 inputs).  Memory-bound; one kernel launch. */
@@ -170,6 +172,18 @@ int attn_bwd_dkdv(const void *q, const void *k, const void *v, const void *dout,
 int attn_bwd_dq(const void *q, const void *k, const void *v, const void *dout,
                 const float *lse, const float *delta, void *dq,
                 int B, int H, int N, int d, int causal, float scale, void *stream);
+
+/* Backward steps 1 and 3 together: writes delta exactly as
+ * attn_bwd_preprocess does (bitwise) and dq exactly as attn_bwd_dq does with
+ * that delta.  For d = 64 and 128 this is one kernel launch: the dQ kernel
+ * forms D of its own rows from o and dout before its loop, summing in the
+ * preprocess kernel's order; for d = 192 and 256 it enqueues the two steps.
+ * attn_bwd_dkdv, which needs every row's D, is enqueued after it.  Same
+ * arguments and errors as attn_bwd_dq, plus o (an input) and delta (an
+ * output, no longer an input). */
+int attn_bwd_dq_delta(const void *q, const void *k, const void *v, const void *o,
+                      const void *dout, const float *lse, float *delta, void *dq,
+                      int B, int H, int N, int d, int causal, float scale, void *stream);
 
 /* Static, NUL-terminated description of a status code (never NULL). */
 const char *attn_status_string(int status);

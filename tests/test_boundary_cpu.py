@@ -36,7 +36,7 @@ def test_header_declares_the_expected_entry_points():
     assert declared_functions() == sorted([
         "attn_fwd", "attn_fwd_qk", "attn_fwd_splitkv", "attn_fwd_splitkv_workspace_size",
         "attn_fwd_splitkv_default_splits", "attn_fwd_fp8", "attn_bwd", "attn_bwd_qk", "attn_bwd_preprocess", "attn_bwd_dkdv",
-        "attn_bwd_dq", "attn_status_string", "attn_last_hip_error"])
+        "attn_bwd_dq", "attn_bwd_dq_delta", "attn_status_string", "attn_last_hip_error"])
 
 
 def test_library_exports_every_declared_symbol(lib):
@@ -122,6 +122,14 @@ def test_backward_argument_checks(lib):
                            None) == A.ATTN_ERR_BAD_SCALE
     assert lib.attn_bwd_dq(P[0], P[1], P[2], P[3], P[4], P[5], P[6], 1, 1, 64, 100, 0, 0.1,
                            None) == A.ATTN_ERR_UNSUPPORTED_D
+    # attn_bwd_dq_delta: q, k, v, o, dout, lse in; delta, dq out
+    dqd = lambda *p, d=64, scale=0.125: lib.attn_bwd_dq_delta(*p, 1, 1, 64, d, 0, scale, None)
+    assert dqd(P[0], P[1], P[2], P[3], P[4], P[5], P[6], P[7], scale=0.0) == A.ATTN_ERR_BAD_SCALE
+    assert dqd(P[0], P[1], P[2], P[3], P[4], P[5], P[6], P[7], d=100) == A.ATTN_ERR_UNSUPPORTED_D
+    assert dqd(P[0], P[1], P[2], None, P[4], P[5], P[6], P[7]) == A.ATTN_ERR_NULLPTR       # o
+    assert dqd(P[0], P[1], P[2], P[3], P[4], P[5], P[3], P[7]) == A.ATTN_ERR_ALIAS         # delta == o
+    assert dqd(P[0], P[1], P[2], P[3], P[4], P[5], P[6], P[6]) == A.ATTN_ERR_ALIAS         # dq == delta
+    assert dqd(P[0], P[1], P[2], P[3], P[4], P[5], P[6], P[7] + 4) == A.ATTN_ERR_MISALIGNED
 
 
 def test_python_binding_raises_with_status(lib):

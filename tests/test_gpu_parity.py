@@ -248,6 +248,27 @@ def test_step_entry_points_equal_the_combined_backward():
     assert np.abs(f64(delta) - ref).max() <= 1e-4 * max(1.0, np.abs(ref).max())
 
 
+@pytest.mark.parametrize("N,d,causal", [(300, 128, True), (257, 64, False), (128, 128, False), (200, 256, True)])
+def test_dq_delta_equals_preprocess_then_dq(N, d, causal):
+    """attn_bwd_dq_delta (d <= 128: one dQ kernel that forms D on the way) writes bitwise the
+    delta of attn_bwd_preprocess and the dq of attn_bwd_dq."""
+    note("dq_delta vs preprocess+dq N=%d d=%d causal=%d" % (N, d, causal))
+    B, H = 1, 3
+    scale = softmax_scale(d)
+    inp = make_inputs(B, H, N, d, seed=29, backward=True)
+    o, lse = gpu_fwd(inp, causal, scale)
+    q, k, v, do = dev(inp["q"]), dev(inp["k"]), dev(inp["v"]), dev(inp["do"])
+    delta1 = torch.full((B, H, N), float("nan"), dtype=torch.float32, device=DEV)
+    delta2 = torch.full_like(delta1, float("nan"))
+    dq1, dq2 = torch.empty_like(q), torch.empty_like(q)
+    A.attn_bwd_preprocess(o, do, delta1, B, H, N, d)
+    A.attn_bwd_dq(q, k, v, do, lse, delta1, dq1, B, H, N, d, causal, scale)
+    A.attn_bwd_dq_delta(q, k, v, o, do, lse, delta2, dq2, B, H, N, d, causal, scale)
+    torch.cuda.synchronize()
+    assert torch.equal(delta1, delta2)
+    assert torch.equal(dq1, dq2)
+
+
 def test_non_default_stream_and_errors_leave_outputs_untouched():
     note("stream + error path")
     B, H, N, d = 1, 1, 128, 64

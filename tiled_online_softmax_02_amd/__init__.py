@@ -55,6 +55,7 @@ _SIGNATURES = {
     "attn_bwd_preprocess": [_P, _P, _P, _I, _I, _I, _I, _P],
     "attn_bwd_dkdv": [_P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _F, _P],
     "attn_bwd_dq": [_P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _F, _P],
+    "attn_bwd_dq_delta": [_P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _F, _P],
 }
 
 
@@ -171,6 +172,11 @@ def attn_bwd_dkdv(q, k, v, dout, lse, delta, dk, dv, B, H, N, d, causal, scale, 
 def attn_bwd_dq(q, k, v, dout, lse, delta, dq, B, H, N, d, causal, scale, stream=None) -> None:
     _call("attn_bwd_dq", _ptr(q), _ptr(k), _ptr(v), _ptr(dout), _ptr(lse), _ptr(delta), _ptr(dq), B, H, N, d,
           int(causal), float(scale), _stream(stream, q, dq))
+
+
+def attn_bwd_dq_delta(q, k, v, o, dout, lse, delta, dq, B, H, N, d, causal, scale, stream=None) -> None:
+    _call("attn_bwd_dq_delta", _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(dout), _ptr(lse), _ptr(delta), _ptr(dq),
+          B, H, N, d, int(causal), float(scale), _stream(stream, q, dq))
 
 
 def _check_inputs(q, k, v, *q_like):

@@ -183,6 +183,11 @@ int bwd_impl(const void *q, const void *k, const void *v, const void *o, const v
     const Range out[] = {range_of(dq, qb), range_of(dk, kb), range_of(dv, kb), range_of(delta, lb)};
     RETURN_IF(check_alias(in, 6, out, 4));
     attn::BwdArgs a{q, k, v, o, dout, lse, dq, dk, dv, delta, B, H, Hk, Nq, Nk, d, causal, scale, stream};
+    if (attn::bwd_dq_fuses_delta(d)) {
+        // d <= 128: the dQ kernel forms D on the way (no preprocess launch), then dK/dV reads it
+        RETURN_IF(hip_status(attn::launch_bwd_dq_delta(a)));
+        return hip_status(attn::launch_bwd_dkdv(a));
+    }
     RETURN_IF(hip_status(attn::launch_bwd_preprocess(a)));
     RETURN_IF(hip_status(attn::launch_bwd_dkdv(a)));
     return hip_status(attn::launch_bwd_dq(a));
@@ -322,6 +327,42 @@ int attn_bwd_dq(const void *q, const void *k, const void *v, const void *dout, c
     a.causal = causal;
     a.scale = scale;
     a.stream = stream;
+    return hip_status(attn::launch_bwd_dq(a));
+}
+
+int attn_bwd_dq_delta(const void *q, const void *k, const void *v, const void *o, const void *dout, const float *lse,
+                      float *delta, void *dq, int B, int H, int N, int d, int causal, float scale, void *stream)
+{
+    bool empty = false;
+    RETURN_IF(validate_common(B, H, H, N, N, d, causal, scale, &empty));
+    if (empty) return ATTN_OK;
+    const long long tb = tensor_bytes(B, H, N, d), lb = vector_bytes(B, H, N);
+    const void *ptrs[] = {q, k, v, o, dout, lse, delta, dq};
+    const long long sizes[] = {tb, tb, tb, tb, tb, lb, lb, tb};
+    RETURN_IF(check_ptrs(ptrs, sizes, 8));
+    const Range in[] = {range_of(q, tb),    range_of(k, tb),    range_of(v, tb),
+                        range_of(o, tb),    range_of(dout, tb), range_of(lse, lb)};
+    const Range out[] = {range_of(delta, lb), range_of(dq, tb)};
+    RETURN_IF(check_alias(in, 6, out, 2));
+    attn::BwdArgs a{};
+    a.q = q;
+    a.k = k;
+    a.v = v;
+    a.o = o;
+    a.dout = dout;
+    a.lse = lse;
+    a.delta = delta;
+    a.dq = dq;
+    a.B = B;
+    a.H = H;
+    a.Hk = H;
+    a.Nq = a.Nk = N;
+    a.d = d;
+    a.causal = causal;
+    a.scale = scale;
+    a.stream = stream;
+    if (attn::bwd_dq_fuses_delta(d)) return hip_status(attn::launch_bwd_dq_delta(a));
+    RETURN_IF(hip_status(attn::launch_bwd_preprocess(a)));
     return hip_status(attn::launch_bwd_dq(a));
 }
 

@@ -807,12 +807,17 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv3_kernel(
 constexpr int kQBM = 128;  // queries per workgroup (32 per wave)
 constexpr int kQBN = 64;   // keys per streamed block
 
-template <int D, bool CAUSAL>
+// FUSE_D (d <= 128): the kernel also forms D = rowsum(dO o O) of its own rows from O and writes
+// it to Dl for the dK/dV kernel that runs after it, in place of the preprocess kernel.  The sum
+// takes the preprocess kernel's order (8-element chunks by fused multiply-add, then the chunks
+// pairwise at distances 8, 4, 2, 1), so D is bitwise the same either way.
+template <int D, bool CAUSAL, bool FUSE_D = false>
 __global__ __launch_bounds__(kThreads, D >= 192 ? 1 : 2) void bwd_dq_kernel(
     const bf16 *__restrict__ Q, const bf16 *__restrict__ K, const bf16 *__restrict__ V, const bf16 *__restrict__ dO,
-    const float *__restrict__ LSE, const float *__restrict__ Dl, bf16 *__restrict__ dQ, int Nq, int Nk, int H, int G,
-    int n_qtiles, float scale, float c_log2)
+    const float *__restrict__ LSE, float *__restrict__ Dl, bf16 *__restrict__ dQ, int Nq, int Nk, int H, int G,
+    int n_qtiles, float scale, float c_log2, const bf16 *__restrict__ O)
 {
+    static_assert(!FUSE_D || D <= 128, "the fused row sum follows the preprocess order for d <= 128");
     constexpr int NKS = D / 16;
     constexpr int NDB = D / 32;
     constexpr int TILE = kQBN * D * 2;
@@ -845,16 +850,50 @@ __global__ __launch_bounds__(kThreads, D >= 192 ? 1 : 2) void bwd_dq_kernel(
     // dS = P (dP - D) is then one multiply per element and dQ accumulates with the opposite sign
     constexpr bool kNegDP = D <= 128;
     bf16x8 qf[NKS], gf[NKS];
+    float dfused = 0.f;
+    {
+        // lane (c32, h) holds 8-element chunks 2 ks + h of its row, ks = 0 .. NKS-1
+        float a[NKS];
+        bf16x8 of[NKS];
+        if constexpr (FUSE_D) {
+            const __amdgpu_buffer_rsrc_t ro = make_rsrc(O + hoff, (uint32_t)Nq * D * 2);
 #pragma unroll
-    for (int ks = 0; ks < NKS; ++ks) {
-        qf[ks] = __builtin_bit_cast(bf16x8, buffer_load16(rq, (uint32_t)(qrow * D + 16 * ks + 8 * h) * 2u));
-        gf[ks] = __builtin_bit_cast(bf16x8, buffer_load16(rg, (uint32_t)(qrow * D + 16 * ks + 8 * h) * 2u) ^
-                                                (kNegDP ? 0x80008000u : 0u));
+            for (int ks = 0; ks < NKS; ++ks)
+                of[ks] = __builtin_bit_cast(bf16x8, buffer_load16(ro, (uint32_t)(qrow * D + 16 * ks + 8 * h) * 2u));
+        }
+#pragma unroll
+        for (int ks = 0; ks < NKS; ++ks) {
+            qf[ks] = __builtin_bit_cast(bf16x8, buffer_load16(rq, (uint32_t)(qrow * D + 16 * ks + 8 * h) * 2u));
+            const u32x4 graw = buffer_load16(rg, (uint32_t)(qrow * D + 16 * ks + 8 * h) * 2u);
+            gf[ks] = __builtin_bit_cast(bf16x8, graw ^ (kNegDP ? 0x80008000u : 0u));
+            if constexpr (FUSE_D) {
+                const bf16x8 g = __builtin_bit_cast(bf16x8, graw);
+                a[ks] = 0.f;
+#pragma unroll
+                for (int e = 0; e < 8; ++e) a[ks] = fmaf((float)of[ks][e], (float)g[e], a[ks]);
+            }
+        }
+        if constexpr (FUSE_D) {
+            // chunks j and j + CPR/2 (ks and ks + NKS/2) first, then halving distances; the last
+            // step pairs the even chunks of lane half 0 with the odd ones of half 1
+#pragma unroll
+            for (int n = NKS / 2; n >= 1; n >>= 1) {
+#pragma unroll
+                for (int ks = 0; ks < n; ++ks) a[ks] = a[ks] + a[ks + n];
+            }
+            dfused = a[0] + __shfl_xor(a[0], 32);
+        }
     }
     // a row past Nq, or a query that sees no key (lse = -inf), gets lse2 = +inf and so P = 0
     const float lse_row = row_ok ? LSE[(size_t)head * Nq + qrow] : -__builtin_inff();
     const float lse2 = (lse_row == -__builtin_inff()) ? __builtin_inff() : lse_row * kLog2e;
-    const float dval = row_ok ? Dl[(size_t)head * Nq + qrow] : 0.f;
+    float dval;
+    if constexpr (FUSE_D) {
+        dval = row_ok ? dfused : 0.f;
+        if (row_ok && h == 0) Dl[(size_t)head * Nq + qrow] = dfused;
+    } else {
+        dval = row_ok ? Dl[(size_t)head * Nq + qrow] : 0.f;
+    }
 
     f32x16 dq[NDB];
 #pragma unroll
@@ -1074,15 +1113,16 @@ hipError_t launch_dkdv_t(const BwdArgs &a)
     return hipGetLastError();
 }
 
-template <int D, bool CAUSAL>
+template <int D, bool CAUSAL, bool FUSE_D = false>
 hipError_t launch_dq_t(const BwdArgs &a)
 {
     const int n_qtiles = (a.Nq + kQBM - 1) / kQBM;
     const long long G = (long long)a.B * a.H * n_qtiles;
     if (G == 0) return hipSuccess;
-    hipLaunchKernelGGL((bwd_dq_kernel<D, CAUSAL>), dim3((unsigned)G), dim3(kThreads), 0, (hipStream_t)a.stream,
+    hipLaunchKernelGGL((bwd_dq_kernel<D, CAUSAL, FUSE_D>), dim3((unsigned)G), dim3(kThreads), 0, (hipStream_t)a.stream,
                        (const bf16 *)a.q, (const bf16 *)a.k, (const bf16 *)a.v, (const bf16 *)a.dout, a.lse,
-                       (const float *)a.delta, (bf16 *)a.dq, a.Nq, a.Nk, a.H, a.H / a.Hk, n_qtiles, a.scale, a.scale * kLog2e);
+                       a.delta, (bf16 *)a.dq, a.Nq, a.Nk, a.H, a.H / a.Hk, n_qtiles, a.scale, a.scale * kLog2e,
+                       (const bf16 *)a.o);
     return hipGetLastError();
 }
 
@@ -1105,6 +1145,17 @@ hipError_t launch_bwd_dkdv(const BwdArgs &a)
     case 128: return a.causal ? launch_dkdv2_t<128, true>(a) : launch_dkdv2_t<128, false>(a);
     case 192: return a.causal ? launch_dkdv3_t<192, true>(a) : launch_dkdv3_t<192, false>(a);
     default: return a.causal ? launch_dkdv3_t<256, true>(a) : launch_dkdv3_t<256, false>(a);
+    }
+}
+
+bool bwd_dq_fuses_delta(int d) { return d <= 128; }
+
+hipError_t launch_bwd_dq_delta(const BwdArgs &a)
+{
+    switch (a.d) {
+    case 64: return a.causal ? launch_dq_t<64, true, true>(a) : launch_dq_t<64, false, true>(a);
+    case 128: return a.causal ? launch_dq_t<128, true, true>(a) : launch_dq_t<128, false, true>(a);
+    default: return hipErrorInvalidValue;
     }
 }
 
