@@ -971,13 +971,77 @@ __global__ __launch_bounds__(kThreads, D >= 192 ? 1 : 2) void bwd_dq_kernel(
         wait_vmem();
         __syncthreads();
     };
-    auto step = [&](int j, auto par) __attribute__((always_inline)) {
+    // CH: an unmasked block of a d <= 128 kernel, run as chunks (below); otherwise the plain step
+    auto step = [&](int j, auto par, auto CH) __attribute__((always_inline)) {
         using PN = std::integral_constant<int, 1 - decltype(par)::value>;
         load_blk(j + 1, PN{});  // past the last block: zeros into the free stage, never read
         const lds_char *ks = kst_l(par);
         const lds_char *vs = vst_l(par);
         const int k0 = j * kQBN;
-        if (kSplitLoops || j < ja_seen) {
+        // Only blocks that cross the diagonal or the end of the keys are masked: their masked
+        // scores become -inf (P = 0) in a branch that the other blocks skip.
+        const bool need_mask = (CAUSAL && (k0 + kQBN - 1 > qw0 + off)) || (k0 + kQBN > Nk);
+        // d <= 128, unmasked block: NC chunks of one matrix instruction and a slice of vector work,
+        // so that one wave's exponentials run under its own products:
+        //   [0, NSH)              S and dP of keys 0..31
+        //   [NSH, 2 NSH)          S and dP of keys 32..63   | P, dS of keys 0..31
+        //   [2 NSH, 2 NSH + NQH)  dQ over keys 0..31        | P, dS of keys 32..63
+        //   [2 NSH + NQH, NC)     dQ over keys 32..63
+        // LDS fragments are fetched two chunks ahead; scheduling barriers keep each chunk whole.
+        if constexpr (decltype(CH)::value) {
+            constexpr int NSH = 2 * NKS, NQH = 2 * NDB, NC = 2 * NSH + 2 * NQH, PF = 2;
+            f32x16 s[2] = {zero16(), zero16()};
+            f32x16 dp[2];  // D - dP (dO is held negated)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) dp[0][r] = dp[1][r] = dval;
+            bf16x8 sb[4];
+            auto fetch = [&](auto C) __attribute__((always_inline)) {
+                constexpr int c = decltype(C)::value;
+                if constexpr (c < 2 * NSH) {
+                    constexpr int kb = c / NSH, i = c % NSH;
+                    return lds_read16((i & 1) ? vs : ks, ko[i >> 1] + 32 * kb * 2 * D);
+                } else {
+                    constexpr int i = c - 2 * NSH, t = i / NDB, db = i % NDB;
+                    const bf16x4 lo = lds_read_tr(ks, vo[db][0] + 16 * t * 2 * D);
+                    const bf16x4 hi = lds_read_tr(ks, vo[db][1] + 16 * t * 2 * D);
+                    return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+                }
+            };
+            auto valu = [&](auto KB, auto R) __attribute__((always_inline)) {
+                constexpr int kb = decltype(KB)::value, r = decltype(R)::value;
+                const float p = fast_exp2(fmaf(s[kb][r], c_log2, -lse2));
+                sb[2 * kb + (r >> 3)][r & 7] = (bf16)(p * dp[kb][r]);
+            };
+            bf16x8 fr[PF + 1];
+            static_for<0, PF>([&](auto F) __attribute__((always_inline)) { fr[decltype(F)::value] = fetch(F); });
+            static_for<0, NC>([&](auto C) __attribute__((always_inline)) {
+                constexpr int c = decltype(C)::value;
+                if constexpr (c + PF < NC) fr[(c + PF) % (PF + 1)] = fetch(std::integral_constant<int, c + PF>{});
+                const bf16x8 fc = fr[c % (PF + 1)];
+                if constexpr (c < 2 * NSH) {
+                    constexpr int kb = c / NSH, i = c % NSH;
+                    if constexpr (i & 1)
+                        dp[kb] = mfma(fc, gf[i >> 1], dp[kb]);
+                    else
+                        s[kb] = mfma(fc, qf[i >> 1], s[kb]);
+                } else {
+                    constexpr int i = c - 2 * NSH, t = i / NDB, db = i % NDB;
+                    dq[db] = mfma(fc, sb[t], dq[db]);
+                }
+                if constexpr (c >= NSH && c < 2 * NSH) {
+                    constexpr int i = c - NSH;
+                    static_for<i * 16 / NSH, (i + 1) * 16 / NSH>([&](auto R) __attribute__((always_inline)) {
+                        valu(std::integral_constant<int, 0>{}, R);
+                    });
+                } else if constexpr (c >= 2 * NSH && c < 2 * NSH + NQH) {
+                    constexpr int i = c - 2 * NSH;
+                    static_for<i * 16 / NQH, (i + 1) * 16 / NQH>([&](auto R) __attribute__((always_inline)) {
+                        valu(std::integral_constant<int, 1>{}, R);
+                    });
+                }
+                __builtin_amdgcn_sched_barrier(0);
+            });
+        } else if (kSplitLoops || j < ja_seen) {
             f32x16 s[2] = {zero16(), zero16()};
             f32x16 dp[2] = {zero16(), zero16()};  // dP, or D - dP (kNegDP)
             if constexpr (kNegDP) {
@@ -993,9 +1057,6 @@ __global__ __launch_bounds__(kThreads, D >= 192 ? 1 : 2) void bwd_dq_kernel(
                     dp[kb] = mfma(lds_read16(vs, off), gf[kst], dp[kb]);
                 }
             }
-            // Only blocks that cross the diagonal or the end of the keys are masked: their masked
-            // scores become -inf (P = 0) in a branch that the other blocks skip.
-            const bool need_mask = (CAUSAL && (k0 + kQBN - 1 > qw0 + off)) || (k0 + kQBN > Nk);
             if (need_mask) {
 #pragma unroll
                 for (int kb = 0; kb < 2; ++kb) {
@@ -1036,13 +1097,25 @@ __global__ __launch_bounds__(kThreads, D >= 192 ? 1 : 2) void bwd_dq_kernel(
         __syncthreads();
     };
 
-    // stage parity of key block j is j & 1
+    // stage parity of key block j is j & 1.  d <= 128: blocks [0, jm) need no mask and run as
+    // chunks; [jm, ja) cross the diagonal or the end of the keys (the need for a mask only grows
+    // with j).  Separate loops keep the two bodies' registers apart.
+    using CHK = std::integral_constant<bool, kFixedOffsets>;
+    using PLAIN = std::false_type;
+    const int jm_c = CAUSAL ? (qw0 + off - (kQBN - 1) >= 0 ? (qw0 + off - (kQBN - 1)) / kQBN + 1 : 0) : ja;
+    const int jm = kFixedOffsets ? max(0, min(ja, min(jm_c, Nk / kQBN))) : 0;
     int j = 0;
-    for (; j + 1 < ja; j += 2) {
-        step(j, P0{});
-        step(j + 1, P1{});
+    for (; j + 1 < jm; j += 2) {
+        step(j, P0{}, CHK{});
+        step(j + 1, P1{}, CHK{});
     }
-    if (j < ja) step(j++, P0{});
+    if (j < jm) step(j++, P0{}, CHK{});
+    if (j < ja && (j & 1)) step(j++, P1{}, PLAIN{});
+    for (; j + 1 < ja; j += 2) {
+        step(j, P0{}, PLAIN{});
+        step(j + 1, P1{}, PLAIN{});
+    }
+    if (j < ja) step(j++, P0{}, PLAIN{});
     if (j < nt && (j & 1)) step_idle(j++, P1{});
     for (; j + 1 < nt; j += 2) {
         step_idle(j, P0{});
