@@ -981,63 +981,91 @@ __global__ __launch_bounds__(kThreads, D >= 192 ? 1 : 2) void bwd_dq_kernel(
         // Only blocks that cross the diagonal or the end of the keys are masked: their masked
         // scores become -inf (P = 0) in a branch that the other blocks skip.
         const bool need_mask = (CAUSAL && (k0 + kQBN - 1 > qw0 + off)) || (k0 + kQBN > Nk);
-        // d <= 128, unmasked block: NC chunks of one matrix instruction and a slice of vector work,
-        // so that one wave's exponentials run under its own products:
-        //   [0, NSH)              S and dP of keys 0..31
-        //   [NSH, 2 NSH)          S and dP of keys 32..63   | P, dS of keys 0..31
-        //   [2 NSH, 2 NSH + NQH)  dQ over keys 0..31        | P, dS of keys 32..63
-        //   [2 NSH + NQH, NC)     dQ over keys 32..63
-        // LDS fragments are fetched two chunks ahead; scheduling barriers keep each chunk whole.
+        // d <= 128, unmasked block: chunks of one matrix instruction and a slice of vector work,
+        // so that one wave's exponentials run under its own products.  LDS fragments are fetched
+        // two chunks ahead; scheduling barriers keep each chunk whole.
         if constexpr (decltype(CH)::value) {
-            constexpr int NSH = 2 * NKS, NQH = 2 * NDB, NC = 2 * NSH + 2 * NQH, PF = 2;
-            f32x16 s[2] = {zero16(), zero16()};
-            f32x16 dp[2];  // D - dP (dO is held negated)
+            // Six phases of L = NKS chunks (2 NDB = NKS): S of keys 0..31 (half 0), dP of half 0,
+            // S of keys 32..63 (half 1), dP of half 1, dQ over half 0, dQ over half 1.  The vector
+            // work goes where its inputs are complete, about one element's P or dS per chunk
+            // (a lane holds 16 elements of each half; elements 0..7 and 8..15 are the two
+            // 16-key groups of dS that the dQ products read):
+            //   phase 1 (dP, half 0):  P of elements 0..7 of half 0
+            //   phase 2 (S, half 1):   P of elements 8..15 of half 0, dS of its elements 0..7
+            //   phase 3 (dP, half 1):  dS of elements 8..15 of half 0, P of elements 0..7 of half 1
+            //   phase 4 (dQ, half 0):  P of elements 8..15 of half 1, dS of its elements 0..7
+            //   phase 5 (dQ, half 1):  dS of elements 8..15 of half 1 in the first L/2 chunks,
+            //                          before the products that read them
+            constexpr int L = NKS, NC = 6 * L, PF = 2;
+            static_assert(2 * NDB == L, "dQ phases are as long as the score phases");
+            f32x16 s[2] = {zero16(), zero16()};  // scores, then P in place
+            f32x16 dp[2];                        // D - dP (dO is held negated)
 #pragma unroll
             for (int r = 0; r < 16; ++r) dp[0][r] = dp[1][r] = dval;
             bf16x8 sb[4];
             auto fetch = [&](auto C) __attribute__((always_inline)) {
-                constexpr int c = decltype(C)::value;
-                if constexpr (c < 2 * NSH) {
-                    constexpr int kb = c / NSH, i = c % NSH;
-                    return lds_read16((i & 1) ? vs : ks, ko[i >> 1] + 32 * kb * 2 * D);
+                constexpr int c = decltype(C)::value, ph = c / L, i = c % L;
+                if constexpr (ph < 4) {
+                    return lds_read16((ph & 1) ? vs : ks, ko[i] + 32 * (ph >> 1) * 2 * D);
                 } else {
-                    constexpr int i = c - 2 * NSH, t = i / NDB, db = i % NDB;
+                    constexpr int t = 2 * (ph - 4) + i / NDB, db = i % NDB;
                     const bf16x4 lo = lds_read_tr(ks, vo[db][0] + 16 * t * 2 * D);
                     const bf16x4 hi = lds_read_tr(ks, vo[db][1] + 16 * t * 2 * D);
                     return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
                 }
             };
-            auto valu = [&](auto KB, auto R) __attribute__((always_inline)) {
-                constexpr int kb = decltype(KB)::value, r = decltype(R)::value;
-                const float p = fast_exp2(fmaf(s[kb][r], c_log2, -lse2));
-                sb[2 * kb + (r >> 3)][r & 7] = (bf16)(p * dp[kb][r]);
+            // P and dS of elements [e0, e1) of half kb (elements e and e + 8 share an 8-element
+            // group of sb; 8 of them are one group)
+            auto p_of = [&](auto KB, auto E0, auto E1) __attribute__((always_inline)) {
+                constexpr int kb = decltype(KB)::value;
+                static_for<decltype(E0)::value, decltype(E1)::value>([&](auto R) __attribute__((always_inline)) {
+                    constexpr int r = decltype(R)::value;
+                    s[kb][r] = fast_exp2(fmaf(s[kb][r], c_log2, -lse2));
+                });
             };
+            auto ds_of = [&](auto KB, auto E0, auto E1) __attribute__((always_inline)) {
+                constexpr int kb = decltype(KB)::value;
+                static_for<decltype(E0)::value, decltype(E1)::value>([&](auto R) __attribute__((always_inline)) {
+                    constexpr int r = decltype(R)::value;
+                    sb[2 * kb + (r >> 3)][r & 7] = (bf16)(s[kb][r] * dp[kb][r]);
+                });
+            };
+            using K0 = std::integral_constant<int, 0>;
+            using K1 = std::integral_constant<int, 1>;
             bf16x8 fr[PF + 1];
             static_for<0, PF>([&](auto F) __attribute__((always_inline)) { fr[decltype(F)::value] = fetch(F); });
             static_for<0, NC>([&](auto C) __attribute__((always_inline)) {
-                constexpr int c = decltype(C)::value;
+                constexpr int c = decltype(C)::value, ph = c / L, i = c % L;
                 if constexpr (c + PF < NC) fr[(c + PF) % (PF + 1)] = fetch(std::integral_constant<int, c + PF>{});
                 const bf16x8 fc = fr[c % (PF + 1)];
-                if constexpr (c < 2 * NSH) {
-                    constexpr int kb = c / NSH, i = c % NSH;
-                    if constexpr (i & 1)
-                        dp[kb] = mfma(fc, gf[i >> 1], dp[kb]);
+                if constexpr (ph < 4) {
+                    constexpr int kb = ph >> 1;
+                    if constexpr (ph & 1)
+                        dp[kb] = mfma(fc, gf[i], dp[kb]);
                     else
-                        s[kb] = mfma(fc, qf[i >> 1], s[kb]);
+                        s[kb] = mfma(fc, qf[i], s[kb]);
                 } else {
-                    constexpr int i = c - 2 * NSH, t = i / NDB, db = i % NDB;
+                    constexpr int t = 2 * (ph - 4) + i / NDB, db = i % NDB;
                     dq[db] = mfma(fc, sb[t], dq[db]);
                 }
-                if constexpr (c >= NSH && c < 2 * NSH) {
-                    constexpr int i = c - NSH;
-                    static_for<i * 16 / NSH, (i + 1) * 16 / NSH>([&](auto R) __attribute__((always_inline)) {
-                        valu(std::integral_constant<int, 0>{}, R);
-                    });
-                } else if constexpr (c >= 2 * NSH && c < 2 * NSH + NQH) {
-                    constexpr int i = c - 2 * NSH;
-                    static_for<i * 16 / NQH, (i + 1) * 16 / NQH>([&](auto R) __attribute__((always_inline)) {
-                        valu(std::integral_constant<int, 1>{}, R);
-                    });
+                // 8 elements over the L chunks of a phase: chunk i takes [8 i / L, 8 (i + 1) / L)
+                using A0 = std::integral_constant<int, 8 * i / L>;
+                using A1 = std::integral_constant<int, 8 * (i + 1) / L>;
+                using B0 = std::integral_constant<int, 8 + 8 * i / L>;
+                using B1 = std::integral_constant<int, 8 + 8 * (i + 1) / L>;
+                if constexpr (ph == 1) {
+                    p_of(K0{}, A0{}, A1{});
+                } else if constexpr (ph == 2) {
+                    p_of(K0{}, B0{}, B1{});
+                    ds_of(K0{}, A0{}, A1{});
+                } else if constexpr (ph == 3) {
+                    ds_of(K0{}, B0{}, B1{});
+                    p_of(K1{}, A0{}, A1{});
+                } else if constexpr (ph == 4) {
+                    p_of(K1{}, B0{}, B1{});
+                    ds_of(K1{}, A0{}, A1{});
+                } else if constexpr (ph == 5 && i < L / 2) {
+                    ds_of(K1{}, std::integral_constant<int, 8 + 16 * i / L>{}, std::integral_constant<int, 8 + 16 * (i + 1) / L>{});
                 }
                 __builtin_amdgcn_sched_barrier(0);
             });
