@@ -35,6 +35,10 @@ METRIC = "attention fwd/bwd TFLOP/s on 1 MI355X and % of bf16 MFMA peak"
 PEAK_BF16_TFLOPS = 2516.6   # 256 CUs x 2.4 GHz x 4096 dense bf16 FLOP/clk/CU
 PEAK_FP8_TFLOPS = 5033.2    # twice the bf16 rate (MI355X dense fp8: 5.0 PFLOP/s)
 PEAK_HBM_GBS = 8000.0
+# The pages' own figure for the fa3 workload: FlashAttention v3's forward at 3.538 ms on an H100
+# (FP16), i.e. 661.0 TFLOP/s in the same convention ("GPU Programming and Kernel Optimization",
+# item 61; "digest_existing.txt", answer q03_fa3).  Another machine: context, not a target.
+PAGES_FA3_TFLOPS = 661.0
 
 
 def fwd_flop(B, H, N, d, causal) -> float:
@@ -181,7 +185,8 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--workload", default="c5", choices=["c2", "c3", "c4", "c5", "dec", "c3f8", "c4f8", "c5g", "c5d256", "c5u"])
+    ap.add_argument("--workload", default="c5", choices=["c2", "c3", "c4", "c5", "dec", "c3f8", "c4f8", "c5g", "c5d256", "c5u",
+                                                        "fa3"])
     ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle work for the CPU baseline")
     ap.add_argument("--ramp-seconds", type=float, default=1.0,
                     help="untimed steps for this long before the warmup steps, so that the GPU clocks "
@@ -334,7 +339,7 @@ def main():
         "ms_per_step": round(ms_per_step, 4),
         "higher_is_better": True,
         "scaling": "weak",
-        "vs_baseline": None,
+        "vs_baseline": round(value / PAGES_FA3_TFLOPS, 3) if w.name == "fa3" else None,
         "dtype": "fp8_e4m3" if fp8 else "bf16",
         "data": "synthetic",
         "config": config,
@@ -345,6 +350,9 @@ def main():
         "kernel_ms_stats": kernel_stats,
         "roofline": roof,
     }
+    if w.name == "fa3":
+        out["baseline"] = {"value": PAGES_FA3_TFLOPS, "unit": "TFLOP/s", "source": "FlashAttention v3 forward, "
+                           "H100 SXM5, FP16, 3.538 ms (the pages' ablation table); another machine and precision"}
     if w.backward:
         bwd_ms = sum(kernel_ms[x] for x in bwd_kernels)
         out["bwd_tflops"] = round(2.5 * workload_fwd_flop(w) / (bwd_ms * 1e-3) / 1e12, 2)

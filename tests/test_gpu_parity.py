@@ -165,6 +165,15 @@ def test_workload_c4_forward_sampled():
     check_fwd_sampled(w, inp, o, lse, [], np.random.default_rng(40))
 
 
+def test_workload_fa3_forward_sampled():
+    """The informational FlashAttention v3 workload (B=4, N=8448 = 33 tiles of 256 rows, non-causal)."""
+    w = WORKLOADS["fa3"]
+    note("fa3 " + w.describe())
+    inp = workload_inputs(w)
+    o, lse = gpu_fwd(inp, w.causal, w.scale)
+    check_fwd_sampled(w, inp, o, lse, [], np.random.default_rng(50))
+
+
 def test_workload_c5_forward_backward():
     w = WORKLOADS["c5"]
     note("c5 " + w.describe())

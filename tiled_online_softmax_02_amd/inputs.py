@@ -92,6 +92,9 @@ WORKLOADS = {
     "c5g": Workload("c5g", 2, 16, 4096, 128, True, backward=True, Hk=4, note="grouped-query attention"),
     "c5d256": Workload("c5d256", 2, 16, 4096, 256, True, backward=True, note="head dimension 256"),
     "c5u": Workload("c5u", 2, 16, 2048, 128, True, backward=True, Nk=4096, note="unequal lengths"),
+    # informational: the forward workload of FlashAttention v3's own ablation table (B=4, N=8448,
+    # H=16, d=128, non-causal), whose times the pages report on an H100 in FP16
+    "fa3": Workload("fa3", 4, 16, 8448, 128, False, note="FlashAttention v3 ablation workload"),
 }
 
 
