@@ -2,8 +2,8 @@
 """Benchmark: attention forward + backward throughput on one MI355X.
 
 One step is one pass of the whole path over resident synthetic inputs: the fused
-forward kernel, then the launches attn_bwd makes (d <= 128: the dQ kernel, which also forms
-D = rowsum(dO o O), then the dK/dV kernel; wider heads: preprocess, dK/dV, dQ).  The default
+forward kernel, then the two launches attn_bwd makes (the dQ kernel, which also forms
+D = rowsum(dO o O), then the dK/dV kernel).  The default
 workload is the forward+backward causal case
 B=2, H=16, N=4096, d=128; ``--workload c2|c3|c4`` times forward-only workloads, ``dec`` the
 split-key forward of a decoding shape, and ``c3f8|c4f8`` the 8-bit forward on the shapes of
@@ -74,10 +74,10 @@ def workload_flop(w) -> float:
 def kernel_algorithmic_flop(kernel, w) -> float:
     """Algorithmic FLOP one launch performs, in units of one Nq x Nk x d product (the
     forward is two of them): fwd 2 (QK^T, PV); dkdv 4 (the recomputed S, dP, dV, dK);
-    dq 1 (dQ; its recomputed S and dP are counted in dkdv); preprocess 0; bwd 5 (the three
-    backward kernels of one attn_bwd_qk call, timed together)."""
+    dq 1 (dQ; its recomputed S and dP are counted in dkdv); bwd 5 (the two backward kernels of
+    one attn_bwd_qk call, timed together)."""
     unit = workload_fwd_flop(w) / 2.0
-    return unit * {"fwd": 2, "fwd_fp8": 2, "dkdv": 4, "dq": 1, "preprocess": 0, "bwd": 5}[kernel]
+    return unit * {"fwd": 2, "fwd_fp8": 2, "dkdv": 4, "dq": 1, "bwd": 5}[kernel]
 
 
 def stored_traffic(kernel: str, workload: str):
@@ -286,10 +286,9 @@ def main():
     torch.cuda.synchronize()
     del cal_src, cal_dst
 
-    # the backward kernels in attn_bwd's order: d <= 128 runs dQ first, forming D of its rows on
-    # the way (attn_bwd_dq_delta), then dK/dV; wider heads run the preprocess, dK/dV and dQ
-    fused_d = d <= 128
-    bwd_kernels = ["bwd"] if qk else (["dq", "dkdv"] if fused_d else ["preprocess", "dkdv", "dq"])
+    # the backward kernels in attn_bwd's order: dQ first, forming D of its rows on the way
+    # (attn_bwd_dq_delta), then dK/dV
+    bwd_kernels = ["bwd"] if qk else ["dq", "dkdv"]
     kernels = (["fwd_splitkv"] if split else ["fwd_fp8"] if fp8 else ["fwd"]) + (bwd_kernels if w.backward else [])
     ev = {kname: [] for kname in kernels}
 
@@ -327,23 +326,13 @@ def main():
             A.attn_bwd_qk(q, k, v, o, do, lse, dq, dk, dv, delta, B, H, Hk, N, Nk, d, causal, scale)
             if record:
                 e[2].record()
-        elif w.backward and fused_d:
+        elif w.backward:
             A.attn_bwd_dq_delta(q, k, v, o, do, lse, delta, dq, B, H, N, d, causal, scale)
             if record:
                 e[2].record()
             A.attn_bwd_dkdv(q, k, v, do, lse, delta, dk, dv, B, H, N, d, causal, scale)
             if record:
                 e[3].record()
-        elif w.backward:
-            A.attn_bwd_preprocess(o, do, delta, B, H, N, d)
-            if record:
-                e[2].record()
-            A.attn_bwd_dkdv(q, k, v, do, lse, delta, dk, dv, B, H, N, d, causal, scale)
-            if record:
-                e[3].record()
-            A.attn_bwd_dq(q, k, v, do, lse, delta, dq, B, H, N, d, causal, scale)
-            if record:
-                e[4].record()
         if record:
             for i, kname in enumerate(kernels):
                 ev[kname].append((e[i], e[i + 1]))

@@ -131,13 +131,12 @@ int attn_fwd_fp8(const void *q, const void *k, const void *v,
                  void *o, float *lse, int B, int H, int Hk, int Nq, int Nk, int d, int causal,
                  float scale, void *stream);
 
-/* Backward pass: for d = 64 and 128 enqueues attn_bwd_dq_delta then
- * attn_bwd_dkdv (two launches); for d = 192 and 256 attn_bwd_preprocess,
- * attn_bwd_dkdv and attn_bwd_dq, in that order on `stream`.  Reads q, k, v, o,
- * dout and the lse written by attn_fwd with the same q, k, v, causal and scale;
- * writes dq, dk, dv [B,H,N,d] (bf16) and delta [B,H,N] (fp32), a caller-owned
- * workspace that holds D on return.  Both orders give bitwise the same
- * results. */
+/* Backward pass: enqueues attn_bwd_dq_delta then attn_bwd_dkdv (two kernel
+ * launches) on `stream`; the results are bitwise those of attn_bwd_preprocess,
+ * attn_bwd_dkdv and attn_bwd_dq run in that order.  Reads q, k, v, o, dout and
+ * the lse written by attn_fwd with the same q, k, v, causal and scale; writes
+ * dq, dk, dv [B,H,N,d] (bf16) and delta [B,H,N] (fp32), a caller-owned
+ * workspace that holds D on return. */
 int attn_bwd(const void *q, const void *k, const void *v, const void *o, const void *dout,
              const float *lse, void *dq, void *dk, void *dv, float *delta,
              int B, int H, int N, int d, int causal, float scale, void *stream);
@@ -173,14 +172,13 @@ int attn_bwd_dq(const void *q, const void *k, const void *v, const void *dout,
                 const float *lse, const float *delta, void *dq,
                 int B, int H, int N, int d, int causal, float scale, void *stream);
 
-/* Backward steps 1 and 3 together: writes delta exactly as
- * attn_bwd_preprocess does (bitwise) and dq exactly as attn_bwd_dq does with
- * that delta.  For d = 64 and 128 this is one kernel launch: the dQ kernel
- * forms D of its own rows from o and dout before its loop, summing in the
- * preprocess kernel's order; for d = 192 and 256 it enqueues the two steps.
- * attn_bwd_dkdv, which needs every row's D, is enqueued after it.  Same
- * arguments and errors as attn_bwd_dq, plus o (an input) and delta (an
- * output, no longer an input). */
+/* Backward steps 1 and 3 together, in one kernel launch: writes delta
+ * exactly as attn_bwd_preprocess does (bitwise) and dq exactly as attn_bwd_dq
+ * does with that delta.  The dQ kernel forms D of its own rows from o and dout
+ * before its loop, summing in the preprocess kernel's order.  attn_bwd_dkdv,
+ * which needs every row's D, is enqueued after it.  Same arguments and errors
+ * as attn_bwd_dq, plus o (an input) and delta (an output, no longer an
+ * input). */
 int attn_bwd_dq_delta(const void *q, const void *k, const void *v, const void *o,
                       const void *dout, const float *lse, float *delta, void *dq,
                       int B, int H, int N, int d, int causal, float scale, void *stream);

@@ -257,10 +257,11 @@ def test_step_entry_points_equal_the_combined_backward():
     assert np.abs(f64(delta) - ref).max() <= 1e-4 * max(1.0, np.abs(ref).max())
 
 
-@pytest.mark.parametrize("N,d,causal", [(300, 128, True), (257, 64, False), (128, 128, False), (200, 256, True)])
+@pytest.mark.parametrize("N,d,causal", [(300, 128, True), (257, 64, False), (128, 128, False), (200, 256, True),
+                                          (130, 192, False)])
 def test_dq_delta_equals_preprocess_then_dq(N, d, causal):
-    """attn_bwd_dq_delta (d <= 128: one dQ kernel that forms D on the way) writes bitwise the
-    delta of attn_bwd_preprocess and the dq of attn_bwd_dq."""
+    """attn_bwd_dq_delta (one dQ kernel that forms D on the way) writes bitwise the delta of
+    attn_bwd_preprocess and the dq of attn_bwd_dq."""
     note("dq_delta vs preprocess+dq N=%d d=%d causal=%d" % (N, d, causal))
     B, H = 1, 3
     scale = softmax_scale(d)

@@ -184,7 +184,7 @@ int bwd_impl(const void *q, const void *k, const void *v, const void *o, const v
     RETURN_IF(check_alias(in, 6, out, 4));
     attn::BwdArgs a{q, k, v, o, dout, lse, dq, dk, dv, delta, B, H, Hk, Nq, Nk, d, causal, scale, stream};
     if (attn::bwd_dq_fuses_delta(d)) {
-        // d <= 128: the dQ kernel forms D on the way (no preprocess launch), then dK/dV reads it
+        // the dQ kernel forms D on the way (no preprocess launch), then dK/dV reads it
         RETURN_IF(hip_status(attn::launch_bwd_dq_delta(a)));
         return hip_status(attn::launch_bwd_dkdv(a));
     }

@@ -807,17 +807,17 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv3_kernel(
 constexpr int kQBM = 128;  // queries per workgroup (32 per wave)
 constexpr int kQBN = 64;   // keys per streamed block
 
-// FUSE_D (d <= 128): the kernel also forms D = rowsum(dO o O) of its own rows from O and writes
-// it to Dl for the dK/dV kernel that runs after it, in place of the preprocess kernel.  The sum
-// takes the preprocess kernel's order (8-element chunks by fused multiply-add, then the chunks
-// pairwise at distances 8, 4, 2, 1), so D is bitwise the same either way.
+// FUSE_D: the kernel also forms D = rowsum(dO o O) of its own rows from O and writes it to Dl for
+// the dK/dV kernel that runs after it, in place of the preprocess kernel.  The sum takes the
+// preprocess kernel's order (8-element chunks by fused multiply-add, then the chunks pairwise at
+// halving distances over a power-of-two count of chunks, the missing ones zero), so D is bitwise
+// the same either way.
 template <int D, bool CAUSAL, bool FUSE_D = false>
 __global__ __launch_bounds__(kThreads, D >= 192 ? 1 : 2) void bwd_dq_kernel(
     const bf16 *__restrict__ Q, const bf16 *__restrict__ K, const bf16 *__restrict__ V, const bf16 *__restrict__ dO,
     const float *__restrict__ LSE, float *__restrict__ Dl, bf16 *__restrict__ dQ, int Nq, int Nk, int H, int G,
     int n_qtiles, float scale, float c_log2, const bf16 *__restrict__ O)
 {
-    static_assert(!FUSE_D || D <= 128, "the fused row sum follows the preprocess order for d <= 128");
     constexpr int NKS = D / 16;
     constexpr int NDB = D / 32;
     constexpr int TILE = kQBN * D * 2;
@@ -852,8 +852,12 @@ __global__ __launch_bounds__(kThreads, D >= 192 ? 1 : 2) void bwd_dq_kernel(
     bf16x8 qf[NKS], gf[NKS];
     float dfused = 0.f;
     {
-        // lane (c32, h) holds 8-element chunks 2 ks + h of its row, ks = 0 .. NKS-1
-        float a[NKS];
+        // lane (c32, h) holds 8-element chunks 2 ks + h of its row, ks = 0 .. NKS-1; the preprocess
+        // kernel sums 2 NKSP chunks, the ones past the row zero (d = 192: 24 of 32)
+        constexpr int NKSP = NKS <= 4 ? 4 : NKS <= 8 ? 8 : 16;
+        float a[NKSP];
+#pragma unroll
+        for (int ks = NKS; ks < NKSP; ++ks) a[ks] = 0.f;
         bf16x8 of[NKS];
         if constexpr (FUSE_D) {
             const __amdgpu_buffer_rsrc_t ro = make_rsrc(O + hoff, (uint32_t)Nq * D * 2);
@@ -877,7 +881,7 @@ __global__ __launch_bounds__(kThreads, D >= 192 ? 1 : 2) void bwd_dq_kernel(
             // chunks j and j + CPR/2 (ks and ks + NKS/2) first, then halving distances; the last
             // step pairs the even chunks of lane half 0 with the odd ones of half 1
 #pragma unroll
-            for (int n = NKS / 2; n >= 1; n >>= 1) {
+            for (int n = NKSP / 2; n >= 1; n >>= 1) {
 #pragma unroll
                 for (int ks = 0; ks < n; ++ks) a[ks] = a[ks] + a[ks + n];
             }
@@ -1249,13 +1253,15 @@ hipError_t launch_bwd_dkdv(const BwdArgs &a)
     }
 }
 
-bool bwd_dq_fuses_delta(int d) { return d <= 128; }
+bool bwd_dq_fuses_delta(int d) { return d == 64 || d == 128 || d == 192 || d == 256; }
 
 hipError_t launch_bwd_dq_delta(const BwdArgs &a)
 {
     switch (a.d) {
     case 64: return a.causal ? launch_dq_t<64, true, true>(a) : launch_dq_t<64, false, true>(a);
     case 128: return a.causal ? launch_dq_t<128, true, true>(a) : launch_dq_t<128, false, true>(a);
+    case 192: return a.causal ? launch_dq_t<192, true, true>(a) : launch_dq_t<192, false, true>(a);
+    case 256: return a.causal ? launch_dq_t<256, true, true>(a) : launch_dq_t<256, false, true>(a);
     default: return hipErrorInvalidValue;
     }
 }

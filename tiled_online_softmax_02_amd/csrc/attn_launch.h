@@ -43,8 +43,8 @@ hipError_t launch_fwd_split(const FwdArgs &a, int n_splits, void *workspace);
 hipError_t launch_bwd_preprocess(const BwdArgs &a);
 hipError_t launch_bwd_dkdv(const BwdArgs &a);
 hipError_t launch_bwd_dq(const BwdArgs &a);
-// d <= 128: the dQ kernel that also forms D of its rows from O and dO and writes it to a.delta
-// (bitwise what the preprocess kernel writes); launched before the dK/dV kernel, which reads D.
+// The dQ kernel that also forms D of its rows from O and dO and writes it to a.delta (bitwise
+// what the preprocess kernel writes); launched before the dK/dV kernel, which reads D.
 bool bwd_dq_fuses_delta(int d);
 hipError_t launch_bwd_dq_delta(const BwdArgs &a);
 
