@@ -147,6 +147,7 @@ def fwd_qk(lib, q=P[0], k=P[1], v=P[2], o=P[3], lse=P[4], B=1, H=1, Hk=None, Nq=
     (dict(Nq=-1), A.ATTN_ERR_BAD_SHAPE),
     (dict(Nk=-1), A.ATTN_ERR_BAD_SHAPE),
     (dict(Nk=1 << 24, d=128), A.ATTN_ERR_BAD_SHAPE),    # (Nk+256)*d*2 > 2^32
+    (dict(Nk=16776960, d=128), A.ATTN_ERR_BAD_SHAPE),   # one row past the longest accepted key length
     (dict(Nq=1 << 24, d=128), A.ATTN_ERR_BAD_SHAPE),
     (dict(d=96), A.ATTN_ERR_UNSUPPORTED_D),
     (dict(causal=3), A.ATTN_ERR_BAD_ARG),
