@@ -92,3 +92,46 @@ def test_split_key_forward_at_the_key_length_limit(kv):
     torch.cuda.synchronize()
     check(o, lse, nq, True, prefix, "split-key, %d pieces" % ns)
 
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_backward_at_the_key_length_limit(kv, causal):
+    """Backward at the same length, by the same closed form: with Q = 0 and K = 0, dQ and dK are
+    exactly 0 (every product has a zero operand), and with dO = 1 each key's dV is the sum of the
+    weights the query rows give it, sum over the rows i that see key j of 1 / n_i (the weights are
+    rounded to bf16 for the dV product, hence a relative bound of 1e-2).  Every one of the
+    16776959 rows of dK and dV is checked, so a row written at a wrong offset, or not at all,
+    fails."""
+    k, v, prefix = kv
+    nq = 64
+    scale = softmax_scale(D)
+    note("attn_bwd_qk B=1 H=1 Nq=%d Nk=%d d=%d causal=%d, Q = K = 0, dO = 1" % (nq, NK_MAX, D, causal))
+    q = torch.zeros((1, 1, nq, D), dtype=torch.bfloat16, device=DEV)
+    do = torch.ones_like(q)
+    o = torch.empty_like(q)
+    lse = torch.empty((1, 1, nq), dtype=torch.float32, device=DEV)
+    A.attn_fwd_qk(q, k, v, o, lse, 1, 1, 1, nq, NK_MAX, D, causal, scale)
+    dq = torch.full_like(q, float("nan"))
+    dk = torch.full_like(k, float("nan"))
+    dv = torch.full_like(v, float("nan"))
+    delta = torch.empty_like(lse)
+    A.attn_bwd_qk(q, k, v, o, do, lse, dq, dk, dv, delta, 1, 1, 1, nq, NK_MAX, D, causal, scale)
+    torch.cuda.synchronize()
+    # expected dV row j: sum over the query rows that see key j of 1 / n_i
+    rows = np.arange(nq)
+    n = (rows + NK_MAX - nq + 1) if causal else np.full(nq, NK_MAX)
+    w = 1.0 / n.astype(np.float64)
+    if causal:
+        # key j is seen by the rows i >= j - (NK_MAX - nq): a suffix of the rows
+        first_row = np.clip(np.arange(NK_MAX) - (NK_MAX - nq), 0, nq)
+        suffix = np.concatenate([np.cumsum(w[::-1])[::-1], [0.0]])
+        dv_ref = suffix[first_row]
+    else:
+        dv_ref = np.full(NK_MAX, w.sum())
+    dv_ref_t = torch.from_numpy(dv_ref).to(DEV)
+    assert bool(torch.all(dq == 0)) and bool(torch.all(dk == 0))
+    # every column of a row is held to the same value: compare the row's extremes
+    hi, lo = dv[0, 0].amax(dim=-1).double(), dv[0, 0].amin(dim=-1).double()
+    rel = max(((hi - dv_ref_t).abs() / dv_ref_t).max().item(), ((lo - dv_ref_t).abs() / dv_ref_t).max().item())
+    note("  causal=%d: dQ, dK all zero; max rel |d dV| = %.3e (dV ~ %.3e)" % (causal, rel, dv_ref[0]))
+    assert rel <= 1e-2, rel
