@@ -224,7 +224,8 @@ __device__ __forceinline__ void load_tile_lds_part(__amdgpu_buffer_rsrc_t r, lds
     const int pchunk = 64 * n + lane;           // physical chunk of this lane
     const int row = pchunk / CPR;
     const int chunk = (pchunk - row * CPR) ^ lds_swz<D>(row);
-    buffer_load_lds16(r, tile + 1024 * n, (uint32_t)((row0 + row) * RB + 16 * chunk));
+    // byte offset in unsigned arithmetic: rows times row bytes reach 2^32 - 1 at the longest lengths
+    buffer_load_lds16(r, tile + 1024 * n, (uint32_t)(row0 + row) * (uint32_t)RB + 16u * (uint32_t)chunk);
 }
 
 // Load rows [row0, row0 + ROWS) of a row-major [*, D] bf16 matrix into a swizzled
