@@ -74,10 +74,11 @@ def workload_flop(w) -> float:
 def kernel_algorithmic_flop(kernel, w) -> float:
     """Algorithmic FLOP one launch performs, in units of one Nq x Nk x d product (the
     forward is two of them): fwd 2 (QK^T, PV); dkdv 4 (the recomputed S, dP, dV, dK);
-    dq 1 (dQ; its recomputed S and dP are counted in dkdv); bwd 5 (the two backward kernels of
-    one attn_bwd_qk call, timed together)."""
+    dq 1 (dQ; its recomputed S and dP are counted in dkdv); preprocess 0 (the step entry point
+    attn_bwd_preprocess); bwd 5 (the two backward kernels of one attn_bwd_qk call, timed
+    together)."""
     unit = workload_fwd_flop(w) / 2.0
-    return unit * {"fwd": 2, "fwd_fp8": 2, "dkdv": 4, "dq": 1, "bwd": 5}[kernel]
+    return unit * {"fwd": 2, "fwd_fp8": 2, "dkdv": 4, "dq": 1, "preprocess": 0, "bwd": 5}[kernel]
 
 
 def stored_traffic(kernel: str, workload: str):
