@@ -804,7 +804,11 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv3_kernel(
 
 // ------------------------------------------------------------ dQ
 
-constexpr int kQBM = 128;  // queries per workgroup (32 per wave)
+// Waves per dQ workgroup (32 queries each): 8 for d <= 128, two per SIMD sharing every K/V block
+// loaded into LDS; 4 for d = 192, 256, one per SIMD (their registers exceed 256).
+template <int D>
+constexpr int dq_waves() { return D <= 128 ? 8 : 4; }
+constexpr int kQBM = 128;  // the smallest query block of a dQ workgroup (bounds the grid size)
 constexpr int kQBN = 64;   // keys per streamed block
 
 // FUSE_D: the kernel also forms D = rowsum(dO o O) of its own rows from O and writes it to Dl for
@@ -813,7 +817,7 @@ constexpr int kQBN = 64;   // keys per streamed block
 // halving distances over a power-of-two count of chunks, the missing ones zero), so D is bitwise
 // the same either way.
 template <int D, bool CAUSAL, bool FUSE_D = false>
-__global__ __launch_bounds__(kThreads, D >= 192 ? 1 : 2) void bwd_dq_kernel(
+__global__ __launch_bounds__(64 * dq_waves<D>(), D >= 192 ? 1 : 8 / dq_waves<D>()) void bwd_dq_kernel(
     const bf16 *__restrict__ Q, const bf16 *__restrict__ K, const bf16 *__restrict__ V, const bf16 *__restrict__ dO,
     const float *__restrict__ LSE, float *__restrict__ Dl, bf16 *__restrict__ dQ, int Nq, int Nk, int H, int G,
     int n_qtiles, float scale, float c_log2, const bf16 *__restrict__ O)
@@ -841,7 +845,9 @@ __global__ __launch_bounds__(kThreads, D >= 192 ? 1 : 2) void bwd_dq_kernel(
     // Causal mask with bottom-right alignment: query i sees keys j <= i + off.
     const int off = Nk - Nq;
 
-    const int q0 = qtile * kQBM;
+    constexpr int NW = dq_waves<D>();
+    constexpr int BMQ = 32 * NW;  // queries per workgroup
+    const int q0 = qtile * BMQ;
     const int qw0 = q0 + 32 * w;  // wave-uniform
     const int qrow = qw0 + c32;
     const bool row_ok = qrow < Nq;
@@ -903,7 +909,7 @@ __global__ __launch_bounds__(kThreads, D >= 192 ? 1 : 2) void bwd_dq_kernel(
 #pragma unroll
     for (int i = 0; i < NDB; ++i) dq[i] = zero16();
 
-    const int kv_end = CAUSAL ? min(Nk, max(0, q0 + kQBM + off)) : Nk;
+    const int kv_end = CAUSAL ? min(Nk, max(0, q0 + BMQ + off)) : Nk;
     const int nt = (kv_end + kQBN - 1) / kQBN;
 
     auto kst_l = [&](auto par) __attribute__((always_inline)) { return (lds_char *)(decltype(par)::value ? k1_raw : k0_raw); };
@@ -913,7 +919,7 @@ __global__ __launch_bounds__(kThreads, D >= 192 ? 1 : 2) void bwd_dq_kernel(
     // instruction's offset field, and every direct load one register plus a buffer base moved by
     // scalar arithmetic.
     constexpr bool kFixedOffsets = D <= 128;
-    constexpr int kLoadNI = kQBN * (D / 8) / 64 / 4;  // direct loads per wave and tile
+    constexpr int kLoadNI = kQBN * (D / 8) / 64 / NW;  // direct loads per wave and tile
     int ko[NKS], vo[NDB][2], go[kLoadNI];
     if constexpr (kFixedOffsets) {
 #pragma unroll
@@ -951,8 +957,8 @@ __global__ __launch_bounds__(kThreads, D >= 192 ? 1 : 2) void bwd_dq_kernel(
 #pragma unroll
             for (int i = 0; i < kLoadNI; ++i) buffer_load_lds16(rvj, vst_l(par) + 1024 * (w * kLoadNI + i), (uint32_t)go[i]);
         } else {
-            load_tile_lds<D, 4>(rk, kst_l(par), j * kQBN, w, lane);
-            load_tile_lds<D, 4>(rv, vst_l(par), j * kQBN, w, lane);
+            load_tile_lds<D, NW>(rk, kst_l(par), j * kQBN, w, lane);
+            load_tile_lds<D, NW>(rv, vst_l(par), j * kQBN, w, lane);
         }
     };
 
@@ -1221,10 +1227,10 @@ hipError_t launch_dkdv_t(const BwdArgs &a)
 template <int D, bool CAUSAL, bool FUSE_D = false>
 hipError_t launch_dq_t(const BwdArgs &a)
 {
-    const int n_qtiles = (a.Nq + kQBM - 1) / kQBM;
+    const int n_qtiles = (a.Nq + 32 * dq_waves<D>() - 1) / (32 * dq_waves<D>());
     const long long G = (long long)a.B * a.H * n_qtiles;
     if (G == 0) return hipSuccess;
-    hipLaunchKernelGGL((bwd_dq_kernel<D, CAUSAL, FUSE_D>), dim3((unsigned)G), dim3(kThreads), 0, (hipStream_t)a.stream,
+    hipLaunchKernelGGL((bwd_dq_kernel<D, CAUSAL, FUSE_D>), dim3((unsigned)G), dim3(64 * dq_waves<D>()), 0, (hipStream_t)a.stream,
                        (const bf16 *)a.q, (const bf16 *)a.k, (const bf16 *)a.v, (const bf16 *)a.dout, a.lse,
                        a.delta, (bf16 *)a.dq, a.Nq, a.Nk, a.H, a.H / a.Hk, n_qtiles, a.scale, a.scale * kLog2e,
                        (const bf16 *)a.o);
