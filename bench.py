@@ -112,8 +112,11 @@ class HipTimer:
 
     def __init__(self):
         import ctypes
+        import torch
         self.ct = ctypes
-        self.hip = ctypes.CDLL("libamdhip64.so.7")
+        # the runtime torch loaded (dlopen of the same file returns the loaded library)
+        bundled = os.path.join(os.path.dirname(torch.__file__), "lib", "libamdhip64.so")
+        self.hip = ctypes.CDLL(bundled if os.path.exists(bundled) else "libamdhip64.so.7")
         P, U = ctypes.c_void_p, ctypes.c_uint
         self.hip.hipEventCreateWithFlags.argtypes = [ctypes.POINTER(P), U]
         self.hip.hipEventRecord.argtypes = [P, P]
