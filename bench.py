@@ -266,7 +266,7 @@ def main():
         q, k, v = (inp[n].to(dev) for n in ("q", "k", "v"))
     B, H, N, d = q.shape
     Hk, Nk = k.shape[1], k.shape[2]
-    # grouped heads or unequal lengths: the _qk entry points (the backward's three kernels are
+    # grouped heads or unequal lengths: the _qk entry points (the backward's two kernels are
     # then one call and are timed together)
     qk = Hk != H or Nk != N
     split = w.name == "dec"  # decoding: the split-key forward (partial pieces, then their merge)

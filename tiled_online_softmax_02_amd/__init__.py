@@ -2,7 +2,7 @@
 
 The functions named like the C entry points (``attn_fwd``, ``attn_fwd_qk``,
 ``attn_fwd_splitkv`` and its two size helpers, ``attn_fwd_fp8``, ``attn_bwd``, ``attn_bwd_qk``,
-``attn_bwd_preprocess``, ``attn_bwd_dkdv``, ``attn_bwd_dq``,
+``attn_bwd_preprocess``, ``attn_bwd_dkdv``, ``attn_bwd_dq``, ``attn_bwd_dq_delta``,
 ``attn_status_string``) only marshal arguments: tensors become device
 pointers, ``stream=None`` becomes the current PyTorch stream of the tensors'
 device, and a nonzero status becomes :class:`AttnError`.  Every step of the
