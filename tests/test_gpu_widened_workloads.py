@@ -1,0 +1,96 @@
+"""The widened bench workloads at their full sizes, in the launch configuration bench.py times.
+
+c5g (grouped K/V heads, Hk = 4 under H = 16), c5u (2048 queries against 4096 keys, bottom-right
+causal alignment) and c5d256 (head dimension 256), all forward + backward at B = 2, N = 4096:
+sampled forward rows of every head against the fp64 oracle, one whole K/V head's gradients against
+the oracle's backward (for grouped heads: the sum over the query heads that share the K/V head,
+by the chain rule; each element within 2e-2 plus the bf16 rounding of the output, 2^-8 |x|), and
+on every head the invariants sum_j dK_j = 0 and sum_j dV_j = the sum of dO over the query rows of
+the heads that read it (each row of P sums to 1; "digest_existing.txt", answer
+q02_flashattention, section 1).
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import tiled_online_softmax_02_amd as A
+from tiled_online_softmax_02_amd.inputs import WORKLOADS, workload_inputs
+
+pytestmark = pytest.mark.gpu
+
+O_TOL = 2e-2
+LSE_RTOL = 1e-3
+G_TOL = 2e-2
+DEV = "cuda:0"
+
+
+def note(msg):
+    print("[widened] " + msg, flush=True)
+
+
+def f64(t):
+    return t.detach().to("cpu", torch.float64).numpy()
+
+
+def sample_rows(n, rng):
+    rows = {0, 1, 31, 32, 63, 64, 127, 128, n // 2, n - 65, n - 64, n - 2, n - 1}
+    rows |= set(rng.integers(0, n, size=12).tolist())
+    return np.array(sorted(r for r in rows if 0 <= r < n))
+
+
+@pytest.mark.parametrize("wname", ["c5g", "c5u", "c5d256"])
+def test_widened_workload_full_size(wname):
+    w = WORKLOADS[wname]
+    note("%s %s" % (wname, w.describe()))
+    inp = workload_inputs(w)
+    B, H, Hk, nq, nk, d = w.B, w.H, w.hk, w.nq, w.nk, w.d
+    G = H // Hk
+    q, k, v, do = (inp[n].to(DEV) for n in ("q", "k", "v", "do"))
+    o, lse = A.fwd(q, k, v, causal=w.causal, scale=w.scale)
+    dq, dk, dv = A.bwd(q, k, v, o, do, lse, causal=w.causal, scale=w.scale)
+    torch.cuda.synchronize()
+    o64, lse64 = f64(o), f64(lse)
+    q64, k64, v64, do64 = (f64(inp[n]) for n in ("q", "k", "v", "do"))
+
+    # forward: sampled rows of every query head
+    rng = np.random.default_rng(70)
+    worst_o, worst_l = 0.0, 0.0
+    for b in range(B):
+        for h in range(H):
+            rows = sample_rows(nq, rng)
+            o_ref, lse_ref = oracle.attn_fwd_rows(q64[b, h, rows], rows, k64[b, h // G], v64[b, h // G], nq,
+                                                  w.causal, w.scale)
+            worst_o = max(worst_o, np.abs(o64[b, h, rows] - o_ref).max())
+            worst_l = max(worst_l, (np.abs(lse64[b, h, rows] - lse_ref) / np.abs(lse_ref)).max())
+    note("  forward sampled rows: max|dO|=%.3e  max rel lse=%.3e" % (worst_o, worst_l))
+    assert np.all(np.isfinite(o64)) and worst_o <= O_TOL and worst_l <= LSE_RTOL
+
+    # backward: the last K/V head of the last batch entry, whole, against the oracle
+    b, hk = B - 1, Hk - 1
+    heads = list(range(hk * G, (hk + 1) * G))
+    kk = np.repeat(k64[b:b + 1, hk:hk + 1], G, axis=1)
+    vv = np.repeat(v64[b:b + 1, hk:hk + 1], G, axis=1)
+    note("  backward: oracle on K/V head (%d,%d), query heads %s" % (b, hk, heads))
+    rdq, rdk, rdv, _ = oracle.attn_bwd_matmul(q64[b:b + 1, heads], kk, vv, do64[b:b + 1, heads], w.causal, w.scale)
+    # bound per element: the 2e-2 budget plus the bf16 rounding of the output itself (at most
+    # 2^-8 |x|); a K/V head shared by G query heads sums G contributions, its |dK|, |dV| grow by
+    # about sqrt(G), and at |x| >= 8 that rounding alone passes 2e-2
+    for name, got, ref in (("Q", f64(dq)[b, heads], rdq[0]), ("K", f64(dk)[b, hk], rdk[0].sum(axis=0)),
+                           ("V", f64(dv)[b, hk], rdv[0].sum(axis=0))):
+        err = np.abs(got - ref)
+        excess = (err - (G_TOL + 2.0 ** -8 * np.abs(ref))).max()
+        note("  backward head d%s: max err %.3e, max |d%s| %.2f, worst margin to the bound %.3e"
+             % (name, err.max(), name, np.abs(ref).max(), -excess))
+        assert np.all(np.isfinite(got)) and excess <= 0.0, (name, excess)
+
+    # invariants on every K/V head
+    dk64, dv64 = f64(dk), f64(dv)
+    sk = np.abs(dk64.sum(axis=2))
+    dO_group = do64.reshape(B, Hk, G, nq, d).sum(axis=(2, 3))
+    sv = np.abs(dv64.sum(axis=2) - dO_group)
+    tk = 16 * np.sqrt((dk64 ** 2).sum(axis=2)) * 2.0 ** -9 + 1e-2
+    tv = 16 * np.sqrt((dv64 ** 2).sum(axis=2)) * 2.0 ** -9 + 1e-2
+    note("  invariants: max|sum dK|=%.3e (tol >= %.3e)  max|sum dV - sum dO|=%.3e (tol >= %.3e)"
+         % (sk.max(), tk.min(), sv.max(), tv.min()))
+    assert np.all(sk <= tk) and np.all(sv <= tv)
