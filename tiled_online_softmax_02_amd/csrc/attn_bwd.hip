@@ -71,6 +71,7 @@ constexpr bool kv_dsplit() { return D >= 192; }
 template <int D>
 constexpr int kv_bn() { return kv_dsplit<D>() ? 64 : 128; }
 constexpr int kKvBM = 64;   // queries per streamed block
+constexpr int kPersistentWGs = 256;  // the CUs of one MI355X: one resident dK/dV workgroup each
 
 template <int D, bool CAUSAL>
 __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(
@@ -302,11 +303,16 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(
 // within a step the two run independently (one barrier per step).  Query-block tiles live in
 // three LDS stages (loading, P wave, dS wave), P in two.  P crosses in bf16, the precision
 // the dV product uses anyway.
+struct Dkdv2Args {
+    const bf16 *Q, *K, *V, *dO;
+    const float *LSE, *Dl;
+    bf16 *dK, *dV;
+    int Nq, Nk, H, G, n_ktiles, n_items;
+    float scale, c_log2;
+};
+
 template <int D, bool CAUSAL>
-__global__ __launch_bounds__(512, 1) void bwd_dkdv2_kernel(
-    const bf16 *__restrict__ Q, const bf16 *__restrict__ K, const bf16 *__restrict__ V, const bf16 *__restrict__ dO,
-    const float *__restrict__ LSE, const float *__restrict__ Dl, bf16 *__restrict__ dK, bf16 *__restrict__ dV, int Nq,
-    int Nk, int H, int G, int n_ktiles, float scale, float c_log2)
+__global__ __launch_bounds__(512, 1) void bwd_dkdv2_kernel(const Dkdv2Args args)
 {
     static_assert(D <= 128, "paired-wave dK/dV kernel: d <= 128");
     constexpr int NKS = D / 16;
@@ -319,255 +325,275 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv2_kernel(
     __shared__ __attribute__((aligned(16))) float s0_raw[2 * kKvBM], s1_raw[2 * kKvBM], s2_raw[2 * kKvBM];  // lse, D
     __shared__ __attribute__((aligned(16))) char p0_raw[PBUF], p1_raw[PBUF];
 
-    int head, ktile;
-    work_item(blockIdx.x, n_ktiles, head, ktile);
-    const int Hk = H / G;
-    const int qh0 = (head / Hk) * H + (head % Hk) * G;
+    // Persistent when the grid is smaller than the item count: each workgroup takes items in
+    // rounds (persistent_item), and the next item's loads start while the last one's stores drain.
+    // Every step ends with a barrier and the epilogue reads no LDS, so a new item may refill
+    // stage 0 at once.
+    // The arguments are read again from the kernel-argument segment in each round (behind an
+    // empty asm, so the loads stay in the loop): held across the rounds they would add two dozen
+    // scalar registers to a loop body that already spills scalars to vector lanes.
+    for (int r = 0;; ++r) {
+        const __attribute__((address_space(4))) Dkdv2Args *ap =
+            (const __attribute__((address_space(4))) Dkdv2Args *)__builtin_amdgcn_kernarg_segment_ptr();
+        asm volatile("" : "+s"(ap));
+        const bf16 *__restrict__ Q = ap->Q, *__restrict__ K = ap->K, *__restrict__ V = ap->V, *__restrict__ dO = ap->dO;
+        const float *__restrict__ LSE = ap->LSE, *__restrict__ Dl = ap->Dl;
+        bf16 *__restrict__ dK = ap->dK, *__restrict__ dV = ap->dV;
+        const int Nq = ap->Nq, Nk = ap->Nk, H = ap->H, G = ap->G, n_ktiles = ap->n_ktiles, n_items = ap->n_items;
+        const float scale = ap->scale, c_log2 = ap->c_log2;
+        const int item = persistent_item(r, (int)blockIdx.x, (int)gridDim.x);
+        if (item >= n_items) break;  // workgroup-uniform; later rounds hold only larger items
+        int head, ktile;
+        work_item_of(item, n_items, n_ktiles, head, ktile);
+        const int Hk = H / G;
+        const int qh0 = (head / Hk) * H + (head % Hk) * G;
 
-    const int tid = threadIdx.x;
-    const int lane = tid & 63, h = lane >> 5, c32 = lane & 31;
-    const int w = wave_uniform(tid >> 6);
-    const int pair = w & 3;
-    const bool pwave = w < 4;  // wave-uniform role
-    const size_t hoff = (size_t)head * (size_t)Nk * D;
-    __amdgpu_buffer_rsrc_t rq, rg, rl, rd;
-    auto bind_query_head = [&](int qh) __attribute__((always_inline)) {
-        const size_t hoff_q = (size_t)qh * (size_t)Nq * D;
-        rq = make_rsrc(Q + hoff_q, (uint32_t)Nq * D * 2);
-        rg = make_rsrc(dO + hoff_q, (uint32_t)Nq * D * 2);
-        rl = make_rsrc(LSE + (size_t)qh * Nq, (uint32_t)Nq * 4);
-        rd = make_rsrc(Dl + (size_t)qh * Nq, (uint32_t)Nq * 4);
-    };
-    const int off = Nk - Nq;
-    const int k0 = ktile * kBN;
-    const int kw0 = k0 + 32 * pair;
-    const int key = kw0 + c32;
+        int tid = threadIdx.x;
+        asm volatile("" : "+v"(tid));  // lane-derived values are formed per round, not held across
+        const int lane = tid & 63, h = lane >> 5, c32 = lane & 31;
+        const int w = wave_uniform(tid >> 6);
+        const int pair = w & 3;
+        const bool pwave = w < 4;  // wave-uniform role
+        const size_t hoff = (size_t)head * (size_t)Nk * D;
+        __amdgpu_buffer_rsrc_t rq, rg, rl, rd;
+        auto bind_query_head = [&](int qh) __attribute__((always_inline)) {
+            const size_t hoff_q = (size_t)qh * (size_t)Nq * D;
+            rq = make_rsrc(Q + hoff_q, (uint32_t)Nq * D * 2);
+            rg = make_rsrc(dO + hoff_q, (uint32_t)Nq * D * 2);
+            rl = make_rsrc(LSE + (size_t)qh * Nq, (uint32_t)Nq * 4);
+            rd = make_rsrc(Dl + (size_t)qh * Nq, (uint32_t)Nq * 4);
+        };
+        const int off = Nk - Nq;
+        const int k0 = ktile * kBN;
+        const int kw0 = k0 + 32 * pair;
+        const int key = kw0 + c32;
 
-    // key-side operand: K for the P wave (S = Q K^T), -V for the dS wave, whose product then
-    // starts from D: D - dO V^T = -(dP - D), so that dS needs one multiply per element; its dK
-    // accumulator holds -dK and is negated with the scale at the end
-    bf16x8 kvf[NKS];
-    {
-        const __amdgpu_buffer_rsrc_t rkv = make_rsrc((pwave ? K : V) + hoff, (uint32_t)Nk * D * 2);
-        const unsigned sign = pwave ? 0u : 0x80008000u;
+        // key-side operand: K for the P wave (S = Q K^T), -V for the dS wave, whose product then
+        // starts from D: D - dO V^T = -(dP - D), so that dS needs one multiply per element; its dK
+        // accumulator holds -dK and is negated with the scale at the end
+        bf16x8 kvf[NKS];
+        {
+            const __amdgpu_buffer_rsrc_t rkv = make_rsrc((pwave ? K : V) + hoff, (uint32_t)Nk * D * 2);
+            const unsigned sign = pwave ? 0u : 0x80008000u;
 #pragma unroll
-        for (int ks = 0; ks < NKS; ++ks)
-            kvf[ks] = __builtin_bit_cast(bf16x8, buffer_load16(rkv, (uint32_t)(key * D + 16 * ks + 8 * h) * 2u) ^ sign);
-    }
+            for (int ks = 0; ks < NKS; ++ks)
+                kvf[ks] = __builtin_bit_cast(bf16x8, buffer_load16(rkv, (uint32_t)(key * D + 16 * ks + 8 * h) * 2u) ^ sign);
+        }
 
-    f32x16 acc[NDB];  // dV (P wave) or dK (dS wave)
+        f32x16 acc[NDB];  // dV (P wave) or dK (dS wave)
 #pragma unroll
-    for (int i = 0; i < NDB; ++i) acc[i] = zero16();
+        for (int i = 0; i < NDB; ++i) acc[i] = zero16();
 
-    const int q_start = CAUSAL ? (max(0, k0 - off) / kKvBM) * kKvBM : 0;
-    const int nsteps = (Nq > q_start) ? (Nq - q_start + kKvBM - 1) / kKvBM : 0;
+        const int q_start = CAUSAL ? (max(0, k0 - off) / kKvBM) * kKvBM : 0;
+        const int nsteps = (Nq > q_start) ? (Nq - q_start + kKvBM - 1) / kKvBM : 0;
 
-    auto qst = [&](auto st) __attribute__((always_inline)) {
-        constexpr int v = decltype(st)::value;
-        return (lds_char *)(v == 0 ? q0_raw : v == 1 ? q1_raw : q2_raw);
-    };
-    auto gst = [&](auto st) __attribute__((always_inline)) {
-        constexpr int v = decltype(st)::value;
-        return (lds_char *)(v == 0 ? g0_raw : v == 1 ? g1_raw : g2_raw);
-    };
-    auto sst = [&](auto st) __attribute__((always_inline)) {
-        constexpr int v = decltype(st)::value;
-        return (lds_char *)(v == 0 ? s0_raw : v == 1 ? s1_raw : s2_raw);
-    };
-    auto pst = [&](auto b) __attribute__((always_inline)) {
-        return (lds_char *)(decltype(b)::value ? p1_raw : p0_raw) + pair * (4 * 64 * 16);
-    };
-    // lse of the block being loaded (wave 0, lanes 0..15): it goes to LDS in log2 units at the end
-    // of the step, so that the P waves form each exponent with one fused multiply-add
-    f32x4 lse_ld;
-    auto load_blk = [&](int i, auto st) __attribute__((always_inline)) {
-        const int qs = q_start + i * kKvBM;
-        load_tile_lds<D, 8>(rq, qst(st), qs, w, lane);
-        load_tile_lds<D, 8>(rg, gst(st), qs, w, lane);
-        if (w == 0 && lane < 16) lse_ld = __builtin_bit_cast(f32x4, buffer_load16(rl, (uint32_t)(qs + 4 * lane) * 4u));
-        if (w == 1 && lane < 16) buffer_load_lds16(rd, sst(st) + 4 * kKvBM, (uint32_t)(qs + 4 * lane) * 4u);
-    };
-    auto store_lse = [&](auto st) __attribute__((always_inline)) {
-        if (w == 0 && lane < 16)
-            *(__attribute__((address_space(3))) f32x4 *)(sst(st) + 16 * lane) = lse_ld * kLog2e;
-    };
-    // Every step runs in full: a block that no query of it sees for this pair's keys (causal:
-    // the first block for the later pairs) is masked to P = 0 and adds nothing, and the P wave's
-    // step past the last block meets zero tiles (dO = 0).  Keeping the block index out of the
-    // control flow keeps the registers of the two roles apart.
-    const bool keys_ok = kw0 < Nk;
+        auto qst = [&](auto st) __attribute__((always_inline)) {
+            constexpr int v = decltype(st)::value;
+            return (lds_char *)(v == 0 ? q0_raw : v == 1 ? q1_raw : q2_raw);
+        };
+        auto gst = [&](auto st) __attribute__((always_inline)) {
+            constexpr int v = decltype(st)::value;
+            return (lds_char *)(v == 0 ? g0_raw : v == 1 ? g1_raw : g2_raw);
+        };
+        auto sst = [&](auto st) __attribute__((always_inline)) {
+            constexpr int v = decltype(st)::value;
+            return (lds_char *)(v == 0 ? s0_raw : v == 1 ? s1_raw : s2_raw);
+        };
+        auto pst = [&](auto b) __attribute__((always_inline)) {
+            return (lds_char *)(decltype(b)::value ? p1_raw : p0_raw) + pair * (4 * 64 * 16);
+        };
+        // lse of the block being loaded (wave 0, lanes 0..15): it goes to LDS in log2 units at the end
+        // of the step, so that the P waves form each exponent with one fused multiply-add
+        f32x4 lse_ld;
+        auto load_blk = [&](int i, auto st) __attribute__((always_inline)) {
+            const int qs = q_start + i * kKvBM;
+            load_tile_lds<D, 8>(rq, qst(st), qs, w, lane);
+            load_tile_lds<D, 8>(rg, gst(st), qs, w, lane);
+            if (w == 0 && lane < 16) lse_ld = __builtin_bit_cast(f32x4, buffer_load16(rl, (uint32_t)(qs + 4 * lane) * 4u));
+            if (w == 1 && lane < 16) buffer_load_lds16(rd, sst(st) + 4 * kKvBM, (uint32_t)(qs + 4 * lane) * 4u);
+        };
+        auto store_lse = [&](auto st) __attribute__((always_inline)) {
+            if (w == 0 && lane < 16)
+                *(__attribute__((address_space(3))) f32x4 *)(sst(st) + 16 * lane) = lse_ld * kLog2e;
+        };
+        // Every step runs in full: a block that no query of it sees for this pair's keys (causal:
+        // the first block for the later pairs) is masked to P = 0 and adds nothing, and the P wave's
+        // step past the last block meets zero tiles (dO = 0).  Keeping the block index out of the
+        // control flow keeps the registers of the two roles apart.
+        const bool keys_ok = kw0 < Nk;
 
-    // Step i: the P wave works on block i (stage S = i % 3, P buffer B = i % 2), the dS wave on
-    // block i - 1 (stage (S + 2) % 3, P buffer 1 - B); block i + 1 is loaded into stage (S + 1) % 3.
-    // Each role runs its own copy of the loop (PW), so that the two roles' registers are never
-    // live at the same time; both copies load and wait at the same barriers.
-    auto run = [&](auto PW) __attribute__((always_inline)) {
-        constexpr bool P_WAVE = decltype(PW)::value;
-        auto step = [&](int i, auto S, auto B, auto FIRST) __attribute__((always_inline)) {
-            constexpr int s_cur = decltype(S)::value;
-            using SN = std::integral_constant<int, (s_cur + 1) % 3>;
-            using SP = std::integral_constant<int, (s_cur + 2) % 3>;
-            using BP = std::integral_constant<int, 1 - decltype(B)::value>;
-            load_blk(i + 1, SN{});  // past the last block: zeros into a free stage, never read
-            if constexpr (P_WAVE || !decltype(FIRST)::value) {
-                if (keys_ok) {
-                    // P wave: rows of Q for S, dO^T for dV, on block i.  dS wave: rows of dO for dP,
-                    // Q^T for dK, on block i - 1.
-                    using SB = std::conditional_t<P_WAVE, decltype(S), SP>;
-                    const lds_char *a_l = P_WAVE ? qst(SB{}) : gst(SB{});
-                    const lds_char *t_l = P_WAVE ? gst(SB{}) : qst(SB{});
-                    const lds_char *st_l = sst(SB{});
-                    lds_char *p_l = P_WAVE ? pst(B) : pst(BP{});
-                    const int qs = q_start + (P_WAVE ? i : i - 1) * kKvBM;
-                    // NC chunks of one matrix instruction and a slice of vector work:
-                    //   [0, HS): first product, queries 0..31     [HS, NS): first product, queries 32..63
-                    //                                              | P or dS of queries 0..31
-                    //   [NS, NS + NA/2): second product over 0..31 | P or dS of queries 32..63
-                    //   [NS + NA/2, NC): second product over 32..63
-                    constexpr int HS = NKS, NS = 2 * NKS, NA = 4 * NDB, NC = NS + NA, PF = 2;
-                    const bool need_mask = P_WAVE && CAUSAL && (qs + off < kw0 + 31);
-                    f32x16 sc[2] = {zero16(), zero16()};
-                    bf16x8 pb[4];     // P (P wave) or -dS (dS wave), bf16, groups of 16 queries
-                    f32x4 v4[2][4];   // lse * log2e of the lane's queries, per half (P wave)
-                    if constexpr (!P_WAVE) {
-                        // dS wave: the products start from D of the lane's queries 32 qb + 8 g + 4 h + u
+        // Step i: the P wave works on block i (stage S = i % 3, P buffer B = i % 2), the dS wave on
+        // block i - 1 (stage (S + 2) % 3, P buffer 1 - B); block i + 1 is loaded into stage (S + 1) % 3.
+        // Each role runs its own copy of the loop (PW), so that the two roles' registers are never
+        // live at the same time; both copies load and wait at the same barriers.
+        auto run = [&](auto PW) __attribute__((always_inline)) {
+            constexpr bool P_WAVE = decltype(PW)::value;
+            auto step = [&](int i, auto S, auto B, auto FIRST) __attribute__((always_inline)) {
+                constexpr int s_cur = decltype(S)::value;
+                using SN = std::integral_constant<int, (s_cur + 1) % 3>;
+                using SP = std::integral_constant<int, (s_cur + 2) % 3>;
+                using BP = std::integral_constant<int, 1 - decltype(B)::value>;
+                load_blk(i + 1, SN{});  // past the last block: zeros into a free stage, never read
+                if constexpr (P_WAVE || !decltype(FIRST)::value) {
+                    if (keys_ok) {
+                        // P wave: rows of Q for S, dO^T for dV, on block i.  dS wave: rows of dO for dP,
+                        // Q^T for dK, on block i - 1.
+                        using SB = std::conditional_t<P_WAVE, decltype(S), SP>;
+                        const lds_char *a_l = P_WAVE ? qst(SB{}) : gst(SB{});
+                        const lds_char *t_l = P_WAVE ? gst(SB{}) : qst(SB{});
+                        const lds_char *st_l = sst(SB{});
+                        lds_char *p_l = P_WAVE ? pst(B) : pst(BP{});
+                        const int qs = q_start + (P_WAVE ? i : i - 1) * kKvBM;
+                        // NC chunks of one matrix instruction and a slice of vector work:
+                        //   [0, HS): first product, queries 0..31     [HS, NS): first product, queries 32..63
+                        //                                              | P or dS of queries 0..31
+                        //   [NS, NS + NA/2): second product over 0..31 | P or dS of queries 32..63
+                        //   [NS + NA/2, NC): second product over 32..63
+                        constexpr int HS = NKS, NS = 2 * NKS, NA = 4 * NDB, NC = NS + NA, PF = 2;
+                        const bool need_mask = P_WAVE && CAUSAL && (qs + off < kw0 + 31);
+                        f32x16 sc[2] = {zero16(), zero16()};
+                        bf16x8 pb[4];     // P (P wave) or -dS (dS wave), bf16, groups of 16 queries
+                        f32x4 v4[2][4];   // lse * log2e of the lane's queries, per half (P wave)
+                        if constexpr (!P_WAVE) {
+                            // dS wave: the products start from D of the lane's queries 32 qb + 8 g + 4 h + u
 #pragma unroll
-                        for (int qb = 0; qb < 2; ++qb) {
+                            for (int qb = 0; qb < 2; ++qb) {
 #pragma unroll
-                            for (int g = 0; g < 4; ++g) {
-                                const f32x4 dv = *(const __attribute__((address_space(3))) f32x4 *)(
-                                    st_l + 4 * (kKvBM + 32 * qb + 8 * g + 4 * h));
+                                for (int g = 0; g < 4; ++g) {
+                                    const f32x4 dv = *(const __attribute__((address_space(3))) f32x4 *)(
+                                        st_l + 4 * (kKvBM + 32 * qb + 8 * g + 4 * h));
 #pragma unroll
-                                for (int u = 0; u < 4; ++u) sc[qb][4 * g + u] = dv[u];
+                                    for (int u = 0; u < 4; ++u) sc[qb][4 * g + u] = dv[u];
+                                }
                             }
                         }
-                    }
-                    bf16x8 pv[2][2];  // P of the half read back from LDS (dS wave)
-                    auto fetch = [&](auto C) __attribute__((always_inline)) {
-                        constexpr int c = decltype(C)::value;
-                        if constexpr (c < NS) {
-                            constexpr int qb = c / HS, kst = c % HS;
-                            return lds_read16(a_l, swz_off<D>(32 * qb + c32, 2 * kst + h));
-                        } else {
-                            constexpr int n = c - NS, t = n / NDB, db = n % NDB;
-                            return lds_read_tr_rows_swz<D>(t_l, 16 * t, 32 * db, lane);
-                        }
-                    };
-                    bf16x8 fr[PF + 1];
-                    static_for<0, PF>([&](auto F) __attribute__((always_inline)) { fr[decltype(F)::value] = fetch(F); });
-                    static_for<0, NC>([&](auto C) __attribute__((always_inline)) {
-                        constexpr int c = decltype(C)::value;
-                        if constexpr (c + PF < NC) fr[(c + PF) % (PF + 1)] = fetch(std::integral_constant<int, c + PF>{});
-                        const bf16x8 fc = fr[c % (PF + 1)];
-                        if constexpr (c < NS) {
-                            constexpr int qb = c / HS, kst = c % HS;
-                            sc[qb] = mfma(fc, kvf[kst], sc[qb]);
-                        } else {
-                            constexpr int n = c - NS, t = n / NDB, db = n % NDB;
-                            acc[db] = mfma(fc, pb[t], acc[db]);
-                        }
-                        // vector work on half qb during window [w0, w0 + L)
-                        constexpr int qb = (c >= HS && c < NS) ? 0 : (c >= NS && c < NS + NA / 2) ? 1 : -1;
-                        if constexpr (qb >= 0) {
-                            constexpr int w0 = qb == 0 ? HS : NS;
-                            constexpr int L = qb == 0 ? NS - HS : NA / 2;
-                            constexpr int k = c - w0;
-                            if constexpr (k == 0) {
-                                // the half's lse (P wave) or P (dS wave) from LDS
-                                if constexpr (P_WAVE) {
+                        bf16x8 pv[2][2];  // P of the half read back from LDS (dS wave)
+                        auto fetch = [&](auto C) __attribute__((always_inline)) {
+                            constexpr int c = decltype(C)::value;
+                            if constexpr (c < NS) {
+                                constexpr int qb = c / HS, kst = c % HS;
+                                return lds_read16(a_l, swz_off<D>(32 * qb + c32, 2 * kst + h));
+                            } else {
+                                constexpr int n = c - NS, t = n / NDB, db = n % NDB;
+                                return lds_read_tr_rows_swz<D>(t_l, 16 * t, 32 * db, lane);
+                            }
+                        };
+                        bf16x8 fr[PF + 1];
+                        static_for<0, PF>([&](auto F) __attribute__((always_inline)) { fr[decltype(F)::value] = fetch(F); });
+                        static_for<0, NC>([&](auto C) __attribute__((always_inline)) {
+                            constexpr int c = decltype(C)::value;
+                            if constexpr (c + PF < NC) fr[(c + PF) % (PF + 1)] = fetch(std::integral_constant<int, c + PF>{});
+                            const bf16x8 fc = fr[c % (PF + 1)];
+                            if constexpr (c < NS) {
+                                constexpr int qb = c / HS, kst = c % HS;
+                                sc[qb] = mfma(fc, kvf[kst], sc[qb]);
+                            } else {
+                                constexpr int n = c - NS, t = n / NDB, db = n % NDB;
+                                acc[db] = mfma(fc, pb[t], acc[db]);
+                            }
+                            // vector work on half qb during window [w0, w0 + L)
+                            constexpr int qb = (c >= HS && c < NS) ? 0 : (c >= NS && c < NS + NA / 2) ? 1 : -1;
+                            if constexpr (qb >= 0) {
+                                constexpr int w0 = qb == 0 ? HS : NS;
+                                constexpr int L = qb == 0 ? NS - HS : NA / 2;
+                                constexpr int k = c - w0;
+                                if constexpr (k == 0) {
+                                    // the half's lse (P wave) or P (dS wave) from LDS
+                                    if constexpr (P_WAVE) {
 #pragma unroll
-                                    for (int g = 0; g < 4; ++g)
-                                        v4[qb][g] = *(const __attribute__((address_space(3))) f32x4 *)(
-                                            st_l + 4 * (32 * qb + 8 * g + 4 * h));
-                                }
-                                if constexpr (!P_WAVE) {
+                                        for (int g = 0; g < 4; ++g)
+                                            v4[qb][g] = *(const __attribute__((address_space(3))) f32x4 *)(
+                                                st_l + 4 * (32 * qb + 8 * g + 4 * h));
+                                    }
+                                    if constexpr (!P_WAVE) {
 #pragma unroll
-                                    for (int tt = 0; tt < 2; ++tt)
-                                        pv[qb][tt] = __builtin_bit_cast(bf16x8, *(const __attribute__((address_space(3))) u32x4 *)(
-                                            p_l + ((2 * qb + tt) * 64 + lane) * 16));
-                                }
-                                if (need_mask) {
-                                    // scores of queries before this lane's key -> -inf (P = 0); a query that
-                                    // sees no key has lse = -inf: keep exp2 away from -inf + inf
+                                        for (int tt = 0; tt < 2; ++tt)
+                                            pv[qb][tt] = __builtin_bit_cast(bf16x8, *(const __attribute__((address_space(3))) u32x4 *)(
+                                                p_l + ((2 * qb + tt) * 64 + lane) * 16));
+                                    }
+                                    if (need_mask) {
+                                        // scores of queries before this lane's key -> -inf (P = 0); a query that
+                                        // sees no key has lse = -inf: keep exp2 away from -inf + inf
 #pragma unroll
-                                    for (int g = 0; g < 4; ++g) {
+                                        for (int g = 0; g < 4; ++g) {
 #pragma unroll
-                                        for (int u = 0; u < 4; ++u) {
-                                            v4[qb][g][u] = fmaxf(v4[qb][g][u], -1e30f);
-                                            if (qs + 32 * qb + 8 * g + 4 * h + u + off < key) sc[qb][4 * g + u] = -__builtin_inff();
+                                            for (int u = 0; u < 4; ++u) {
+                                                v4[qb][g][u] = fmaxf(v4[qb][g][u], -1e30f);
+                                                if (qs + 32 * qb + 8 * g + 4 * h + u + off < key) sc[qb][4 * g + u] = -__builtin_inff();
+                                            }
                                         }
                                     }
                                 }
-                            }
-                            static_for<k * 16 / L, (k + 1) * 16 / L>([&](auto RR) __attribute__((always_inline)) {
-                                constexpr int r = decltype(RR)::value, g = r >> 2, u = r & 3;
-                                if constexpr (P_WAVE)
-                                    pb[2 * qb + (r >> 3)][r & 7] = (bf16)fast_exp2(fmaf(sc[qb][r], c_log2, -v4[qb][g][u]));
-                                else
-                                    pb[2 * qb + (r >> 3)][r & 7] = (bf16)((float)pv[qb][r >> 3][r & 7] * sc[qb][r]);
-                            });
-                            if constexpr (P_WAVE && k == L - 1) {
+                                static_for<k * 16 / L, (k + 1) * 16 / L>([&](auto RR) __attribute__((always_inline)) {
+                                    constexpr int r = decltype(RR)::value, g = r >> 2, u = r & 3;
+                                    if constexpr (P_WAVE)
+                                        pb[2 * qb + (r >> 3)][r & 7] = (bf16)fast_exp2(fmaf(sc[qb][r], c_log2, -v4[qb][g][u]));
+                                    else
+                                        pb[2 * qb + (r >> 3)][r & 7] = (bf16)((float)pv[qb][r >> 3][r & 7] * sc[qb][r]);
+                                });
+                                if constexpr (P_WAVE && k == L - 1) {
 #pragma unroll
-                                for (int tt = 0; tt < 2; ++tt)
-                                    lds_write16(p_l, ((2 * qb + tt) * 64 + lane) * 16, __builtin_bit_cast(u32x4, pb[2 * qb + tt]));
+                                    for (int tt = 0; tt < 2; ++tt)
+                                        lds_write16(p_l, ((2 * qb + tt) * 64 + lane) * 16, __builtin_bit_cast(u32x4, pb[2 * qb + tt]));
+                                }
                             }
-                        }
-                        __builtin_amdgcn_sched_barrier(0);
-                    });
+                            __builtin_amdgcn_sched_barrier(0);
+                        });
+                    }
                 }
+                wait_vmem();
+                store_lse(SN{});
+                __syncthreads();
+            };
+
+            using I0 = std::integral_constant<int, 0>;
+            using I1 = std::integral_constant<int, 1>;
+            using I2 = std::integral_constant<int, 2>;
+            using F = std::false_type;
+            for (int gq = 0; gq < G; ++gq) {
+                bind_query_head(qh0 + gq);
+                load_blk(0, I0{});  // the previous query head's last step ended with a barrier
+                wait_vmem();
+                store_lse(I0{});
+                __syncthreads();
+                // steps 0 .. nsteps (the dS wave's last block is nsteps - 1); stage i % 3, P buffer
+                // i % 2; in step 0 only the P wave works
+                if (nsteps == 0) continue;
+                step(0, I0{}, I0{}, std::true_type{});
+                const int n = nsteps + 1;
+                int i = 1;
+                for (; i + 5 < n; i += 6) {
+                    step(i, I1{}, I1{}, F{});
+                    step(i + 1, I2{}, I0{}, F{});
+                    step(i + 2, I0{}, I1{}, F{});
+                    step(i + 3, I1{}, I0{}, F{});
+                    step(i + 4, I2{}, I1{}, F{});
+                    step(i + 5, I0{}, I0{}, F{});
+                }
+                if (i < n) step(i++, I1{}, I1{}, F{});
+                if (i < n) step(i++, I2{}, I0{}, F{});
+                if (i < n) step(i++, I0{}, I1{}, F{});
+                if (i < n) step(i++, I1{}, I0{}, F{});
+                if (i < n) step(i++, I2{}, I1{}, F{});
             }
-            wait_vmem();
-            store_lse(SN{});
-            __syncthreads();
         };
+        if (pwave)
+            run(std::true_type{});
+        else
+            run(std::false_type{});
 
-        using I0 = std::integral_constant<int, 0>;
-        using I1 = std::integral_constant<int, 1>;
-        using I2 = std::integral_constant<int, 2>;
-        using F = std::false_type;
-        for (int gq = 0; gq < G; ++gq) {
-            bind_query_head(qh0 + gq);
-            load_blk(0, I0{});  // the previous query head's last step ended with a barrier
-            wait_vmem();
-            store_lse(I0{});
-            __syncthreads();
-            // steps 0 .. nsteps (the dS wave's last block is nsteps - 1); stage i % 3, P buffer
-            // i % 2; in step 0 only the P wave works
-            if (nsteps == 0) continue;
-            step(0, I0{}, I0{}, std::true_type{});
-            const int n = nsteps + 1;
-            int i = 1;
-            for (; i + 5 < n; i += 6) {
-                step(i, I1{}, I1{}, F{});
-                step(i + 1, I2{}, I0{}, F{});
-                step(i + 2, I0{}, I1{}, F{});
-                step(i + 3, I1{}, I0{}, F{});
-                step(i + 4, I2{}, I1{}, F{});
-                step(i + 5, I0{}, I0{}, F{});
-            }
-            if (i < n) step(i++, I1{}, I1{}, F{});
-            if (i < n) step(i++, I2{}, I0{}, F{});
-            if (i < n) step(i++, I0{}, I1{}, F{});
-            if (i < n) step(i++, I1{}, I0{}, F{});
-            if (i < n) step(i++, I2{}, I1{}, F{});
-        }
-    };
-    if (pwave)
-        run(std::true_type{});
-    else
-        run(std::false_type{});
-
-    if (key < Nk) {
-        bf16 *row = (pwave ? dV : dK) + hoff + (size_t)key * D;
-        const float f = pwave ? 1.f : -scale;
+        if (key < Nk) {
+            bf16 *row = (pwave ? dV : dK) + hoff + (size_t)key * D;
+            const float f = pwave ? 1.f : -scale;
 #pragma unroll
-        for (int db = 0; db < NDB; ++db) {
+            for (int db = 0; db < NDB; ++db) {
 #pragma unroll
-            for (int g = 0; g < 4; ++g) {
-                bf16x4 v4;
+                for (int g = 0; g < 4; ++g) {
+                    bf16x4 v4;
 #pragma unroll
-                for (int u = 0; u < 4; ++u) v4[u] = (bf16)(acc[db][4 * g + u] * f);
-                *(bf16x4 *)(row + 32 * db + 8 * g + 4 * h) = v4;
+                    for (int u = 0; u < 4; ++u) v4[u] = (bf16)(acc[db][4 * g + u] * f);
+                    *(bf16x4 *)(row + 32 * db + 8 * g + 4 * h) = v4;
+                }
             }
         }
     }
@@ -1192,11 +1218,16 @@ template <int D, bool CAUSAL>
 hipError_t launch_dkdv2_t(const BwdArgs &a)
 {
     const int n_ktiles = (a.Nk + 127) / 128;
-    const long long G = (long long)a.B * a.Hk * n_ktiles;
-    if (G == 0) return hipSuccess;
-    hipLaunchKernelGGL((bwd_dkdv2_kernel<D, CAUSAL>), dim3((unsigned)G), dim3(512), 0, (hipStream_t)a.stream,
-                       (const bf16 *)a.q, (const bf16 *)a.k, (const bf16 *)a.v, (const bf16 *)a.dout, a.lse,
-                       (const float *)a.delta, (bf16 *)a.dk, (bf16 *)a.dv, a.Nq, a.Nk, a.H, a.H / a.Hk, n_ktiles, a.scale, a.scale * kLog2e);
+    const long long n_items = (long long)a.B * a.Hk * n_ktiles;
+    if (n_items == 0) return hipSuccess;
+    // one workgroup per CU fits (LDS); with more items than CUs and heads spread evenly over the
+    // XCDs, one persistent workgroup per CU takes them in rounds
+    const bool persistent = n_items > kPersistentWGs && (a.B * a.Hk) % 8 == 0;
+    const long long G = persistent ? kPersistentWGs : n_items;
+    const Dkdv2Args args{(const bf16 *)a.q, (const bf16 *)a.k, (const bf16 *)a.v, (const bf16 *)a.dout, a.lse,
+                         (const float *)a.delta, (bf16 *)a.dk, (bf16 *)a.dv, a.Nq, a.Nk, a.H, a.H / a.Hk, n_ktiles,
+                         (int)n_items, a.scale, a.scale * kLog2e};
+    hipLaunchKernelGGL((bwd_dkdv2_kernel<D, CAUSAL>), dim3((unsigned)G), dim3(512), 0, (hipStream_t)a.stream, args);
     return hipGetLastError();
 }
 

@@ -122,9 +122,8 @@ __device__ __forceinline__ int xcd_remap(int g, int G)
 // position 1, ...): dispatch is then longest-first over the whole grid when position 0
 // is the largest tile, and head h always lands on XCD h % 8, so that its K and V stay in
 // one L2.  Otherwise every XCD takes a contiguous head-major range of items.
-__device__ __forceinline__ void work_item(int g, int n_tiles, int &head, int &t)
+__device__ __forceinline__ void work_item_of(int g, int G, int n_tiles, int &head, int &t)
 {
-    const int G = (int)gridDim.x;
     const int n_heads = G / n_tiles;
     if ((n_heads & 7) == 0) {
         t = g / n_heads;
@@ -134,6 +133,24 @@ __device__ __forceinline__ void work_item(int g, int n_tiles, int &head, int &t)
         head = id / n_tiles;
         t = id - head * n_tiles;
     }
+}
+
+// The same for a grid of exactly n_heads * n_tiles workgroups, one item each.
+__device__ __forceinline__ void work_item(int g, int n_tiles, int &head, int &t)
+{
+    work_item_of(g, (int)gridDim.x, n_tiles, head, t);
+}
+
+// Item that workgroup g of a persistent grid of P workgroups takes in round r, when items are in
+// longest-first order and round r covers items r P .. r P + P - 1.  In odd rounds the order is
+// reversed within each XCD (g = x + 8 c takes x + 8 (P/8 - 1 - c)), so a workgroup that had one
+// of the longest items of a round gets one of the shortest of the next; item j keeps
+// j % 8 == g % 8, so a head stays on the XCD it started on.  P is a multiple of 8 when it is
+// below the item count (with one round, the item is g).
+__device__ __forceinline__ int persistent_item(int r, int g, int P)
+{
+    if ((r & 1) == 0 || (P & 7) != 0) return r * P + g;
+    return r * P + (g & 7) + 8 * (P / 8 - 1 - (g >> 3));
 }
 
 }  // namespace attn
