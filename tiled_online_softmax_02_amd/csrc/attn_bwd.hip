@@ -416,10 +416,10 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv2_kernel(const Dkdv2Args args)
             if (w == 0 && lane < 16)
                 *(__attribute__((address_space(3))) f32x4 *)(sst(st) + 16 * lane) = lse_ld * kLog2e;
         };
-        // Every step runs in full: a block that no query of it sees for this pair's keys (causal:
-        // the first block for the later pairs) is masked to P = 0 and adds nothing, and the P wave's
-        // step past the last block meets zero tiles (dO = 0).  Keeping the block index out of the
-        // control flow keeps the registers of the two roles apart.
+        // A block that no query of it sees for this pair's keys (causal: the first block for the
+        // later pairs) runs in full, masked to P = 0, so that the block index stays out of the
+        // step's control flow.  The one exception is the P wave's step past the last block (only
+        // zero tiles there, dO = 0): it skips its work, and the dS wave has the SIMD to itself.
         const bool keys_ok = kw0 < Nk;
 
         // Step i: the P wave works on block i (stage S = i % 3, P buffer B = i % 2), the dS wave on
@@ -435,7 +435,7 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv2_kernel(const Dkdv2Args args)
                 using BP = std::integral_constant<int, 1 - decltype(B)::value>;
                 load_blk(i + 1, SN{});  // past the last block: zeros into a free stage, never read
                 if constexpr (P_WAVE || !decltype(FIRST)::value) {
-                    if (keys_ok) {
+                    if (keys_ok && (!P_WAVE || i < nsteps)) {
                         // P wave: rows of Q for S, dO^T for dV, on block i.  dS wave: rows of dO for dP,
                         // Q^T for dK, on block i - 1.
                         using SB = std::conditional_t<P_WAVE, decltype(S), SP>;
