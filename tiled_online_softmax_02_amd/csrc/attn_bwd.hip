@@ -701,7 +701,7 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv3_kernel(
             using BP = std::integral_constant<int, 1 - decltype(B)::value>;
             load_blk(i + 1, SN{});  // past the last block: zeros into a free stage, never read
             if constexpr (P_WAVE || !decltype(FIRST)::value) {
-                if (keys_ok) {
+                if (keys_ok && (!P_WAVE || i < nsteps)) {  // P wave: no work past the last block
                     using SB = std::conditional_t<P_WAVE, decltype(S), SP>;
                     const lds_char *a_l = P_WAVE ? qst(SB{}) : gst(SB{});
                     const lds_char *t_l = P_WAVE ? gst(SB{}) : qst(SB{});
