@@ -1,12 +1,13 @@
 """The dK/dV kernel (d <= 128) when its grid is persistent: with more key blocks than the chip
 has CUs and a head count that is a multiple of 8, 256 workgroups take the (head, key block)
-items in rounds, every other round in reverse order within each XCD.
+items in passes, every other pass in reverse order within each XCD.
 
 B = 1, H = 8, N = 4097, d = 128, causal: 33 key blocks of 128 per head (the last holds one
-key), 264 items, so round 0 is full and round 1 (reversed) holds 8 items.  Every element of
-dQ, dK and dV of every head is compared with the fp64 oracle's backward (the gradient formulas
-of the backward pass in "digest_existing.txt", answer q02_flashattention) at the bf16 bar of
-2e-2; an item taken twice or never would leave a whole key block wrong.
+key), 264 items: the first pass over the workgroups is full and the second (reversed) holds
+8.  Every element of dQ, dK and dV of every head is compared with the fp64 oracle's backward
+(the gradient formulas of the backward pass in "digest_existing.txt", answer
+q02_flashattention) at the bf16 bar of 2e-2; an item taken twice or never would leave a whole
+key block wrong.
 """
 import numpy as np
 import pytest
