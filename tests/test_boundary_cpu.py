@@ -66,6 +66,9 @@ def fwd(lib, q=P[0], k=P[1], v=P[2], o=P[3], lse=P[4], B=1, H=1, N=64, d=64, cau
     (dict(d=160), A.ATTN_ERR_UNSUPPORTED_D),
     (dict(N=1 << 24, d=128), A.ATTN_ERR_BAD_SHAPE),   # (N+256)*d*2 > 2^32
     (dict(N=(1 << 24) - 200, d=128), A.ATTN_ERR_BAD_SHAPE),  # (N+256)*d*2 just above 2^32
+    (dict(N=2**31 - 1, d=64), A.ATTN_ERR_BAD_SHAPE),   # INT_MAX rows: N + 256 is formed in 64 bits
+    (dict(N=2**31 - 200, d=64), A.ATTN_ERR_BAD_SHAPE),
+    (dict(B=2**31 - 1, H=2**31 - 1, N=2**31 - 1, d=256), A.ATTN_ERR_BAD_SHAPE),
     (dict(causal=2), A.ATTN_ERR_BAD_ARG),
     (dict(causal=-1), A.ATTN_ERR_BAD_ARG),
     (dict(scale=0.0), A.ATTN_ERR_BAD_SCALE),
@@ -149,6 +152,8 @@ def fwd_qk(lib, q=P[0], k=P[1], v=P[2], o=P[3], lse=P[4], B=1, H=1, Hk=None, Nq=
     (dict(Nk=1 << 24, d=128), A.ATTN_ERR_BAD_SHAPE),    # (Nk+256)*d*2 > 2^32
     (dict(Nk=16776960, d=128), A.ATTN_ERR_BAD_SHAPE),   # one row past the longest accepted key length
     (dict(Nq=1 << 24, d=128), A.ATTN_ERR_BAD_SHAPE),
+    (dict(Nq=2**31 - 1), A.ATTN_ERR_BAD_SHAPE),         # INT_MAX lengths: no signed overflow in the checks
+    (dict(Nk=2**31 - 1), A.ATTN_ERR_BAD_SHAPE),
     (dict(d=96), A.ATTN_ERR_UNSUPPORTED_D),
     (dict(causal=3), A.ATTN_ERR_BAD_ARG),
     (dict(k=None), A.ATTN_ERR_NULLPTR),                 # Nk > 0: k is required

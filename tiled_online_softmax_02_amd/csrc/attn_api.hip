@@ -4,6 +4,8 @@
 #include <math.h>
 #include <stdint.h>
 
+#include <atomic>
+
 #include "../../include/attn.h"
 #include "attn_launch.h"
 
@@ -31,7 +33,7 @@ int check_shape(int B, int H, int Hk, int Nq, int Nk, int d, bool *empty)
     const long long rows_q = (long long)B * H * Nq, rows_k = (long long)B * Hk * Nk;
     if (rows_q > ((1LL << 62) / d) || rows_k > ((1LL << 62) / d)) return ATTN_ERR_BAD_SHAPE;
     // per-head byte offsets, including the padding rows of the last tile, are 32-bit
-    if ((long long)(Nq + 256) * d * 2 > 0xFFFFFFFFLL || (long long)(Nk + 256) * d * 2 > 0xFFFFFFFFLL)
+    if (((long long)Nq + 256) * d * 2 > 0xFFFFFFFFLL || ((long long)Nk + 256) * d * 2 > 0xFFFFFFFFLL)
         return ATTN_ERR_BAD_SHAPE;
     // work-group counts of the launches must fit a 32-bit grid
     if (attn::fwd_grid_size(B, H, Nq) >= (1LL << 31) || attn::bwd_dkdv_grid_size(B, Hk, Nk) >= (1LL << 31) ||
@@ -74,6 +76,36 @@ int hip_status(hipError_t e)
     return ATTN_ERR_HIP;
 }
 
+// Compute units and XCDs of the device that `stream` belongs to (the current device for the null
+// stream), queried once per device and then cached.
+constexpr int kMaxDevices = 64;
+std::atomic<long long> g_shape[kMaxDevices];  // (cus << 32) | nx, 0 until queried
+
+int device_shape(void *stream, attn::DeviceShape *out)
+{
+    int dev = 0;
+    hipError_t e = stream ? hipStreamGetDevice((hipStream_t)stream, &dev) : hipGetDevice(&dev);
+    if (e != hipSuccess) return hip_status(e);
+    if (dev >= 0 && dev < kMaxDevices) {
+        const long long v = g_shape[dev].load(std::memory_order_relaxed);
+        if (v != 0) {
+            out->cus = (int)(v >> 32);
+            out->nx = (int)(v & 0xFFFFFFFF);
+            return ATTN_OK;
+        }
+    }
+    int cus = 0, nx = 0;
+    e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+    if (e != hipSuccess) return hip_status(e);
+    e = hipDeviceGetAttribute(&nx, hipDeviceAttributeNumberOfXccs, dev);
+    if (e != hipSuccess) return hip_status(e);
+    if (cus < 1 || nx < 1) return hip_status(hipErrorInvalidDevice);
+    out->cus = cus;
+    out->nx = nx;
+    if (dev >= 0 && dev < kMaxDevices) g_shape[dev].store(((long long)cus << 32) | nx, std::memory_order_relaxed);
+    return ATTN_OK;
+}
+
 #define RETURN_IF(x)               \
     do {                           \
         const int rc_ = (x);       \
@@ -105,7 +137,8 @@ int fwd_impl(const void *q, const void *k, const void *v, void *o, float *lse, i
     const Range in[] = {range_of(q, qb), range_of(k, kb), range_of(v, kb)};
     const Range out[] = {range_of(o, qb), range_of(lse, lb)};
     RETURN_IF(check_alias(in, 3, out, 2));
-    attn::FwdArgs a{q, k, v, o, lse, B, H, Hk, Nq, Nk, d, causal, scale, stream};
+    attn::FwdArgs a{q, k, v, o, lse, B, H, Hk, Nq, Nk, d, causal, scale, stream, {}};
+    RETURN_IF(device_shape(stream, &a.dev));
     return hip_status(attn::launch_fwd(a));
 }
 
@@ -127,7 +160,8 @@ int fwd_split_impl(const void *q, const void *k, const void *v, void *o, float *
     const Range in[] = {range_of(q, qb), range_of(k, kb), range_of(v, kb)};
     const Range out[] = {range_of(o, qb), range_of(lse, lb), range_of(workspace, wb)};
     RETURN_IF(check_alias(in, 3, out, 3));
-    attn::FwdArgs a{q, k, v, o, lse, B, H, Hk, Nq, Nk, d, causal, scale, stream};
+    attn::FwdArgs a{q, k, v, o, lse, B, H, Hk, Nq, Nk, d, causal, scale, stream, {}};
+    RETURN_IF(device_shape(stream, &a.dev));
     return hip_status(attn::launch_fwd_split(a, num_splits, workspace));
 }
 
@@ -163,7 +197,8 @@ int fwd_fp8_impl(const void *q, const void *k, const void *v, const float *desca
                         range_of(descale_q, sqb), range_of(descale_k, skb), range_of(descale_v, skb)};
     const Range out[] = {range_of(o, qb), range_of(lse, lb)};
     RETURN_IF(check_alias(in, 6, out, 2));
-    attn::Fp8FwdArgs a{q, k, v, descale_q, descale_k, descale_v, o, lse, B, H, Hk, Nq, Nk, d, causal, scale, stream};
+    attn::Fp8FwdArgs a{q, k, v, descale_q, descale_k, descale_v, o, lse, B, H, Hk, Nq, Nk, d, causal, scale, stream, {}};
+    RETURN_IF(device_shape(stream, &a.dev));
     return hip_status(attn::launch_fwd_fp8(a));
 }
 
@@ -182,7 +217,8 @@ int bwd_impl(const void *q, const void *k, const void *v, const void *o, const v
                         range_of(o, qb), range_of(dout, qb), range_of(lse, lb)};
     const Range out[] = {range_of(dq, qb), range_of(dk, kb), range_of(dv, kb), range_of(delta, lb)};
     RETURN_IF(check_alias(in, 6, out, 4));
-    attn::BwdArgs a{q, k, v, o, dout, lse, dq, dk, dv, delta, B, H, Hk, Nq, Nk, d, causal, scale, stream};
+    attn::BwdArgs a{q, k, v, o, dout, lse, dq, dk, dv, delta, B, H, Hk, Nq, Nk, d, causal, scale, stream, {}};
+    RETURN_IF(device_shape(stream, &a.dev));
     if (attn::bwd_dq_fuses_delta(d)) {
         // the dQ kernel forms D on the way (no preprocess launch), then dK/dV reads it
         RETURN_IF(hip_status(attn::launch_bwd_dq_delta(a)));
@@ -260,6 +296,7 @@ int attn_bwd_preprocess(const void *o, const void *dout, float *delta, int B, in
     a.Nq = a.Nk = N;
     a.d = d;
     a.stream = stream;
+    RETURN_IF(device_shape(stream, &a.dev));
     return hip_status(attn::launch_bwd_preprocess(a));
 }
 
@@ -294,6 +331,7 @@ int attn_bwd_dkdv(const void *q, const void *k, const void *v, const void *dout,
     a.causal = causal;
     a.scale = scale;
     a.stream = stream;
+    RETURN_IF(device_shape(stream, &a.dev));
     return hip_status(attn::launch_bwd_dkdv(a));
 }
 
@@ -327,6 +365,7 @@ int attn_bwd_dq(const void *q, const void *k, const void *v, const void *dout, c
     a.causal = causal;
     a.scale = scale;
     a.stream = stream;
+    RETURN_IF(device_shape(stream, &a.dev));
     return hip_status(attn::launch_bwd_dq(a));
 }
 
@@ -361,6 +400,7 @@ int attn_bwd_dq_delta(const void *q, const void *k, const void *v, const void *o
     a.causal = causal;
     a.scale = scale;
     a.stream = stream;
+    RETURN_IF(device_shape(stream, &a.dev));
     if (attn::bwd_dq_fuses_delta(d)) return hip_status(attn::launch_bwd_dq_delta(a));
     RETURN_IF(hip_status(attn::launch_bwd_preprocess(a)));
     return hip_status(attn::launch_bwd_dq(a));

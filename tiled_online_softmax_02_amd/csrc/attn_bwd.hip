@@ -13,9 +13,9 @@
 // Splitting dQ into its own kernel keeps every sum in registers of a single
 // workgroup: no atomics, bitwise reproducible results.
 //
-// Two dK/dV kernels: bwd_dkdv2_kernel (d <= 128) splits each key block's work between the
-// two waves of a SIMD (one computes P and dV, the other dS and dK); bwd_dkdv_kernel
-// (d = 192, 256) has one wave per SIMD doing all four products.
+// Two dK/dV kernels, both splitting each key block's work between the two waves of a SIMD (one
+// computes P and dV, the other dS and dK): bwd_dkdv2_kernel for d <= 128 and bwd_dkdv3_kernel for
+// d = 192 and 256, where each wave also takes one half of the columns of dK and dV.
 //
 // MFMA layouts follow attn_device.h.  In the dK/dV kernels the scores are
 // computed as S = Q K^T (each lane: one key, 16 queries of a 32-query block),
@@ -60,237 +60,10 @@ __global__ __launch_bounds__(kThreads) void bwd_preprocess_kernel(const bf16 *__
 
 // ------------------------------------------------------------ dK / dV
 
-// One wave per SIMD; launched for d = 192 and 256 (d <= 128 launches the paired-wave kernel
-// below; the code here is written for every width).  d <= 128: each of the 4 waves owns 32 keys
-// (128 keys per workgroup) and all of d.  d = 192 and 256: the dK/dV accumulators
-// of 32 keys over all of d do not fit next to the K and V fragments, so waves w and w + 2 share
-// 32 keys and take one half of the columns of dK and dV each (64 keys per workgroup); both
-// compute the same S and dP.
+// Keys per dK/dV workgroup: 128 for d <= 128 (paired-wave kernel below), 64 for d = 192 and 256.
 template <int D>
-constexpr bool kv_dsplit() { return D >= 192; }
-template <int D>
-constexpr int kv_bn() { return kv_dsplit<D>() ? 64 : 128; }
+constexpr int kv_bn() { return D >= 192 ? 64 : 128; }
 constexpr int kKvBM = 64;   // queries per streamed block
-constexpr int kPersistentWGs = 256;  // the CUs of one MI355X: one resident dK/dV workgroup each
-
-template <int D, bool CAUSAL>
-__global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(
-    const bf16 *__restrict__ Q, const bf16 *__restrict__ K, const bf16 *__restrict__ V, const bf16 *__restrict__ dO,
-    const float *__restrict__ LSE, const float *__restrict__ Dl, bf16 *__restrict__ dK, bf16 *__restrict__ dV, int Nq, int Nk,
-    int H, int G, int n_ktiles, float scale, float c_log2)
-{
-    constexpr int NKS = D / 16;
-    constexpr int NDB = D / 32;
-    constexpr int TILE = kKvBM * D * 2;
-    // One LDS array per stage and operand (swizzled tiles filled by direct loads): reads of
-    // one stage are known not to alias the loads in flight into the other.
-    __shared__ __attribute__((aligned(16))) char q0_raw[TILE], q1_raw[TILE], g0_raw[TILE], g1_raw[TILE];
-    __shared__ __attribute__((aligned(16))) float s0_raw[2 * kKvBM], s1_raw[2 * kKvBM];  // lse, then D
-
-    // `head` is a K/V head (one of B * H/G); its G query heads (grouped-query attention; G = 1
-    // for multi-head attention) all add to its dK and dV.
-    int head, ktile;
-    work_item(blockIdx.x, n_ktiles, head, ktile);  // causal: key block 0 sees the most queries and goes first
-    const int Hk = H / G;
-    const int qh0 = (head / Hk) * H + (head % Hk) * G;  // first query head of the group
-
-    const int tid = threadIdx.x;
-    const int lane = tid & 63, h = lane >> 5, c32 = lane & 31;
-    const int w = wave_uniform(tid >> 6);
-    const size_t hoff = (size_t)head * (size_t)Nk * D;    // K, V, dK and dV of this head
-    const __amdgpu_buffer_rsrc_t rk = make_rsrc(K + hoff, (uint32_t)Nk * D * 2);
-    const __amdgpu_buffer_rsrc_t rv = make_rsrc(V + hoff, (uint32_t)Nk * D * 2);
-    // Q, dO, lse and D of the query head being worked on
-    __amdgpu_buffer_rsrc_t rq, rg, rl, rd;
-    auto bind_query_head = [&](int qh) __attribute__((always_inline)) {
-        const size_t hoff_q = (size_t)qh * (size_t)Nq * D;
-        rq = make_rsrc(Q + hoff_q, (uint32_t)Nq * D * 2);
-        rg = make_rsrc(dO + hoff_q, (uint32_t)Nq * D * 2);
-        rl = make_rsrc(LSE + (size_t)qh * Nq, (uint32_t)Nq * 4);
-        rd = make_rsrc(Dl + (size_t)qh * Nq, (uint32_t)Nq * 4);
-    };
-    // Causal mask with bottom-right alignment: query i sees keys j <= i + off.
-    const int off = Nk - Nq;
-
-    constexpr int kKvBN = kv_bn<D>();
-    constexpr int NDBH = kv_dsplit<D>() ? NDB / 2 : NDB;  // 32-column blocks of dK, dV per wave
-    const int db0 = kv_dsplit<D>() ? (w >> 1) * NDBH : 0;  // first of them
-    const int k0 = ktile * kKvBN;
-    const int kw0 = k0 + 32 * (kv_dsplit<D>() ? (w & 1) : w);  // wave-uniform
-    const int key = kw0 + c32;
-
-    // K and V fragments (B operands of S = Q K^T and dP = dO V^T): lane holds row `key` (zeros past Nk).
-    bf16x8 kf[NKS], vf[NKS];
-#pragma unroll
-    for (int ks = 0; ks < NKS; ++ks) {
-        kf[ks] = __builtin_bit_cast(bf16x8, buffer_load16(rk, (uint32_t)(key * D + 16 * ks + 8 * h) * 2u));
-        vf[ks] = __builtin_bit_cast(bf16x8, buffer_load16(rv, (uint32_t)(key * D + 16 * ks + 8 * h) * 2u));
-    }
-
-    f32x16 dk[NDBH], dv[NDBH];
-#pragma unroll
-    for (int i = 0; i < NDBH; ++i) {
-        dk[i] = zero16();
-        dv[i] = zero16();
-    }
-
-    // causal: the first query that sees key k0 is k0 - off
-    const int q_start = CAUSAL ? (max(0, k0 - off) / kKvBM) * kKvBM : 0;
-    const int nsteps = (Nq > q_start) ? (Nq - q_start + kKvBM - 1) / kKvBM : 0;
-
-    auto qst = [&](auto par) __attribute__((always_inline)) { return (lds_char *)(decltype(par)::value ? q1_raw : q0_raw); };
-    auto gst = [&](auto par) __attribute__((always_inline)) { return (lds_char *)(decltype(par)::value ? g1_raw : g0_raw); };
-    auto sst = [&](auto par) __attribute__((always_inline)) { return (lds_char *)(decltype(par)::value ? s1_raw : s0_raw); };
-    // Q, dO, lse and D of query block i.  Rows past Nq read as zeros: such a row has Q = dO = 0,
-    // so its P = exp2(0 - 0) = 1 meets zero operands in every product and contributes nothing.
-    auto load_blk = [&](int i, auto par) __attribute__((always_inline)) {
-        const int qs = q_start + i * kKvBM;
-        load_tile_lds<D, 4>(rq, qst(par), qs, w, lane);
-        load_tile_lds<D, 4>(rg, gst(par), qs, w, lane);
-        if (w == 0 && lane < 16) buffer_load_lds16(rl, sst(par), (uint32_t)(qs + 4 * lane) * 4u);
-        if (w == 1 && lane < 16) buffer_load_lds16(rd, sst(par) + 4 * kKvBM, (uint32_t)(qs + 4 * lane) * 4u);
-    };
-
-    using P0 = std::integral_constant<int, 0>;
-    using P1 = std::integral_constant<int, 1>;
-
-    auto step = [&](int i, auto par) __attribute__((always_inline)) {
-        using PN = std::integral_constant<int, 1 - decltype(par)::value>;
-        load_blk(i + 1, PN{});  // past the last block: zeros into the free stage, never read
-        const lds_char *q_l = qst(par);
-        const lds_char *g_l = gst(par);
-        const lds_char *st_l = sst(par);
-        const int qs = q_start + i * kKvBM;
-        // some query of this block sees some key of this wave
-        if ((kw0 < Nk) && (!CAUSAL || qs + kKvBM - 1 + off >= kw0)) {
-            // The step is NC chunks of one matrix instruction each, in four phases:
-            //   A: S and dP of queries 0..31      B: S and dP of queries 32..63
-            //   C: dV and dK over queries 0..31   D: dV and dK over queries 32..63
-            // P and dS of queries 0..31 are computed on the vector units during B, those of
-            // queries 32..63 during C.  LDS fragments are fetched PF chunks ahead; scheduling
-            // barriers keep each chunk whole.
-            const bool need_mask = CAUSAL && (qs + off < kw0 + 31);
-            constexpr int PA = 2 * NKS;   // chunks of an S/dP phase (A, B)
-            constexpr int PC = 4 * NDBH;  // chunks of a dV/dK phase (C, D): 2 groups of 16 queries x NDBH x 2
-            constexpr int NC = 2 * PA + 2 * PC;
-            constexpr int PF = 3;
-            f32x16 s[2], dp[2];
-            bf16x8 pb[4], sb[4];
-            f32x4 l4[2][4], d4[2][4];  // lse and D of the lane's query rows, per half and row group
-#pragma unroll
-            for (int qb = 0; qb < 2; ++qb) s[qb] = dp[qb] = zero16();
-            auto fetch = [&](auto C) __attribute__((always_inline)) {
-                constexpr int c = decltype(C)::value;
-                if constexpr (c < 2 * PA) {
-                    constexpr int qb = c / PA, m = c % PA, kst = m / 2;
-                    return lds_read16((m & 1) ? g_l : q_l, swz_off<D>(32 * qb + c32, 2 * kst + h));
-                } else {
-                    constexpr int qb = (c - 2 * PA) / PC, n = (c - 2 * PA) % PC;
-                    constexpr int t = 2 * qb + n / (2 * NDBH), db = (n / 2) % NDBH;
-                    // dV takes dO^T, dK takes Q^T (columns of this wave's part of d)
-                    return lds_read_tr_rows_swz<D>((n & 1) ? q_l : g_l, 16 * t, 32 * (db0 + db), lane);
-                }
-            };
-            bf16x8 fr[PF + 1];
-            static_for<0, PF>([&](auto F) __attribute__((always_inline)) { fr[decltype(F)::value] = fetch(F); });
-            static_for<0, NC>([&](auto C) __attribute__((always_inline)) {
-                constexpr int c = decltype(C)::value;
-                if constexpr (c + PF < NC) fr[(c + PF) % (PF + 1)] = fetch(std::integral_constant<int, c + PF>{});
-                // lse and D of a half's rows, read one phase before they are needed
-                if constexpr (c % PA < 8 && c < 2 * PA) {
-                    constexpr int qb = c / PA, g = (c % PA) / 2;
-                    const int qloc = 32 * qb + 8 * g + 4 * h;  // first of 4 consecutive queries
-                    if constexpr ((c % PA) % 2 == 0)
-                        l4[qb][g] = *(const __attribute__((address_space(3))) f32x4 *)(st_l + 4 * qloc);
-                    else
-                        d4[qb][g] = *(const __attribute__((address_space(3))) f32x4 *)(st_l + 4 * (kKvBM + qloc));
-                }
-                const bf16x8 fc = fr[c % (PF + 1)];
-                if constexpr (c < 2 * PA) {
-                    constexpr int qb = c / PA, m = c % PA, kst = m / 2;
-                    if constexpr (m & 1)
-                        dp[qb] = mfma(fc, vf[kst], dp[qb]);
-                    else
-                        s[qb] = mfma(fc, kf[kst], s[qb]);
-                } else {
-                    constexpr int qb = (c - 2 * PA) / PC, n = (c - 2 * PA) % PC;
-                    constexpr int t = 2 * qb + n / (2 * NDBH), db = (n / 2) % NDBH;
-                    if constexpr (n & 1)
-                        dk[db] = mfma(fc, sb[t], dk[db]);
-                    else
-                        dv[db] = mfma(fc, pb[t], dv[db]);
-                }
-                if constexpr (c == PA || c == 2 * PA) {
-                    // On blocks that cross the diagonal, scores of queries before this lane's key
-                    // become -inf (P = 0) before their half is exponentiated; other blocks skip this.
-                    constexpr int qb = c / PA - 1;
-                    if (need_mask) {
-#pragma unroll
-                        for (int r = 0; r < 16; ++r)
-                            if (qs + 32 * qb + 8 * (r >> 2) + 4 * h + (r & 3) + off < key) s[qb][r] = -__builtin_inff();
-                        // a query that sees no key at all has lse = -inf: a finite stand-in keeps
-                        // its P at exp2(-inf) = 0 instead of exp2(-inf + inf)
-#pragma unroll
-                        for (int g = 0; g < 4; ++g) {
-#pragma unroll
-                            for (int u = 0; u < 4; ++u) l4[qb][g][u] = fmaxf(l4[qb][g][u], -1e30f);
-                        }
-                    }
-                }
-                if constexpr (c >= PA && c < 2 * PA + PC) {
-                    // P = exp2(S scale log2e - lse log2e), dS = P (dP - D) for half qb: the
-                    // first half during phase B, the second during phase C; chunk i of a phase of
-                    // L chunks takes elements [16 i / L, 16 (i + 1) / L)
-                    constexpr int qb = c < 2 * PA ? 0 : 1;
-                    constexpr int L = c < 2 * PA ? PA : PC;
-                    constexpr int i = c < 2 * PA ? c - PA : c - 2 * PA;
-                    static_for<i * 16 / L, (i + 1) * 16 / L>([&](auto RR) __attribute__((always_inline)) {
-                        constexpr int r = decltype(RR)::value, g = r >> 2, u = r & 3;
-                        const float p = fast_exp2(fmaf(s[qb][r], c_log2, -l4[qb][g][u] * kLog2e));
-                        const float ds = p * (dp[qb][r] - d4[qb][g][u]);
-                        pb[2 * qb + (r >> 3)][r & 7] = (bf16)p;
-                        sb[2 * qb + (r >> 3)][r & 7] = (bf16)ds;
-                    });
-                }
-                __builtin_amdgcn_sched_barrier(0);
-            });
-        }
-        wait_vmem();
-        __syncthreads();
-    };
-
-    for (int gq = 0; gq < G; ++gq) {
-        bind_query_head(qh0 + gq);
-        load_blk(0, P0{});  // the previous query head's last step ended with a barrier
-        wait_vmem();
-        __syncthreads();
-        int i = 0;
-        for (; i + 1 < nsteps; i += 2) {
-            step(i, P0{});
-            step(i + 1, P1{});
-        }
-        if (i < nsteps) step(i, P0{});
-    }
-
-    if (key < Nk) {
-        bf16 *dkrow = dK + hoff + (size_t)key * D;
-        bf16 *dvrow = dV + hoff + (size_t)key * D;
-#pragma unroll
-        for (int db = 0; db < NDBH; ++db) {
-#pragma unroll
-            for (int g = 0; g < 4; ++g) {
-                bf16x4 kv4, vv4;
-#pragma unroll
-                for (int u = 0; u < 4; ++u) {
-                    kv4[u] = (bf16)(dk[db][4 * g + u] * scale);
-                    vv4[u] = (bf16)dv[db][4 * g + u];
-                }
-                *(bf16x4 *)(dkrow + 32 * (db0 + db) + 8 * g + 4 * h) = kv4;
-                *(bf16x4 *)(dvrow + 32 * (db0 + db) + 8 * g + 4 * h) = vv4;
-            }
-        }
-    }
-}
 
 // ------------------------------------------------------------ dK / dV, paired waves (d <= 128)
 
@@ -307,7 +80,7 @@ struct Dkdv2Args {
     const bf16 *Q, *K, *V, *dO;
     const float *LSE, *Dl;
     bf16 *dK, *dV;
-    int Nq, Nk, H, G, n_ktiles, n_items;
+    int Nq, Nk, H, G, n_ktiles, n_items, nx;
     float scale, c_log2;
 };
 
@@ -341,10 +114,10 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv2_kernel(const Dkdv2Args args)
         bf16 *__restrict__ dK = ap->dK, *__restrict__ dV = ap->dV;
         const int Nq = ap->Nq, Nk = ap->Nk, H = ap->H, G = ap->G, n_ktiles = ap->n_ktiles, n_items = ap->n_items;
         const float scale = ap->scale, c_log2 = ap->c_log2;
-        const int item = persistent_item(r, (int)blockIdx.x, (int)gridDim.x);
+        const int item = persistent_item(r, (int)blockIdx.x, (int)gridDim.x, ap->nx);
         if (item >= n_items) break;  // workgroup-uniform; later rounds hold only larger items
         int head, ktile;
-        work_item_of(item, n_items, n_ktiles, head, ktile);
+        work_item_of(item, n_items, n_ktiles, ap->nx, head, ktile);
         const int Hk = H / G;
         const int qh0 = (head / Hk) * H + (head % Hk) * G;
 
@@ -612,7 +385,7 @@ template <int D, bool CAUSAL>
 __global__ __launch_bounds__(512, 1) void bwd_dkdv3_kernel(
     const bf16 *__restrict__ Q, const bf16 *__restrict__ K, const bf16 *__restrict__ V, const bf16 *__restrict__ dO,
     const float *__restrict__ LSE, const float *__restrict__ Dl, bf16 *__restrict__ dK, bf16 *__restrict__ dV, int Nq,
-    int Nk, int H, int G, int n_ktiles, float scale, float c_log2)
+    int Nk, int H, int G, int n_ktiles, float scale, float c_log2, int nx)
 {
     static_assert(D == 192 || D == 256, "wide-head dK/dV kernel");
     constexpr int NKS = D / 16;
@@ -627,7 +400,7 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv3_kernel(
     __shared__ __attribute__((aligned(16))) char p0_raw[PBUF], p1_raw[PBUF];
 
     int head, ktile;
-    work_item(blockIdx.x, n_ktiles, head, ktile);
+    work_item(blockIdx.x, n_ktiles, nx, head, ktile);
     const int Hk = H / G;
     const int qh0 = (head / Hk) * H + (head % Hk) * G;
 
@@ -846,7 +619,7 @@ template <int D, bool CAUSAL, bool FUSE_D = false>
 __global__ __launch_bounds__(64 * dq_waves<D>(), D >= 192 ? 1 : 8 / dq_waves<D>()) void bwd_dq_kernel(
     const bf16 *__restrict__ Q, const bf16 *__restrict__ K, const bf16 *__restrict__ V, const bf16 *__restrict__ dO,
     const float *__restrict__ LSE, float *__restrict__ Dl, bf16 *__restrict__ dQ, int Nq, int Nk, int H, int G,
-    int n_qtiles, float scale, float c_log2, const bf16 *__restrict__ O)
+    int n_qtiles, float scale, float c_log2, const bf16 *__restrict__ O, int nx)
 {
     constexpr int NKS = D / 16;
     constexpr int NDB = D / 32;
@@ -854,7 +627,7 @@ __global__ __launch_bounds__(64 * dq_waves<D>(), D >= 192 ? 1 : 8 / dq_waves<D>(
     __shared__ __attribute__((aligned(16))) char k0_raw[TILE], k1_raw[TILE], v0_raw[TILE], v1_raw[TILE];
 
     int head, t_in;
-    work_item(blockIdx.x, n_qtiles, head, t_in);
+    work_item(blockIdx.x, n_qtiles, nx, head, t_in);
     const int qtile = CAUSAL ? (n_qtiles - 1 - t_in) : t_in;
 
     const int tid = threadIdx.x;
@@ -1222,11 +995,11 @@ hipError_t launch_dkdv2_t(const BwdArgs &a)
     if (n_items == 0) return hipSuccess;
     // one workgroup per CU fits (LDS); with more items than CUs and heads spread evenly over the
     // XCDs, one persistent workgroup per CU takes them in rounds
-    const bool persistent = n_items > kPersistentWGs && (a.B * a.Hk) % 8 == 0;
-    const long long G = persistent ? kPersistentWGs : n_items;
+    const long long P = persistent_grid(n_items, (long long)a.B * a.Hk, a.dev.cus, a.dev.nx);
+    const long long G = P > 0 ? P : n_items;
     const Dkdv2Args args{(const bf16 *)a.q, (const bf16 *)a.k, (const bf16 *)a.v, (const bf16 *)a.dout, a.lse,
                          (const float *)a.delta, (bf16 *)a.dk, (bf16 *)a.dv, a.Nq, a.Nk, a.H, a.H / a.Hk, n_ktiles,
-                         (int)n_items, a.scale, a.scale * kLog2e};
+                         (int)n_items, a.dev.nx, a.scale, a.scale * kLog2e};
     hipLaunchKernelGGL((bwd_dkdv2_kernel<D, CAUSAL>), dim3((unsigned)G), dim3(512), 0, (hipStream_t)a.stream, args);
     return hipGetLastError();
 }
@@ -1239,19 +1012,8 @@ hipError_t launch_dkdv3_t(const BwdArgs &a)
     if (G == 0) return hipSuccess;
     hipLaunchKernelGGL((bwd_dkdv3_kernel<D, CAUSAL>), dim3((unsigned)G), dim3(512), 0, (hipStream_t)a.stream,
                        (const bf16 *)a.q, (const bf16 *)a.k, (const bf16 *)a.v, (const bf16 *)a.dout, a.lse,
-                       (const float *)a.delta, (bf16 *)a.dk, (bf16 *)a.dv, a.Nq, a.Nk, a.H, a.H / a.Hk, n_ktiles, a.scale, a.scale * kLog2e);
-    return hipGetLastError();
-}
-
-template <int D, bool CAUSAL>
-hipError_t launch_dkdv_t(const BwdArgs &a)
-{
-    const int n_ktiles = (a.Nk + kv_bn<D>() - 1) / kv_bn<D>();
-    const long long G = (long long)a.B * a.Hk * n_ktiles;
-    if (G == 0) return hipSuccess;
-    hipLaunchKernelGGL((bwd_dkdv_kernel<D, CAUSAL>), dim3((unsigned)G), dim3(kThreads), 0, (hipStream_t)a.stream,
-                       (const bf16 *)a.q, (const bf16 *)a.k, (const bf16 *)a.v, (const bf16 *)a.dout, a.lse,
-                       (const float *)a.delta, (bf16 *)a.dk, (bf16 *)a.dv, a.Nq, a.Nk, a.H, a.H / a.Hk, n_ktiles, a.scale, a.scale * kLog2e);
+                       (const float *)a.delta, (bf16 *)a.dk, (bf16 *)a.dv, a.Nq, a.Nk, a.H, a.H / a.Hk, n_ktiles, a.scale, a.scale * kLog2e,
+                       a.dev.nx);
     return hipGetLastError();
 }
 
@@ -1264,7 +1026,7 @@ hipError_t launch_dq_t(const BwdArgs &a)
     hipLaunchKernelGGL((bwd_dq_kernel<D, CAUSAL, FUSE_D>), dim3((unsigned)G), dim3(64 * dq_waves<D>()), 0, (hipStream_t)a.stream,
                        (const bf16 *)a.q, (const bf16 *)a.k, (const bf16 *)a.v, (const bf16 *)a.dout, a.lse,
                        a.delta, (bf16 *)a.dq, a.Nq, a.Nk, a.H, a.H / a.Hk, n_qtiles, a.scale, a.scale * kLog2e,
-                       (const bf16 *)a.o);
+                       (const bf16 *)a.o, a.dev.nx);
     return hipGetLastError();
 }
 

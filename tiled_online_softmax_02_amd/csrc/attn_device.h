@@ -18,6 +18,8 @@
 
 #include <hip/hip_runtime.h>
 #include <type_traits>
+
+#include "attn_sched.h"
 #include <stdint.h>
 
 namespace attn {
@@ -105,52 +107,11 @@ __device__ __forceinline__ void static_for(F &&f)
     }
 }
 
-// Workgroups are dispatched round-robin over the 8 XCDs of the chip, each with
-// its own L2.  Map dispatch index g to a work id so that every XCD receives a
-// contiguous range of work ids (work that shares K/V then shares an L2).
-__device__ __forceinline__ int xcd_remap(int g, int G)
+// Work item of workgroup g in a grid of exactly n_heads * n_tiles workgroups, one item each, on a
+// device of nx XCDs (the maps themselves are in attn_sched.h).
+__device__ __forceinline__ void work_item(int g, int n_tiles, int nx, int &head, int &t)
 {
-    constexpr int NX = 8;
-    const int per = G / NX, rem = G % NX;
-    const int x = g % NX, i = g / NX;
-    return x * per + (x < rem ? x : rem) + i;
-}
-
-// Work item of workgroup g when the grid holds n_heads * n_tiles workgroups: a head and
-// the position t of its tile in issue order (t = 0 goes out first).  When n_heads is a
-// multiple of the 8 XCDs, items go out position-major (position 0 of every head, then
-// position 1, ...): dispatch is then longest-first over the whole grid when position 0
-// is the largest tile, and head h always lands on XCD h % 8, so that its K and V stay in
-// one L2.  Otherwise every XCD takes a contiguous head-major range of items.
-__device__ __forceinline__ void work_item_of(int g, int G, int n_tiles, int &head, int &t)
-{
-    const int n_heads = G / n_tiles;
-    if ((n_heads & 7) == 0) {
-        t = g / n_heads;
-        head = g - t * n_heads;
-    } else {
-        const int id = xcd_remap(g, G);
-        head = id / n_tiles;
-        t = id - head * n_tiles;
-    }
-}
-
-// The same for a grid of exactly n_heads * n_tiles workgroups, one item each.
-__device__ __forceinline__ void work_item(int g, int n_tiles, int &head, int &t)
-{
-    work_item_of(g, (int)gridDim.x, n_tiles, head, t);
-}
-
-// Item that workgroup g of a persistent grid of P workgroups takes in round r, when items are in
-// longest-first order and round r covers items r P .. r P + P - 1.  In odd rounds the order is
-// reversed within each XCD (g = x + 8 c takes x + 8 (P/8 - 1 - c)), so a workgroup that had one
-// of the longest items of a round gets one of the shortest of the next; item j keeps
-// j % 8 == g % 8, so a head stays on the XCD it started on.  P is a multiple of 8 when it is
-// below the item count (with one round, the item is g).
-__device__ __forceinline__ int persistent_item(int r, int g, int P)
-{
-    if ((r & 1) == 0 || (P & 7) != 0) return r * P + g;
-    return r * P + (g & 7) + 8 * (P / 8 - 1 - (g >> 3));
+    work_item_of(g, (int)gridDim.x, n_tiles, nx, head, t);
 }
 
 }  // namespace attn

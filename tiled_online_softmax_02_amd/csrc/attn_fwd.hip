@@ -68,7 +68,7 @@ __global__ __launch_bounds__(64 * fwd_waves<D>(), fwd_min_blocks<D>()) void fwd_
                                                           const bf16 *__restrict__ V, bf16 *__restrict__ O,
                                                           float *__restrict__ LSE, int Nq, int Nk, int H, int G, int n_qtiles,
                                                           float scale, float c_log2, int n_splits, int split_blocks,
-                                                          float *__restrict__ OP, float *__restrict__ LP)
+                                                          float *__restrict__ OP, float *__restrict__ LP, int nx)
 {
     using L = FwdSmem<D>;
     constexpr int kFwdWaves = fwd_waves<D>();
@@ -85,7 +85,7 @@ __global__ __launch_bounds__(64 * fwd_waves<D>(), fwd_min_blocks<D>()) void fwd_
     // Split: one (query block, key piece) per workgroup.
     const int n_pos = SPLIT ? n_qtiles * n_splits : (CAUSAL ? (n_qtiles + 1) / 2 : n_qtiles);
     int head, pos;
-    work_item(blockIdx.x, n_pos, head, pos);
+    work_item(blockIdx.x, n_pos, nx, head, pos);
     const int split = SPLIT ? pos % n_splits : 0;
 
     const int tid = threadIdx.x;
@@ -430,7 +430,7 @@ hipError_t launch_fwd_t(const FwdArgs &a)
     const float c_log2 = a.scale * kLog2e;
     hipLaunchKernelGGL((fwd_kernel<D, CAUSAL, false>), dim3((unsigned)G), dim3(kThreads), 0, (hipStream_t)a.stream,
                        (const bf16 *)a.q, (const bf16 *)a.k, (const bf16 *)a.v, (bf16 *)a.o, a.lse, a.Nq, a.Nk,
-                       a.H, a.H / a.Hk, n_qtiles, a.scale, c_log2, 1, 0, (float *)nullptr, (float *)nullptr);
+                       a.H, a.H / a.Hk, n_qtiles, a.scale, c_log2, 1, 0, (float *)nullptr, (float *)nullptr, a.dev.nx);
     return hipGetLastError();
 }
 
@@ -480,7 +480,7 @@ hipError_t launch_fwd_split_t(const FwdArgs &a, int n_splits, float *op, float *
     const float c_log2 = a.scale * kLog2e;
     hipLaunchKernelGGL((fwd_kernel<D, CAUSAL, true>), dim3((unsigned)G), dim3(kThreads), 0, (hipStream_t)a.stream,
                        (const bf16 *)a.q, (const bf16 *)a.k, (const bf16 *)a.v, (bf16 *)a.o, a.lse, a.Nq, a.Nk,
-                       a.H, a.H / a.Hk, n_qtiles, a.scale, c_log2, n_splits, split_blocks, op, lp);
+                       a.H, a.H / a.Hk, n_qtiles, a.scale, c_log2, n_splits, split_blocks, op, lp, a.dev.nx);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     const long long rows = (long long)a.B * a.H * a.Nq;

@@ -85,7 +85,7 @@ template <int D, bool CAUSAL>
 __global__ __launch_bounds__(64 * f8_waves<D>(), 8 / f8_waves<D>()) void fwd_fp8_kernel(
     const uint8_t *__restrict__ Q, const uint8_t *__restrict__ K, const uint8_t *__restrict__ V,
     const float *__restrict__ DSQ, const float *__restrict__ DSK, const float *__restrict__ DSV, bf16 *__restrict__ O,
-    float *__restrict__ LSE, int Nq, int Nk, int H, int G, int n_qtiles, float scale)
+    float *__restrict__ LSE, int Nq, int Nk, int H, int G, int n_qtiles, float scale, int nx)
 {
     constexpr int NW = f8_waves<D>();
     constexpr int BM = f8_bm<D>();
@@ -97,7 +97,7 @@ __global__ __launch_bounds__(64 * f8_waves<D>(), 8 / f8_waves<D>()) void fwd_fp8
     // causal: workgroup `pos` takes query blocks T-1-pos and then pos (equal work per workgroup)
     const int n_pos = CAUSAL ? (n_qtiles + 1) / 2 : n_qtiles;
     int head, pos;
-    work_item(blockIdx.x, n_pos, head, pos);
+    work_item(blockIdx.x, n_pos, nx, head, pos);
 
     const int tid = threadIdx.x;
     const int lane = tid & 63, h = lane >> 5, c32 = lane & 31;
@@ -397,7 +397,7 @@ hipError_t launch_fwd_fp8_t(const Fp8FwdArgs &a)
     hipLaunchKernelGGL((fwd_fp8_kernel<D, CAUSAL>), dim3((unsigned)G), dim3(64 * f8_waves<D>()), 0,
                        (hipStream_t)a.stream, (const uint8_t *)a.q, (const uint8_t *)a.k, (const uint8_t *)a.v,
                        a.descale_q, a.descale_k, a.descale_v, (bf16 *)a.o, a.lse, a.Nq, a.Nk, a.H, a.H / a.Hk,
-                       n_qtiles, a.scale);
+                       n_qtiles, a.scale, a.dev.nx);
     return hipGetLastError();
 }
 

@@ -6,6 +6,12 @@
 
 namespace attn {
 
+// Shape of the device the launch goes to: compute units and XCDs (each XCD has its own L2; consecutive
+// workgroups are dispatched to the XCDs in turn).
+struct DeviceShape {
+    int cus, nx;
+};
+
 struct FwdArgs {
     const void *q, *k, *v;
     void *o;
@@ -13,6 +19,7 @@ struct FwdArgs {
     int B, H, Hk, Nq, Nk, d, causal;  // H query heads, Hk K/V heads; Nq query rows, Nk key rows per head
     float scale;
     void *stream;
+    DeviceShape dev;
 };
 
 struct BwdArgs {
@@ -23,6 +30,7 @@ struct BwdArgs {
     int B, H, Hk, Nq, Nk, d, causal;  // H query heads, Hk K/V heads; Nq query rows, Nk key rows per head
     float scale;
     void *stream;
+    DeviceShape dev;
 };
 
 // Forward pass on e4m3 inputs with per-head scales (d = 64 or 128).
@@ -34,6 +42,7 @@ struct Fp8FwdArgs {
     int B, H, Hk, Nq, Nk, d, causal;
     float scale;
     void *stream;
+    DeviceShape dev;
 };
 
 hipError_t launch_fwd(const FwdArgs &a);
