@@ -15,6 +15,7 @@ import torch
 
 import oracle
 import tiled_online_softmax_02_amd as A
+from parity_util import check_grad
 from tiled_online_softmax_02_amd.inputs import make_inputs, softmax_scale
 
 pytestmark = pytest.mark.gpu
@@ -54,8 +55,8 @@ def test_persistent_dkdv_grouped_heads_two_passes():
     N = 4096, causal: 512 items, two full passes (key blocks 0..15 of every head in the first,
     16..31 in the reversed second), each item looping over its G = 2 query heads.  One whole K/V
     head's dK and dV, and its query heads' dQ, against the oracle (for the K/V head: the sum over
-    its query heads, by the chain rule), each element within 2e-2 plus the bf16 rounding of the
-    output (2^-8 |x|, as for every grouped-head gradient); on every K/V head, sum_j dK_j = 0 and
+    its query heads, by the chain rule), each element within 2e-2, plus its own half bf16 ulp where
+    |x| >= 8 (as for every grouped-head gradient); on every K/V head, sum_j dK_j = 0 and
     sum_j dV_j = the sum of dO over the query rows of the heads that read it."""
     B, H, Hk, N, d, causal = 2, 16, 8, 4096, 128, True
     G = H // Hk
@@ -74,10 +75,9 @@ def test_persistent_dkdv_grouped_heads_two_passes():
     rdq, rdk, rdv, _ = oracle.attn_bwd_matmul(q64[b:b + 1, heads], kk, vv, do64[b:b + 1, heads], causal, scale)
     for name, got, ref in (("Q", f64(dq)[b, heads], rdq[0]), ("K", f64(dk)[b, hk], rdk[0].sum(axis=0)),
                            ("V", f64(dv)[b, hk], rdv[0].sum(axis=0))):
-        err = np.abs(got - ref)
-        excess = (err - (G_TOL + 2.0 ** -8 * np.abs(ref))).max()
-        note("  K/V head (%d,%d) d%s: max err %.3e, worst margin to the bound %.3e" % (b, hk, name, err.max(), -excess))
-        assert np.all(np.isfinite(got)) and excess <= 0.0, (name, excess)
+        ok, margin, report = check_grad(got, ref)
+        note("  K/V head (%d,%d) d%s: worst margin to the bound %.3e; %s" % (b, hk, name, margin, report))
+        assert ok, (name, margin)
     dk64, dv64 = f64(dk), f64(dv)
     sk = np.abs(dk64.sum(axis=2))
     sv = np.abs(dv64.sum(axis=2) - do64.reshape(B, Hk, G, N, d).sum(axis=(2, 3)))

@@ -4,7 +4,9 @@ c5g (grouped K/V heads, Hk = 4 under H = 16), c5u (2048 queries against 4096 key
 causal alignment) and c5d256 (head dimension 256), all forward + backward at B = 2, N = 4096:
 sampled forward rows of every head against the fp64 oracle, one whole K/V head's gradients against
 the oracle's backward (for grouped heads: the sum over the query heads that share the K/V head,
-by the chain rule; each element within 2e-2 plus the bf16 rounding of the output, 2^-8 |x|), and
+by the chain rule; each element within 2e-2, plus its own half bf16 ulp where |x| >= 8, where the
+output rounding alone can pass 2e-2; the error against the bf16-rounded reference is reported by
+magnitude band), and
 on every head the invariants sum_j dK_j = 0 and sum_j dV_j = the sum of dO over the query rows of
 the heads that read it (each row of P sums to 1; "digest_existing.txt", answer
 q02_flashattention, section 1).
@@ -15,6 +17,7 @@ import torch
 
 import oracle
 import tiled_online_softmax_02_amd as A
+from parity_util import check_grad
 from tiled_online_softmax_02_amd.inputs import WORKLOADS, workload_inputs
 
 pytestmark = pytest.mark.gpu
@@ -73,16 +76,14 @@ def test_widened_workload_full_size(wname):
     vv = np.repeat(v64[b:b + 1, hk:hk + 1], G, axis=1)
     note("  backward: oracle on K/V head (%d,%d), query heads %s" % (b, hk, heads))
     rdq, rdk, rdv, _ = oracle.attn_bwd_matmul(q64[b:b + 1, heads], kk, vv, do64[b:b + 1, heads], w.causal, w.scale)
-    # bound per element: the 2e-2 budget plus the bf16 rounding of the output itself (at most
-    # 2^-8 |x|); a K/V head shared by G query heads sums G contributions, its |dK|, |dV| grow by
-    # about sqrt(G), and at |x| >= 8 that rounding alone passes 2e-2
+    # a K/V head shared by G query heads sums G contributions: its |dK|, |dV| grow by about sqrt(G),
+    # and from |x| = 8 on the bf16 rounding of the output alone can pass 2e-2 (parity_util)
     for name, got, ref in (("Q", f64(dq)[b, heads], rdq[0]), ("K", f64(dk)[b, hk], rdk[0].sum(axis=0)),
                            ("V", f64(dv)[b, hk], rdv[0].sum(axis=0))):
-        err = np.abs(got - ref)
-        excess = (err - (G_TOL + 2.0 ** -8 * np.abs(ref))).max()
-        note("  backward head d%s: max err %.3e, max |d%s| %.2f, worst margin to the bound %.3e"
-             % (name, err.max(), name, np.abs(ref).max(), -excess))
-        assert np.all(np.isfinite(got)) and excess <= 0.0, (name, excess)
+        ok, margin, report = check_grad(got, ref)
+        note("  backward head d%s: max |d%s| %.2f, worst margin to the bound %.3e; %s"
+             % (name, name, np.abs(ref).max(), margin, report))
+        assert ok, (name, margin)
 
     # invariants on every K/V head
     dk64, dv64 = f64(dk), f64(dv)
