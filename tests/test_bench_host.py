@@ -69,3 +69,15 @@ def test_widened_workloads_flop():
     pairs = sum(2048 + i + 1 for i in range(2048))
     assert bench.workload_flop(w) == pytest.approx(3.5 * 4.0 * 2 * 16 * 128 * pairs)
     assert bench.workload_flop(WORKLOADS["c5d256"]) == bench.step_flop(2, 16, 4096, 256, True, True)
+
+
+def test_gpu_monitor_reports_why_it_has_no_samples():
+    """Without a readable GPU (this host) the clock and power monitor stays silent and says why."""
+    m = bench.GpuMonitor(period=0.01)
+    m.start()
+    m.stop()
+    w = m.window(0.0, 1e12)
+    if m.error is not None:
+        assert w["samples"] == 0 and w["gfx_clock_mhz_median"] is None and w["error"] == m.error
+    else:  # a GPU host: the sampled clocks are plausible
+        assert w["gfx_clock_mhz_median"] is None or 100 < w["gfx_clock_mhz_median"] < 5000
