@@ -69,7 +69,8 @@ enum attn_status {
     ATTN_ERR_BAD_ARG = 6,        /* causal is not 0 or 1, or num_splits is not in 1..256 */
     ATTN_ERR_ALIAS = 7,          /* an output overlaps an input or another output */
     ATTN_ERR_HIP = 8,            /* the HIP runtime reported an error at launch */
-    ATTN_ERR_WORKSPACE = 9       /* a workspace is smaller than the call needs */
+    ATTN_ERR_WORKSPACE = 9,      /* a workspace is smaller than the call needs */
+    ATTN_ERR_SCRATCH = 10        /* the call needs more than the library's static scratch buffer */
 };
 
 /* Forward pass.  Reads q, k, v; writes o [B,H,N,d] (bf16, rounded to nearest
@@ -100,6 +101,23 @@ int attn_fwd_qk(const void *q, const void *k, const void *v, void *o, float *lse
 int attn_fwd_splitkv(const void *q, const void *k, const void *v, void *o, float *lse,
                      int B, int H, int Hk, int Nq, int Nk, int d, int causal, float scale,
                      int num_splits, void *workspace, long long workspace_bytes, void *stream);
+
+/* For callers that cannot allocate device memory (code under HIP graph capture,
+ * tight serving loops, harnesses that forbid hipMalloc): attn_fwd_splitkv with
+ * its workspace taken from a static device buffer of ATTN_NOALLOC_SCRATCH_BYTES
+ * (16 MiB) that the library holds on every GPU it runs on until the process
+ * ends.  The call allocates nothing.  Same arguments, results (bitwise) and
+ * errors as attn_fwd_splitkv without workspace and workspace_bytes, plus
+ * ATTN_ERR_SCRATCH when attn_fwd_splitkv_workspace_size(B, H, Nq, d,
+ * num_splits) exceeds the buffer (checked on the host, nothing enqueued).
+ * Every call on a GPU uses that GPU's one buffer: calls that overlap in time
+ * on one GPU (different streams or host threads) race and must be ordered by
+ * the caller; calls on one stream are ordered.  The first call on a device
+ * looks up the buffer's device address once (a host query, no allocation). */
+#define ATTN_NOALLOC_SCRATCH_BYTES (16LL << 20)
+int attn_fwd_splitkv_noalloc(const void *q, const void *k, const void *v, void *o, float *lse,
+                             int B, int H, int Hk, int Nq, int Nk, int d, int causal, float scale,
+                             int num_splits, void *stream);
 
 /* Bytes of workspace attn_fwd_splitkv needs: num_splits * B * H * Nq * (d + 1) * 4;
  * -1 for invalid arguments. */

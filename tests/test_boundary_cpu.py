@@ -34,7 +34,7 @@ def declared_functions():
 
 def test_header_declares_the_expected_entry_points():
     assert declared_functions() == sorted([
-        "attn_fwd", "attn_fwd_qk", "attn_fwd_splitkv", "attn_fwd_splitkv_workspace_size",
+        "attn_fwd", "attn_fwd_qk", "attn_fwd_splitkv", "attn_fwd_splitkv_workspace_size", "attn_fwd_splitkv_noalloc",
         "attn_fwd_splitkv_default_splits", "attn_fwd_fp8", "attn_bwd", "attn_bwd_qk", "attn_bwd_preprocess", "attn_bwd_dkdv",
         "attn_bwd_dq", "attn_bwd_dq_delta", "attn_status_string", "attn_last_hip_error"])
 
@@ -45,7 +45,7 @@ def test_library_exports_every_declared_symbol(lib):
 
 
 def test_status_strings(lib):
-    for code in range(0, 10):
+    for code in range(0, 11):
         s = A.attn_status_string(code)
         assert s and s != "unknown status"
     assert A.attn_status_string(99) == "unknown status"
@@ -237,6 +237,41 @@ def test_splitkv_argument_checks(lib, kw, status):
 
 def test_splitkv_empty_is_a_no_op(lib):
     assert splitkv(lib, q=None, k=None, v=None, o=None, lse=None, ws=None, Nq=0) == A.ATTN_OK
+
+
+def splitkv_noalloc(lib, q=P[0], k=P[1], v=P[2], o=P[3], lse=P[4], B=1, H=2, Nq=4, Nk=512, d=64, causal=0,
+                    scale=0.125, ns=4):
+    return lib.attn_fwd_splitkv_noalloc(q, k, v, o, lse, B, H, H, Nq, Nk, d, causal, scale, ns, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(ns=0), A.ATTN_ERR_BAD_ARG),
+    (dict(ns=257), A.ATTN_ERR_BAD_ARG),
+    (dict(q=None), A.ATTN_ERR_NULLPTR),
+    (dict(lse=P[4] + 4), A.ATTN_ERR_MISALIGNED),
+    (dict(o=P[1] + 64), A.ATTN_ERR_ALIAS),
+    (dict(Nk=-5), A.ATTN_ERR_BAD_SHAPE),
+    (dict(d=80), A.ATTN_ERR_UNSUPPORTED_D),
+    (dict(scale=0.0), A.ATTN_ERR_BAD_SCALE),
+    (dict(causal=3), A.ATTN_ERR_BAD_ARG),
+    # pieces of 64 heads x 4096 rows x 129 floats x 4 splits: far beyond the 16 MiB buffer
+    (dict(H=64, Nq=4096, d=128), A.ATTN_ERR_SCRATCH),
+    # the smallest single-head size past the buffer fails the same way, before any pointer is looked at
+    (dict(q=None, H=1, Nq=8129, d=128, ns=4), A.ATTN_ERR_SCRATCH),
+])
+def test_splitkv_noalloc_argument_checks(lib, kw, status):
+    assert splitkv_noalloc(lib, **kw) == status
+
+
+def test_splitkv_noalloc_scratch_limit_matches_the_workspace_size(lib):
+    # the largest single-head problem that fits: ns * Nq * (d + 1) * 4 <= 16 MiB
+    assert A.attn_fwd_splitkv_workspace_size(1, 1, 8129, 128, 4) > A.ATTN_NOALLOC_SCRATCH_BYTES
+    assert A.attn_fwd_splitkv_workspace_size(1, 1, 8128, 128, 4) <= A.ATTN_NOALLOC_SCRATCH_BYTES
+
+
+def test_splitkv_noalloc_empty_is_a_no_op(lib):
+    assert splitkv_noalloc(lib, q=None, k=None, v=None, o=None, lse=None, Nq=0) == A.ATTN_OK
+    assert splitkv_noalloc(lib, q=None, k=None, v=None, o=None, lse=None, B=0) == A.ATTN_OK
 
 
 def fwd8(lib, q=P[0], k=P[1], v=P[2], dq=P[5], dk=P[6], dv=P[7], o=P[3], lse=P[4], B=1, H=2, Hk=1, Nq=64, Nk=80,

@@ -1,7 +1,7 @@
 """Python binding of libattn.so, the gfx950 attention library (C ABI in include/attn.h).
 
 The functions named like the C entry points (``attn_fwd``, ``attn_fwd_qk``,
-``attn_fwd_splitkv`` and its two size helpers, ``attn_fwd_fp8``, ``attn_bwd``, ``attn_bwd_qk``,
+``attn_fwd_splitkv`` and its two size helpers, ``attn_fwd_splitkv_noalloc``, ``attn_fwd_fp8``, ``attn_bwd``, ``attn_bwd_qk``,
 ``attn_bwd_preprocess``, ``attn_bwd_dkdv``, ``attn_bwd_dq``, ``attn_bwd_dq_delta``,
 ``attn_status_string``) only marshal arguments: tensors become device
 pointers, ``stream=None`` becomes the current PyTorch stream of the tensors'
@@ -37,6 +37,9 @@ ATTN_ERR_BAD_ARG = 6
 ATTN_ERR_ALIAS = 7
 ATTN_ERR_HIP = 8
 ATTN_ERR_WORKSPACE = 9
+ATTN_ERR_SCRATCH = 10
+# bytes of the static device buffer attn_fwd_splitkv_noalloc keeps its pieces in
+ATTN_NOALLOC_SCRATCH_BYTES = 16 << 20
 
 _lock = threading.Lock()
 _lib = None
@@ -50,6 +53,7 @@ _SIGNATURES = {
     "attn_fwd_qk": [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _F, _P],
     "attn_bwd_qk": [_P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _F, _P],
     "attn_fwd_splitkv": [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _F, _I, _P, ctypes.c_longlong, _P],
+    "attn_fwd_splitkv_noalloc": [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _F, _I, _P],
     "attn_fwd_fp8": [_P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _F, _P],
     "attn_bwd": [_P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _F, _P],
     "attn_bwd_preprocess": [_P, _P, _P, _I, _I, _I, _I, _P],
@@ -134,6 +138,11 @@ def attn_fwd_splitkv(q, k, v, o, lse, B, H, Hk, Nq, Nk, d, causal, scale, num_sp
                      stream=None) -> None:
     _call("attn_fwd_splitkv", _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, H, Hk, Nq, Nk, d, int(causal),
           float(scale), int(num_splits), _ptr(workspace), int(workspace_bytes), _stream(stream, q, o))
+
+
+def attn_fwd_splitkv_noalloc(q, k, v, o, lse, B, H, Hk, Nq, Nk, d, causal, scale, num_splits, stream=None) -> None:
+    _call("attn_fwd_splitkv_noalloc", _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, H, Hk, Nq, Nk, d,
+          int(causal), float(scale), int(num_splits), _stream(stream, q, o))
 
 
 def attn_fwd_splitkv_workspace_size(B, H, Nq, d, num_splits) -> int:

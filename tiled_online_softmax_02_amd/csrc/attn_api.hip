@@ -76,6 +76,11 @@ int hip_status(hipError_t e)
     return ATTN_ERR_HIP;
 }
 
+// Scratch of the no-allocation split-key forward: one static buffer per device, holding the pieces'
+// partial outputs and log-sum-exps between the two launches.  In host code the array's name is only a
+// stand-in; its device address on each device is looked up once (scratch_address) and used instead.
+static __device__ __align__(256) char scratch[ATTN_NOALLOC_SCRATCH_BYTES];
+
 // Compute units and XCDs of the device that `stream` belongs to (the current device for the null
 // stream), queried once per device and then cached.
 constexpr int kMaxDevices = 64;
@@ -103,6 +108,39 @@ int device_shape(void *stream, attn::DeviceShape *out)
     out->cus = cus;
     out->nx = nx;
     if (dev >= 0 && dev < kMaxDevices) g_shape[dev].store(((long long)cus << 32) | nx, std::memory_order_relaxed);
+    return ATTN_OK;
+}
+
+// Device address of `scratch` on the device that `stream` belongs to, looked up once per device with
+// that device current and then cached.
+std::atomic<void *> g_scratch[kMaxDevices];
+
+int scratch_address(void *stream, void **out)
+{
+    int dev = 0;
+    hipError_t e = stream ? hipStreamGetDevice((hipStream_t)stream, &dev) : hipGetDevice(&dev);
+    if (e != hipSuccess) return hip_status(e);
+    if (dev >= 0 && dev < kMaxDevices) {
+        void *p = g_scratch[dev].load(std::memory_order_acquire);
+        if (p) {
+            *out = p;
+            return ATTN_OK;
+        }
+    }
+    int cur = 0;
+    e = hipGetDevice(&cur);
+    if (e != hipSuccess) return hip_status(e);
+    if (cur != dev && (e = hipSetDevice(dev)) != hipSuccess) return hip_status(e);
+    void *p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (cur != dev) {
+        const hipError_t e2 = hipSetDevice(cur);
+        if (e == hipSuccess) e = e2;
+    }
+    if (e != hipSuccess) return hip_status(e);
+    if (!p) return hip_status(hipErrorInvalidSymbol);
+    if (dev >= 0 && dev < kMaxDevices) g_scratch[dev].store(p, std::memory_order_release);
+    *out = p;
     return ATTN_OK;
 }
 
@@ -163,6 +201,34 @@ int fwd_split_impl(const void *q, const void *k, const void *v, void *o, float *
     attn::FwdArgs a{q, k, v, o, lse, B, H, Hk, Nq, Nk, d, causal, scale, stream, {}};
     RETURN_IF(device_shape(stream, &a.dev));
     return hip_status(attn::launch_fwd_split(a, num_splits, workspace));
+}
+
+// The split-key forward with its workspace in the static scratch buffer: the same checks without the
+// workspace argument, and the workspace size against the buffer's.
+int fwd_split_noalloc_impl(const void *q, const void *k, const void *v, void *o, float *lse, int B, int H, int Hk,
+                           int Nq, int Nk, int d, int causal, float scale, int num_splits, void *stream)
+{
+    bool empty = false;
+    RETURN_IF(validate_common(B, H, Hk, Nq, Nk, d, causal, scale, &empty));
+    if (num_splits < 1 || num_splits > 256) return ATTN_ERR_BAD_ARG;
+    const long long qb = tensor_bytes(B, H, Nq, d), kb = tensor_bytes(B, Hk, Nk, d), lb = vector_bytes(B, H, Nq);
+    if (qb == 0) return ATTN_OK;  // no query rows: nothing to write
+    if (attn::fwd_split_grid_size(B, H, Nq, num_splits) >= (1LL << 31)) return ATTN_ERR_BAD_SHAPE;
+    const long long wb = attn::fwd_split_workspace_bytes(B, H, Nq, d, num_splits);
+    if (wb > ATTN_NOALLOC_SCRATCH_BYTES) return ATTN_ERR_SCRATCH;
+    const void *ptrs[] = {q, k, v, o, lse};
+    const long long sizes[] = {qb, kb, kb, qb, lb};
+    RETURN_IF(check_ptrs(ptrs, sizes, 5));
+    const Range in[] = {range_of(q, qb), range_of(k, kb), range_of(v, kb)};
+    const Range out[] = {range_of(o, qb), range_of(lse, lb)};
+    RETURN_IF(check_alias(in, 3, out, 2));
+    void *ws = nullptr;
+    RETURN_IF(scratch_address(stream, &ws));
+    attn::FwdArgs a{q, k, v, o, lse, B, H, Hk, Nq, Nk, d, causal, scale, stream, {}};
+    RETURN_IF(device_shape(stream, &a.dev));
+    // every piece of every row is written by the first launch before the merge reads it, so the buffer
+    // needs no clearing between calls
+    return hip_status(attn::launch_fwd_split(a, num_splits, ws));
 }
 
 // Per-head scale arrays of the 8-bit forward: non-null (unless empty) and 4-byte aligned.
@@ -251,6 +317,12 @@ int attn_fwd_splitkv(const void *q, const void *k, const void *v, void *o, float
 {
     return fwd_split_impl(q, k, v, o, lse, B, H, Hk, Nq, Nk, d, causal, scale, num_splits, workspace,
                           workspace_bytes, stream);
+}
+
+int attn_fwd_splitkv_noalloc(const void *q, const void *k, const void *v, void *o, float *lse, int B, int H, int Hk,
+                             int Nq, int Nk, int d, int causal, float scale, int num_splits, void *stream)
+{
+    return fwd_split_noalloc_impl(q, k, v, o, lse, B, H, Hk, Nq, Nk, d, causal, scale, num_splits, stream);
 }
 
 int attn_fwd_fp8(const void *q, const void *k, const void *v, const float *descale_q, const float *descale_k,
@@ -433,6 +505,7 @@ const char *attn_status_string(int status)
     case ATTN_ERR_ALIAS: return "an output overlaps an input or another output";
     case ATTN_ERR_HIP: return "the HIP runtime reported an error at launch";
     case ATTN_ERR_WORKSPACE: return "the workspace is smaller than the size the call needs";
+    case ATTN_ERR_SCRATCH: return "the call needs more than the library's static scratch buffer (16 MiB)";
     default: return "unknown status";
     }
 }
