@@ -30,8 +30,12 @@ int check_shape(int B, int H, int Hk, int Nq, int Nk, int d, bool *empty)
     if (B < 0 || H < 0 || Hk < 0 || Nq < 0 || Nk < 0) return ATTN_ERR_BAD_SHAPE;
     if (H > 0 && (Hk < 1 || H % Hk != 0)) return ATTN_ERR_BAD_SHAPE;
     if (d != 64 && d != 128 && d != 192 && d != 256) return ATTN_ERR_UNSUPPORTED_D;
-    const long long rows_q = (long long)B * H * Nq, rows_k = (long long)B * Hk * Nk;
-    if (rows_q > ((1LL << 62) / d) || rows_k > ((1LL << 62) / d)) return ATTN_ERR_BAD_SHAPE;
+    // B * H * N of three ints can pass 2^63: form the products with an overflow check
+    long long rows_q = 0, rows_k = 0;
+    if (__builtin_mul_overflow((long long)B * H, (long long)Nq, &rows_q) ||
+        __builtin_mul_overflow((long long)B * Hk, (long long)Nk, &rows_k))
+        return ATTN_ERR_BAD_SHAPE;
+    if (rows_q > ((1LL << 62) - 1) / d || rows_k > ((1LL << 62) - 1) / d) return ATTN_ERR_BAD_SHAPE;  // B*H*N*d < 2^62
     // per-head byte offsets, including the padding rows of the last tile, are 32-bit
     if (((long long)Nq + 256) * d * 2 > 0xFFFFFFFFLL || ((long long)Nk + 256) * d * 2 > 0xFFFFFFFFLL)
         return ATTN_ERR_BAD_SHAPE;
@@ -191,6 +195,7 @@ int fwd_split_impl(const void *q, const void *k, const void *v, void *o, float *
     if (qb == 0) return ATTN_OK;  // no query rows: nothing to write
     if (attn::fwd_split_grid_size(B, H, Nq, num_splits) >= (1LL << 31)) return ATTN_ERR_BAD_SHAPE;
     const long long wb = attn::fwd_split_workspace_bytes(B, H, Nq, d, num_splits);
+    if (wb < 0) return ATTN_ERR_BAD_SHAPE;
     const void *ptrs[] = {q, k, v, o, lse, workspace};
     const long long sizes[] = {qb, kb, kb, qb, lb, wb};
     RETURN_IF(check_ptrs(ptrs, sizes, 6));
@@ -215,6 +220,7 @@ int fwd_split_noalloc_impl(const void *q, const void *k, const void *v, void *o,
     if (qb == 0) return ATTN_OK;  // no query rows: nothing to write
     if (attn::fwd_split_grid_size(B, H, Nq, num_splits) >= (1LL << 31)) return ATTN_ERR_BAD_SHAPE;
     const long long wb = attn::fwd_split_workspace_bytes(B, H, Nq, d, num_splits);
+    if (wb < 0) return ATTN_ERR_BAD_SHAPE;
     if (wb > ATTN_NOALLOC_SCRATCH_BYTES) return ATTN_ERR_SCRATCH;
     const void *ptrs[] = {q, k, v, o, lse};
     const long long sizes[] = {qb, kb, kb, qb, lb};

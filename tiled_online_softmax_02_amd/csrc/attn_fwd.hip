@@ -519,7 +519,12 @@ hipError_t launch_fwd_split(const FwdArgs &a, int n_splits, void *workspace)
 
 long long fwd_split_workspace_bytes(int B, int H, int Nq, int d, int n_splits)
 {
-    return (long long)n_splits * B * H * Nq * (d + 1) * 4;
+    // n_splits * B * H * Nq * (d + 1) * 4 bytes; -1 where that reaches 2^62
+    long long r = 0;
+    if (__builtin_mul_overflow((long long)B * H, (long long)Nq, &r) ||
+        __builtin_mul_overflow(r, (long long)(d + 1) * 4 * n_splits, &r) || r >= (1LL << 62))
+        return -1;
+    return r;
 }
 
 long long fwd_split_grid_size(int B, int H, int Nq, int n_splits)
