@@ -74,13 +74,20 @@ enum attn_status {
 };
 
 /* Forward pass.  Reads q, k, v; writes o [B,H,N,d] (bf16, rounded to nearest
- * even) and lse [B,H,N] (fp32, natural log).  One kernel launch. */
+ * even) and lse [B,H,N] (fp32, natural log).  One kernel launch.
+ * Defines: O = softmax(scale Q K^T) V ("digest_existing.txt", answer
+ * q02_flashattention, section 1), computed blockwise with the running maximum
+ * and sum of section 2 and the rescaling of "GPU Programming and Kernel
+ * Optimization", item 58; lse is the log of that softmax's denominator. */
 int attn_fwd(const void *q, const void *k, const void *v, void *o, float *lse,
              int B, int H, int N, int d, int causal, float scale, void *stream);
 
 /* Forward pass with H query heads and Hk K/V heads, Nq query rows and Nk
  * key/value rows per head (see the conventions above for grouped heads, the
- * causal alignment and rows that see no key).
+ * causal alignment and rows that see no key).  Defines: the same O and lse
+ * as attn_fwd, with the bottom-right causal alignment of "GPU Programming and
+ * Kernel Optimization", item 59, and the separate query and K/V head counts
+ * of the "FlashAttention v3 (Tri Dao et al.)" page, "Runtime parameters".
  * attn_fwd(..., H, N, ...) is attn_fwd_qk(..., H, H, N, N, ...). */
 int attn_fwd_qk(const void *q, const void *k, const void *v, void *o, float *lse,
                 int B, int H, int Hk, int Nq, int Nk, int d, int causal, float scale, void *stream);
@@ -119,13 +126,18 @@ int attn_fwd_splitkv_noalloc(const void *q, const void *k, const void *v, void *
                              int B, int H, int Hk, int Nq, int Nk, int d, int causal, float scale,
                              int num_splits, void *stream);
 
-/* Bytes of workspace attn_fwd_splitkv needs: num_splits * B * H * Nq * (d + 1) * 4;
- * -1 for invalid arguments. */
+/* Bytes of workspace attn_fwd_splitkv needs: num_splits * B * H * Nq * (d + 1) * 4
+ * (one fp32 output row and one lse per piece and query row, the partial results
+ * that "GPU Programming and Kernel Optimization", item 59, combines in a second
+ * kernel); -1 for invalid arguments or a size of 2^62 bytes or more. */
 long long attn_fwd_splitkv_workspace_size(int B, int H, int Nq, int d, int num_splits);
 
 /* A number of pieces that gives the GPU about one workgroup per compute unit
  * while keeping at least two 64-key blocks per piece; 1 when splitting does
- * not help or the arguments are invalid. */
+ * not help or the arguments are invalid.  (A launch heuristic: the pages say
+ * only that small-query attention is split across thread blocks, "GPU
+ * Programming and Kernel Optimization", item 59, and that too few blocks leave
+ * the GPU underused.) */
 int attn_fwd_splitkv_default_splits(int B, int H, int Nq, int Nk, int d);
 
 /* Forward pass on 8-bit inputs ("FlashAttention v3 (Tri Dao et al.)",
@@ -149,8 +161,13 @@ int attn_fwd_fp8(const void *q, const void *k, const void *v,
                  void *o, float *lse, int B, int H, int Hk, int Nq, int Nk, int d, int causal,
                  float scale, void *stream);
 
-/* Backward pass: enqueues attn_bwd_dq_delta then attn_bwd_dkdv (two kernel
- * launches) on `stream`; the results are bitwise those of attn_bwd_preprocess,
+/* Backward pass: the gradients of attn_fwd's O with respect to q, k and v
+ * given dout = dL/dO, regenerating P from q, k and the saved lse instead of
+ * storing it ("GPU Programming and Kernel Optimization", item 58); the
+ * derivative itself is the chain rule of the definition in
+ * "digest_existing.txt", answer q02_flashattention, section 1 (the pages print
+ * no backward formula).  Enqueues attn_bwd_dq_delta then attn_bwd_dkdv (two
+ * kernel launches) on `stream`; the results are bitwise those of attn_bwd_preprocess,
  * attn_bwd_dkdv and attn_bwd_dq run in that order.  Reads q, k, v, o, dout and
  * the lse written by attn_fwd with the same q, k, v, causal and scale; writes
  * dq, dk, dv [B,H,N,d] (bf16) and delta [B,H,N] (fp32), a caller-owned
@@ -160,7 +177,10 @@ int attn_bwd(const void *q, const void *k, const void *v, const void *o, const v
              int B, int H, int N, int d, int causal, float scale, void *stream);
 
 /* Backward pass with H query heads and Hk K/V heads, Nq query rows and Nk
- * key/value rows per head; the same kernels as attn_bwd (the dK/dV
+ * key/value rows per head (the gradients of attn_fwd_qk; the alignment of
+ * "GPU Programming and Kernel Optimization", item 59, and the head counts of
+ * the "FlashAttention v3 (Tri Dao et al.)" page, "Runtime parameters"); the
+ * same kernels as attn_bwd (the dK/dV
  * kernel loops over the H / Hk query heads of each K/V head).  delta is
  * [B, H, Nq].  With Nq = 0 it writes dk = dv = 0; with Nk = 0 it writes dq = 0. */
 int attn_bwd_qk(const void *q, const void *k, const void *v, const void *o, const void *dout,
@@ -171,20 +191,25 @@ int attn_bwd_qk(const void *q, const void *k, const void *v, const void *o, cons
  * that each kernel can be enqueued and timed on its own. */
 
 /* Backward step 1: delta[i] = sum_c dout[i][c] * o[i][c] (fp32 products and
- * sums of the bf16 inputs).  Memory-bound; one kernel launch. */
+ * sums of the bf16 inputs).  Memory-bound; one kernel launch.  D_i is the
+ * softmax chain rule's sum_j P_ij dP_ij, which equals <dO_i, O_i> because
+ * O_i = sum_j P_ij v_j (section 1 of the digest's q02 answer). */
 int attn_bwd_preprocess(const void *o, const void *dout, float *delta,
                         int B, int H, int N, int d, void *stream);
 
-/* Backward step 2: for every key block, loops over the query blocks that see
- * it, regenerates P = exp(scale * Q K^T - lse) and accumulates
+/* Backward step 2 (P regenerated from the saved statistics, "GPU Programming
+ * and Kernel Optimization", item 58): for every key block, loops over the
+ * query blocks that see it, regenerates P = exp(scale * Q K^T - lse) and
+ * accumulates
  * dv = P^T dout and dk = scale * dS^T q with dS = P * (dout V^T - delta).
  * Writes dk and dv; one kernel launch. */
 int attn_bwd_dkdv(const void *q, const void *k, const void *v, const void *dout,
                   const float *lse, const float *delta, void *dk, void *dv,
                   int B, int H, int N, int d, int causal, float scale, void *stream);
 
-/* Backward step 3: for every query block, loops over the key blocks it sees,
- * regenerates P and dS as above and accumulates dq = scale * dS k.  Writes dq;
+/* Backward step 3 (as step 2, item 58): for every query block, loops over the
+ * key blocks it sees, regenerates P and dS as above and accumulates
+ * dq = scale * dS k.  Writes dq;
  * one kernel launch.  No atomics: results are bitwise reproducible. */
 int attn_bwd_dq(const void *q, const void *k, const void *v, const void *dout,
                 const float *lse, const float *delta, void *dq,
@@ -201,11 +226,12 @@ int attn_bwd_dq_delta(const void *q, const void *k, const void *v, const void *o
                       const void *dout, const float *lse, float *delta, void *dq,
                       int B, int H, int N, int d, int causal, float scale, void *stream);
 
-/* Static, NUL-terminated description of a status code (never NULL). */
+/* Static, NUL-terminated description of a status code (never NULL).  Error
+ * reporting of this library; not an operation of the pages. */
 const char *attn_status_string(int status);
 
 /* The hipError_t value behind the last ATTN_ERR_HIP returned on the calling
- * thread (0 if none). */
+ * thread (0 if none).  Error reporting of this library, as above. */
 int attn_last_hip_error(void);
 
 #ifdef __cplusplus
