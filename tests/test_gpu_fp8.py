@@ -10,16 +10,21 @@ probabilities, so lse carries only the score error):
   + (eps_i + 2^-9) P_ij) |V_jc| + 2^-8 |O_ref[i,c]| + 1e-6.
   2^-4 is e4m3's relative half-spacing; 2^-10 its absolute half-spacing below 2^-6 in the
   kernel's units, where the largest probability of a row is at least 1 (so l >= 1/Pmax);
-  eps_i = 2 * 2^-10 * max_j scale * sum_k |q_ik k_jk| bounds the scores' summation error
-  (the 8-bit products of the matrix cores were measured to sum with at most 2^-12.3 of
-  sum |products|; 2^-10 leaves margin); 2^-9 P covers the fp32 accumulation of P V and
-  2^-8 |O| the bf16 rounding of the output.
+  eps_i = 2 * U_DOT * max_j scale * sum_k |q_ik k_jk| bounds the relative change of P_ij caused
+  by score errors of at most U_DOT * scale * sum_k |q_ik k_jk| each (a shift of every score by
+  at most delta moves each normalised probability by a factor within exp(+-2 delta)); 2^-9 P
+  covers the fp32 accumulation of P V and 2^-8 |O| the bf16 rounding of the output.
+  U_DOT is the accuracy of the matrix cores' 8-bit dot product relative to sum |products|.
+  The hardware documents at hand state no figure for it, so test_fp8_score_sum_accuracy
+  measures it through the C ABI (with one key per row, lse is that row's score) and requires
+  at most U_DOT / 2.
 * overall, statistical: rms(O - O_ref) <= 1.5 * rms of the predicted error, whose variance
   per element is sum_j (2^-4 P_ij)^2 / 3 * V_jc^2 + (2^-9 O_ref)^2 / 3 (rounding errors
   uniform within half a spacing).  This is what catches a wrong result in rows whose
   softmax is flat, where the rigorous bound exceeds |O| itself.
-* lse: |lse - lse_ref| <= eps_i + 1e-5 max(1, |lse_ref|); rows with no visible key must
-  give lse = -inf and O = 0.
+* lse: |lse - lse_ref| <= eps_i + 1e-5 max(1, |lse_ref|) (eps_i is twice the score error
+  bound, which is all lse can move by); rows with no visible key must give lse = -inf and
+  O = 0.
 """
 import numpy as np
 import pytest
@@ -31,6 +36,8 @@ from tiled_online_softmax_02_amd.inputs import WORKLOADS, make_fp8_inputs, softm
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda:0"
+# accuracy of the 8-bit dot products relative to sum |products| that the bound assumes
+U_DOT = 2.0 ** -10
 
 
 def note(msg):
@@ -72,7 +79,7 @@ def bound_rows(q_rows, rows, k, v, nq, causal, scale, o_ref):
     p[live] = np.exp(s[live] - m[live])
     p[live] /= p[live].sum(axis=1, keepdims=True)
     pmax = p.max(axis=1, keepdims=True)
-    eps = 2 * 2.0**-10 * np.where(vis, sabs, 0).max(axis=1, initial=0.0)
+    eps = 2 * U_DOT * np.where(vis, sabs, 0).max(axis=1, initial=0.0)
     w = np.maximum(2.0**-4 * p, 2.0**-10 * pmax) + (eps[:, None] + 2.0**-9) * p
     bound = w @ np.abs(v) + 2.0**-8 * np.abs(o_ref) + 1e-6
     var = ((2.0**-4 * p) ** 2 / 3) @ (v ** 2) + (2.0**-9 * o_ref) ** 2 / 3
@@ -184,3 +191,39 @@ def test_fp8_scales_enter_as_stated():
     inp3 = dict(inp, descale_q=inp["descale_q"] * 2, descale_k=inp["descale_k"] / 2)
     o3, l3 = gpu_fwd8(inp3, True, softmax_scale(d))
     assert np.array_equal(o3, o1) and np.array_equal(l3, l1)
+
+
+@pytest.mark.parametrize("d", [64, 128])
+def test_fp8_score_sum_accuracy(d):
+    """The bound's U_DOT, measured.  With one key, every row's softmax is that key alone and the
+    kernel's lse is the row's score scale * <q_i, k_0>, formed by the same 8-bit matrix-core
+    products and sums as every other score.  The exact score is an fp64 sum of products of
+    decoded codes: each product of two e4m3 values and the sum of up to 256 of them fit in
+    fp64's 53 bits (products span 2^-18 .. 2^17.6 with 8 significant bits), so it carries no
+    rounding.  Codes are drawn uniformly from all 254 finite e4m3 values (every exponent, both
+    signs, heavy cancellation) and, separately, as per-head scaled normal values.  The error,
+    relative to scale * sum_k |q_ik k_0k|, also holds the few fp32 roundings between the score
+    and lse (about 2^-22 of |score|)."""
+    g = np.random.default_rng(80 + d)
+    H, Nq = 4, 16384
+    finite = np.array([c for c in range(256) if (c & 0x7F) != 0x7F], dtype=np.uint8)
+    q8 = g.choice(finite, size=(1, H, Nq, d))
+    k8 = g.choice(finite, size=(1, H, 1, d))
+    v8 = g.choice(finite, size=(1, H, 1, d))
+    ones = torch.ones((1, H), dtype=torch.float32)
+    uniform = {"q8": torch.from_numpy(q8), "k8": torch.from_numpy(k8), "v8": torch.from_numpy(v8),
+               "descale_q": ones, "descale_k": ones, "descale_v": ones}
+    normal = make_fp8_inputs(1, H, Nq, d, nk=1, seed=81 + d)
+    scale = softmax_scale(d)
+    worst = 0.0
+    for what, inp in (("uniform codes", uniform), ("normal values", normal)):
+        _, lse = gpu_fwd8(inp, False, scale)
+        q, k = real(inp, "q"), real(inp, "k")
+        exact = scale * np.einsum("bhnd,bhd->bhn", q, k[:, :, 0])
+        mag = scale * np.einsum("bhnd,bhd->bhn", np.abs(q), np.abs(k[:, :, 0]))
+        assert np.all(np.isfinite(lse))
+        rel = np.abs(lse - exact) / np.maximum(mag, np.finfo(np.float64).tiny)
+        note("  d=%d %s: max |lse - score| / sum|products| = %.3e (2^%.2f) over %d rows"
+             % (d, what, rel.max(), np.log2(max(rel.max(), 2.0 ** -60)), rel.size))
+        worst = max(worst, float(rel.max()))
+    assert worst <= U_DOT / 2, worst

@@ -436,6 +436,33 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv3_kernel(
 #pragma unroll
     for (int i = 0; i < NDBH; ++i) acc[i] = zero16();
 
+    // The lane's byte offsets inside a swizzled Q / dO tile, computed once and kept opaque so that
+    // each LDS read is one register plus a constant (stage, 16-row group) in the instruction's
+    // offset field; otherwise the compiler rebuilds the swizzled addresses at every use.
+    // The swizzle changes only chunk bits below 2 * kAoN (bits 0..3 at d = 256, 0..2 at d = 192), so
+    // chunk 2 kst + h lies at ao[kst % kAoN] plus (kst / kAoN) * 2 kAoN chunks.
+    constexpr int kAoN = D == 192 ? 4 : 8;
+    int ao[kAoN];        // A operand of the first product: row c32, chunk 2 kst + h, kst < kAoN
+    int to[NDBH][2];     // transposed reads: rows 4 (G / 2) + s / 4 and + 8 of a 16-row group
+#pragma unroll
+    for (int kst = 0; kst < kAoN; ++kst) {
+        ao[kst] = swz_off<D>(c32, 2 * kst + h);
+        asm volatile("" : "+v"(ao[kst]));
+    }
+    auto a_off = [&](int kst) __attribute__((always_inline)) { return ao[kst % kAoN] + (kst / kAoN) * 32 * kAoN; };
+    {
+        const int G4 = lane >> 4, s16 = lane & 15;
+        const int tr = 4 * (G4 >> 1) + (s16 >> 2);
+#pragma unroll
+        for (int db = 0; db < NDBH; ++db) {
+            const int byte = 2 * (32 * (db0 + db) + 16 * (G4 & 1) + 4 * (s16 & 3));
+            to[db][0] = swz_off<D>(tr, byte >> 4) + (byte & 15);
+            to[db][1] = swz_off<D>(tr + 8, byte >> 4) + (byte & 15);
+            asm volatile("" : "+v"(to[db][0]));
+            asm volatile("" : "+v"(to[db][1]));
+        }
+    }
+
     const int q_start = CAUSAL ? (max(0, k0 - off) / BMQ) * BMQ : 0;
     const int nsteps = (Nq > q_start) ? (Nq - q_start + BMQ - 1) / BMQ : 0;
 
@@ -485,13 +512,6 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv3_kernel(
                     f32x16 sc = zero16();
                     constexpr int PF = 2;
                     bf16x8 fr[PF + 1];
-                    // LDS offsets: at d = 256 each is recomputed where it is used (the opaque copy keeps
-                    // the compiler from holding all of them, which spilled), at d = 192 they are kept
-                    auto a_off = [&](int kst) __attribute__((always_inline)) {
-                        int row = c32;
-                        if constexpr (D == 256) asm volatile("" : "+v"(row));
-                        return swz_off<D>(row, 2 * kst + h);
-                    };
                     static_for<0, PF>([&](auto F) __attribute__((always_inline)) {
                         constexpr int f = decltype(F)::value;
                         fr[f] = lds_read16(a_l, a_off(f));
@@ -541,9 +561,9 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv3_kernel(
                     // second product: dV^T += dO^T P or dK^T += Q^T dS over this wave's columns
                     static_for<0, 2 * NDBH>([&](auto C) __attribute__((always_inline)) {
                         constexpr int c = decltype(C)::value, t = c / NDBH, db = c % NDBH;
-                        int ln = lane;
-                        if constexpr (D == 256) asm volatile("" : "+v"(ln));
-                        acc[db] = mfma(lds_read_tr_rows_swz<D>(t_l, 16 * t, 32 * (db0 + db), ln), pb[t], acc[db]);
+                        const bf16x4 lo = lds_read_tr(t_l, to[db][0] + 16 * t * 2 * D);
+                        const bf16x4 hi = lds_read_tr(t_l, to[db][1] + 16 * t * 2 * D);
+                        acc[db] = mfma(__builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7), pb[t], acc[db]);
                         __builtin_amdgcn_sched_barrier(0);
                     });
                 }
@@ -638,8 +658,6 @@ __global__ __launch_bounds__(64 * dq_waves<D>(), D >= 192 ? 1 : 8 / dq_waves<D>(
     const int kvh = (head / H) * (H / G) + (head % H) / G;
     const size_t hoff_k = (size_t)kvh * (size_t)Nk * D;
     const __amdgpu_buffer_rsrc_t rq = make_rsrc(Q + hoff, (uint32_t)Nq * D * 2);
-    const __amdgpu_buffer_rsrc_t rk = make_rsrc(K + hoff_k, (uint32_t)Nk * D * 2);
-    const __amdgpu_buffer_rsrc_t rv = make_rsrc(V + hoff_k, (uint32_t)Nk * D * 2);
     const __amdgpu_buffer_rsrc_t rg = make_rsrc(dO + hoff, (uint32_t)Nq * D * 2);
     // Causal mask with bottom-right alignment: query i sees keys j <= i + off.
     const int off = Nk - Nq;
@@ -651,9 +669,8 @@ __global__ __launch_bounds__(64 * dq_waves<D>(), D >= 192 ? 1 : 8 / dq_waves<D>(
     const int qrow = qw0 + c32;
     const bool row_ok = qrow < Nq;
 
-    // d <= 128: dO is held negated, so that the dP product starts from D and yields D - dP;
-    // dS = P (dP - D) is then one multiply per element and dQ accumulates with the opposite sign
-    constexpr bool kNegDP = D <= 128;
+    // dO is held negated, so that the dP product starts from D and yields D - dP; dS = P (dP - D)
+    // is then one multiply per element and dQ accumulates with the opposite sign
     bf16x8 qf[NKS], gf[NKS];
     float dfused = 0.f;
     {
@@ -674,7 +691,7 @@ __global__ __launch_bounds__(64 * dq_waves<D>(), D >= 192 ? 1 : 8 / dq_waves<D>(
         for (int ks = 0; ks < NKS; ++ks) {
             qf[ks] = __builtin_bit_cast(bf16x8, buffer_load16(rq, (uint32_t)(qrow * D + 16 * ks + 8 * h) * 2u));
             const u32x4 graw = buffer_load16(rg, (uint32_t)(qrow * D + 16 * ks + 8 * h) * 2u);
-            gf[ks] = __builtin_bit_cast(bf16x8, graw ^ (kNegDP ? 0x80008000u : 0u));
+            gf[ks] = __builtin_bit_cast(bf16x8, graw ^ 0x80008000u);
             if constexpr (FUSE_D) {
                 const bf16x8 g = __builtin_bit_cast(bf16x8, graw);
                 a[ks] = 0.f;
@@ -713,14 +730,13 @@ __global__ __launch_bounds__(64 * dq_waves<D>(), D >= 192 ? 1 : 8 / dq_waves<D>(
 
     auto kst_l = [&](auto par) __attribute__((always_inline)) { return (lds_char *)(decltype(par)::value ? k1_raw : k0_raw); };
     auto vst_l = [&](auto par) __attribute__((always_inline)) { return (lds_char *)(decltype(par)::value ? v1_raw : v0_raw); };
-    // d <= 128: the lane's byte offsets inside a swizzled K/V tile are computed once and kept
-    // opaque, so that every LDS read of the loop is one register plus a constant in the
-    // instruction's offset field, and every direct load one register plus a buffer base moved by
-    // scalar arithmetic.
-    constexpr bool kFixedOffsets = D <= 128;
+    // The lane's byte offsets inside a swizzled K/V tile are computed once and kept opaque, so
+    // that every LDS read of the loop is one register plus a constant in the instruction's offset
+    // field, and every direct load one register plus a buffer base moved by scalar arithmetic;
+    // otherwise the compiler rebuilds the swizzled addresses at every use.
     constexpr int kLoadNI = kQBN * (D / 8) / 64 / NW;  // direct loads per wave and tile
     int ko[NKS], vo[NDB][2], go[kLoadNI];
-    if constexpr (kFixedOffsets) {
+    {
 #pragma unroll
         for (int kst = 0; kst < NKS; ++kst) {
             ko[kst] = swz_off<D>(c32, 2 * kst + h);
@@ -746,19 +762,14 @@ __global__ __launch_bounds__(64 * dq_waves<D>(), D >= 192 ? 1 : 8 / dq_waves<D>(
         }
     }
     auto load_blk = [&](int j, auto par) __attribute__((always_inline)) {
-        if constexpr (kFixedOffsets) {
-            // rows past Nk read as zeros
-            const int r0 = min(j * kQBN, Nk);
-            const __amdgpu_buffer_rsrc_t rkj = make_rsrc(K + hoff_k + (size_t)r0 * D, (uint32_t)(Nk - r0) * D * 2);
-            const __amdgpu_buffer_rsrc_t rvj = make_rsrc(V + hoff_k + (size_t)r0 * D, (uint32_t)(Nk - r0) * D * 2);
+        // rows past Nk read as zeros
+        const int r0 = min(j * kQBN, Nk);
+        const __amdgpu_buffer_rsrc_t rkj = make_rsrc(K + hoff_k + (size_t)r0 * D, (uint32_t)(Nk - r0) * D * 2);
+        const __amdgpu_buffer_rsrc_t rvj = make_rsrc(V + hoff_k + (size_t)r0 * D, (uint32_t)(Nk - r0) * D * 2);
 #pragma unroll
-            for (int i = 0; i < kLoadNI; ++i) buffer_load_lds16(rkj, kst_l(par) + 1024 * (w * kLoadNI + i), (uint32_t)go[i]);
+        for (int i = 0; i < kLoadNI; ++i) buffer_load_lds16(rkj, kst_l(par) + 1024 * (w * kLoadNI + i), (uint32_t)go[i]);
 #pragma unroll
-            for (int i = 0; i < kLoadNI; ++i) buffer_load_lds16(rvj, vst_l(par) + 1024 * (w * kLoadNI + i), (uint32_t)go[i]);
-        } else {
-            load_tile_lds<D, NW>(rk, kst_l(par), j * kQBN, w, lane);
-            load_tile_lds<D, NW>(rv, vst_l(par), j * kQBN, w, lane);
-        }
+        for (int i = 0; i < kLoadNI; ++i) buffer_load_lds16(rvj, vst_l(par) + 1024 * (w * kLoadNI + i), (uint32_t)go[i]);
     };
 
     using P0 = std::integral_constant<int, 0>;
@@ -767,20 +778,17 @@ __global__ __launch_bounds__(64 * dq_waves<D>(), D >= 192 ? 1 : 8 / dq_waves<D>(
     wait_vmem();
     __syncthreads();
 
-    // d <= 128: the wave works on key blocks [0, ja) and only loads and waits on [ja, nt) (causal:
-    // the blocks wholly above its rows); separate loops keep the block index out of the step.
-    // d = 192, 256: one loop with the test inside the step, which measured faster there.
-    constexpr bool kSplitLoops = D <= 128;
+    // The wave works on key blocks [0, ja) and only loads and waits on [ja, nt) (causal: the blocks
+    // wholly above its rows); separate loops keep the block index out of the step.
     const int last_key = qw0 + 31 + off;
-    const int ja_seen = (qw0 >= Nq) ? 0 : (!CAUSAL ? nt : (last_key < 0 ? 0 : min(nt, last_key / kQBN + 1)));
-    const int ja = kSplitLoops ? ja_seen : nt;
+    const int ja = (qw0 >= Nq) ? 0 : (!CAUSAL ? nt : (last_key < 0 ? 0 : min(nt, last_key / kQBN + 1)));
     auto step_idle = [&](int j, auto par) __attribute__((always_inline)) {
         using PN = std::integral_constant<int, 1 - decltype(par)::value>;
         load_blk(j + 1, PN{});
         wait_vmem();
         __syncthreads();
     };
-    // CH: an unmasked block of a d <= 128 kernel, run as chunks (below); otherwise the plain step
+    // CH: an unmasked block, run as chunks (below); otherwise the plain step
     auto step = [&](int j, auto par, auto CH) __attribute__((always_inline)) {
         using PN = std::integral_constant<int, 1 - decltype(par)::value>;
         load_blk(j + 1, PN{});  // past the last block: zeros into the free stage, never read
@@ -790,7 +798,7 @@ __global__ __launch_bounds__(64 * dq_waves<D>(), D >= 192 ? 1 : 8 / dq_waves<D>(
         // Only blocks that cross the diagonal or the end of the keys are masked: their masked
         // scores become -inf (P = 0) in a branch that the other blocks skip.
         const bool need_mask = (CAUSAL && (k0 + kQBN - 1 > qw0 + off)) || (k0 + kQBN > Nk);
-        // d <= 128, unmasked block: chunks of one matrix instruction and a slice of vector work,
+        // Unmasked block: chunks of one matrix instruction and a slice of vector work,
         // so that one wave's exponentials run under its own products.  LDS fragments are fetched
         // two chunks ahead; scheduling barriers keep each chunk whole.
         if constexpr (decltype(CH)::value) {
@@ -878,18 +886,16 @@ __global__ __launch_bounds__(64 * dq_waves<D>(), D >= 192 ? 1 : 8 / dq_waves<D>(
                 }
                 __builtin_amdgcn_sched_barrier(0);
             });
-        } else if (kSplitLoops || j < ja_seen) {
+        } else {
             f32x16 s[2] = {zero16(), zero16()};
-            f32x16 dp[2] = {zero16(), zero16()};  // dP, or D - dP (kNegDP)
-            if constexpr (kNegDP) {
+            f32x16 dp[2];  // D - dP
 #pragma unroll
-                for (int r = 0; r < 16; ++r) dp[0][r] = dp[1][r] = dval;
-            }
+            for (int r = 0; r < 16; ++r) dp[0][r] = dp[1][r] = dval;
 #pragma unroll
             for (int kst = 0; kst < NKS; ++kst) {
 #pragma unroll
                 for (int kb = 0; kb < 2; ++kb) {
-                    const int off = kFixedOffsets ? ko[kst] + 32 * kb * 2 * D : swz_off<D>(32 * kb + c32, 2 * kst + h);
+                    const int off = ko[kst] + 32 * kb * 2 * D;
                     s[kb] = mfma(lds_read16(ks, off), qf[kst], s[kb]);
                     dp[kb] = mfma(lds_read16(vs, off), gf[kst], dp[kb]);
                 }
@@ -910,7 +916,7 @@ __global__ __launch_bounds__(64 * dq_waves<D>(), D >= 192 ? 1 : 8 / dq_waves<D>(
 #pragma unroll
                 for (int r = 0; r < 16; ++r) {
                     const float p = fast_exp2(fmaf(s[kb][r], c_log2, -lse2));
-                    sb[2 * kb + (r >> 3)][r & 7] = kNegDP ? (bf16)(p * dp[kb][r]) : (bf16)(p * (dp[kb][r] - dval));
+                    sb[2 * kb + (r >> 3)][r & 7] = (bf16)(p * dp[kb][r]);
                 }
             }
             // dQ^T += K^T dS^T over 4 groups of 16 keys
@@ -918,15 +924,9 @@ __global__ __launch_bounds__(64 * dq_waves<D>(), D >= 192 ? 1 : 8 / dq_waves<D>(
             for (int t = 0; t < kQBN / 16; ++t) {
 #pragma unroll
                 for (int db = 0; db < NDB; ++db) {
-                    bf16x8 kt;
-                    if constexpr (kFixedOffsets) {
-                        const bf16x4 lo = lds_read_tr(ks, vo[db][0] + 16 * t * 2 * D);
-                        const bf16x4 hi = lds_read_tr(ks, vo[db][1] + 16 * t * 2 * D);
-                        kt = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-                    } else {
-                        kt = lds_read_tr_rows_swz<D>(ks, 16 * t, 32 * db, lane);
-                    }
-                    dq[db] = mfma(kt, sb[t], dq[db]);
+                    const bf16x4 lo = lds_read_tr(ks, vo[db][0] + 16 * t * 2 * D);
+                    const bf16x4 hi = lds_read_tr(ks, vo[db][1] + 16 * t * 2 * D);
+                    dq[db] = mfma(__builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7), sb[t], dq[db]);
                 }
             }
         }
@@ -934,13 +934,13 @@ __global__ __launch_bounds__(64 * dq_waves<D>(), D >= 192 ? 1 : 8 / dq_waves<D>(
         __syncthreads();
     };
 
-    // stage parity of key block j is j & 1.  d <= 128: blocks [0, jm) need no mask and run as
-    // chunks; [jm, ja) cross the diagonal or the end of the keys (the need for a mask only grows
-    // with j).  Separate loops keep the two bodies' registers apart.
-    using CHK = std::integral_constant<bool, kFixedOffsets>;
+    // stage parity of key block j is j & 1.  Blocks [0, jm) need no mask and run as chunks;
+    // [jm, ja) cross the diagonal or the end of the keys (the need for a mask only grows with j).
+    // Separate loops keep the two bodies' registers apart.
+    using CHK = std::true_type;
     using PLAIN = std::false_type;
     const int jm_c = CAUSAL ? (qw0 + off - (kQBN - 1) >= 0 ? (qw0 + off - (kQBN - 1)) / kQBN + 1 : 0) : ja;
-    const int jm = kFixedOffsets ? max(0, min(ja, min(jm_c, Nk / kQBN))) : 0;
+    const int jm = max(0, min(ja, min(jm_c, Nk / kQBN)));
     int j = 0;
     for (; j + 1 < jm; j += 2) {
         step(j, P0{}, CHK{});
@@ -968,7 +968,7 @@ __global__ __launch_bounds__(64 * dq_waves<D>(), D >= 192 ? 1 : 8 / dq_waves<D>(
             for (int g = 0; g < 4; ++g) {
                 bf16x4 v4;
 #pragma unroll
-                for (int u = 0; u < 4; ++u) v4[u] = (bf16)(dq[db][4 * g + u] * (kNegDP ? -scale : scale));
+                for (int u = 0; u < 4; ++u) v4[u] = (bf16)(dq[db][4 * g + u] * -scale);
                 *(bf16x4 *)(qrow_p + 32 * db + 8 * g + 4 * h) = v4;
             }
         }

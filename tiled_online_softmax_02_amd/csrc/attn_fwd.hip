@@ -96,21 +96,19 @@ __global__ __launch_bounds__(64 * fwd_waves<D>(), fwd_min_blocks<D>()) void fwd_
     const int kvh = (head / H) * (H / G) + (head % H) / G;
     const size_t hoff_k = (size_t)kvh * (size_t)Nk * D;
     const __amdgpu_buffer_rsrc_t rq = make_rsrc(Q + hoff, (uint32_t)Nq * D * 2);
-    const __amdgpu_buffer_rsrc_t rk = make_rsrc(K + hoff_k, (uint32_t)Nk * D * 2);
-    const __amdgpu_buffer_rsrc_t rv = make_rsrc(V + hoff_k, (uint32_t)Nk * D * 2);
     // Causal mask with bottom-right alignment: query i sees keys j <= i + off.
     const int off = Nk - Nq;
 
-    // d <= 128: the lane's byte offsets inside a swizzled K/V tile are computed once and kept
-    // opaque, so that every LDS read of the loop is one register plus a constant (stage and row
-    // block) in the instruction's offset field, and every direct load one register plus a buffer
-    // base moved by scalar arithmetic; otherwise the compiler rebuilt them with vector adds.
-    constexpr bool kFixedOffsets = D <= 128;
+    // The lane's byte offsets inside a swizzled K/V tile are computed once and kept opaque, so
+    // that every LDS read of the loop is one register plus a constant (stage and row block) in the
+    // instruction's offset field, and every direct load one register plus a buffer base moved by
+    // scalar arithmetic; otherwise the compiler rebuilds the swizzled addresses with vector
+    // arithmetic at every use (at d = 256 about 20 instructions per transposed V read).
     constexpr int kLoadNI = kFwdBN * (D / 8) / 64 / kFwdWaves;  // direct loads per wave and tile
     int ko[NKS];         // K fragment of reduction step kst: row c32, chunk 2 kst + h
     int vo[NDB][2];      // V^T fragment of column block db: rows r and r + 8 of a 16-row block
     int go[kLoadNI];     // source of direct load i within a tile
-    if constexpr (kFixedOffsets) {
+    {
 #pragma unroll
         for (int kst = 0; kst < NKS; ++kst) {
             ko[kst] = swz_off<D>(c32, 2 * kst + h);
@@ -168,18 +166,14 @@ __global__ __launch_bounds__(64 * fwd_waves<D>(), fwd_min_blocks<D>()) void fwd_
         auto kstage = [&](auto par) __attribute__((always_inline)) { return (lds_char *)(decltype(par)::value ? k1_raw : k0_raw); };
         auto vstage = [&](auto par) __attribute__((always_inline)) { return (lds_char *)(decltype(par)::value ? v1_raw : v0_raw); };
         // key rows [j * BN, j * BN + BN) of K or V into a stage; rows past Nk read as zeros
-        auto load_blk = [&](const bf16 *src, __amdgpu_buffer_rsrc_t r, lds_char *tile, int j) __attribute__((always_inline)) {
-            if constexpr (kFixedOffsets) {
-                const int r0 = min(j * kFwdBN, Nk);
-                const __amdgpu_buffer_rsrc_t rj = make_rsrc(src + hoff_k + (size_t)r0 * D, (uint32_t)(Nk - r0) * D * 2);
+        auto load_blk = [&](const bf16 *src, lds_char *tile, int j) __attribute__((always_inline)) {
+            const int r0 = min(j * kFwdBN, Nk);
+            const __amdgpu_buffer_rsrc_t rj = make_rsrc(src + hoff_k + (size_t)r0 * D, (uint32_t)(Nk - r0) * D * 2);
 #pragma unroll
-                for (int i = 0; i < kLoadNI; ++i) buffer_load_lds16(rj, tile + 1024 * (w * kLoadNI + i), (uint32_t)go[i]);
-            } else {
-                load_tile_lds<D, kFwdWaves>(r, tile, j * kFwdBN, w, lane);
-            }
+            for (int i = 0; i < kLoadNI; ++i) buffer_load_lds16(rj, tile + 1024 * (w * kLoadNI + i), (uint32_t)go[i]);
         };
-        auto load_k = [&](int j, auto par) __attribute__((always_inline)) { load_blk(K, rk, kstage(par), j); };
-        auto load_v = [&](int j, auto par) __attribute__((always_inline)) { load_blk(V, rv, vstage(par), j); };
+        auto load_k = [&](int j, auto par) __attribute__((always_inline)) { load_blk(K, kstage(par), j); };
+        auto load_v = [&](int j, auto par) __attribute__((always_inline)) { load_blk(V, vstage(par), j); };
 
         // S^T block (64 keys x 32 queries) of key block j
         auto scores = [&](auto par, f32x16 *s) __attribute__((always_inline)) {
@@ -285,27 +279,15 @@ __global__ __launch_bounds__(64 * fwd_waves<D>(), fwd_min_blocks<D>()) void fwd_
                 constexpr auto is_s = [](int c) { return c < NS / 2 || (c >= NS / 2 + NPV / 2 && c < NS + NPV / 2); };
                 auto fetch = [&](auto C) __attribute__((always_inline)) {
                     constexpr int c = decltype(C)::value;
-                    if constexpr (is_s(c) && kFixedOffsets) {
+                    if constexpr (is_s(c)) {
                         constexpr int s = c < NS / 2 ? c : c - NPV / 2;
                         return lds_read16(ks, ko[s >> 1] + 32 * (s & 1) * 2 * D);
-                    } else if constexpr (kFixedOffsets) {
+                    } else {
                         constexpr int p = c < NS / 2 + NPV / 2 ? c - NS / 2 : c - NS;
                         constexpr int rb = 16 * (p / NDB) * 2 * D;
                         const bf16x4 lo = lds_read_tr(vs, vo[p % NDB][0] + rb);
                         const bf16x4 hi = lds_read_tr(vs, vo[p % NDB][1] + rb);
                         return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-                    } else if constexpr (is_s(c)) {
-                        constexpr int s = c < NS / 2 ? c : c - NPV / 2;
-                        // at d = 256 the offsets are recomputed where they are used (an opaque copy of
-                        // the row keeps the compiler from holding all of them, which spilled)
-                        int row = c32;
-                        if constexpr (D == 256) asm volatile("" : "+v"(row));
-                        return lds_read16(ks, swz_off<D>(32 * (s & 1) + row, 2 * (s >> 1) + h));
-                    } else {
-                        constexpr int p = c < NS / 2 + NPV / 2 ? c - NS / 2 : c - NS;
-                        int ln = lane;
-                        if constexpr (D == 256) asm volatile("" : "+v"(ln));
-                        return lds_read_tr_rows_swz<D>(vs, 16 * (p / NDB), 32 * (p % NDB), ln);
                     }
                 };
                 nxt[0] = zero16();
