@@ -165,10 +165,13 @@ __global__ __launch_bounds__(64 * fwd_waves<D>(), fwd_min_blocks<D>()) void fwd_
         // stage of block j is j & 1; callers pass the parity as a compile-time constant
         auto kstage = [&](auto par) __attribute__((always_inline)) { return (lds_char *)(decltype(par)::value ? k1_raw : k0_raw); };
         auto vstage = [&](auto par) __attribute__((always_inline)) { return (lds_char *)(decltype(par)::value ? v1_raw : v0_raw); };
-        // key rows [j * BN, j * BN + BN) of K or V into a stage; rows past Nk read as zeros
+        // key rows [j * BN, j * BN + BN) of K or V into a stage.  Rows past the last block this
+        // workgroup needs read as zeros without touching memory (the pipeline's loads one and two
+        // blocks past the end), as do rows past Nk.
+        const int kv_lim = min(Nk, je * kFwdBN);
         auto load_blk = [&](const bf16 *src, lds_char *tile, int j) __attribute__((always_inline)) {
-            const int r0 = min(j * kFwdBN, Nk);
-            const __amdgpu_buffer_rsrc_t rj = make_rsrc(src + hoff_k + (size_t)r0 * D, (uint32_t)(Nk - r0) * D * 2);
+            const int r0 = min(j * kFwdBN, kv_lim);
+            const __amdgpu_buffer_rsrc_t rj = make_rsrc(src + hoff_k + (size_t)r0 * D, (uint32_t)(kv_lim - r0) * D * 2);
 #pragma unroll
             for (int i = 0; i < kLoadNI; ++i) buffer_load_lds16(rj, tile + 1024 * (w * kLoadNI + i), (uint32_t)go[i]);
         };
@@ -234,7 +237,9 @@ __global__ __launch_bounds__(64 * fwd_waves<D>(), fwd_min_blocks<D>()) void fwd_
             __syncthreads();
         };
         // One pipeline step on key block j: scores of j are in `cur`, scores of j+1 go to `nxt`.
-        auto step = [&](int j, auto par, f32x16 *cur, f32x16 *nxt) __attribute__((always_inline)) {
+        // LAST: the wave's last block; the scores of j+1 are not needed and are not computed.
+        auto step = [&](int j, auto par, f32x16 *cur, f32x16 *nxt, auto LAST) __attribute__((always_inline)) {
+            constexpr bool last = decltype(LAST)::value;
             using PN = std::integral_constant<int, 1 - decltype(par)::value>;  // parity of j + 1
             {
                 const int k0 = j * kFwdBN;
@@ -290,23 +295,28 @@ __global__ __launch_bounds__(64 * fwd_waves<D>(), fwd_min_blocks<D>()) void fwd_
                         return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
                     }
                 };
-                nxt[0] = zero16();
-                nxt[1] = zero16();
+                if constexpr (!last) {
+                    nxt[0] = zero16();
+                    nxt[1] = zero16();
+                }
                 bf16x8 pb[kFwdBN / 16];
                 float rs = 0.f, mx = -__builtin_inff();
                 constexpr int PF = 2;
                 bf16x8 fr[PF + 1];
-                static_for<0, PF>([&](auto F) __attribute__((always_inline)) { fr[decltype(F)::value] = fetch(F); });
+                static_for<0, PF>([&](auto F) __attribute__((always_inline)) {
+                    if constexpr (!(last && is_s(decltype(F)::value))) fr[decltype(F)::value] = fetch(F);
+                });
                 static_assert(NS / 2 == NPV / 2, "phases S1 and V1 must have equal length");
                 constexpr int PH = NS / 2;  // chunks per phase
                 static_for<0, NC>([&](auto C) __attribute__((always_inline)) {
                     constexpr int c = decltype(C)::value;
-                    if constexpr (c + PF < NC) fr[(c + PF) % (PF + 1)] = fetch(std::integral_constant<int, c + PF>{});
-                    const bf16x8 fc = fr[c % (PF + 1)];
+                    if constexpr (c + PF < NC && !(last && is_s(c + PF)))
+                        fr[(c + PF) % (PF + 1)] = fetch(std::integral_constant<int, c + PF>{});
                     if constexpr (is_s(c)) {
                         constexpr int s = c < NS / 2 ? c : c - NPV / 2;
-                        nxt[s & 1] = mfma(fc, qf[s >> 1], nxt[s & 1]);
+                        if constexpr (!last) nxt[s & 1] = mfma(fr[c % (PF + 1)], qf[s >> 1], nxt[s & 1]);
                     } else {
+                        const bf16x8 fc = fr[c % (PF + 1)];
                         constexpr int p = c < NS / 2 + NPV / 2 ? c - NS / 2 : c - NS;
                         oacc[p % NDB] = mfma(fc, pb[p / NDB], oacc[p % NDB]);
                     }
@@ -331,7 +341,7 @@ __global__ __launch_bounds__(64 * fwd_waves<D>(), fwd_min_blocks<D>()) void fwd_
                         // keep the slice in this chunk: the sum is only read after the step, and
                         // without a use here the compiler sinks the whole chain past the barrier
                         asm volatile("" : "+v"(rs));
-                    } else {
+                    } else if constexpr (!last) {
                         constexpr int i = c - 3 * PH;
                         static_for<i * 32 / PH, (i + 1) * 32 / PH>([&](auto RR) __attribute__((always_inline)) {
                             constexpr int r = decltype(RR)::value;
@@ -349,13 +359,15 @@ __global__ __launch_bounds__(64 * fwd_waves<D>(), fwd_min_blocks<D>()) void fwd_
             __syncthreads();
         };
 
-        // stage parity of block j is (j - jb) & 1
+        // stage parity of block j is (j - jb) & 1; the wave's last block, ja - 1, runs as LAST
+        using NL = std::false_type;
+        using LS = std::true_type;
         int j = jb;
         for (; j + 1 < ja; j += 2) {
-            step(j, P0{}, sa, sb);
-            step(j + 1, P1{}, sb, sa);
+            step(j, P0{}, sa, sb, NL{});
+            step(j + 1, P1{}, sb, sa, NL{});
         }
-        if (j < ja) step(j++, P0{}, sa, sb);
+        if (j < ja) step(j++, P0{}, sa, sb, LS{});
         if (j < je && ((j - jb) & 1)) step_idle(j++, P1{});
         for (; j + 1 < je; j += 2) {
             step_idle(j, P0{});
