@@ -181,10 +181,12 @@ __global__ __launch_bounds__(64 * f8_waves<D>(), 8 / f8_waves<D>()) void fwd_fp8
 
         auto kstage = [&](auto par) __attribute__((always_inline)) { return (lds_char *)(decltype(par)::value ? k1_raw : k0_raw); };
         auto vstage = [&](auto par) __attribute__((always_inline)) { return (lds_char *)(decltype(par)::value ? v1_raw : v0_raw); };
-        // key rows [j * BN, j * BN + BN) of K or V into a stage; rows past Nk read as zeros
+        // key rows [j * BN, j * BN + BN) of K or V into a stage.  Rows past the last block this
+        // workgroup needs, and rows past Nk, read as zeros without touching memory.
+        const int kv_lim = min(Nk, je * kF8BN);
         auto load_blk = [&](const uint8_t *src, lds_char *tile, int j) __attribute__((always_inline)) {
-            const int r0 = min(j * kF8BN, Nk);
-            const __amdgpu_buffer_rsrc_t rj = make_rsrc(src + hoff_k + (size_t)r0 * D, (uint32_t)(Nk - r0) * D);
+            const int r0 = min(j * kF8BN, kv_lim);
+            const __amdgpu_buffer_rsrc_t rj = make_rsrc(src + hoff_k + (size_t)r0 * D, (uint32_t)(kv_lim - r0) * D);
 #pragma unroll
             for (int i = 0; i < kLoadNI; ++i) buffer_load_lds16(rj, tile + 1024 * (w * kLoadNI + i), (uint32_t)go[i]);
         };
@@ -251,7 +253,9 @@ __global__ __launch_bounds__(64 * f8_waves<D>(), 8 / f8_waves<D>()) void fwd_fp8
             wait_vmem();
             __syncthreads();
         };
-        auto step = [&](int j, auto par, f32x16 *cur, f32x16 *nxt) __attribute__((always_inline)) {
+        // LAST: the wave's last block; the scores of block j+1 are not computed.
+        auto step = [&](int j, auto par, f32x16 *cur, f32x16 *nxt, auto LAST) __attribute__((always_inline)) {
+            constexpr bool last = decltype(LAST)::value;
             using PN = std::integral_constant<int, 1 - decltype(par)::value>;
             {
                 const int k0 = j * kF8BN;
@@ -293,21 +297,25 @@ __global__ __launch_bounds__(64 * f8_waves<D>(), 8 / f8_waves<D>()) void fwd_fp8
                     if constexpr (c < NS) return kfrag(ks, c & 1, c >> 1);
                     else return vfrag(vs, c - NS);
                 };
-                nxt[0] = zero16();
-                nxt[1] = zero16();
+                if constexpr (!last) {
+                    nxt[0] = zero16();
+                    nxt[1] = zero16();
+                }
                 float rs = 0.f, mx = -__builtin_inff();
                 constexpr int PF = 1;
                 i32x8 fr[PF + 1];
-                static_for<0, PF>([&](auto F) __attribute__((always_inline)) { fr[decltype(F)::value] = fetch(F); });
+                static_for<0, PF>([&](auto F) __attribute__((always_inline)) {
+                    if constexpr (!(last && decltype(F)::value < NS)) fr[decltype(F)::value] = fetch(F);
+                });
                 static_for<0, NC>([&](auto C) __attribute__((always_inline)) {
                     constexpr int c = decltype(C)::value;
-                    if constexpr (c + PF < NC) fr[(c + PF) % (PF + 1)] = fetch(std::integral_constant<int, c + PF>{});
-                    const i32x8 fc = fr[c % (PF + 1)];
+                    if constexpr (c + PF < NC && !(last && c + PF < NS))
+                        fr[(c + PF) % (PF + 1)] = fetch(std::integral_constant<int, c + PF>{});
                     if constexpr (c < NS) {
-                        nxt[c & 1] = mfma8(fc, qf[c >> 1], nxt[c & 1]);
+                        if constexpr (!last) nxt[c & 1] = mfma8(fr[c % (PF + 1)], qf[c >> 1], nxt[c & 1]);
                     } else {
                         const i32x8 pb = i32x8{pw[0], pw[1], pw[2], pw[3], pw[4], pw[5], pw[6], pw[7]};
-                        oacc[c - NS] = mfma8(fc, pb, oacc[c - NS]);
+                        oacc[c - NS] = mfma8(fr[c % (PF + 1)], pb, oacc[c - NS]);
                     }
                     if constexpr (c == 0) load_k(j + 2, par);
                     if constexpr (c == 1) load_v(j + 1, PN{});
@@ -334,7 +342,7 @@ __global__ __launch_bounds__(64 * f8_waves<D>(), 8 / f8_waves<D>()) void fwd_fp8
                         // keep each slice in its chunk: the sum and the maximum are only read after
                         // the step, and without a use here the compiler sinks them past the barrier
                         asm volatile("" : "+v"(rs));
-                        if constexpr (i >= 1) {
+                        if constexpr (i >= 1 && !last) {
                             // maximum of block j+1 once its scores are complete
                             static_for<(i - 1) * 32 / (NDB - 1), i * 32 / (NDB - 1)>([&](auto RR) __attribute__((always_inline)) {
                                 constexpr int r = decltype(RR)::value;
@@ -353,12 +361,13 @@ __global__ __launch_bounds__(64 * f8_waves<D>(), 8 / f8_waves<D>()) void fwd_fp8
             __syncthreads();
         };
 
+        // an odd count of blocks ends with a LAST step
         int j = 0;
         for (; j + 1 < ja; j += 2) {
-            step(j, P0{}, sa, sb);
-            step(j + 1, P1{}, sb, sa);
+            step(j, P0{}, sa, sb, std::false_type{});
+            step(j + 1, P1{}, sb, sa, std::false_type{});
         }
-        if (j < ja) step(j++, P0{}, sa, sb);
+        if (j < ja) step(j++, P0{}, sa, sb, std::true_type{});
         if (j < je && (j & 1)) step_idle(j++, P1{});
         for (; j + 1 < je; j += 2) {
             step_idle(j, P0{});
