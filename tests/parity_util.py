@@ -5,7 +5,7 @@ rounding itself a large part of the 2e-2 budget.
 The GPU writes every output in bf16 (nearest even) from an fp32 value.  Against the unrounded fp64
 reference its error is therefore (arithmetic error) + (output rounding), and the rounding alone can
 reach half a bf16 ulp: 2^-8 * 2^floor(log2|x|), i.e. 0.0078 for |x| in [2, 4), 0.0156 in [4, 8) and
-0.031 in [8, 16).  The bound below keeps the 2e-2 of the spec bar for every element whose
+0.031 in [8, 16).  The bound below keeps the 2e-2 bar for every element whose
 magnitude is below GRAD_ROUNDING_FROM, and above it adds exactly that element's half ulp: there the
 2e-2 bar is applied to the arithmetic, with the unavoidable output quantisation counted separately.
 """
