@@ -398,6 +398,10 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv3_kernel(
     __shared__ __attribute__((aligned(16))) char g0_raw[TILE], g1_raw[TILE], g2_raw[TILE];
     __shared__ __attribute__((aligned(16))) float s0_raw[2 * BMQ], s1_raw[2 * BMQ], s2_raw[2 * BMQ];  // lse, D
     __shared__ __attribute__((aligned(16))) char p0_raw[PBUF], p1_raw[PBUF];
+    // d = 256: the first product's partial sums over each column half of d, exchanged between the
+    // two waves of a column pair (16 floats a lane, 4 KB a wave)
+    constexpr bool kSplit = D == 256;
+    __shared__ __attribute__((aligned(16))) char x_raw[kSplit ? 8 * 64 * 16 * 4 : 16];
 
     int head, ktile;
     work_item(blockIdx.x, n_ktiles, nx, head, ktile);
@@ -425,12 +429,18 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv3_kernel(
     const int key = kw0 + c32;
     const bool keys_ok = kw0 < Nk;
 
-    bf16x8 kvf[NKS];  // K (P wave) or V (dS wave) of the lane's key, over all of d
+    // d = 256: each wave of a column pair forms the first product (S or dP) over its own half of d,
+    // kst in [ch NKSH, (ch + 1) NKSH), and the pair adds the two partial sums through LDS (one more
+    // barrier a step, a third less matrix work).  d = 192: both waves form it over all of d (the
+    // exchange measured 5% slower there).
+    constexpr int NKSH = kSplit ? NKS / 2 : NKS;
+    const int kst0 = kSplit ? ch * NKSH : 0;
+    bf16x8 kvf[NKSH];  // K (P wave) or V (dS wave) of the lane's key, over kst in [kst0, kst0 + NKSH)
     {
         const __amdgpu_buffer_rsrc_t rkv = make_rsrc((pwave ? K : V) + hoff, (uint32_t)Nk * D * 2);
 #pragma unroll
-        for (int ks = 0; ks < NKS; ++ks)
-            kvf[ks] = __builtin_bit_cast(bf16x8, buffer_load16(rkv, (uint32_t)(key * D + 16 * ks + 8 * h) * 2u));
+        for (int ks = 0; ks < NKSH; ++ks)
+            kvf[ks] = __builtin_bit_cast(bf16x8, buffer_load16(rkv, (uint32_t)(key * D + 16 * (kst0 + ks) + 8 * h) * 2u));
     }
     f32x16 acc[NDBH];  // dV (P wave) or dK (dS wave), columns 32 (db0 + i)
 #pragma unroll
@@ -439,17 +449,17 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv3_kernel(
     // The lane's byte offsets inside a swizzled Q / dO tile, computed once and kept opaque so that
     // each LDS read is one register plus a constant (stage, 16-row group) in the instruction's
     // offset field; otherwise the compiler rebuilds the swizzled addresses at every use.
-    // The swizzle changes only chunk bits below 2 * kAoN (bits 0..3 at d = 256, 0..2 at d = 192), so
-    // chunk 2 kst + h lies at ao[kst % kAoN] plus (kst / kAoN) * 2 kAoN chunks.
-    constexpr int kAoN = D == 192 ? 4 : 8;
-    int ao[kAoN];        // A operand of the first product: row c32, chunk 2 kst + h, kst < kAoN
+    // d = 192: the swizzle changes only chunk bits 0..2, so chunk 2 kst + h lies at ao[kst % 4]
+    // plus (kst / 4) * 8 chunks and 4 registers hold all 12 offsets.
+    constexpr int NAO = kSplit ? NKSH : 4;
+    int ao[NAO];         // A operand of the first product: row c32, chunk 2 (kst0 + kst) + h
     int to[NDBH][2];     // transposed reads: rows 4 (G / 2) + s / 4 and + 8 of a 16-row group
 #pragma unroll
-    for (int kst = 0; kst < kAoN; ++kst) {
-        ao[kst] = swz_off<D>(c32, 2 * kst + h);
+    for (int kst = 0; kst < NAO; ++kst) {
+        ao[kst] = swz_off<D>(c32, 2 * (kst0 + kst) + h);
         asm volatile("" : "+v"(ao[kst]));
     }
-    auto a_off = [&](int kst) __attribute__((always_inline)) { return ao[kst % kAoN] + (kst / kAoN) * 32 * kAoN; };
+    auto a_off = [&](int kst) __attribute__((always_inline)) { return ao[kst % NAO] + (kst / NAO) * 32 * NAO; };
     {
         const int G4 = lane >> 4, s16 = lane & 15;
         const int tr = 4 * (G4 >> 1) + (s16 >> 2);
@@ -500,28 +510,50 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv3_kernel(
             using SP = std::integral_constant<int, (s_cur + 2) % 3>;
             using BP = std::integral_constant<int, 1 - decltype(B)::value>;
             load_blk(i + 1, SN{});  // past the last block: zeros into a free stage, never read
+            // P wave: no work past the last block; dS wave: none in the first step
+            const bool work = (P_WAVE || !decltype(FIRST)::value) && keys_ok && (!P_WAVE || i < nsteps);
+            using SB = std::conditional_t<P_WAVE, decltype(S), SP>;
+            // first product: S = Q K^T (P wave) or dP = dO V^T (dS wave), this wave's half of d
+            f32x16 sc = zero16();
+            if (work) {
+                const lds_char *a_l = P_WAVE ? qst(SB{}) : gst(SB{});
+                constexpr int PF = 2;
+                bf16x8 fr[PF + 1];
+                static_for<0, PF>([&](auto F) __attribute__((always_inline)) {
+                    constexpr int f = decltype(F)::value;
+                    fr[f] = lds_read16(a_l, a_off(f));
+                });
+                static_for<0, NKSH>([&](auto C) __attribute__((always_inline)) {
+                    constexpr int c = decltype(C)::value;
+                    if constexpr (c + PF < NKSH) fr[(c + PF) % (PF + 1)] = lds_read16(a_l, a_off(c + PF));
+                    sc = mfma(fr[c % (PF + 1)], kvf[c], sc);
+                    __builtin_amdgcn_sched_barrier(0);
+                });
+                if constexpr (kSplit) {
+#pragma unroll
+                    for (int g = 0; g < 4; ++g)
+                        *(__attribute__((address_space(3))) f32x4 *)(x_raw + ((w * 4 + g) * 64 + lane) * 16) =
+                            f32x4{sc[4 * g], sc[4 * g + 1], sc[4 * g + 2], sc[4 * g + 3]};
+                }
+            }
+            // both halves of every column pair are in LDS (no wait on this step's loads in flight)
+            if constexpr (kSplit) barrier_wait_vmem_upto<15>();
             if constexpr (P_WAVE || !decltype(FIRST)::value) {
-                if (keys_ok && (!P_WAVE || i < nsteps)) {  // P wave: no work past the last block
-                    using SB = std::conditional_t<P_WAVE, decltype(S), SP>;
-                    const lds_char *a_l = P_WAVE ? qst(SB{}) : gst(SB{});
+                if (work) {
+                    // the other half's sum, from the wave of the same role and key group (w ^ 2); both
+                    // waves form own + other, which is the same fp32 sum either way round
+                    if constexpr (kSplit) {
+#pragma unroll
+                        for (int g = 0; g < 4; ++g) {
+                            const f32x4 o4 = *(const __attribute__((address_space(3))) f32x4 *)(x_raw + (((w ^ 2) * 4 + g) * 64 + lane) * 16);
+#pragma unroll
+                            for (int u = 0; u < 4; ++u) sc[4 * g + u] += o4[u];
+                        }
+                    }
                     const lds_char *t_l = P_WAVE ? gst(SB{}) : qst(SB{});
                     const lds_char *st_l = sst(SB{});
                     lds_char *p_l = P_WAVE ? pst(B) : pst(BP{});
                     const int qs = q_start + (P_WAVE ? i : i - 1) * BMQ;
-                    // first product: S = Q K^T (P wave) or dP = dO V^T (dS wave) over all of d
-                    f32x16 sc = zero16();
-                    constexpr int PF = 2;
-                    bf16x8 fr[PF + 1];
-                    static_for<0, PF>([&](auto F) __attribute__((always_inline)) {
-                        constexpr int f = decltype(F)::value;
-                        fr[f] = lds_read16(a_l, a_off(f));
-                    });
-                    static_for<0, NKS>([&](auto C) __attribute__((always_inline)) {
-                        constexpr int c = decltype(C)::value;
-                        if constexpr (c + PF < NKS) fr[(c + PF) % (PF + 1)] = lds_read16(a_l, a_off(c + PF));
-                        sc = mfma(fr[c % (PF + 1)], kvf[c], sc);
-                        __builtin_amdgcn_sched_barrier(0);
-                    });
                     f32x4 v4[4];  // lse (P wave) or D (dS wave) of the lane's queries 8g + 4h + u
 #pragma unroll
                     for (int g = 0; g < 4; ++g)
