@@ -376,11 +376,13 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv2_kernel(const Dkdv2Args args)
 
 // The paired-wave scheme of bwd_dkdv2_kernel for the wide heads: eight waves in four SIMD pairs;
 // wave w has role w / 4 (P wave or dS wave), key group w % 2 (32 keys; 64 keys per workgroup)
-// and column half (w / 2) % 2 of dK and dV.  The two waves of a column pair both form S (P
-// waves) or dP (dS waves) over all of d, and each accumulates its half of the columns, which
-// keeps every wave's registers (one key-side operand over d, half an accumulator) under the
-// 256 that two waves per SIMD allow.  Query blocks are 32 rows so that three stages of Q and dO
-// fit in LDS.  The P wave of column half 0 leaves P in LDS for the dS waves, one block behind.
+// and column half (w / 2) % 2 of dK and dV.  Both waves of a column pair need the whole of S (P
+// waves) or dP (dS waves) and each accumulates its half of the columns, which keeps every wave's
+// registers (half an accumulator) under the 256 that two waves per SIMD allow.  At d = 192 each
+// wave forms the first product over all of d; at d = 256 each forms it over its own half of d
+// and the pair adds the two partial sums through LDS.  Query blocks are 32 rows so that three
+// stages of Q and dO fit in LDS.  The P wave of column half 0 leaves P in LDS for the dS waves,
+// one block behind.
 template <int D, bool CAUSAL>
 __global__ __launch_bounds__(512, 1) void bwd_dkdv3_kernel(
     const bf16 *__restrict__ Q, const bf16 *__restrict__ K, const bf16 *__restrict__ V, const bf16 *__restrict__ dO,
