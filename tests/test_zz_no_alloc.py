@@ -124,3 +124,46 @@ def test_noalloc_on_a_side_stream():
         without_workspace(case, q, k, v, *got)
     s.synchronize()
     assert same_bits(got[0], ref[0]) and same_bits(got[1], ref[1])
+
+
+def test_noalloc_under_graph_capture():
+    """The callers this entry point is for include code under HIP graph capture.  A first eager call
+    looks up the buffer's address and the device shape; the captured call then allocates nothing,
+    and each replay (with eager work of other shapes, which also uses the buffer, between replays)
+    must reproduce the eager result bit for bit."""
+    case = (2, 4, 2, 33, 3000, 128, False, 6)
+    other = (1, 2, 2, 5, 1500, 64, True, 3)
+    note("graph capture %s, eager work between replays %s, seeds 45/46" % (case, other))
+    _, q, k, v = setup(case, 45)
+    _, q2, k2, v2 = setup(other, 46)
+    ref = with_workspace(case, q, k, v)
+    ref2 = with_workspace(other, q2, k2, v2)
+    got = outputs(case)
+    without_workspace(case, q, k, v, *got)      # eager first call: address and device shape cached
+    torch.cuda.synchronize()
+    assert same_bits(got[0], ref[0]) and same_bits(got[1], ref[1])
+    got[0].fill_(float("nan"))
+    got[1].fill_(float("nan"))
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        with torch.cuda.graph(g, stream=s):
+            without_workspace(case, q, k, v, *got)
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    for rep in range(4):
+        g.replay()
+        torch.cuda.synchronize()
+        ok = same_bits(got[0], ref[0]) and same_bits(got[1], ref[1])
+        note("  replay %d: bitwise equal %s" % (rep, ok))
+        assert ok, rep
+        # eager work in between that overwrites the shared buffer with another problem's pieces
+        got2 = outputs(other)
+        without_workspace(other, q2, k2, v2, *got2)
+        torch.cuda.synchronize()
+        assert same_bits(got2[0], ref2[0]) and same_bits(got2[1], ref2[1])
+        got[0].fill_(float("nan"))
+        got[1].fill_(float("nan"))
+        torch.cuda.synchronize()
