@@ -69,6 +69,13 @@ int main()
             }
         }
     }
+    // causal pairing: only while the paired grid fills every resident slot
+    EXPECT(attn::causal_pairs(32, 16, 256), "c5 shape pairs (256 workgroups)");
+    EXPECT(attn::causal_pairs(64, 16, 256), "c3 shape pairs");
+    EXPECT(!attn::causal_pairs(32, 8, 256), "2048 query rows on 32 heads: 128 paired workgroups do not fill 256");
+    EXPECT(!attn::causal_pairs(1, 1, 256), "one block");
+    EXPECT(attn::causal_pairs(1, 3, 2) && !attn::causal_pairs(1, 3, 3), "odd count: the middle block is a pair of its own");
+    checks += 5;
     printf("%lld checks, %d failures\n", checks, failures);
     return failures == 0 ? 0 : 1;
 }

@@ -68,7 +68,7 @@ __global__ __launch_bounds__(64 * fwd_waves<D>(), fwd_min_blocks<D>()) void fwd_
                                                           const bf16 *__restrict__ V, bf16 *__restrict__ O,
                                                           float *__restrict__ LSE, int Nq, int Nk, int H, int G, int n_qtiles,
                                                           float scale, float c_log2, int n_splits, int split_blocks,
-                                                          float *__restrict__ OP, float *__restrict__ LP, int nx)
+                                                          float *__restrict__ OP, float *__restrict__ LP, int nx, int pair)
 {
     using L = FwdSmem<D>;
     constexpr int kFwdWaves = fwd_waves<D>();
@@ -79,11 +79,11 @@ __global__ __launch_bounds__(64 * fwd_waves<D>(), fwd_min_blocks<D>()) void fwd_
     // direct loads into the other (no wait on those loads before the reads)
     __shared__ __attribute__((aligned(16))) char k0_raw[L::TILE], k1_raw[L::TILE], v0_raw[L::TILE], v1_raw[L::TILE];
 
-    // Causal: workgroup `pos` of a head takes query blocks T-1-pos and then pos (T = n_qtiles),
-    // so every workgroup but a middle one does the same T+1 blocks' worth of work and the
-    // grid needs no longest-first balancing.  Non-causal: one query block per workgroup.
+    // Causal with `pair` set: workgroup `pos` of a head takes query blocks T-1-pos and then pos
+    // (T = n_qtiles), so every workgroup but a middle one does the same T+1 blocks' worth of work.
+    // Otherwise one query block per workgroup; causal blocks go longest first (T-1-pos).
     // Split: one (query block, key piece) per workgroup.
-    const int n_pos = SPLIT ? n_qtiles * n_splits : (CAUSAL ? (n_qtiles + 1) / 2 : n_qtiles);
+    const int n_pos = SPLIT ? n_qtiles * n_splits : (pair ? (n_qtiles + 1) / 2 : n_qtiles);
     int head, pos;
     work_item(blockIdx.x, n_pos, nx, head, pos);
     const int split = SPLIT ? pos % n_splits : 0;
@@ -134,7 +134,7 @@ __global__ __launch_bounds__(64 * fwd_waves<D>(), fwd_min_blocks<D>()) void fwd_
         }
     }
 
-    for (int pass = 0; pass < ((CAUSAL && !SPLIT) ? 2 : 1); ++pass) {
+    for (int pass = 0; pass < ((CAUSAL && !SPLIT && pair) ? 2 : 1); ++pass) {
         const int qtile = SPLIT ? pos / n_splits : (pass == 0 ? (CAUSAL ? n_qtiles - 1 - pos : pos) : pos);
         if (pass == 1 && qtile == n_qtiles - 1 - pos) break;  // odd T: the middle block is alone
         const int q0 = qtile * kFwdBM;
@@ -419,12 +419,15 @@ hipError_t launch_fwd_t(const FwdArgs &a)
     constexpr int kFwdBM = fwd_bm<D>();
     constexpr int kThreads = 64 * fwd_waves<D>();
     const int n_qtiles = (a.Nq + kFwdBM - 1) / kFwdBM;
-    const long long G = (long long)a.B * a.H * (CAUSAL ? (n_qtiles + 1) / 2 : n_qtiles);
+    const long long n_heads = (long long)a.B * a.H;
+    const bool pair = CAUSAL && causal_pairs(n_heads, n_qtiles, (long long)a.dev.cus * fwd_min_blocks<D>());
+    const long long G = n_heads * (pair ? (n_qtiles + 1) / 2 : n_qtiles);
     if (G == 0) return hipSuccess;
     const float c_log2 = a.scale * kLog2e;
     hipLaunchKernelGGL((fwd_kernel<D, CAUSAL, false>), dim3((unsigned)G), dim3(kThreads), 0, (hipStream_t)a.stream,
                        (const bf16 *)a.q, (const bf16 *)a.k, (const bf16 *)a.v, (bf16 *)a.o, a.lse, a.Nq, a.Nk,
-                       a.H, a.H / a.Hk, n_qtiles, a.scale, c_log2, 1, 0, (float *)nullptr, (float *)nullptr, a.dev.nx);
+                       a.H, a.H / a.Hk, n_qtiles, a.scale, c_log2, 1, 0, (float *)nullptr, (float *)nullptr, a.dev.nx,
+                       (int)pair);
     return hipGetLastError();
 }
 
@@ -474,7 +477,7 @@ hipError_t launch_fwd_split_t(const FwdArgs &a, int n_splits, float *op, float *
     const float c_log2 = a.scale * kLog2e;
     hipLaunchKernelGGL((fwd_kernel<D, CAUSAL, true>), dim3((unsigned)G), dim3(kThreads), 0, (hipStream_t)a.stream,
                        (const bf16 *)a.q, (const bf16 *)a.k, (const bf16 *)a.v, (bf16 *)a.o, a.lse, a.Nq, a.Nk,
-                       a.H, a.H / a.Hk, n_qtiles, a.scale, c_log2, n_splits, split_blocks, op, lp, a.dev.nx);
+                       a.H, a.H / a.Hk, n_qtiles, a.scale, c_log2, n_splits, split_blocks, op, lp, a.dev.nx, 0);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     const long long rows = (long long)a.B * a.H * a.Nq;

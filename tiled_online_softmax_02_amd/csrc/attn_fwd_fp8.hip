@@ -85,7 +85,7 @@ template <int D, bool CAUSAL>
 __global__ __launch_bounds__(64 * f8_waves<D>(), 8 / f8_waves<D>()) void fwd_fp8_kernel(
     const uint8_t *__restrict__ Q, const uint8_t *__restrict__ K, const uint8_t *__restrict__ V,
     const float *__restrict__ DSQ, const float *__restrict__ DSK, const float *__restrict__ DSV, bf16 *__restrict__ O,
-    float *__restrict__ LSE, int Nq, int Nk, int H, int G, int n_qtiles, float scale, int nx)
+    float *__restrict__ LSE, int Nq, int Nk, int H, int G, int n_qtiles, float scale, int nx, int pair)
 {
     constexpr int NW = f8_waves<D>();
     constexpr int BM = f8_bm<D>();
@@ -94,8 +94,9 @@ __global__ __launch_bounds__(64 * f8_waves<D>(), 8 / f8_waves<D>()) void fwd_fp8
     constexpr int TILE = kF8BN * D;
     __shared__ __attribute__((aligned(16))) char k0_raw[TILE], k1_raw[TILE], v0_raw[TILE], v1_raw[TILE];
 
-    // causal: workgroup `pos` takes query blocks T-1-pos and then pos (equal work per workgroup)
-    const int n_pos = CAUSAL ? (n_qtiles + 1) / 2 : n_qtiles;
+    // causal with `pair` set: workgroup `pos` takes query blocks T-1-pos and then pos (equal work per
+    // workgroup); otherwise one query block per workgroup, causal ones longest first
+    const int n_pos = pair ? (n_qtiles + 1) / 2 : n_qtiles;
     int head, pos;
     work_item(blockIdx.x, n_pos, nx, head, pos);
 
@@ -148,7 +149,7 @@ __global__ __launch_bounds__(64 * f8_waves<D>(), 8 / f8_waves<D>()) void fwd_fp8
     const float dsv = DSV[kvh];
     const float grow_thr = kF8RescaleLog2 / c_log2;
 
-    for (int pass = 0; pass < (CAUSAL ? 2 : 1); ++pass) {
+    for (int pass = 0; pass < ((CAUSAL && pair) ? 2 : 1); ++pass) {
         const int qtile = pass == 0 ? (CAUSAL ? n_qtiles - 1 - pos : pos) : pos;
         if (pass == 1 && qtile == n_qtiles - 1 - pos) break;  // odd T: the middle block is alone
         const int q0 = qtile * BM;
@@ -401,12 +402,14 @@ hipError_t launch_fwd_fp8_t(const Fp8FwdArgs &a)
 {
     constexpr int BM = f8_bm<D>();
     const int n_qtiles = (a.Nq + BM - 1) / BM;
-    const long long G = (long long)a.B * a.H * (CAUSAL ? (n_qtiles + 1) / 2 : n_qtiles);
+    const long long n_heads = (long long)a.B * a.H;
+    const bool pair = CAUSAL && causal_pairs(n_heads, n_qtiles, (long long)a.dev.cus * (8 / f8_waves<D>()));
+    const long long G = n_heads * (pair ? (n_qtiles + 1) / 2 : n_qtiles);
     if (G == 0) return hipSuccess;
     hipLaunchKernelGGL((fwd_fp8_kernel<D, CAUSAL>), dim3((unsigned)G), dim3(64 * f8_waves<D>()), 0,
                        (hipStream_t)a.stream, (const uint8_t *)a.q, (const uint8_t *)a.k, (const uint8_t *)a.v,
                        a.descale_q, a.descale_k, a.descale_v, (bf16 *)a.o, a.lse, a.Nq, a.Nk, a.H, a.H / a.Hk,
-                       n_qtiles, a.scale, a.dev.nx);
+                       n_qtiles, a.scale, a.dev.nx, (int)pair);
     return hipGetLastError();
 }
 

@@ -59,4 +59,13 @@ __host__ __device__ inline long long persistent_grid(long long n_items, long lon
     return (n_items > P && n_heads % nx == 0) ? P : 0;
 }
 
+// Causal forward: pair each workgroup's long and short query block (T-1-p, then p) only while the
+// paired grid, n_heads * ceil(T / 2) workgroups of equal work, still fills the `slots` workgroups
+// the device holds at once.  Below that a paired grid leaves compute units idle for its whole run,
+// and one query block per workgroup, issued longest-first, finishes sooner.
+__host__ __device__ inline bool causal_pairs(long long n_heads, int n_qtiles, long long slots)
+{
+    return n_heads * ((n_qtiles + 1) / 2) >= slots;
+}
+
 }  // namespace attn
