@@ -4,8 +4,8 @@ c5g (grouped K/V heads, Hk = 4 under H = 16), c5u (2048 queries against 4096 key
 causal alignment) and c5d256 (head dimension 256), all forward + backward at B = 2, N = 4096:
 sampled forward rows of every head against the fp64 oracle, one whole K/V head's gradients against
 the oracle's backward (for grouped heads: the sum over the query heads that share the K/V head,
-by the chain rule; each element within 2e-2, plus its own half bf16 ulp where |x| >= 8, where the
-output rounding alone can pass 2e-2; the error against the bf16-rounded reference is reported by
+by the chain rule; each element within 2e-2, plus its own half bf16 ulp where |x| >= 4, where the
+output rounding alone takes most of 2e-2; the error against the bf16-rounded reference is reported by
 magnitude band), and
 on every head the invariants sum_j dK_j = 0 and sum_j dV_j = the sum of dO over the query rows of
 the heads that read it (each row of P sums to 1; "digest_existing.txt", answer
@@ -77,7 +77,7 @@ def test_widened_workload_full_size(wname):
     note("  backward: oracle on K/V head (%d,%d), query heads %s" % (b, hk, heads))
     rdq, rdk, rdv, _ = oracle.attn_bwd_matmul(q64[b:b + 1, heads], kk, vv, do64[b:b + 1, heads], w.causal, w.scale)
     # a K/V head shared by G query heads sums G contributions: its |dK|, |dV| grow by about sqrt(G),
-    # and from |x| = 8 on the bf16 rounding of the output alone can pass 2e-2 (parity_util)
+    # and from |x| = 4 on the bf16 rounding of the output alone takes most of 2e-2 (parity_util)
     for name, got, ref in (("Q", f64(dq)[b, heads], rdq[0]), ("K", f64(dk)[b, hk], rdk[0].sum(axis=0)),
                            ("V", f64(dv)[b, hk], rdv[0].sum(axis=0))):
         ok, margin, report = check_grad(got, ref)

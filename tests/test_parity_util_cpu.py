@@ -26,6 +26,7 @@ def test_bf16_half_ulp():
     assert np.all(np.abs(bf16_round(y) - y) <= bf16_half_ulp(y))
 
 
-def test_grad_bound_adds_rounding_only_from_eight():
-    ref = np.array([0.5, 3.9, 7.9, 8.0, -12.0])
-    assert np.array_equal(grad_bound(ref), np.array([2e-2, 2e-2, 2e-2, 2e-2 + 2 ** -5, 2e-2 + 2 ** -5]))
+def test_grad_bound_adds_rounding_only_from_four():
+    ref = np.array([0.5, 3.9, 4.0, 7.9, 8.0, -12.0])
+    want = np.array([2e-2, 2e-2, 2e-2 + 2 ** -6, 2e-2 + 2 ** -6, 2e-2 + 2 ** -5, 2e-2 + 2 ** -5])
+    assert np.array_equal(grad_bound(ref), want)
