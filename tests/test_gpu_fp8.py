@@ -227,3 +227,26 @@ def test_fp8_score_sum_accuracy(d):
              % (d, what, rel.max(), np.log2(max(rel.max(), 2.0 ** -60)), rel.size))
         worst = max(worst, float(rel.max()))
     assert worst <= U_DOT / 2, worst
+
+
+def draw_fp8_cases(n, seed):
+    g = np.random.default_rng(seed)
+    out = []
+    for i in range(n):
+        d = int(g.choice([64, 128]))
+        B = int(g.integers(1, 3))
+        H = int(g.choice([1, 2, 4]))
+        Hk = int(g.choice([x for x in (1, 2, 4) if H % x == 0]))
+        base = int(g.integers(1, 600))
+        kind = g.integers(0, 3)
+        Nq, Nk = (base, base) if kind == 0 else ((base, int(g.integers(1, base + 1))) if kind == 1
+                                                 else (int(g.integers(1, base + 1)), base))
+        out.append((B, H, Hk, Nq, Nk, d, bool(g.integers(0, 2))))
+    return out
+
+
+@pytest.mark.parametrize("B,H,Hk,Nq,Nk,d,causal", draw_fp8_cases(16, 2027))
+def test_fp8_random_shapes(B, H, Hk, Nq, Nk, d, causal):
+    """Seeded random shapes (grouped heads, ragged unequal lengths, both masks) against the oracle with
+    the same bounds as the fixed cases above."""
+    test_fp8_forward_against_oracle(B, H, Hk, Nq, Nk, d, causal)
