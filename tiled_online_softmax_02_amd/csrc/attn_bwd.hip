@@ -382,7 +382,10 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv2_kernel(const Dkdv2Args args)
 // wave forms the first product over all of d; at d = 256 each forms it over its own half of d
 // and the pair adds the two partial sums through LDS.  Query blocks are 32 rows so that three
 // stages of Q and dO fit in LDS.  The P wave of column half 0 leaves P in LDS for the dS waves,
-// one block behind.
+// one block behind.  As in bwd_dkdv2_kernel, the dS waves hold -V so that their product starts
+// from D and -dS is one multiply per element, lse reaches LDS in log2 units, and LDS fragments
+// are fetched two matrix instructions ahead with the vector work placed under the matrix
+// instructions of the other 16 queries.
 template <int D, bool CAUSAL>
 __global__ __launch_bounds__(512, 1) void bwd_dkdv3_kernel(
     const bf16 *__restrict__ Q, const bf16 *__restrict__ K, const bf16 *__restrict__ V, const bf16 *__restrict__ dO,
@@ -437,12 +440,16 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv3_kernel(
     // exchange measured 5% slower there).
     constexpr int NKSH = kSplit ? NKS / 2 : NKS;
     const int kst0 = kSplit ? ch * NKSH : 0;
-    bf16x8 kvf[NKSH];  // K (P wave) or V (dS wave) of the lane's key, over kst in [kst0, kst0 + NKSH)
+    // K (P wave) or -V (dS wave) of the lane's key, over kst in [kst0, kst0 + NKSH): with -V the dS
+    // wave's product starts from D and gives D - dP, so that -dS = P (D - dP) is one multiply per
+    // element; its accumulator holds -dK, negated with the scale at the end
+    bf16x8 kvf[NKSH];
     {
         const __amdgpu_buffer_rsrc_t rkv = make_rsrc((pwave ? K : V) + hoff, (uint32_t)Nk * D * 2);
+        const unsigned sign = pwave ? 0u : 0x80008000u;
 #pragma unroll
         for (int ks = 0; ks < NKSH; ++ks)
-            kvf[ks] = __builtin_bit_cast(bf16x8, buffer_load16(rkv, (uint32_t)(key * D + 16 * (kst0 + ks) + 8 * h) * 2u));
+            kvf[ks] = __builtin_bit_cast(bf16x8, buffer_load16(rkv, (uint32_t)(key * D + 16 * (kst0 + ks) + 8 * h) * 2u) ^ sign);
     }
     f32x16 acc[NDBH];  // dV (P wave) or dK (dS wave), columns 32 (db0 + i)
 #pragma unroll
@@ -493,127 +500,208 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv3_kernel(
     auto pst = [&](auto b) __attribute__((always_inline)) {
         return (lds_char *)(decltype(b)::value ? p1_raw : p0_raw) + kg * (2 * 64 * 16);
     };
-    // Q by waves 0..3 and dO by waves 4..7 (a tile of 32 rows is 12 or 16 wave loads)
-    auto load_blk = [&](int i, auto st) __attribute__((always_inline)) {
+    // Loads of block i (query rows q_start + 32 i ..): Q by waves 0..3, dO by waves 4..7 (a tile of 32
+    // rows is 12 or 16 wave loads), D straight to LDS (wave 1) and lse into registers (wave 0,
+    // lanes 0..7).  lse goes to LDS in log2 units once it has arrived, so that the P waves form
+    // each exponent with one fused multiply-add; two registers, by block parity, because the next
+    // block's lse is requested before the last one is stored.
+    constexpr int NQL = BMQ * (D / 8) / 64 / 4;  // direct loads per wave and tile
+    f32x4 lse_ld[2];
+    auto load_q = [&](int i, auto st) __attribute__((always_inline)) {
+        if (w < 4) load_tile_lds<D, 4, BMQ>(rq, qst(st), q_start + i * BMQ, w & 3, lane);
+    };
+    auto load_g = [&](int i, auto st, auto par) __attribute__((always_inline)) {
         const int qs = q_start + i * BMQ;
-        if (w < 4)
-            load_tile_lds<D, 4, BMQ>(rq, qst(st), qs, w & 3, lane);
-        else
-            load_tile_lds<D, 4, BMQ>(rg, gst(st), qs, w & 3, lane);
-        if (w == 0 && lane < 8) buffer_load_lds16(rl, sst(st), (uint32_t)(qs + 4 * lane) * 4u);
+        if (w >= 4) load_tile_lds<D, 4, BMQ>(rg, gst(st), qs, w & 3, lane);
+        if (w == 0 && lane < 8)
+            lse_ld[decltype(par)::value] = __builtin_bit_cast(f32x4, buffer_load16(rl, (uint32_t)(qs + 4 * lane) * 4u));
         if (w == 1 && lane < 8) buffer_load_lds16(rd, sst(st) + 4 * BMQ, (uint32_t)(qs + 4 * lane) * 4u);
     };
+    auto store_lse = [&](auto st, auto par) __attribute__((always_inline)) {
+        if (w == 0 && lane < 8)
+            *(__attribute__((address_space(3))) f32x4 *)(sst(st) + 16 * lane) = lse_ld[decltype(par)::value] * kLog2e;
+    };
 
-    auto run = [&](auto PW) __attribute__((always_inline)) {
+    using I0 = std::integral_constant<int, 0>;
+    using I1 = std::integral_constant<int, 1>;
+    using I2 = std::integral_constant<int, 2>;
+    // One copy of the loop per role and column half (CH), so that which wave starts the dS sum
+    // from D and which wave hands P to the dS waves are compile-time facts.
+    //
+    // The two roles run their products in opposite order within a step:
+    //   P wave:  first product of block i     | second product of block i
+    //   dS wave: second product of block i-1  | first product of block i
+    // At d = 256 a barrier separates the halves (the exchange of partial sums).  On each SIMD one
+    // wave's chain of first-product instructions then runs while the other wave reads its
+    // partner's sums, forms P or dS and feeds its second product, instead of both waves waiting
+    // for the exchange at the same time.
+    auto run = [&](auto PW, auto CHc) __attribute__((always_inline)) {
         constexpr bool P_WAVE = decltype(PW)::value;
+        constexpr int CH = decltype(CHc)::value;
+        constexpr int PF = 2;  // LDS fragments fetched this many instructions ahead
+        // First product over this wave's part of d: S = Q K^T (P wave) or D - dO V^T (dS wave, -V
+        // in registers; one wave of a column pair starts from D), then this wave's partial sums to
+        // LDS for its partner.
+        auto first = [&](const lds_char *a_l, const lds_char *st_l, f32x16 &sc) __attribute__((always_inline)) {
+            if constexpr (!P_WAVE && (!kSplit || CH == 0)) {
+#pragma unroll
+                for (int g = 0; g < 4; ++g) {
+                    const f32x4 dv = *(const __attribute__((address_space(3))) f32x4 *)(st_l + 4 * (BMQ + 8 * g + 4 * h));
+#pragma unroll
+                    for (int u = 0; u < 4; ++u) sc[4 * g + u] = dv[u];
+                }
+            } else {
+                sc = zero16();
+            }
+            bf16x8 fr[PF + 1];
+            static_for<0, PF>([&](auto F) __attribute__((always_inline)) {
+                fr[decltype(F)::value] = lds_read16(a_l, a_off(decltype(F)::value));
+            });
+            static_for<0, NKSH>([&](auto C) __attribute__((always_inline)) {
+                constexpr int c = decltype(C)::value;
+                if constexpr (c + PF < NKSH) fr[(c + PF) % (PF + 1)] = lds_read16(a_l, a_off(c + PF));
+                sc = mfma(fr[c % (PF + 1)], kvf[c], sc);
+                __builtin_amdgcn_sched_barrier(0);
+            });
+            if constexpr (kSplit) {
+#pragma unroll
+                for (int g = 0; g < 4; ++g)
+                    *(__attribute__((address_space(3))) f32x4 *)(x_raw + ((w * 4 + g) * 64 + lane) * 16) =
+                        f32x4{sc[4 * g], sc[4 * g + 1], sc[4 * g + 2], sc[4 * g + 3]};
+            }
+        };
+        // Second product: the partner's partial sums added, P = exp2(S scale log2e - lse log2e) or
+        // -dS = P (D - dP) in bf16, then dV^T += dO^T P or -dK^T += Q^T (-dS) over this wave's
+        // columns, 16 queries t at a time.
+        auto second = [&](const lds_char *t_l, const lds_char *st_l, lds_char *p_l, int qs, f32x16 &sc)
+                          __attribute__((always_inline)) {
+            f32x4 o4[4];     // the partner's partial sums (d = 256)
+            f32x4 v4[4];     // lse * log2e of the lane's queries 8 g + 4 h + u (P wave)
+            bf16x8 pv[2];    // P of the block, from the P wave (dS wave)
+            if constexpr (kSplit) {
+                // from the wave of the same role and key group (w ^ 2); both waves form own + other,
+                // which is the same fp32 sum either way round
+#pragma unroll
+                for (int g = 0; g < 4; ++g)
+                    o4[g] = *(const __attribute__((address_space(3))) f32x4 *)(x_raw + (((w ^ 2) * 4 + g) * 64 + lane) * 16);
+            }
+            if constexpr (P_WAVE) {
+#pragma unroll
+                for (int g = 0; g < 4; ++g)
+                    v4[g] = *(const __attribute__((address_space(3))) f32x4 *)(st_l + 4 * (8 * g + 4 * h));
+            } else {
+#pragma unroll
+                for (int t = 0; t < 2; ++t)
+                    pv[t] = __builtin_bit_cast(bf16x8, *(const __attribute__((address_space(3))) u32x4 *)(p_l + (t * 64 + lane) * 16));
+            }
+            auto fetch = [&](auto N) __attribute__((always_inline)) {
+                constexpr int n = decltype(N)::value, t = n / NDBH, db = n % NDBH;
+                const bf16x4 lo = lds_read_tr(t_l, to[db][0] + 16 * t * 2 * D);
+                const bf16x4 hi = lds_read_tr(t_l, to[db][1] + 16 * t * 2 * D);
+                return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+            };
+            bf16x8 fr[PF + 1];
+            static_for<0, PF>([&](auto F) __attribute__((always_inline)) { fr[decltype(F)::value] = fetch(F); });
+            if constexpr (kSplit) {
+#pragma unroll
+                for (int g = 0; g < 4; ++g) {
+#pragma unroll
+                    for (int u = 0; u < 4; ++u) sc[4 * g + u] += o4[g][u];
+                }
+            }
+            if constexpr (P_WAVE) {
+                if (CAUSAL && (qs + off < kw0 + 31)) {
+                    // scores of queries before this lane's key -> -inf (P = 0); a query that
+                    // sees no key has lse = -inf: keep exp2 away from -inf + inf
+#pragma unroll
+                    for (int g = 0; g < 4; ++g) {
+#pragma unroll
+                        for (int u = 0; u < 4; ++u) {
+                            v4[g][u] = fmaxf(v4[g][u], -1e30f);
+                            if (qs + 8 * g + 4 * h + u + off < key) sc[4 * g + u] = -__builtin_inff();
+                        }
+                    }
+                }
+            }
+            bf16x8 pb[2];
+            auto form = [&](auto RR) __attribute__((always_inline)) {
+                constexpr int r = decltype(RR)::value;
+                if constexpr (P_WAVE)
+                    pb[r >> 3][r & 7] = (bf16)fast_exp2(fmaf(sc[r], c_log2, -v4[r >> 2][r & 3]));
+                else
+                    pb[r >> 3][r & 7] = (bf16)((float)pv[r >> 3][r & 7] * sc[r]);
+            };
+            static_for<0, 8>(form);  // the first group before its matrix instructions
+            static_for<0, 2 * NDBH>([&](auto N) __attribute__((always_inline)) {
+                constexpr int n = decltype(N)::value, t = n / NDBH, db = n % NDBH;
+                if constexpr (n + PF < 2 * NDBH) fr[(n + PF) % (PF + 1)] = fetch(std::integral_constant<int, n + PF>{});
+                acc[db] = mfma(fr[n % (PF + 1)], pb[t], acc[db]);
+                if constexpr (t == 0) {
+                    // the second group under the first group's matrix instructions
+                    static_for<8 + db * 8 / NDBH, 8 + (db + 1) * 8 / NDBH>(form);
+                    if constexpr (P_WAVE && CH == 0 && db == NDBH - 1) {
+#pragma unroll
+                        for (int tt = 0; tt < 2; ++tt) lds_write16(p_l, (tt * 64 + lane) * 16, __builtin_bit_cast(u32x4, pb[tt]));
+                    }
+                }
+                __builtin_amdgcn_sched_barrier(0);
+            });
+        };
+
+        // Step i: the P wave works on block i (stage S, P buffer B), the dS wave on blocks i - 1
+        // (stage (S + 2) % 3, P buffer 1 - B) and i.  Loads run two blocks ahead where the stages
+        // allow: dO, lse and D of block i + 2 go at the start of the step into the stage of block
+        // i - 1 (last read in step i - 1); Q of block i + 2 into the same stage after the middle
+        // barrier (the dS wave reads Q of block i - 1 before it) at d = 256, and Q of block i + 1 at
+        // the start at d = 192 (no middle barrier).  At the end of the step only block i + 1 must
+        // have arrived; the loads issued after it stay in flight.
+        f32x16 sc;  // dS wave: D - dP of block i, formed in step i and used in step i + 1
         auto step = [&](int i, auto S, auto B, auto FIRST) __attribute__((always_inline)) {
             constexpr int s_cur = decltype(S)::value;
             using SN = std::integral_constant<int, (s_cur + 1) % 3>;
             using SP = std::integral_constant<int, (s_cur + 2) % 3>;
             using BP = std::integral_constant<int, 1 - decltype(B)::value>;
-            load_blk(i + 1, SN{});  // past the last block: zeros into a free stage, never read
-            // P wave: no work past the last block; dS wave: none in the first step
-            const bool work = (P_WAVE || !decltype(FIRST)::value) && keys_ok && (!P_WAVE || i < nsteps);
-            using SB = std::conditional_t<P_WAVE, decltype(S), SP>;
-            // first product: S = Q K^T (P wave) or dP = dO V^T (dS wave), this wave's half of d
-            f32x16 sc = zero16();
-            if (work) {
-                const lds_char *a_l = P_WAVE ? qst(SB{}) : gst(SB{});
-                constexpr int PF = 2;
-                bf16x8 fr[PF + 1];
-                static_for<0, PF>([&](auto F) __attribute__((always_inline)) {
-                    constexpr int f = decltype(F)::value;
-                    fr[f] = lds_read16(a_l, a_off(f));
-                });
-                static_for<0, NKSH>([&](auto C) __attribute__((always_inline)) {
-                    constexpr int c = decltype(C)::value;
-                    if constexpr (c + PF < NKSH) fr[(c + PF) % (PF + 1)] = lds_read16(a_l, a_off(c + PF));
-                    sc = mfma(fr[c % (PF + 1)], kvf[c], sc);
-                    __builtin_amdgcn_sched_barrier(0);
-                });
+            // past the last block: zeros into free stages, never read
+            load_g(i + 2, SP{}, B);  // block i + 2 has the parity of block i
+            if constexpr (!kSplit) load_q(i + 1, SN{});
+            const bool cur = keys_ok && i < nsteps;  // block i exists (none in the last step)
+            if constexpr (P_WAVE) {
+                if (cur) first(qst(S), sst(S), sc);
                 if constexpr (kSplit) {
-#pragma unroll
-                    for (int g = 0; g < 4; ++g)
-                        *(__attribute__((address_space(3))) f32x4 *)(x_raw + ((w * 4 + g) * 64 + lane) * 16) =
-                            f32x4{sc[4 * g], sc[4 * g + 1], sc[4 * g + 2], sc[4 * g + 3]};
+                    barrier_wait_vmem_upto<15>();  // no wait on the loads in flight
+                    load_q(i + 2, SP{});
                 }
-            }
-            // both halves of every column pair are in LDS (no wait on this step's loads in flight)
-            if constexpr (kSplit) barrier_wait_vmem_upto<15>();
-            if constexpr (P_WAVE || !decltype(FIRST)::value) {
-                if (work) {
-                    // the other half's sum, from the wave of the same role and key group (w ^ 2); both
-                    // waves form own + other, which is the same fp32 sum either way round
-                    if constexpr (kSplit) {
-#pragma unroll
-                        for (int g = 0; g < 4; ++g) {
-                            const f32x4 o4 = *(const __attribute__((address_space(3))) f32x4 *)(x_raw + (((w ^ 2) * 4 + g) * 64 + lane) * 16);
-#pragma unroll
-                            for (int u = 0; u < 4; ++u) sc[4 * g + u] += o4[u];
-                        }
-                    }
-                    const lds_char *t_l = P_WAVE ? gst(SB{}) : qst(SB{});
-                    const lds_char *st_l = sst(SB{});
-                    lds_char *p_l = P_WAVE ? pst(B) : pst(BP{});
-                    const int qs = q_start + (P_WAVE ? i : i - 1) * BMQ;
-                    f32x4 v4[4];  // lse (P wave) or D (dS wave) of the lane's queries 8g + 4h + u
-#pragma unroll
-                    for (int g = 0; g < 4; ++g)
-                        v4[g] = *(const __attribute__((address_space(3))) f32x4 *)(st_l + 4 * ((P_WAVE ? 0 : BMQ) + 8 * g + 4 * h));
-                    bf16x8 pb[2];  // P (P wave) or dS (dS wave), two groups of 16 queries
-                    if constexpr (P_WAVE) {
-                        if (CAUSAL && (qs + off < kw0 + 31)) {
-                            // scores of queries before this lane's key -> -inf (P = 0); a query that
-                            // sees no key has lse = -inf: keep exp2 away from -inf + inf
-#pragma unroll
-                            for (int g = 0; g < 4; ++g) {
-#pragma unroll
-                                for (int u = 0; u < 4; ++u) {
-                                    v4[g][u] = fmaxf(v4[g][u], -1e30f);
-                                    if (qs + 8 * g + 4 * h + u + off < key) sc[4 * g + u] = -__builtin_inff();
-                                }
-                            }
-                        }
-#pragma unroll
-                        for (int r = 0; r < 16; ++r)
-                            pb[r >> 3][r & 7] = (bf16)fast_exp2(fmaf(sc[r], c_log2, -v4[r >> 2][r & 3] * kLog2e));
-                        if (ch == 0) {
-#pragma unroll
-                            for (int t = 0; t < 2; ++t) lds_write16(p_l, (t * 64 + lane) * 16, __builtin_bit_cast(u32x4, pb[t]));
-                        }
-                    } else {
-#pragma unroll
-                        for (int t = 0; t < 2; ++t) {
-                            const bf16x8 pv = __builtin_bit_cast(bf16x8, *(const __attribute__((address_space(3))) u32x4 *)(p_l + (t * 64 + lane) * 16));
-#pragma unroll
-                            for (int e = 0; e < 8; ++e) {
-                                const int r = 8 * t + e;
-                                pb[t][e] = (bf16)((float)pv[e] * (sc[r] - v4[r >> 2][r & 3]));
-                            }
-                        }
-                    }
-                    // second product: dV^T += dO^T P or dK^T += Q^T dS over this wave's columns
-                    static_for<0, 2 * NDBH>([&](auto C) __attribute__((always_inline)) {
-                        constexpr int c = decltype(C)::value, t = c / NDBH, db = c % NDBH;
-                        const bf16x4 lo = lds_read_tr(t_l, to[db][0] + 16 * t * 2 * D);
-                        const bf16x4 hi = lds_read_tr(t_l, to[db][1] + 16 * t * 2 * D);
-                        acc[db] = mfma(__builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7), pb[t], acc[db]);
-                        __builtin_amdgcn_sched_barrier(0);
-                    });
+                if (cur) second(gst(S), sst(S), pst(B), q_start + i * BMQ, sc);
+            } else {
+                if constexpr (!decltype(FIRST)::value) {
+                    if (keys_ok) second(qst(SP{}), sst(SP{}), pst(BP{}), 0, sc);
                 }
+                if constexpr (kSplit) {
+                    barrier_wait_vmem_upto<15>();
+                    load_q(i + 2, SP{});
+                }
+                if (cur) first(gst(S), sst(S), sc);
             }
-            wait_vmem();
-            __syncthreads();
+            // loads issued after block i + 1's: Q of block i + 2 (P waves, d = 256) or dO of block
+            // i + 2 (dS waves); at d = 192 the P waves' last loads are block i + 1's Q
+            constexpr int NV = (P_WAVE && !kSplit) ? 0 : NQL;
+            wait_vmem_upto<NV>();
+            store_lse(SN{}, BP{});  // lse of block i + 1 (parity 1 - B)
+            barrier_wait_vmem_upto<NV>();
         };
 
-        using I0 = std::integral_constant<int, 0>;
-        using I1 = std::integral_constant<int, 1>;
-        using I2 = std::integral_constant<int, 2>;
         using F = std::false_type;
         for (int gq = 0; gq < G; ++gq) {
             bind_query_head(qh0 + gq);
-            load_blk(0, I0{});  // the previous query head's last step ended with a barrier
+            // blocks 0 and 1; the previous query head's last step ended with a barrier, and its
+            // loads past the end complete before these (each wave's loads complete in order)
+            load_g(0, I0{}, I0{});
+            load_q(0, I0{});
+            load_g(1, I1{}, I1{});
+            if constexpr (kSplit) load_q(1, I1{});  // at d = 192 the first step loads it
             wait_vmem();
+            store_lse(I0{}, I0{});
+            store_lse(I1{}, I1{});
             __syncthreads();
             if (nsteps == 0) continue;
             step(0, I0{}, I0{}, std::true_type{});
@@ -634,14 +722,20 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv3_kernel(
             if (i < n) step(i++, I2{}, I1{}, F{});
         }
     };
-    if (pwave)
-        run(std::true_type{});
-    else
-        run(std::false_type{});
-
+    if (pwave) {
+        if (ch == 0)
+            run(std::true_type{}, I0{});
+        else
+            run(std::true_type{}, I1{});
+    } else {
+        if (ch == 0)
+            run(std::false_type{}, I0{});
+        else
+            run(std::false_type{}, I1{});
+    }
     if (key < Nk) {
         bf16 *row = (pwave ? dV : dK) + hoff + (size_t)key * D;
-        const float f = pwave ? 1.f : scale;
+        const float f = pwave ? 1.f : -scale;
 #pragma unroll
         for (int db = 0; db < NDBH; ++db) {
 #pragma unroll

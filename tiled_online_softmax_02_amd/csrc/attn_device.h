@@ -174,6 +174,15 @@ __device__ __forceinline__ void buffer_load_lds16(__amdgpu_buffer_rsrc_t r, lds_
 // Wait until this wave's vector-memory loads (including direct LDS loads) are done.
 __device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 
+// Wait until at most N of this wave's vector-memory loads (direct LDS loads included) are
+// outstanding; loads complete in the order they were issued.
+template <int N>
+__device__ __forceinline__ void wait_vmem_upto()
+{
+    static_assert(N >= 0 && N < 16, "vmcnt field is 4 bits here");
+    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+
 // Workgroup barrier that first waits until at most N of this wave's vector-memory loads
 // (direct LDS loads included) are outstanding and all its LDS accesses are done.  Unlike
 // __syncthreads() it carries no release fence, which would wait for every load in flight;
