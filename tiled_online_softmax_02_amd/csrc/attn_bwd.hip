@@ -903,15 +903,15 @@ __global__ __launch_bounds__(64 * dq_waves<D>(), D >= 192 ? 1 : 8 / dq_waves<D>(
             asm volatile("" : "+v"(go[i]));
         }
     }
-    auto load_blk = [&](int j, auto par) __attribute__((always_inline)) {
-        // rows past Nk read as zeros
+    // direct load I of key block j: K instructions, then V instructions; rows past Nk read as zeros
+    auto load_part = [&](int j, auto par, auto I) __attribute__((always_inline)) {
+        constexpr int i = decltype(I)::value;
         const int r0 = min(j * kQBN, Nk);
-        const __amdgpu_buffer_rsrc_t rkj = make_rsrc(K + hoff_k + (size_t)r0 * D, (uint32_t)(Nk - r0) * D * 2);
-        const __amdgpu_buffer_rsrc_t rvj = make_rsrc(V + hoff_k + (size_t)r0 * D, (uint32_t)(Nk - r0) * D * 2);
-#pragma unroll
-        for (int i = 0; i < kLoadNI; ++i) buffer_load_lds16(rkj, kst_l(par) + 1024 * (w * kLoadNI + i), (uint32_t)go[i]);
-#pragma unroll
-        for (int i = 0; i < kLoadNI; ++i) buffer_load_lds16(rvj, vst_l(par) + 1024 * (w * kLoadNI + i), (uint32_t)go[i]);
+        const __amdgpu_buffer_rsrc_t rj = make_rsrc((i < kLoadNI ? K : V) + hoff_k + (size_t)r0 * D, (uint32_t)(Nk - r0) * D * 2);
+        buffer_load_lds16(rj, (i < kLoadNI ? kst_l(par) : vst_l(par)) + 1024 * (w * kLoadNI + i % kLoadNI), (uint32_t)go[i % kLoadNI]);
+    };
+    auto load_blk = [&](int j, auto par) __attribute__((always_inline)) {
+        static_for<0, 2 * kLoadNI>([&](auto I) __attribute__((always_inline)) { load_part(j, par, I); });
     };
 
     using P0 = std::integral_constant<int, 0>;
@@ -933,7 +933,9 @@ __global__ __launch_bounds__(64 * dq_waves<D>(), D >= 192 ? 1 : 8 / dq_waves<D>(
     // CH: an unmasked block, run as chunks (below); otherwise the plain step
     auto step = [&](int j, auto par, auto CH) __attribute__((always_inline)) {
         using PN = std::integral_constant<int, 1 - decltype(par)::value>;
-        load_blk(j + 1, PN{});  // past the last block: zeros into the free stage, never read
+        // past the last block: zeros into the free stage, never read; the chunked step issues the
+        // loads one every second chunk from chunk 1 on
+        if constexpr (!decltype(CH)::value) load_blk(j + 1, PN{});
         const lds_char *ks = kst_l(par);
         const lds_char *vs = vst_l(par);
         const int k0 = j * kQBN;
@@ -1026,6 +1028,7 @@ __global__ __launch_bounds__(64 * dq_waves<D>(), D >= 192 ? 1 : 8 / dq_waves<D>(
                 } else if constexpr (ph == 5 && i < L / 2) {
                     ds_of(K1{}, std::integral_constant<int, 8 + 16 * i / L>{}, std::integral_constant<int, 8 + 16 * (i + 1) / L>{});
                 }
+                if constexpr (c % 2 == 1 && c / 2 < 2 * kLoadNI) load_part(j + 1, PN{}, std::integral_constant<int, c / 2>{});
                 __builtin_amdgcn_sched_barrier(0);
             });
         } else {

@@ -175,6 +175,11 @@ __global__ __launch_bounds__(64 * fwd_waves<D>(), fwd_min_blocks<D>()) void fwd_
 #pragma unroll
             for (int i = 0; i < kLoadNI; ++i) buffer_load_lds16(rj, tile + 1024 * (w * kLoadNI + i), (uint32_t)go[i]);
         };
+        auto load_part = [&](const bf16 *src, lds_char *tile, int j, int i) __attribute__((always_inline)) {
+            const int r0 = min(j * kFwdBN, kv_lim);
+            const __amdgpu_buffer_rsrc_t rj = make_rsrc(src + hoff_k + (size_t)r0 * D, (uint32_t)(kv_lim - r0) * D * 2);
+            buffer_load_lds16(rj, tile + 1024 * (w * kLoadNI + i), (uint32_t)go[i]);
+        };
         auto load_k = [&](int j, auto par) __attribute__((always_inline)) { load_blk(K, kstage(par), j); };
         auto load_v = [&](int j, auto par) __attribute__((always_inline)) { load_blk(V, vstage(par), j); };
 
@@ -307,6 +312,7 @@ __global__ __launch_bounds__(64 * fwd_waves<D>(), fwd_min_blocks<D>()) void fwd_
                     if constexpr (!(last && is_s(decltype(F)::value))) fr[decltype(F)::value] = fetch(F);
                 });
                 static_assert(NS / 2 == NPV / 2, "phases S1 and V1 must have equal length");
+                static_assert(4 * kLoadNI <= NC, "the direct loads fit in the step's odd chunks");
                 constexpr int PH = NS / 2;  // chunks per phase
                 static_for<0, NC>([&](auto C) __attribute__((always_inline)) {
                     constexpr int c = decltype(C)::value;
@@ -320,8 +326,10 @@ __global__ __launch_bounds__(64 * fwd_waves<D>(), fwd_min_blocks<D>()) void fwd_
                         constexpr int p = c < NS / 2 + NPV / 2 ? c - NS / 2 : c - NS;
                         oacc[p % NDB] = mfma(fc, pb[p / NDB], oacc[p % NDB]);
                     }
-                    if constexpr (c == 1) load_k(j + 2, par);
-                    if constexpr (c == 3) load_v(j + 1, PN{});
+                    // the direct loads one every second chunk from chunk 1 on, K of block j + 2 and then
+                    // V of block j + 1, rather than in two bursts (at d = 256, 8 instructions each)
+                    if constexpr (c % 2 == 1 && c / 2 < kLoadNI) load_part(K, kstage(par), j + 2, c / 2);
+                    else if constexpr (c % 2 == 1 && c / 2 < 2 * kLoadNI) load_part(V, vstage(PN{}), j + 1, c / 2 - kLoadNI);
                     if constexpr (c < 2 * PH) {
                         // exponentials: keys 0..31 during S1, 32..63 during V1; chunk i of the phase
                         // takes elements [16 i / PH, 16 (i + 1) / PH)
