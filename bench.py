@@ -94,9 +94,11 @@ def kernel_algorithmic_flop(kernel, w) -> float:
 def stored_traffic(kernel: str, workload: str):
     """HBM bytes per launch from committed rocprofv3 counter summaries, or None when the
     kernel sources changed since the counters were taken.  The split-key forward is two
-    launches (pieces, then their merge): its traffic is their sum."""
+    launches (pieces, then their merge): its traffic is their sum.  With few query rows per head
+    the pieces come from the decoding kernel (fwd_decode), else from the forward kernel (fwd)."""
     if kernel == "fwd_splitkv":
-        parts = [stored_traffic("fwd", workload), stored_traffic("combine", workload)]
+        pieces = "fwd_decode" if os.path.exists(os.path.join(ROOT, "profiles", "hbm_traffic_fwd_decode_%s.txt" % workload)) else "fwd"
+        parts = [stored_traffic(pieces, workload), stored_traffic("combine", workload)]
         return None if None in parts else sum(parts)
     path = os.path.join(ROOT, "profiles", "hbm_traffic_%s_%s.txt" % (kernel, workload))
     if not os.path.exists(path):
@@ -431,7 +433,7 @@ def run_workload(w, args, timer, monitor, dev):
     qk = Hk != H or Nk != N
     split = w.name == "dec"  # decoding: the split-key forward (partial pieces, then their merge)
     if split:
-        ns = A.attn_fwd_splitkv_default_splits(B, H, N, Nk, d)
+        ns = A.attn_fwd_splitkv_default_splits_qk(B, H, Hk, N, Nk, d)
         ws_bytes = A.attn_fwd_splitkv_workspace_size(B, H, N, d, ns)
         ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
     causal, scale = w.causal, w.scale

@@ -100,6 +100,10 @@ int attn_fwd_qk(const void *q, const void *k, const void *v, void *o, float *lse
  * `workspace`; a second launch merges the pieces of each row with the merge
  * rule of the running maxima and sums: lse = log sum_s exp(lse_s),
  * O = sum_s exp(lse_s - lse) O_s.  Results equal attn_fwd_qk's up to rounding.
+ * With at most 4 query rows per head and d = 64, 128 or 256 (decoding) the
+ * pieces come from a kernel that reads each piece's keys and values once for
+ * all query rows of a K/V head (in groups of up to 4 rows) and keeps P in fp32;
+ * otherwise from the tiled forward kernel.
  * workspace: caller-owned device memory of at least
  * attn_fwd_splitkv_workspace_size(B, H, Nq, d, num_splits) bytes, 16-byte
  * aligned, not overlapping any input or output; its contents on entry do not
@@ -132,12 +136,18 @@ int attn_fwd_splitkv_noalloc(const void *q, const void *k, const void *v, void *
  * kernel); -1 for invalid arguments or a size of 2^62 bytes or more. */
 long long attn_fwd_splitkv_workspace_size(int B, int H, int Nq, int d, int num_splits);
 
-/* A number of pieces that gives the GPU about one workgroup per compute unit
- * while keeping at least two 64-key blocks per piece; 1 when splitting does
- * not help or the arguments are invalid.  (A launch heuristic: the pages say
- * only that small-query attention is split across thread blocks, "GPU
- * Programming and Kernel Optimization", item 59, and that too few blocks leave
- * the GPU underused.) */
+/* A number of pieces for attn_fwd_splitkv with Hk K/V heads under H query heads
+ * (Hk divides H): enough workgroups to fill the GPU (about one 8-wave workgroup
+ * per compute unit; with at most 4 query rows per head, where the pieces come
+ * from 4-wave workgroups over groups of up to 4 query rows of a K/V head, about
+ * 512 of them) while keeping at least two 64-key blocks per piece and at most
+ * 128 pieces; 1 when splitting does not help or the arguments are invalid.  (A
+ * launch heuristic: the pages say only that small-query attention is split
+ * across thread blocks, "GPU Programming and Kernel Optimization", item 59, and
+ * that too few blocks leave the GPU underused.) */
+int attn_fwd_splitkv_default_splits_qk(int B, int H, int Hk, int Nq, int Nk, int d);
+
+/* attn_fwd_splitkv_default_splits_qk with Hk = H. */
 int attn_fwd_splitkv_default_splits(int B, int H, int Nq, int Nk, int d);
 
 /* Forward pass on 8-bit inputs ("FlashAttention v3 (Tri Dao et al.)",

@@ -264,6 +264,14 @@ void check_splitkv_sizes()
                         ++g_fail;
                         std::fprintf(stderr, "MISMATCH size helpers at %d %d %d %d: %lld %d\n", b, h, nq, d, w, ds);
                     }
+                    for (int hk : vals) {
+                        const int dq = attn_fwd_splitkv_default_splits_qk(b, h, hk, nq, INT_MAX, d);
+                        ++g_calls;
+                        if (dq < 1 || dq > 256) {
+                            ++g_fail;
+                            std::fprintf(stderr, "MISMATCH default splits at %d %d %d %d %d: %d\n", b, h, hk, nq, d, dq);
+                        }
+                    }
                 }
     // the no-allocation variant: the first size past its static buffer
     Sizes t;

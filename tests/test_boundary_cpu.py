@@ -35,7 +35,7 @@ def declared_functions():
 def test_header_declares_the_expected_entry_points():
     assert declared_functions() == sorted([
         "attn_fwd", "attn_fwd_qk", "attn_fwd_splitkv", "attn_fwd_splitkv_workspace_size", "attn_fwd_splitkv_noalloc",
-        "attn_fwd_splitkv_default_splits", "attn_fwd_fp8", "attn_bwd", "attn_bwd_qk", "attn_bwd_preprocess", "attn_bwd_dkdv",
+        "attn_fwd_splitkv_default_splits", "attn_fwd_splitkv_default_splits_qk", "attn_fwd_fp8", "attn_bwd", "attn_bwd_qk", "attn_bwd_preprocess", "attn_bwd_dkdv",
         "attn_bwd_dq", "attn_bwd_dq_delta", "attn_status_string", "attn_last_hip_error"])
 
 
@@ -202,9 +202,18 @@ def test_splitkv_workspace_size_and_default_splits(lib):
     assert A.attn_fwd_splitkv_workspace_size(1, 1, 1, 96, 1) == -1
     assert A.attn_fwd_splitkv_workspace_size(1, 1, 1, 64, 0) == -1
     assert A.attn_fwd_splitkv_workspace_size(1, 1, -1, 64, 2) == -1
-    # decoding: 1 query row per head, 64 heads, 16384 keys -> enough pieces for ~256 workgroups
-    assert A.attn_fwd_splitkv_default_splits(4, 16, 1, 16384, 128) == 4
-    assert A.attn_fwd_splitkv_default_splits(2, 16, 1, 65536, 128) == 8
+    # decoding: 1 query row per head -> enough pieces for ~512 workgroups of the decoding kernel
+    assert A.attn_fwd_splitkv_default_splits(4, 16, 1, 16384, 128) == 8     # 64 heads
+    assert A.attn_fwd_splitkv_default_splits(2, 16, 1, 65536, 128) == 16    # 32 heads
+    # grouped heads: the rows of a K/V head share workgroups (up to 4 rows each), so fewer items
+    assert A.attn_fwd_splitkv_default_splits_qk(2, 32, 8, 1, 32768, 128) == 32   # 16 items
+    assert A.attn_fwd_splitkv_default_splits_qk(2, 64, 8, 1, 32768, 128) == 16   # 8 rows: 2 groups
+    assert A.attn_fwd_splitkv_default_splits_qk(2, 16, 16, 1, 65536, 128) == \
+        A.attn_fwd_splitkv_default_splits(2, 16, 1, 65536, 128)
+    assert A.attn_fwd_splitkv_default_splits_qk(2, 16, 3, 1, 4096, 128) == 1     # Hk must divide H
+    # d = 192 and more than 4 rows per head: matrix-instruction pieces, ~256 workgroups
+    assert A.attn_fwd_splitkv_default_splits(2, 16, 1, 65536, 192) == 8
+    assert A.attn_fwd_splitkv_default_splits(2, 16, 8, 65536, 128) == 8
     # few keys: at least two 64-key blocks per piece
     assert A.attn_fwd_splitkv_default_splits(1, 1, 1, 256, 128) == 2
     assert A.attn_fwd_splitkv_default_splits(1, 1, 1, 64, 128) == 1

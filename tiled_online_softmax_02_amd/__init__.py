@@ -93,6 +93,8 @@ def library() -> ctypes.CDLL:
             lib.attn_fwd_splitkv_workspace_size.restype = ctypes.c_longlong
             lib.attn_fwd_splitkv_default_splits.argtypes = [_I, _I, _I, _I, _I]
             lib.attn_fwd_splitkv_default_splits.restype = _I
+            lib.attn_fwd_splitkv_default_splits_qk.argtypes = [_I, _I, _I, _I, _I, _I]
+            lib.attn_fwd_splitkv_default_splits_qk.restype = _I
             _lib = lib
     return _lib
 
@@ -151,6 +153,10 @@ def attn_fwd_splitkv_workspace_size(B, H, Nq, d, num_splits) -> int:
 
 def attn_fwd_splitkv_default_splits(B, H, Nq, Nk, d) -> int:
     return int(library().attn_fwd_splitkv_default_splits(B, H, Nq, Nk, d))
+
+
+def attn_fwd_splitkv_default_splits_qk(B, H, Hk, Nq, Nk, d) -> int:
+    return int(library().attn_fwd_splitkv_default_splits_qk(B, H, Hk, Nq, Nk, d))
 
 
 def attn_fwd_fp8(q, k, v, descale_q, descale_k, descale_v, o, lse, B, H, Hk, Nq, Nk, d, causal, scale,
@@ -237,7 +243,7 @@ def fwd_splitkv(q, k, v, causal: bool = False, scale: float | None = None, num_s
     Hk, Nk = k.shape[1], k.shape[2]
     scale = default_scale(d) if scale is None else scale
     if num_splits is None:
-        num_splits = attn_fwd_splitkv_default_splits(B, H, Nq, Nk, d)
+        num_splits = attn_fwd_splitkv_default_splits_qk(B, H, Hk, Nq, Nk, d)
     o = torch.empty_like(q)
     lse = torch.empty((B, H, Nq), dtype=torch.float32, device=q.device)
     nbytes = attn_fwd_splitkv_workspace_size(B, H, Nq, d, num_splits)

@@ -345,11 +345,16 @@ long long attn_fwd_splitkv_workspace_size(int B, int H, int Nq, int d, int num_s
     return attn::fwd_split_workspace_bytes(B, H, Nq, d, num_splits);
 }
 
-int attn_fwd_splitkv_default_splits(int B, int H, int Nq, int Nk, int d)
+int attn_fwd_splitkv_default_splits_qk(int B, int H, int Hk, int Nq, int Nk, int d)
 {
     bool empty = false;
-    if (check_shape(B, H, H, Nq, Nk, d, &empty) != ATTN_OK) return 1;
-    return attn::fwd_split_default(B, H, Nq, Nk, d);
+    if (check_shape(B, H, Hk, Nq, Nk, d, &empty) != ATTN_OK) return 1;
+    return attn::fwd_split_default(B, H, Hk, Nq, Nk, d);
+}
+
+int attn_fwd_splitkv_default_splits(int B, int H, int Nq, int Nk, int d)
+{
+    return attn_fwd_splitkv_default_splits_qk(B, H, H, Nq, Nk, d);
 }
 
 int attn_bwd_preprocess(const void *o, const void *dout, float *delta, int B, int H, int N, int d, void *stream)

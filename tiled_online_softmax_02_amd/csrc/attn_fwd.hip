@@ -451,15 +451,19 @@ __global__ __launch_bounds__(256) void fwd_combine_kernel(const float *__restric
     const long long row = (long long)blockIdx.x * 4 + (threadIdx.x >> 6);
     const int lane = threadIdx.x & 63;
     if (row >= rows) return;
+    // the pieces' lse: lanes take pieces s = lane, lane + 64, ..., then a wave maximum
     float m = -__builtin_inff();
-    for (int s = 0; s < n_splits; ++s) m = fmaxf(m, LP[(size_t)s * rows + row]);
+    for (int s = lane; s < n_splits; s += 64) m = fmaxf(m, LP[(size_t)s * rows + row]);
+#pragma unroll
+    for (int x = 32; x > 0; x >>= 1) m = fmaxf(m, __shfl_xor(m, x));
     float acc[E] = {};
     float wsum = 0.f;
     if (m != -__builtin_inff()) {
+        // no branch on empty pieces (weight 0), so that the loads of several pieces are in flight
+#pragma unroll 4
         for (int s = 0; s < n_splits; ++s) {
             const float ls = LP[(size_t)s * rows + row];
-            if (ls == -__builtin_inff()) continue;
-            const float wgt = expf(ls - m);
+            const float wgt = (ls == -__builtin_inff()) ? 0.f : expf(ls - m);
             wsum += wgt;
             const float *op = OP + ((size_t)s * rows + row) * D + lane * E;
 #pragma unroll
@@ -470,6 +474,230 @@ __global__ __launch_bounds__(256) void fwd_combine_kernel(const float *__restric
 #pragma unroll
     for (int e = 0; e < E; ++e) O[row * D + lane * E + e] = (bf16)(acc[e] * inv);
     if (lane == 0) LSE[row] = wsum > 0.f ? m + logf(wsum) : -__builtin_inff();
+}
+
+// ------------------------------------------------------------ decoding (a query row or two per head)
+
+// Split-key pieces for few query rows (Nq <= kDecRows), written in fwd_kernel<.., SPLIT>'s
+// workspace layout for fwd_combine_kernel.  The G Nq rows that share a K/V head (grouped-query
+// attention: the G query heads of the K/V head, Nq rows each) go to workgroups in groups of
+// kDecRows, so that K and V are read once per group.  With one or two rows the score tile of the matrix instructions
+// would be 1/32 or 1/16 useful, and the piece is bound by the rate at which K and V arrive; this
+// kernel streams them straight into registers instead.  A key row is D/8 lanes of 16 bytes; a wave
+// load covers 64 / (D/8) keys, each wave of the workgroup takes U loads of K and of V per tile,
+// and the next tile's loads are in flight while a tile is worked on.  Per key: q.k over the
+// lane's 8 elements with bf16 dot products in fp32, summed over the row's lanes by DPP adds;
+// the running maximum and sum of the online softmax per lane (every lane of a key slot sees the
+// same keys); O += p V in fp32.  At the end the key slots of a wave and then the four waves are
+// merged by the same rule as the pieces ("GPU Programming and Kernel Optimization", item 57).
+constexpr int kDecRows = 4;  // query rows per head up to which the decoding kernel is used; rows per workgroup
+template <int D>
+constexpr bool dec_supported() { return D == 64 || D == 128 || D == 256; }
+
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+// sum over the L lanes of an aligned group (L = 8, 16, 32), the result in every lane of the group
+template <int L>
+__device__ __forceinline__ float group_sum(float x)
+{
+    auto dpp_add = [](float v, auto CTRL) __attribute__((always_inline)) {
+        constexpr int ctrl = decltype(CTRL)::value;
+        return v + __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), ctrl, 0xf, 0xf, false));
+    };
+    x = dpp_add(x, std::integral_constant<int, 0xB1>{});   // quad_perm [1,0,3,2]: lanes i ^ 1
+    x = dpp_add(x, std::integral_constant<int, 0x4E>{});   // quad_perm [2,3,0,1]: lanes i ^ 2
+    x = dpp_add(x, std::integral_constant<int, 0x141>{});  // row_half_mirror: quad pairs of 8
+    if constexpr (L >= 16) x = dpp_add(x, std::integral_constant<int, 0x140>{});  // row_mirror: halves of 16
+    if constexpr (L >= 32) x += __shfl_xor(x, 16);
+    return x;
+}
+
+// unnormalised merge of (m, l, o) with another piece (m in exp2 units, -inf when empty)
+__device__ __forceinline__ void merge_piece(float &m, float &l, float *o, float m2, float l2, const float *o2)
+{
+    const float mn = fmaxf(m, m2);
+    const float a = (m == -__builtin_inff()) ? 0.f : fast_exp2(m - mn);
+    const float b = (m2 == -__builtin_inff()) ? 0.f : fast_exp2(m2 - mn);
+    l = l * a + l2 * b;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) o[e] = o[e] * a + o2[e] * b;
+    m = mn;
+}
+
+// NT: one row group per K/V head, so that every key and value is read by one workgroup alone:
+// non-temporal loads (12-15% faster there; where several groups read a K/V head again from the
+// caches they made that 39% slower).
+template <int D, bool CAUSAL, int R, bool NT>
+__global__ __launch_bounds__(256) void fwd_decode_kernel(const bf16 *__restrict__ Q, const bf16 *__restrict__ K,
+                                                         const bf16 *__restrict__ V, float *__restrict__ OP,
+                                                         float *__restrict__ LP, int Nq, int Nk, int H, int G,
+                                                         int n_groups, int n_splits, int split_keys, float c_log2)
+{
+    constexpr int LPR = D / 8;       // lanes per key row
+    constexpr int KPW = 64 / LPR;    // keys per wave load
+    constexpr int U = 4;             // loads of K and of V per lane and tile
+    constexpr int TK = 4 * U * KPW;  // keys per tile (four waves)
+    const int item = (int)blockIdx.x / n_splits;  // (b * Hk + K/V head) * n_groups + row group
+    const int split = (int)blockIdx.x - item * n_splits;
+    const int kvh = item / n_groups;
+    const int r0 = (item - kvh * n_groups) * R;  // first row of the group
+    const int w = wave_uniform((int)threadIdx.x >> 6);
+    const int lane = (int)threadIdx.x & 63;
+    const int c = lane % LPR, slot = lane / LPR;
+    const int Hk = H / G;
+    const int head0 = (kvh / Hk) * H + (kvh % Hk) * G;  // b * H + first query head of the K/V head
+    const size_t hoff_k = (size_t)kvh * (size_t)Nk * D;
+    const int off = Nk - Nq;  // bottom-right causal alignment: row q sees keys j <= q + off
+    const int nrows = G * Nq;  // row n of the K/V head: query head head0 + n / Nq, query n % Nq
+
+    // the lane's 8 elements of each query row of the group (zeros for rows past nrows)
+    bf16x2 q[R][4];
+    {
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+            const __amdgpu_buffer_rsrc_t rq = make_rsrc(Q + ((size_t)head0 * Nq + r0 + r) * D, r0 + r < nrows ? D * 2 : 0);
+            const u32x4 v = buffer_load16(rq, (uint32_t)(8 * c) * 2u);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const unsigned vi = v[i];  // bit_cast of a vector element read element 0 here
+                q[r][i] = __builtin_bit_cast(bf16x2, vi);
+            }
+        }
+    }
+    const long long k_lo_l = (long long)split * split_keys;
+    const int k_lo = (int)(k_lo_l < Nk ? k_lo_l : Nk);
+    const int k_hi = (int)(k_lo_l + split_keys < Nk ? k_lo_l + split_keys : Nk);
+    const int n_tiles = (k_hi - k_lo + TK - 1) / TK;
+    // last key each row sees
+    int klast[R];
+#pragma unroll
+    for (int r = 0; r < R; ++r) klast[r] = CAUSAL ? min(k_hi - 1, (r0 + r) % Nq + off) : k_hi - 1;
+
+    float m[R], l[R], o[R][8];
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+        m[r] = -__builtin_inff();
+        l[r] = 0.f;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) o[r][e] = 0.f;
+    }
+    constexpr float thr = 8.0f;  // offset moves when a score exceeds it by 2^8 (as in fwd_kernel)
+
+    u32x4 kb[2][U], vb[2][U];
+    // tile t: keys k_lo + t TK + (w U + u) KPW + slot; keys past k_hi read as zeros and are masked
+    auto load = [&](int t, auto BUF) __attribute__((always_inline)) {
+        constexpr int b = decltype(BUF)::value;
+        const int k0 = k_lo + t * TK;
+        const uint32_t bytes = (uint32_t)min(k_hi - k0, TK) * D * 2;  // rows of this tile only
+        const __amdgpu_buffer_rsrc_t rk = make_rsrc(K + hoff_k + (size_t)k0 * D, bytes);
+        const __amdgpu_buffer_rsrc_t rv = make_rsrc(V + hoff_k + (size_t)k0 * D, bytes);
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const uint32_t byte = (uint32_t)(((w * U + u) * KPW + slot) * D + 8 * c) * 2u;
+            kb[b][u] = __builtin_amdgcn_raw_buffer_load_b128(rk, (int)byte, 0, NT ? 2 : 0);
+            vb[b][u] = __builtin_amdgcn_raw_buffer_load_b128(rv, (int)byte, 0, NT ? 2 : 0);
+        }
+    };
+    auto work = [&](int t, auto BUF) __attribute__((always_inline)) {
+        constexpr int b = decltype(BUF)::value;
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int key = k_lo + t * TK + (w * U + u) * KPW + slot;
+            float vf[8];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                vf[2 * i] = __builtin_bit_cast(float, vb[b][u][i] << 16);
+                vf[2 * i + 1] = __builtin_bit_cast(float, vb[b][u][i] & 0xffff0000u);
+            }
+#pragma unroll
+            for (int r = 0; r < R; ++r) {
+                float s = 0.f;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const unsigned ki = kb[b][u][i];
+                    s = __builtin_amdgcn_fdot2_f32_bf16(q[r][i], __builtin_bit_cast(bf16x2, ki), s, false);
+                }
+                s = group_sum<LPR>(s);
+                s = (key <= klast[r]) ? s * c_log2 : -__builtin_inff();
+                if (__builtin_amdgcn_ballot_w64(s > m[r] + thr)) {
+                    const bool grow = s > m[r] + thr;
+                    const float mn = grow ? s : m[r];
+                    const float a = (grow && m[r] != -__builtin_inff()) ? fast_exp2(m[r] - mn) : (grow ? 0.f : 1.f);
+                    l[r] *= a;
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) o[r][e] *= a;
+                    m[r] = mn;
+                }
+                const float p = fast_exp2(s - (m[r] == -__builtin_inff() ? 0.f : m[r]));
+                l[r] += p;
+#pragma unroll
+                for (int e = 0; e < 8; ++e) o[r][e] = fmaf(p, vf[e], o[r][e]);
+            }
+        }
+    };
+    using B0 = std::integral_constant<int, 0>;
+    using B1 = std::integral_constant<int, 1>;
+    // two register buffers: the loads of tile t + 1 are in flight while tile t is worked on (the
+    // compiler waits on each buffer's loads before their first use; loads complete in order)
+    if (n_tiles > 0) load(0, B0{});
+    int t = 0;
+    for (; t + 1 < n_tiles; t += 2) {
+        load(t + 1, B1{});
+        work(t, B0{});
+        if (t + 2 < n_tiles) load(t + 2, B0{});
+        work(t + 1, B1{});
+    }
+    if (t < n_tiles) work(t, B0{});
+
+    // merge the key slots of the wave (lanes c, c + LPR, ...), then the four waves through LDS
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+#pragma unroll
+        for (int x = LPR; x < 64; x *= 2) {
+            float o2[8];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) o2[e] = __shfl_xor(o[r][e], x);
+            merge_piece(m[r], l[r], o[r], __shfl_xor(m[r], x), __shfl_xor(l[r], x), o2);
+        }
+    }
+    __shared__ float red[4][R][D + 2];
+    if (slot == 0) {
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) red[w][r][8 * c + e] = o[r][e];
+            if (c == 0) {
+                red[w][r][D] = m[r];
+                red[w][r][D + 1] = l[r];
+            }
+        }
+    }
+    __syncthreads();
+    if (w == 0 && slot == 0) {
+        const int n_heads = (int)gridDim.x / (n_splits * n_groups) * G;  // B * H
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+            if (r0 + r >= nrows) break;
+            for (int ww = 1; ww < 4; ++ww) {
+                float o2[8];
+#pragma unroll
+                for (int e = 0; e < 8; ++e) o2[e] = red[ww][r][8 * c + e];
+                merge_piece(m[r], l[r], o[r], red[ww][r][D], red[ww][r][D + 1], o2);
+            }
+            const size_t prow = ((size_t)split * n_heads + head0) * Nq + r0 + r;  // consecutive heads' rows are consecutive
+            const float inv = l[r] > 0.f ? 1.f / l[r] : 0.f;
+            f32x4 lo, hi;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                lo[e] = o[r][e] * inv;
+                hi[e] = o[r][4 + e] * inv;
+            }
+            *(f32x4 *)(OP + prow * D + 8 * c) = lo;
+            *(f32x4 *)(OP + prow * D + 8 * c + 4) = hi;
+            // lse = ln(2^m l) = (m + log2 l) ln 2
+            if (c == 0) LP[prow] = l[r] > 0.f ? (m[r] + __log2f(l[r])) * 0.69314718055994530942f : -__builtin_inff();
+        }
+    }
 }
 
 template <int D, bool CAUSAL>
@@ -483,9 +711,34 @@ hipError_t launch_fwd_split_t(const FwdArgs &a, int n_splits, float *op, float *
     const int blocks = (a.Nk + kFwdBN - 1) / kFwdBN;
     const int split_blocks = (blocks + n_splits - 1) / n_splits;
     const float c_log2 = a.scale * kLog2e;
-    hipLaunchKernelGGL((fwd_kernel<D, CAUSAL, true>), dim3((unsigned)G), dim3(kThreads), 0, (hipStream_t)a.stream,
-                       (const bf16 *)a.q, (const bf16 *)a.k, (const bf16 *)a.v, (bf16 *)a.o, a.lse, a.Nq, a.Nk,
-                       a.H, a.H / a.Hk, n_qtiles, a.scale, c_log2, n_splits, split_blocks, op, lp, a.dev.nx, 0);
+    if (dec_supported<D>() && a.Nq <= kDecRows) {
+        const int rows_kv = (a.H / a.Hk) * a.Nq;  // query rows per K/V head
+        const int n_groups = (rows_kv + kDecRows - 1) / kDecRows;
+        const long long Gd = (long long)a.B * a.Hk * n_groups * n_splits;
+        const int split_keys = split_blocks * kFwdBN;
+        auto go = [&](auto RR, auto NT) {
+            hipLaunchKernelGGL((fwd_decode_kernel<D, CAUSAL, decltype(RR)::value, decltype(NT)::value>), dim3((unsigned)Gd),
+                               dim3(256), 0, (hipStream_t)a.stream, (const bf16 *)a.q, (const bf16 *)a.k,
+                               (const bf16 *)a.v, op, lp, a.Nq, a.Nk, a.H, a.H / a.Hk, n_groups, n_splits, split_keys,
+                               c_log2);
+        };
+        using R1 = std::integral_constant<int, 1>;
+        using R2 = std::integral_constant<int, 2>;
+        using R4 = std::integral_constant<int, 4>;
+        static_assert(kDecRows == 4, "row counts 1, 2, 4");
+        if (rows_kv == 1)
+            go(R1{}, std::true_type{});
+        else if (rows_kv == 2)
+            go(R2{}, std::true_type{});
+        else if (n_groups == 1)
+            go(R4{}, std::true_type{});
+        else
+            go(R4{}, std::false_type{});
+    } else {
+        hipLaunchKernelGGL((fwd_kernel<D, CAUSAL, true>), dim3((unsigned)G), dim3(kThreads), 0, (hipStream_t)a.stream,
+                           (const bf16 *)a.q, (const bf16 *)a.k, (const bf16 *)a.v, (bf16 *)a.o, a.lse, a.Nq, a.Nk,
+                           a.H, a.H / a.Hk, n_qtiles, a.scale, c_log2, n_splits, split_blocks, op, lp, a.dev.nx, 0);
+    }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     const long long rows = (long long)a.B * a.H * a.Nq;
@@ -537,14 +790,24 @@ long long fwd_split_grid_size(int B, int H, int Nq, int n_splits)
     return (long long)B * H * ((Nq + fwd_bm<64>() - 1) / fwd_bm<64>()) * n_splits;
 }
 
-int fwd_split_default(int B, int H, int Nq, int Nk, int d)
+int fwd_split_default(int B, int H, int Hk, int Nq, int Nk, int d)
 {
-    // about one workgroup per compute unit (measured best for decoding shapes: one 8-wave
-    // workgroup already fills a compute unit), at least two key blocks per piece
-    const int bm = d == 128 ? fwd_bm<128>() : fwd_bm<64>();  // 128 rows for d = 64, 192 and 256
-    const long long base = (long long)B * H * ((Nq + bm - 1) / bm);
+    // Matrix-instruction pieces: about one workgroup per compute unit (one 8-wave workgroup already
+    // fills a compute unit).  Decoding pieces (Nq <= kDecRows, 4-wave workgroups over row groups of
+    // a K/V head): about 512 workgroups (measured flat from 256 to 1024 with one query head per K/V
+    // head; grouped heads, with fewer items, needed 512).  At least two key blocks per piece.
+    long long base, target;
+    if ((d == 64 || d == 128 || d == 256) && Nq <= kDecRows && Hk > 0 && H % Hk == 0) {
+        const long long rows_kv = (long long)(H / Hk) * Nq;
+        base = (long long)B * Hk * ((rows_kv + kDecRows - 1) / kDecRows);
+        target = 512;
+    } else {
+        const int bm = d == 128 ? fwd_bm<128>() : fwd_bm<64>();  // 128 rows for d = 64, 192 and 256
+        base = (long long)B * H * ((Nq + bm - 1) / bm);
+        target = 256;
+    }
     const int blocks = (Nk + kFwdBN - 1) / kFwdBN;
-    long long s = base > 0 ? (256 + base - 1) / base : 1;
+    long long s = base > 0 ? (target + base - 1) / base : 1;
     s = s < blocks / 2 ? s : blocks / 2;
     s = s < 128 ? s : 128;
     return s < 1 ? 1 : (int)s;

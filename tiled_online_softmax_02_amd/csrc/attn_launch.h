@@ -60,7 +60,7 @@ hipError_t launch_bwd_dq_delta(const BwdArgs &a);
 long long fwd_grid_size(int B, int H, int Nq);
 long long fwd_split_grid_size(int B, int H, int Nq, int n_splits);
 long long fwd_split_workspace_bytes(int B, int H, int Nq, int d, int n_splits);
-int fwd_split_default(int B, int H, int Nq, int Nk, int d);
+int fwd_split_default(int B, int H, int Hk, int Nq, int Nk, int d);
 long long bwd_dkdv_grid_size(int B, int Hk, int Nk);
 long long bwd_dq_grid_size(int B, int H, int Nq);
 
