@@ -97,3 +97,39 @@ def test_decode_large_scores_rescale():
     rel = (np.abs(f64(lse) - lse_ref) / np.abs(lse_ref)).max()
     note("  max|dO|=%.3e  max rel lse=%.3e" % (err, rel))
     assert err <= O_TOL and rel <= LSE_RTOL
+
+
+def draw_cases(n, seed):
+    g = np.random.default_rng(seed)
+    cases = []
+    for i in range(n):
+        d = int(g.choice([64, 128, 256]))
+        Hk = int(g.choice([1, 2, 4]))
+        G = int(g.choice([1, 2, 3, 4]))
+        Nq = int(g.integers(1, 5))
+        Nk = int(g.integers(1, 5000))
+        cases.append((i, int(g.integers(1, 3)), Hk * G, Hk, Nq, Nk, d, bool(g.integers(0, 2)), int(g.integers(1, 41))))
+    return cases
+
+
+@pytest.mark.parametrize("case", draw_cases(16, 2027), ids=lambda c: "case%d" % c[0])
+def test_decode_random_shapes(case):
+    """Seeded random decoding shapes: 1-4 query rows per head and 1-4 query heads per K/V head,
+    so 1-16 rows per K/V head in one or several row groups; 1-4999 keys, 1-40 pieces."""
+    i, B, H, Hk, Nq, Nk, d, causal, ns = case
+    note("random case %d: B=%d H=%d Hk=%d Nq=%d Nk=%d d=%d causal=%d splits=%d seed=%d" % (i, B, H, Hk, Nq, Nk, d, causal, ns, 500 + i))
+    scale = softmax_scale(d)
+    inp = make_inputs(B, H, Nq, d, nk=Nk, seed=500 + i, Hk=Hk)
+    q, k, v = (inp[n].to(DEV) for n in "qkv")
+    o, lse = A.fwd_splitkv(q, k, v, causal=causal, scale=scale, num_splits=ns)
+    torch.cuda.synchronize()
+    G = H // Hk
+    o_ref, lse_ref = oracle.attn_fwd(f64(inp["q"]), np.repeat(f64(inp["k"]), G, axis=1), np.repeat(f64(inp["v"]), G, axis=1), causal, scale)
+    o, lse = f64(o), f64(lse)
+    masked = np.isneginf(lse_ref)
+    assert np.all(np.isneginf(lse[masked])) and np.all(o[masked] == 0), "rows that see no key"
+    fin = ~masked
+    rel = (np.abs(lse[fin] - lse_ref[fin]) / np.abs(lse_ref[fin])).max() if fin.any() else 0.0
+    err = np.abs(o - o_ref).max()
+    note("  max|dO|=%.3e  max rel lse=%.3e  rows without keys %d" % (err, rel, int(masked.sum())))
+    assert np.all(np.isfinite(o)) and err <= O_TOL and rel <= LSE_RTOL, (err, rel)
