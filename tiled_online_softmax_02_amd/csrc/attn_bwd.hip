@@ -13,9 +13,10 @@
 // Splitting dQ into its own kernel keeps every sum in registers of a single
 // workgroup: no atomics, bitwise reproducible results.
 //
-// Two dK/dV kernels, both splitting each key block's work between the two waves of a SIMD (one
-// computes P and dV, the other dS and dK): bwd_dkdv2_kernel for d <= 128 and bwd_dkdv3_kernel for
-// d = 192 and 256, where each wave also takes one half of the columns of dK and dV.
+// Two dK/dV kernels: bwd_dkdv2_kernel for d <= 128 splits each key block's work between the two
+// waves of a SIMD (one computes P and dV, the other dS and dK); bwd_dkdv4_kernel for d = 192 and
+// 256 runs one wave per SIMD with up to 512 registers, each wave doing all four products for its
+// keys.
 //
 // MFMA layouts follow attn_device.h.  In the dK/dV kernels the scores are
 // computed as S = Q K^T (each lane: one key, 16 queries of a 32-query block),
@@ -386,41 +387,32 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv2_kernel(const Dkdv2Args args)
     }
 }
 
-// ------------------------------------------------------------ dK / dV, paired waves (d = 192, 256)
+// ------------------------------------------------------------ dK / dV, one wave per SIMD (d = 192, 256)
 
-// The paired-wave scheme of bwd_dkdv2_kernel for the wide heads: eight waves in four SIMD pairs;
-// wave w has role w / 4 (P wave or dS wave), key group w % 2 (32 keys; 64 keys per workgroup)
-// and column half (w / 2) % 2 of dK and dV.  Both waves of a column pair need the whole of S (P
-// waves) or dP (dS waves) and each accumulates its half of the columns, which keeps every wave's
-// registers (half an accumulator) under the 256 that two waves per SIMD allow.  At d = 192 each
-// wave forms the first product over all of d; at d = 256 each forms it over its own half of d
-// and the pair adds the two partial sums through LDS.  Query blocks are 32 rows so that three
-// stages of Q and dO fit in LDS.  The P wave of column half 0 leaves P in LDS for the dS waves,
-// one block behind.  As in bwd_dkdv2_kernel, the dS waves hold -V so that their product starts
-// from D and -dS is one multiply per element, lse reaches LDS in log2 units, and LDS fragments
-// are fetched two matrix instructions ahead with the vector work placed under the matrix
-// instructions of the other 16 queries.
+// Four waves, one per SIMD with up to 512 registers.  Wave w owns 32 keys (128 per workgroup): it
+// holds K and -V of its keys over all of d, and both accumulators, dV^T and -dK^T (d columns by 32
+// keys each), which only the matrix instructions touch (the compiler keeps them in AGPRs).  Per
+// 32-query block it forms S - lse / scale and D - dP = D + dO (-V)^T as two interleaved chains of
+// matrix instructions, then P = exp2(S scale log2e - lse log2e) and -dS = P (D - dP), then
+// dV^T += dO^T P and -dK^T += Q^T (-dS) with dO^T and Q^T read by transposing reads.  Every wave
+// does all four products for its keys: no partial sums or P pass between waves, one barrier per
+// block, about 1 KB of LDS read per matrix instruction.  Q/dO tiles live in two LDS stages
+// (working, loading).
 template <int D, bool CAUSAL>
-__global__ __launch_bounds__(512, 1) void bwd_dkdv3_kernel(
+__global__ __launch_bounds__(256, 1) void bwd_dkdv4_kernel(
     const bf16 *__restrict__ Q, const bf16 *__restrict__ K, const bf16 *__restrict__ V, const bf16 *__restrict__ dO,
     const float *__restrict__ LSE, const float *__restrict__ Dl, bf16 *__restrict__ dK, bf16 *__restrict__ dV, int Nq,
     int Nk, int H, int G, int n_ktiles, float scale, float c_log2, int nx)
 {
     static_assert(D == 192 || D == 256, "wide-head dK/dV kernel");
-    constexpr int NKS = D / 16;
-    constexpr int NDBH = D / 64;     // 32-column blocks of each half of dK, dV
-    constexpr int BMQ = 32;          // queries per streamed block
+    constexpr int NKS = D / 16;  // reduction steps over d of S and dP
+    constexpr int NDB = D / 32;  // 32-column blocks of dK and dV
+    constexpr int BMQ = 32;      // queries per streamed block
     constexpr int TILE = BMQ * D * 2;
-    constexpr int kBN = 64;
-    constexpr int PBUF = 2 * 2 * 64 * 16;  // P of the two key groups (2 KB each)
-    __shared__ __attribute__((aligned(16))) char q0_raw[TILE], q1_raw[TILE], q2_raw[TILE];
-    __shared__ __attribute__((aligned(16))) char g0_raw[TILE], g1_raw[TILE], g2_raw[TILE];
-    __shared__ __attribute__((aligned(16))) float s0_raw[2 * BMQ], s1_raw[2 * BMQ], s2_raw[2 * BMQ];  // lse, D
-    __shared__ __attribute__((aligned(16))) char p0_raw[PBUF], p1_raw[PBUF];
-    // d = 256: the first product's partial sums over each column half of d, exchanged between the
-    // two waves of a column pair (16 floats a lane, 4 KB a wave)
-    constexpr bool kSplit = D == 256;
-    __shared__ __attribute__((aligned(16))) char x_raw[kSplit ? 8 * 64 * 16 * 4 : 16];
+    constexpr int kBN = 128;     // keys per workgroup
+    __shared__ __attribute__((aligned(1024))) char q0_raw[TILE], q1_raw[TILE];
+    __shared__ __attribute__((aligned(1024))) char g0_raw[TILE], g1_raw[TILE];
+    __shared__ __attribute__((aligned(16))) float s0_raw[2 * BMQ], s1_raw[2 * BMQ];  // lse log2e, D
 
     int head, ktile;
     work_item(blockIdx.x, n_ktiles, nx, head, ktile);
@@ -430,9 +422,6 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv3_kernel(
     const int tid = threadIdx.x;
     const int lane = tid & 63, h = lane >> 5, c32 = lane & 31;
     const int w = wave_uniform(tid >> 6);
-    const int kg = w & 1, ch = (w >> 1) & 1;
-    const bool pwave = w < 4;
-    const int db0 = ch * NDBH;
     const size_t hoff = (size_t)head * (size_t)Nk * D;
     __amdgpu_buffer_rsrc_t rq, rg, rl, rd;
     auto bind_query_head = [&](int qh) __attribute__((always_inline)) {
@@ -444,42 +433,43 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv3_kernel(
     };
     const int off = Nk - Nq;
     const int k0 = ktile * kBN;
-    const int kw0 = k0 + 32 * kg;
+    const int kw0 = k0 + 32 * w;
     const int key = kw0 + c32;
     const bool keys_ok = kw0 < Nk;
 
-    // d = 256: each wave of a column pair forms the first product (S or dP) over its own half of d,
-    // kst in [ch NKSH, (ch + 1) NKSH), and the pair adds the two partial sums through LDS (one more
-    // barrier a step, a third less matrix work).  d = 192: both waves form it over all of d (the
-    // exchange measured 5% slower there).
-    constexpr int NKSH = kSplit ? NKS / 2 : NKS;
-    const int kst0 = kSplit ? ch * NKSH : 0;
-    // K (P wave) or -V (dS wave) of the lane's key, over kst in [kst0, kst0 + NKSH): with -V the dS
-    // wave's product starts from D and gives D - dP, so that -dS = P (D - dP) is one multiply per
-    // element; its accumulator holds -dK, negated with the scale at the end
-    bf16x8 kvf[NKSH];
+    // K and -V of the lane's key: B operands of S = Q K^T and of D + dO (-V)^T = D - dP, whose
+    // accumulator starts from D, so that -dS = P (D - dP) is one multiply per element; the dK
+    // accumulator holds -dK, negated with the scale at the end
+    bf16x8 kf[NKS], vf[NKS];
     {
-        const __amdgpu_buffer_rsrc_t rkv = make_rsrc((pwave ? K : V) + hoff, (uint32_t)Nk * D * 2);
-        const unsigned sign = pwave ? 0u : 0x80008000u;
+        const __amdgpu_buffer_rsrc_t rk = make_rsrc(K + hoff, (uint32_t)Nk * D * 2);
+        const __amdgpu_buffer_rsrc_t rv = make_rsrc(V + hoff, (uint32_t)Nk * D * 2);
 #pragma unroll
-        for (int ks = 0; ks < NKSH; ++ks)
-            kvf[ks] = __builtin_bit_cast(bf16x8, buffer_load16(rkv, (uint32_t)(key * D + 16 * (kst0 + ks) + 8 * h) * 2u) ^ sign);
+        for (int ks = 0; ks < NKS; ++ks) {
+            const uint32_t byte = (uint32_t)(key * D + 16 * ks + 8 * h) * 2u;
+            kf[ks] = __builtin_bit_cast(bf16x8, buffer_load16(rk, byte));
+            vf[ks] = __builtin_bit_cast(bf16x8, buffer_load16(rv, byte) ^ 0x80008000u);
+        }
     }
-    f32x16 acc[NDBH];  // dV (P wave) or dK (dS wave), columns 32 (db0 + i)
+    f32x16 av[NDB], ak[NDB];  // dV^T and -dK^T: columns 32 db .. 32 db + 31, the lane's key
 #pragma unroll
-    for (int i = 0; i < NDBH; ++i) acc[i] = zero16();
+    for (int i = 0; i < NDB; ++i) {
+        av[i] = zero16();
+        ak[i] = zero16();
+    }
 
-    // The lane's byte offsets inside a swizzled Q / dO tile, computed once and kept opaque so that
-    // each LDS read is one register plus a constant (stage, 16-row group) in the instruction's
-    // offset field; otherwise the compiler rebuilds the swizzled addresses at every use.
-    // d = 192: the swizzle changes only chunk bits 0..2, so chunk 2 kst + h lies at ao[kst % 4]
-    // plus (kst / 4) * 8 chunks and 4 registers hold all 12 offsets.
-    constexpr int NAO = kSplit ? NKSH : 4;
-    int ao[NAO];         // A operand of the first product: row c32, chunk 2 (kst0 + kst) + h
-    int to[NDBH][2];     // transposed reads: rows 4 (G / 2) + s / 4 and + 8 of a 16-row group
+    // The lane's byte offsets inside a swizzled Q / dO tile, computed once and kept opaque (each
+    // LDS read is then one register plus a constant in the offset field).  The swizzle changes only
+    // chunk bits 0..3 (d = 256) or 0..2 (d = 192), so chunk 2 kst + h lies at ao[kst % NAO] plus
+    // (kst / NAO) 2 NAO chunks, and the transposed reads of column block db at to[db % NTO] plus
+    // (db / NTO) 4 NTO chunks.
+    constexpr int NAO = D == 256 ? 8 : 4;
+    constexpr int NTO = D == 256 ? 4 : 2;
+    int ao[NAO];      // A operand of S and dP: row c32, chunk 2 kst + h
+    int to[NTO][2];   // transposed reads of column block db: rows 4 (G4 / 2) + s / 4 and + 8 of a 16-row group
 #pragma unroll
     for (int kst = 0; kst < NAO; ++kst) {
-        ao[kst] = swz_off<D>(c32, 2 * (kst0 + kst) + h);
+        ao[kst] = swz_off<D>(c32, 2 * kst + h);
         asm volatile("" : "+v"(ao[kst]));
     }
     auto a_off = [&](int kst) __attribute__((always_inline)) { return ao[kst % NAO] + (kst / NAO) * 32 * NAO; };
@@ -487,277 +477,169 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv3_kernel(
         const int G4 = lane >> 4, s16 = lane & 15;
         const int tr = 4 * (G4 >> 1) + (s16 >> 2);
 #pragma unroll
-        for (int db = 0; db < NDBH; ++db) {
-            const int byte = 2 * (32 * (db0 + db) + 16 * (G4 & 1) + 4 * (s16 & 3));
+        for (int db = 0; db < NTO; ++db) {
+            const int byte = 2 * (32 * db + 16 * (G4 & 1) + 4 * (s16 & 3));
             to[db][0] = swz_off<D>(tr, byte >> 4) + (byte & 15);
             to[db][1] = swz_off<D>(tr + 8, byte >> 4) + (byte & 15);
             asm volatile("" : "+v"(to[db][0]));
             asm volatile("" : "+v"(to[db][1]));
         }
     }
+    auto t_off = [&](int db, int j) __attribute__((always_inline)) { return to[db % NTO][j] + (db / NTO) * 64 * NTO; };
 
     const int q_start = CAUSAL ? (max(0, k0 - off) / BMQ) * BMQ : 0;
     const int nsteps = (Nq > q_start) ? (Nq - q_start + BMQ - 1) / BMQ : 0;
 
-    auto qst = [&](auto st) __attribute__((always_inline)) {
-        constexpr int v = decltype(st)::value;
-        return (lds_char *)(v == 0 ? q0_raw : v == 1 ? q1_raw : q2_raw);
-    };
-    auto gst = [&](auto st) __attribute__((always_inline)) {
-        constexpr int v = decltype(st)::value;
-        return (lds_char *)(v == 0 ? g0_raw : v == 1 ? g1_raw : g2_raw);
-    };
-    auto sst = [&](auto st) __attribute__((always_inline)) {
-        constexpr int v = decltype(st)::value;
-        return (lds_char *)(v == 0 ? s0_raw : v == 1 ? s1_raw : s2_raw);
-    };
-    auto pst = [&](auto b) __attribute__((always_inline)) {
-        return (lds_char *)(decltype(b)::value ? p1_raw : p0_raw) + kg * (2 * 64 * 16);
-    };
-    // Loads of block i (query rows q_start + 32 i ..): Q by waves 0..3, dO by waves 4..7 (a tile of 32
-    // rows is 12 or 16 wave loads), D straight to LDS (wave 1) and lse into registers (wave 0,
-    // lanes 0..7).  lse goes to LDS in log2 units once it has arrived, so that the P waves form
-    // each exponent with one fused multiply-add; two registers, by block parity, because the next
-    // block's lse is requested before the last one is stored.
-    constexpr int NQL = BMQ * (D / 8) / 64 / 4;  // direct loads per wave and tile
-    f32x4 lse_ld[2];
-    auto load_q = [&](int i, auto st) __attribute__((always_inline)) {
-        if (w < 4) load_tile_lds<D, 4, BMQ>(rq, qst(st), q_start + i * BMQ, w & 3, lane);
-    };
-    auto load_g = [&](int i, auto st, auto par) __attribute__((always_inline)) {
+    auto qst = [&](auto st) __attribute__((always_inline)) { return (lds_char *)(decltype(st)::value ? q1_raw : q0_raw); };
+    auto gst = [&](auto st) __attribute__((always_inline)) { return (lds_char *)(decltype(st)::value ? g1_raw : g0_raw); };
+    auto sst = [&](auto st) __attribute__((always_inline)) { return (lds_char *)(decltype(st)::value ? s1_raw : s0_raw); };
+    // block i: Q and dO tiles by all four waves; D straight to LDS (wave 1); lse into registers
+    // (wave 0), to LDS as -lse / scale once it has arrived: the score accumulator starts from it,
+    // so S - lse / scale comes out of the matrix instructions and P = exp2((S - lse / scale) scale
+    // log2e) is a multiply and an exponential (a row that sees no key, lse = -inf, starts from 1e30
+    // and is masked to -inf)
+    f32x4 lse_ld;
+    auto load_blk = [&](int i, auto st) __attribute__((always_inline)) {
         const int qs = q_start + i * BMQ;
-        if (w >= 4) load_tile_lds<D, 4, BMQ>(rg, gst(st), qs, w & 3, lane);
-        if (w == 0 && lane < 8)
-            lse_ld[decltype(par)::value] = __builtin_bit_cast(f32x4, buffer_load16(rl, (uint32_t)(qs + 4 * lane) * 4u));
+        load_tile_lds<D, 4, BMQ>(rq, qst(st), qs, w, lane);
+        load_tile_lds<D, 4, BMQ>(rg, gst(st), qs, w, lane);
+        if (w == 0 && lane < 8) lse_ld = __builtin_bit_cast(f32x4, buffer_load16(rl, (uint32_t)(qs + 4 * lane) * 4u));
         if (w == 1 && lane < 8) buffer_load_lds16(rd, sst(st) + 4 * BMQ, (uint32_t)(qs + 4 * lane) * 4u);
     };
-    auto store_lse = [&](auto st, auto par) __attribute__((always_inline)) {
+    auto store_lse = [&](auto st) __attribute__((always_inline)) {
         if (w == 0 && lane < 8)
-            *(__attribute__((address_space(3))) f32x4 *)(sst(st) + 16 * lane) = lse_ld[decltype(par)::value] * kLog2e;
+        {
+            f32x4 v = lse_ld * (-1.f / scale);
+#pragma unroll
+            for (int u = 0; u < 4; ++u) v[u] = fminf(v[u], 1e30f);
+            *(__attribute__((address_space(3))) f32x4 *)(sst(st) + 16 * lane) = v;
+        }
+    };
+
+    // Step i on block i (stage S); block i + 1 loads into the other stage, which block i - 1 left
+    // at the last barrier.
+    auto step = [&](int i, auto S) __attribute__((always_inline)) {
+        using SN = std::integral_constant<int, 1 - decltype(S)::value>;
+        load_blk(i + 1, SN{});  // past the last block: zeros into the free stage, never read
+        if (keys_ok) {
+            const lds_char *ql = qst(S), *gl = gst(S), *sl = sst(S);
+            const int qs = q_start + i * BMQ;
+            // the accumulators start from -lse / scale and from D of the lane's queries 8 g + 4 h + u
+            f32x16 sc, dp;
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+                const f32x4 l4 = *(const __attribute__((address_space(3))) f32x4 *)(sl + 4 * (8 * g + 4 * h));
+                const f32x4 d4 = *(const __attribute__((address_space(3))) f32x4 *)(sl + 4 * (BMQ + 8 * g + 4 * h));
+#pragma unroll
+                for (int u = 0; u < 4; ++u) {
+                    sc[4 * g + u] = l4[u];
+                    dp[4 * g + u] = d4[u];
+                }
+            }
+            // first products: S and D - dP as two interleaved chains; fragment c is Q (even c) or
+            // dO (odd c) rows for reduction step c / 2, fetched PF instructions ahead
+            constexpr int PF = 2, N1 = 2 * NKS;
+            auto fetch1 = [&](auto C) __attribute__((always_inline)) {
+                constexpr int c = decltype(C)::value;
+                return lds_read16((c & 1) ? gl : ql, a_off(c >> 1));
+            };
+            bf16x8 fr[PF + 1];
+            static_for<0, PF>([&](auto F) __attribute__((always_inline)) { fr[decltype(F)::value] = fetch1(F); });
+            static_for<0, N1>([&](auto C) __attribute__((always_inline)) {
+                constexpr int c = decltype(C)::value;
+                if constexpr (c + PF < N1) fr[(c + PF) % (PF + 1)] = fetch1(std::integral_constant<int, c + PF>{});
+                if constexpr (c & 1)
+                    dp = mfma(fr[c % (PF + 1)], vf[c >> 1], dp);
+                else
+                    sc = mfma(fr[c % (PF + 1)], kf[c >> 1], sc);
+                __builtin_amdgcn_sched_barrier(0);
+            });
+            if (CAUSAL && (qs + off < kw0 + 31)) {
+                // scores of queries before this lane's key -> -inf (P = 0)
+#pragma unroll
+                for (int g = 0; g < 4; ++g) {
+#pragma unroll
+                    for (int u = 0; u < 4; ++u)
+                        if (qs + 8 * g + 4 * h + u + off < key) sc[4 * g + u] = -__builtin_inff();
+                }
+            }
+            // P and -dS in bf16, two groups of 16 queries
+            bf16x8 pb[2], sb[2];
+            auto form_p = [&](auto RR) __attribute__((always_inline)) {
+                constexpr int r = decltype(RR)::value;
+                sc[r] = fast_exp2(sc[r] * c_log2);
+                pb[r >> 3][r & 7] = (bf16)sc[r];
+            };
+            auto form_ds = [&](auto RR) __attribute__((always_inline)) {
+                constexpr int r = decltype(RR)::value;
+                sb[r >> 3][r & 7] = (bf16)(sc[r] * dp[r]);
+            };
+            // second products: chunk n < 2 NDB is dV over query group n / NDB, column block n % NDB
+            // (dO^T fragments); n >= 2 NDB is -dK likewise (Q^T fragments)
+            constexpr int N2 = 4 * NDB;
+            auto fetch2 = [&](auto NN) __attribute__((always_inline)) {
+                constexpr int n = decltype(NN)::value, m = n % (2 * NDB), t = m / NDB, db = m % NDB;
+                const lds_char *tl = n < 2 * NDB ? gl : ql;
+                const bf16x4 lo = lds_read_tr(tl, t_off(db, 0) + 16 * t * 2 * D);
+                const bf16x4 hi = lds_read_tr(tl, t_off(db, 1) + 16 * t * 2 * D);
+                return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+            };
+            static_for<0, PF>([&](auto F) __attribute__((always_inline)) { fr[decltype(F)::value] = fetch2(F); });
+            static_for<0, 8>(form_p);  // P of the first 16 queries before the products that read it
+            static_for<0, N2>([&](auto NN) __attribute__((always_inline)) {
+                constexpr int n = decltype(NN)::value, m = n % (2 * NDB), t = m / NDB, db = m % NDB;
+                if constexpr (n + PF < N2) fr[(n + PF) % (PF + 1)] = fetch2(std::integral_constant<int, n + PF>{});
+                if constexpr (n < 2 * NDB)
+                    av[db] = mfma(fr[n % (PF + 1)], pb[t], av[db]);
+                else
+                    ak[db] = mfma(fr[n % (PF + 1)], sb[t], ak[db]);
+                // vector work under the products: P of the second group and -dS of the first during
+                // dV over the first group, -dS of the second during dV over the second
+                if constexpr (n < NDB) {
+                    static_for<8 + n * 8 / NDB, 8 + (n + 1) * 8 / NDB>(form_p);
+                    static_for<n * 8 / NDB, (n + 1) * 8 / NDB>(form_ds);
+                } else if constexpr (n < 2 * NDB) {
+                    static_for<8 + (n - NDB) * 8 / NDB, 8 + (n - NDB + 1) * 8 / NDB>(form_ds);
+                }
+                __builtin_amdgcn_sched_barrier(0);
+            });
+        }
+        wait_vmem();
+        store_lse(SN{});
+        __syncthreads();
     };
 
     using I0 = std::integral_constant<int, 0>;
     using I1 = std::integral_constant<int, 1>;
-    using I2 = std::integral_constant<int, 2>;
-    // One copy of the loop per role and column half (CH), so that which wave starts the dS sum
-    // from D and which wave hands P to the dS waves are compile-time facts.
-    //
-    // The two roles run their products in opposite order within a step:
-    //   P wave:  first product of block i     | second product of block i
-    //   dS wave: second product of block i-1  | first product of block i
-    // At d = 256 a barrier separates the halves (the exchange of partial sums).  On each SIMD one
-    // wave's chain of first-product instructions then runs while the other wave reads its
-    // partner's sums, forms P or dS and feeds its second product, instead of both waves waiting
-    // for the exchange at the same time.
-    auto run = [&](auto PW, auto CHc) __attribute__((always_inline)) {
-        constexpr bool P_WAVE = decltype(PW)::value;
-        constexpr int CH = decltype(CHc)::value;
-        constexpr int PF = 2;  // LDS fragments fetched this many instructions ahead
-        // First product over this wave's part of d: S = Q K^T (P wave) or D - dO V^T (dS wave, -V
-        // in registers; one wave of a column pair starts from D), then this wave's partial sums to
-        // LDS for its partner.
-        auto first = [&](const lds_char *a_l, const lds_char *st_l, f32x16 &sc) __attribute__((always_inline)) {
-            if constexpr (!P_WAVE && (!kSplit || CH == 0)) {
-#pragma unroll
-                for (int g = 0; g < 4; ++g) {
-                    const f32x4 dv = *(const __attribute__((address_space(3))) f32x4 *)(st_l + 4 * (BMQ + 8 * g + 4 * h));
-#pragma unroll
-                    for (int u = 0; u < 4; ++u) sc[4 * g + u] = dv[u];
-                }
-            } else {
-                sc = zero16();
-            }
-            bf16x8 fr[PF + 1];
-            static_for<0, PF>([&](auto F) __attribute__((always_inline)) {
-                fr[decltype(F)::value] = lds_read16(a_l, a_off(decltype(F)::value));
-            });
-            static_for<0, NKSH>([&](auto C) __attribute__((always_inline)) {
-                constexpr int c = decltype(C)::value;
-                if constexpr (c + PF < NKSH) fr[(c + PF) % (PF + 1)] = lds_read16(a_l, a_off(c + PF));
-                sc = mfma(fr[c % (PF + 1)], kvf[c], sc);
-                __builtin_amdgcn_sched_barrier(0);
-            });
-            if constexpr (kSplit) {
-#pragma unroll
-                for (int g = 0; g < 4; ++g)
-                    *(__attribute__((address_space(3))) f32x4 *)(x_raw + ((w * 4 + g) * 64 + lane) * 16) =
-                        f32x4{sc[4 * g], sc[4 * g + 1], sc[4 * g + 2], sc[4 * g + 3]};
-            }
-        };
-        // Second product: the partner's partial sums added, P = exp2(S scale log2e - lse log2e) or
-        // -dS = P (D - dP) in bf16, then dV^T += dO^T P or -dK^T += Q^T (-dS) over this wave's
-        // columns, 16 queries t at a time.
-        auto second = [&](const lds_char *t_l, const lds_char *st_l, lds_char *p_l, int qs, f32x16 &sc)
-                          __attribute__((always_inline)) {
-            f32x4 o4[4];     // the partner's partial sums (d = 256)
-            f32x4 v4[4];     // lse * log2e of the lane's queries 8 g + 4 h + u (P wave)
-            bf16x8 pv[2];    // P of the block, from the P wave (dS wave)
-            if constexpr (kSplit) {
-                // from the wave of the same role and key group (w ^ 2); both waves form own + other,
-                // which is the same fp32 sum either way round
-#pragma unroll
-                for (int g = 0; g < 4; ++g)
-                    o4[g] = *(const __attribute__((address_space(3))) f32x4 *)(x_raw + (((w ^ 2) * 4 + g) * 64 + lane) * 16);
-            }
-            if constexpr (P_WAVE) {
-#pragma unroll
-                for (int g = 0; g < 4; ++g)
-                    v4[g] = *(const __attribute__((address_space(3))) f32x4 *)(st_l + 4 * (8 * g + 4 * h));
-            } else {
-#pragma unroll
-                for (int t = 0; t < 2; ++t)
-                    pv[t] = __builtin_bit_cast(bf16x8, *(const __attribute__((address_space(3))) u32x4 *)(p_l + (t * 64 + lane) * 16));
-            }
-            auto fetch = [&](auto N) __attribute__((always_inline)) {
-                constexpr int n = decltype(N)::value, t = n / NDBH, db = n % NDBH;
-                const bf16x4 lo = lds_read_tr(t_l, to[db][0] + 16 * t * 2 * D);
-                const bf16x4 hi = lds_read_tr(t_l, to[db][1] + 16 * t * 2 * D);
-                return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-            };
-            bf16x8 fr[PF + 1];
-            static_for<0, PF>([&](auto F) __attribute__((always_inline)) { fr[decltype(F)::value] = fetch(F); });
-            if constexpr (kSplit) {
-#pragma unroll
-                for (int g = 0; g < 4; ++g) {
-#pragma unroll
-                    for (int u = 0; u < 4; ++u) sc[4 * g + u] += o4[g][u];
-                }
-            }
-            if constexpr (P_WAVE) {
-                if (CAUSAL && (qs + off < kw0 + 31)) {
-                    // scores of queries before this lane's key -> -inf (P = 0); a query that
-                    // sees no key has lse = -inf: keep exp2 away from -inf + inf
-#pragma unroll
-                    for (int g = 0; g < 4; ++g) {
-#pragma unroll
-                        for (int u = 0; u < 4; ++u) {
-                            v4[g][u] = fmaxf(v4[g][u], -1e30f);
-                            if (qs + 8 * g + 4 * h + u + off < key) sc[4 * g + u] = -__builtin_inff();
-                        }
-                    }
-                }
-            }
-            bf16x8 pb[2];
-            auto form = [&](auto RR) __attribute__((always_inline)) {
-                constexpr int r = decltype(RR)::value;
-                if constexpr (P_WAVE)
-                    pb[r >> 3][r & 7] = (bf16)fast_exp2(fmaf(sc[r], c_log2, -v4[r >> 2][r & 3]));
-                else
-                    pb[r >> 3][r & 7] = (bf16)((float)pv[r >> 3][r & 7] * sc[r]);
-            };
-            static_for<0, 8>(form);  // the first group before its matrix instructions
-            static_for<0, 2 * NDBH>([&](auto N) __attribute__((always_inline)) {
-                constexpr int n = decltype(N)::value, t = n / NDBH, db = n % NDBH;
-                if constexpr (n + PF < 2 * NDBH) fr[(n + PF) % (PF + 1)] = fetch(std::integral_constant<int, n + PF>{});
-                acc[db] = mfma(fr[n % (PF + 1)], pb[t], acc[db]);
-                if constexpr (t == 0) {
-                    // the second group under the first group's matrix instructions
-                    static_for<8 + db * 8 / NDBH, 8 + (db + 1) * 8 / NDBH>(form);
-                    if constexpr (P_WAVE && CH == 0 && db == NDBH - 1) {
-#pragma unroll
-                        for (int tt = 0; tt < 2; ++tt) lds_write16(p_l, (tt * 64 + lane) * 16, __builtin_bit_cast(u32x4, pb[tt]));
-                    }
-                }
-                __builtin_amdgcn_sched_barrier(0);
-            });
-        };
-
-        // Step i: the P wave works on block i (stage S, P buffer B), the dS wave on blocks i - 1
-        // (stage (S + 2) % 3, P buffer 1 - B) and i.  Loads run two blocks ahead where the stages
-        // allow: dO, lse and D of block i + 2 go at the start of the step into the stage of block
-        // i - 1 (last read in step i - 1); Q of block i + 2 into the same stage after the middle
-        // barrier (the dS wave reads Q of block i - 1 before it) at d = 256, and Q of block i + 1 at
-        // the start at d = 192 (no middle barrier).  At the end of the step only block i + 1 must
-        // have arrived; the loads issued after it stay in flight.
-        f32x16 sc;  // dS wave: D - dP of block i, formed in step i and used in step i + 1
-        auto step = [&](int i, auto S, auto B, auto FIRST) __attribute__((always_inline)) {
-            constexpr int s_cur = decltype(S)::value;
-            using SN = std::integral_constant<int, (s_cur + 1) % 3>;
-            using SP = std::integral_constant<int, (s_cur + 2) % 3>;
-            using BP = std::integral_constant<int, 1 - decltype(B)::value>;
-            // past the last block: zeros into free stages, never read
-            load_g(i + 2, SP{}, B);  // block i + 2 has the parity of block i
-            if constexpr (!kSplit) load_q(i + 1, SN{});
-            const bool cur = keys_ok && i < nsteps;  // block i exists (none in the last step)
-            if constexpr (P_WAVE) {
-                if (cur) first(qst(S), sst(S), sc);
-                if constexpr (kSplit) {
-                    barrier_wait_vmem_upto<15>();  // no wait on the loads in flight
-                    load_q(i + 2, SP{});
-                }
-                if (cur) second(gst(S), sst(S), pst(B), q_start + i * BMQ, sc);
-            } else {
-                if constexpr (!decltype(FIRST)::value) {
-                    if (keys_ok) second(qst(SP{}), sst(SP{}), pst(BP{}), 0, sc);
-                }
-                if constexpr (kSplit) {
-                    barrier_wait_vmem_upto<15>();
-                    load_q(i + 2, SP{});
-                }
-                if (cur) first(gst(S), sst(S), sc);
-            }
-            // loads issued after block i + 1's: Q of block i + 2 (P waves, d = 256) or dO of block
-            // i + 2 (dS waves); at d = 192 the P waves' last loads are block i + 1's Q
-            constexpr int NV = (P_WAVE && !kSplit) ? 0 : NQL;
-            wait_vmem_upto<NV>();
-            store_lse(SN{}, BP{});  // lse of block i + 1 (parity 1 - B)
-            barrier_wait_vmem_upto<NV>();
-        };
-
-        using F = std::false_type;
-        for (int gq = 0; gq < G; ++gq) {
-            bind_query_head(qh0 + gq);
-            // blocks 0 and 1; the previous query head's last step ended with a barrier, and its
-            // loads past the end complete before these (each wave's loads complete in order)
-            load_g(0, I0{}, I0{});
-            load_q(0, I0{});
-            load_g(1, I1{}, I1{});
-            if constexpr (kSplit) load_q(1, I1{});  // at d = 192 the first step loads it
-            wait_vmem();
-            store_lse(I0{}, I0{});
-            store_lse(I1{}, I1{});
-            __syncthreads();
-            if (nsteps == 0) continue;
-            step(0, I0{}, I0{}, std::true_type{});
-            const int n = nsteps + 1;
-            int i = 1;
-            for (; i + 5 < n; i += 6) {
-                step(i, I1{}, I1{}, F{});
-                step(i + 1, I2{}, I0{}, F{});
-                step(i + 2, I0{}, I1{}, F{});
-                step(i + 3, I1{}, I0{}, F{});
-                step(i + 4, I2{}, I1{}, F{});
-                step(i + 5, I0{}, I0{}, F{});
-            }
-            if (i < n) step(i++, I1{}, I1{}, F{});
-            if (i < n) step(i++, I2{}, I0{}, F{});
-            if (i < n) step(i++, I0{}, I1{}, F{});
-            if (i < n) step(i++, I1{}, I0{}, F{});
-            if (i < n) step(i++, I2{}, I1{}, F{});
+    for (int gq = 0; gq < G; ++gq) {
+        bind_query_head(qh0 + gq);
+        load_blk(0, I0{});  // the previous query head's last step ended with a barrier and no load in flight
+        wait_vmem();
+        store_lse(I0{});
+        __syncthreads();
+        int i = 0;
+        for (; i + 1 < nsteps; i += 2) {
+            step(i, I0{});
+            step(i + 1, I1{});
         }
-    };
-    if (pwave) {
-        if (ch == 0)
-            run(std::true_type{}, I0{});
-        else
-            run(std::true_type{}, I1{});
-    } else {
-        if (ch == 0)
-            run(std::false_type{}, I0{});
-        else
-            run(std::false_type{}, I1{});
+        if (i < nsteps) step(i, I0{});
     }
+
     if (key < Nk) {
-        bf16 *row = (pwave ? dV : dK) + hoff + (size_t)key * D;
-        const float f = pwave ? 1.f : -scale;
+        bf16 *rv_ = dV + hoff + (size_t)key * D;
+        bf16 *rk_ = dK + hoff + (size_t)key * D;
 #pragma unroll
-        for (int db = 0; db < NDBH; ++db) {
+        for (int db = 0; db < NDB; ++db) {
 #pragma unroll
             for (int g = 0; g < 4; ++g) {
-                bf16x4 v4;
+                bf16x4 v4, k4;
 #pragma unroll
-                for (int u = 0; u < 4; ++u) v4[u] = (bf16)(acc[db][4 * g + u] * f);
-                *(bf16x4 *)(row + 32 * (db0 + db) + 8 * g + 4 * h) = v4;
+                for (int u = 0; u < 4; ++u) {
+                    v4[u] = (bf16)av[db][4 * g + u];
+                    k4[u] = (bf16)(ak[db][4 * g + u] * -scale);
+                }
+                *(bf16x4 *)(rv_ + 32 * db + 8 * g + 4 * h) = v4;
+                *(bf16x4 *)(rk_ + 32 * db + 8 * g + 4 * h) = k4;
             }
         }
     }
@@ -1150,15 +1032,15 @@ hipError_t launch_dkdv2_t(const BwdArgs &a)
 }
 
 template <int D, bool CAUSAL>
-hipError_t launch_dkdv3_t(const BwdArgs &a)
+hipError_t launch_dkdv4_t(const BwdArgs &a)
 {
-    const int n_ktiles = (a.Nk + 63) / 64;
+    const int n_ktiles = (a.Nk + 127) / 128;
     const long long G = (long long)a.B * a.Hk * n_ktiles;
     if (G == 0) return hipSuccess;
-    hipLaunchKernelGGL((bwd_dkdv3_kernel<D, CAUSAL>), dim3((unsigned)G), dim3(512), 0, (hipStream_t)a.stream,
+    hipLaunchKernelGGL((bwd_dkdv4_kernel<D, CAUSAL>), dim3((unsigned)G), dim3(256), 0, (hipStream_t)a.stream,
                        (const bf16 *)a.q, (const bf16 *)a.k, (const bf16 *)a.v, (const bf16 *)a.dout, a.lse,
-                       (const float *)a.delta, (bf16 *)a.dk, (bf16 *)a.dv, a.Nq, a.Nk, a.H, a.H / a.Hk, n_ktiles, a.scale, a.scale * kLog2e,
-                       a.dev.nx);
+                       (const float *)a.delta, (bf16 *)a.dk, (bf16 *)a.dv, a.Nq, a.Nk, a.H, a.H / a.Hk, n_ktiles, a.scale,
+                       a.scale * kLog2e, a.dev.nx);
     return hipGetLastError();
 }
 
@@ -1192,8 +1074,8 @@ hipError_t launch_bwd_dkdv(const BwdArgs &a)
     switch (a.d) {
     case 64: return a.causal ? launch_dkdv2_t<64, true>(a) : launch_dkdv2_t<64, false>(a);
     case 128: return a.causal ? launch_dkdv2_t<128, true>(a) : launch_dkdv2_t<128, false>(a);
-    case 192: return a.causal ? launch_dkdv3_t<192, true>(a) : launch_dkdv3_t<192, false>(a);
-    default: return a.causal ? launch_dkdv3_t<256, true>(a) : launch_dkdv3_t<256, false>(a);
+    case 192: return a.causal ? launch_dkdv4_t<192, true>(a) : launch_dkdv4_t<192, false>(a);
+    default: return a.causal ? launch_dkdv4_t<256, true>(a) : launch_dkdv4_t<256, false>(a);
     }
 }
 

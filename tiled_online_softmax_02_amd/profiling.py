@@ -29,7 +29,7 @@ KERNEL_SOURCES = ["attn_device.h", "attn_sched.h", "attn_fwd.hip", "attn_bwd.hip
 CALIBRATION_BYTES = 256 << 20   # bench.py copies 64 Mi int32 values before timing
 SHORT = {"fwd_kernel": "fwd", "fwd_decode_kernel": "fwd_decode", "fwd_fp8_kernel": "fwd_fp8",
          "fwd_combine_kernel": "combine", "bwd_dkdv2_kernel": "dkdv",
-         "bwd_dkdv3_kernel": "dkdv", "bwd_dq_kernel": "dq",
+         "bwd_dkdv4_kernel": "dkdv", "bwd_dq_kernel": "dq",
          "bwd_preprocess_kernel": "preprocess"}
 
 
