@@ -390,14 +390,14 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv2_kernel(const Dkdv2Args args)
 // ------------------------------------------------------------ dK / dV, one wave per SIMD (d = 192, 256)
 
 // Four waves, one per SIMD with up to 512 registers.  Wave w owns 32 keys (128 per workgroup): it
-// holds K and -V of its keys over all of d, and both accumulators, dV^T and -dK^T (d columns by 32
-// keys each), which only the matrix instructions touch (the compiler keeps them in AGPRs).  Per
-// 32-query block it forms S - lse / scale and D - dP = D + dO (-V)^T as two interleaved chains of
-// matrix instructions, then P = exp2(S scale log2e - lse log2e) and -dS = P (D - dP), then
-// dV^T += dO^T P and -dK^T += Q^T (-dS) with dO^T and Q^T read by transposing reads.  Every wave
-// does all four products for its keys: no partial sums or P pass between waves, one barrier per
-// block, about 1 KB of LDS read per matrix instruction.  Q/dO tiles live in two LDS stages
-// (working, loading).
+// holds K (and V, except at causal d = 256) of its keys over all of d, and both accumulators,
+// dV^T and dK^T / scale (d columns by 32 keys each), which only the matrix instructions touch (the
+// compiler keeps them in AGPRs).  Per 32-query block it forms S - lse / scale and dP - D =
+// dO V^T - D as two interleaved chains of matrix instructions, then P = exp2(S scale log2e -
+// lse log2e) and dS = P (dP - D), then dV^T += dO^T P and dK^T += Q^T dS with dO^T and Q^T read
+// by transposing reads.  Every wave does all four products for its keys: no partial sums or P pass
+// between waves, one barrier per block, about 1 KB of LDS read per matrix instruction.  Q/dO tiles
+// live in two LDS stages (working, loading).
 template <int D, bool CAUSAL>
 __global__ __launch_bounds__(256, 1) void bwd_dkdv4_kernel(
     const bf16 *__restrict__ Q, const bf16 *__restrict__ K, const bf16 *__restrict__ V, const bf16 *__restrict__ dO,
@@ -412,7 +412,13 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv4_kernel(
     constexpr int kBN = 128;     // keys per workgroup
     __shared__ __attribute__((aligned(1024))) char q0_raw[TILE], q1_raw[TILE];
     __shared__ __attribute__((aligned(1024))) char g0_raw[TILE], g1_raw[TILE];
-    __shared__ __attribute__((aligned(16))) float s0_raw[2 * BMQ], s1_raw[2 * BMQ];  // lse log2e, D
+    __shared__ __attribute__((aligned(16))) float s0_raw[2 * BMQ], s1_raw[2 * BMQ];  // -lse / scale, -D
+    // causal d = 256: V of the workgroup's keys in LDS (64 KB), the registers it frees removing the
+    // spills of the register form (measured faster on causal tiles, which are short; on full rows
+    // the extra LDS reads cost more than the spills).  16-byte aligned, so that the 1 KB aligned
+    // stages keep the first 64 KB (the LDS instructions' offset field).
+    constexpr bool kVLds = D == 256 && CAUSAL;
+    __shared__ __attribute__((aligned(16))) char v_raw[kVLds ? kBN * D * 2 : 16];
 
     int head, ktile;
     work_item(blockIdx.x, n_ktiles, nx, head, ktile);
@@ -437,10 +443,11 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv4_kernel(
     const int key = kw0 + c32;
     const bool keys_ok = kw0 < Nk;
 
-    // K and -V of the lane's key: B operands of S = Q K^T and of D + dO (-V)^T = D - dP, whose
-    // accumulator starts from D, so that -dS = P (D - dP) is one multiply per element; the dK
-    // accumulator holds -dK, negated with the scale at the end
-    bf16x8 kf[NKS], vf[NKS];
+    // K and V of the lane's key: B operands of S = Q K^T and of dO V^T - D = dP - D, whose
+    // accumulator starts from -D, so that dS = P (dP - D) is one multiply per element.  d = 256: V
+    // from its LDS copy instead of registers (causal).
+    constexpr int NVR = kVLds ? 1 : NKS;
+    bf16x8 kf[NKS], vf[NVR];
     {
         const __amdgpu_buffer_rsrc_t rk = make_rsrc(K + hoff, (uint32_t)Nk * D * 2);
         const __amdgpu_buffer_rsrc_t rv = make_rsrc(V + hoff, (uint32_t)Nk * D * 2);
@@ -448,8 +455,11 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv4_kernel(
         for (int ks = 0; ks < NKS; ++ks) {
             const uint32_t byte = (uint32_t)(key * D + 16 * ks + 8 * h) * 2u;
             kf[ks] = __builtin_bit_cast(bf16x8, buffer_load16(rk, byte));
-            vf[ks] = __builtin_bit_cast(bf16x8, buffer_load16(rv, byte) ^ 0x80008000u);
+            if constexpr (!kVLds) vf[ks] = __builtin_bit_cast(bf16x8, buffer_load16(rv, byte));
         }
+        // each wave copies its own 32 rows of V (rows past Nk read as zeros); its first wait on
+        // its loads precedes every read
+        if constexpr (kVLds) load_tile_lds<D, 1, 32>(rv, (lds_char *)v_raw + w * 32 * 2 * D, kw0, 0, lane);
     }
     f32x16 av[NDB], ak[NDB];  // dV^T and -dK^T: columns 32 db .. 32 db + 31, the lane's key
 #pragma unroll
@@ -473,6 +483,23 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv4_kernel(
         asm volatile("" : "+v"(ao[kst]));
     }
     auto a_off = [&](int kst) __attribute__((always_inline)) { return ao[kst % NAO] + (kst / NAO) * 32 * NAO; };
+    // V fragments (causal d = 256): rows c32 of the wave's 32-row block of the V copy, the same swizzled
+    // positions as ao, relative to the first stage so that the offset field stays small
+    int vo[kVLds ? NAO : 1];
+    if constexpr (kVLds) {
+        const int vbase = (int)((lds_char *)v_raw - (lds_char *)q0_raw) + w * 32 * 2 * D;
+#pragma unroll
+        for (int kst = 0; kst < NAO; ++kst) {
+            vo[kst] = ao[kst] + vbase;
+            asm volatile("" : "+v"(vo[kst]));
+        }
+    }
+    auto v_frag = [&](int kst) __attribute__((always_inline)) {
+        if constexpr (kVLds)
+            return lds_read16((lds_char *)q0_raw, vo[kst % NAO] + (kst / NAO) * 32 * NAO);
+        else
+            return vf[kst];
+    };
     {
         const int G4 = lane >> 4, s16 = lane & 15;
         const int tr = 4 * (G4 >> 1) + (s16 >> 2);
@@ -493,26 +520,24 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv4_kernel(
     auto qst = [&](auto st) __attribute__((always_inline)) { return (lds_char *)(decltype(st)::value ? q1_raw : q0_raw); };
     auto gst = [&](auto st) __attribute__((always_inline)) { return (lds_char *)(decltype(st)::value ? g1_raw : g0_raw); };
     auto sst = [&](auto st) __attribute__((always_inline)) { return (lds_char *)(decltype(st)::value ? s1_raw : s0_raw); };
-    // block i: Q and dO tiles by all four waves; D straight to LDS (wave 1); lse into registers
-    // (wave 0), to LDS as -lse / scale once it has arrived: the score accumulator starts from it,
-    // so S - lse / scale comes out of the matrix instructions and P = exp2((S - lse / scale) scale
-    // log2e) is a multiply and an exponential (a row that sees no key, lse = -inf, starts from 1e30
-    // and is masked to -inf)
-    f32x4 lse_ld;
+    // block i: Q and dO tiles by all four waves; lse (wave 0) and D (wave 1) into registers, to LDS
+    // once they have arrived as -lse / scale and -D, the starting values of the two first-product
+    // accumulators: S - lse / scale comes out of the matrix instructions, so P = exp2((S - lse /
+    // scale) scale log2e) is a multiply and an exponential (a row that sees no key, lse = -inf,
+    // starts from 1e30 and is masked to -inf), and dO V^T - D = dP - D
+    f32x4 sd_ld;
     auto load_blk = [&](int i, auto st) __attribute__((always_inline)) {
         const int qs = q_start + i * BMQ;
         load_tile_lds<D, 4, BMQ>(rq, qst(st), qs, w, lane);
         load_tile_lds<D, 4, BMQ>(rg, gst(st), qs, w, lane);
-        if (w == 0 && lane < 8) lse_ld = __builtin_bit_cast(f32x4, buffer_load16(rl, (uint32_t)(qs + 4 * lane) * 4u));
-        if (w == 1 && lane < 8) buffer_load_lds16(rd, sst(st) + 4 * BMQ, (uint32_t)(qs + 4 * lane) * 4u);
+        if (w < 2 && lane < 8) sd_ld = __builtin_bit_cast(f32x4, buffer_load16(w == 0 ? rl : rd, (uint32_t)(qs + 4 * lane) * 4u));
     };
     auto store_lse = [&](auto st) __attribute__((always_inline)) {
-        if (w == 0 && lane < 8)
-        {
-            f32x4 v = lse_ld * (-1.f / scale);
+        if (w < 2 && lane < 8) {
+            f32x4 v = sd_ld * (w == 0 ? -1.f / scale : -1.f);
 #pragma unroll
             for (int u = 0; u < 4; ++u) v[u] = fminf(v[u], 1e30f);
-            *(__attribute__((address_space(3))) f32x4 *)(sst(st) + 16 * lane) = v;
+            *(__attribute__((address_space(3))) f32x4 *)(sst(st) + 4 * (w * BMQ + 4 * lane)) = v;
         }
     };
 
@@ -524,7 +549,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv4_kernel(
         if (keys_ok) {
             const lds_char *ql = qst(S), *gl = gst(S), *sl = sst(S);
             const int qs = q_start + i * BMQ;
-            // the accumulators start from -lse / scale and from D of the lane's queries 8 g + 4 h + u
+            // the accumulators start from -lse / scale and from -D of the lane's queries 8 g + 4 h + u
             f32x16 sc, dp;
 #pragma unroll
             for (int g = 0; g < 4; ++g) {
@@ -543,13 +568,20 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv4_kernel(
                 constexpr int c = decltype(C)::value;
                 return lds_read16((c & 1) ? gl : ql, a_off(c >> 1));
             };
-            bf16x8 fr[PF + 1];
-            static_for<0, PF>([&](auto F) __attribute__((always_inline)) { fr[decltype(F)::value] = fetch1(F); });
+            bf16x8 fr[PF + 1], vr[PF + 1];  // vr: V fragments of the dP chunks (causal d = 256)
+            static_for<0, PF>([&](auto F) __attribute__((always_inline)) {
+                constexpr int f = decltype(F)::value;
+                fr[f] = fetch1(F);
+                if constexpr (kVLds && (f & 1)) vr[f] = v_frag(f >> 1);
+            });
             static_for<0, N1>([&](auto C) __attribute__((always_inline)) {
                 constexpr int c = decltype(C)::value;
-                if constexpr (c + PF < N1) fr[(c + PF) % (PF + 1)] = fetch1(std::integral_constant<int, c + PF>{});
+                if constexpr (c + PF < N1) {
+                    fr[(c + PF) % (PF + 1)] = fetch1(std::integral_constant<int, c + PF>{});
+                    if constexpr (kVLds && ((c + PF) & 1)) vr[(c + PF) % (PF + 1)] = v_frag((c + PF) >> 1);
+                }
                 if constexpr (c & 1)
-                    dp = mfma(fr[c % (PF + 1)], vf[c >> 1], dp);
+                    dp = mfma(fr[c % (PF + 1)], kVLds ? vr[c % (PF + 1)] : v_frag(c >> 1), dp);
                 else
                     sc = mfma(fr[c % (PF + 1)], kf[c >> 1], sc);
                 __builtin_amdgcn_sched_barrier(0);
@@ -563,7 +595,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv4_kernel(
                         if (qs + 8 * g + 4 * h + u + off < key) sc[4 * g + u] = -__builtin_inff();
                 }
             }
-            // P and -dS in bf16, two groups of 16 queries
+            // P and dS in bf16, two groups of 16 queries
             bf16x8 pb[2], sb[2];
             auto form_p = [&](auto RR) __attribute__((always_inline)) {
                 constexpr int r = decltype(RR)::value;
@@ -575,7 +607,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv4_kernel(
                 sb[r >> 3][r & 7] = (bf16)(sc[r] * dp[r]);
             };
             // second products: chunk n < 2 NDB is dV over query group n / NDB, column block n % NDB
-            // (dO^T fragments); n >= 2 NDB is -dK likewise (Q^T fragments)
+            // (dO^T fragments); n >= 2 NDB is dK / scale likewise (Q^T fragments)
             constexpr int N2 = 4 * NDB;
             auto fetch2 = [&](auto NN) __attribute__((always_inline)) {
                 constexpr int n = decltype(NN)::value, m = n % (2 * NDB), t = m / NDB, db = m % NDB;
@@ -636,7 +668,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv4_kernel(
 #pragma unroll
                 for (int u = 0; u < 4; ++u) {
                     v4[u] = (bf16)av[db][4 * g + u];
-                    k4[u] = (bf16)(ak[db][4 * g + u] * -scale);
+                    k4[u] = (bf16)(ak[db][4 * g + u] * scale);
                 }
                 *(bf16x4 *)(rv_ + 32 * db + 8 * g + 4 * h) = v4;
                 *(bf16x4 *)(rk_ + 32 * db + 8 * g + 4 * h) = k4;
