@@ -1,6 +1,9 @@
-"""Head dimensions 192 and 256 on the GPU against the fp64 oracle: forward, backward (the
-dK/dV kernel splits the columns of dK and dV between two waves that share the keys), the
-split-key forward, unequal lengths and grouped heads, on small and ragged shapes."""
+"""Head dimensions 192 and 256 on the GPU against the fp64 oracle: forward, backward (one wave per
+SIMD in every kernel, each dK/dV wave doing all four products for its keys), the split-key forward,
+unequal lengths and grouped heads, on small and ragged shapes; and inputs whose row maxima grow
+along the keys, so that the forward moves its running offset and rescales O many times per row
+(the online-softmax recurrence of "digest_existing.txt", answer q02_flashattention; a row's offset
+moves only when its maximum outgrows it by more than 2^8 in exp2 units)."""
 import numpy as np
 import pytest
 import torch
@@ -72,3 +75,47 @@ def test_large_head_dims(B, H, Hk, Nq, Nk, d, causal):
         err = np.abs(g - r).max()
         note("  max|d%s err|=%.3e" % (name, err))
         assert np.all(np.isfinite(g)) and err <= G_TOL, (name, err)
+
+
+RESCALE_CASES = [
+    # B, H, Nq, Nk, d, causal
+    (1, 2, 300, 300, 192, True),
+    (1, 2, 300, 300, 192, False),
+    (1, 2, 257, 257, 256, True),
+    (1, 1, 200, 450, 256, False),
+]
+
+
+@pytest.mark.parametrize("B,H,Nq,Nk,d,causal", RESCALE_CASES)
+def test_large_head_dims_growing_maxima(B, H, Nq, Nk, d, causal):
+    """Every 7th query row scaled by 8 and key row j by 1 + j / 64 (then rounded to bf16): the
+    scores of later key blocks are several times larger, so each row's maximum grows past the
+    offset block after block (by up to ~100 in exp2 units for the scaled rows).  V is halved: with
+    so peaked a softmax an output row is close to a single row of V, and halving keeps |O| below
+    2.5, where the bf16 output rounding (at most 0.0078) leaves room for the arithmetic under the
+    2e-2 bar (full-size V rows reach |O| >= 4, where the rounding alone can take 0.0156)."""
+    note("growing maxima: B=%d H=%d Nq=%d Nk=%d d=%d causal=%d seed=53" % (B, H, Nq, Nk, d, causal))
+    scale = softmax_scale(d)
+    qi = make_inputs(B, H, Nq, d, nk=0, seed=53)
+    kv = make_inputs(B, H, 0, d, nk=Nk, seed=54)
+    q32 = qi["q"].float()
+    q32[:, :, ::7, :] *= 8.0
+    ramp = 1.0 + torch.arange(Nk, dtype=torch.float32) / 64.0
+    k32 = kv["k"].float() * ramp[None, None, :, None]
+    qb, kb, vb = q32.to(torch.bfloat16), k32.to(torch.bfloat16), kv["v"] * 0.5
+    q, k, v = qb.to(DEV), kb.to(DEV), vb.to(DEV)
+    o, lse = A.fwd(q, k, v, causal=causal, scale=scale)
+    o_s, lse_s = A.fwd_splitkv(q, k, v, causal=causal, scale=scale, num_splits=3)
+    torch.cuda.synchronize()
+    o_ref, lse_ref = oracle.attn_fwd(f64(qb), f64(kb), f64(vb), causal, scale)
+    # the inputs do what they are for: some row's maximum grows by more than 2^8 (exp2 units)
+    # past the maximum of its first 64 keys
+    s = np.einsum("bhid,bhjd->bhij", f64(qb), f64(kb)) * scale * np.log2(np.e)
+    if causal:
+        s = np.where(np.arange(Nk)[None, :] > np.arange(Nq)[:, None] + (Nk - Nq), -np.inf, s)
+    first = s[..., :64].max(axis=-1)
+    growth = s.max(axis=-1) - first
+    note("  largest growth of a row maximum past its first 64 keys: %.1f (exp2 units)" % np.nanmax(growth[np.isfinite(growth)]))
+    assert np.nanmax(growth[np.isfinite(growth)]) > 64.0
+    check_fwd(o, lse, o_ref, lse_ref, "fwd")
+    check_fwd(o_s, lse_s, o_ref, lse_ref, "split fwd")

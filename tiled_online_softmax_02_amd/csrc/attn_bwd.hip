@@ -390,10 +390,10 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv2_kernel(const Dkdv2Args args)
 // ------------------------------------------------------------ dK / dV, one wave per SIMD (d = 192, 256)
 
 // Four waves, one per SIMD with up to 512 registers.  Wave w owns 32 keys (128 per workgroup): it
-// holds K (and V, except at causal d = 256) of its keys over all of d, and both accumulators,
-// dV^T and dK^T / scale (d columns by 32 keys each), which only the matrix instructions touch (the
-// compiler keeps them in AGPRs).  Per 32-query block it forms S - lse / scale and dP - D =
-// dO V^T - D as two interleaved chains of matrix instructions, then P = exp2(S scale log2e -
+// holds K and V of its keys over all of d, and both accumulators, dV^T and dK^T / scale (d columns
+// by 32 keys each), which only the matrix instructions touch (the compiler keeps them in AGPRs).
+// Per 32-query block it forms S - lse / scale and dP - D = dO V^T - D as two interleaved chains of
+// matrix instructions with VGPR accumulators (mfma_vgpr), then P = exp2(S scale log2e -
 // lse log2e) and dS = P (dP - D), then dV^T += dO^T P and dK^T += Q^T dS with dO^T and Q^T read
 // by transposing reads.  Every wave does all four products for its keys: no partial sums or P pass
 // between waves, one barrier per block, about 1 KB of LDS read per matrix instruction.  Q/dO tiles
@@ -413,12 +413,6 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv4_kernel(
     __shared__ __attribute__((aligned(1024))) char q0_raw[TILE], q1_raw[TILE];
     __shared__ __attribute__((aligned(1024))) char g0_raw[TILE], g1_raw[TILE];
     __shared__ __attribute__((aligned(16))) float s0_raw[2 * BMQ], s1_raw[2 * BMQ];  // -lse / scale, -D
-    // causal d = 256: V of the workgroup's keys in LDS (64 KB), the registers it frees removing the
-    // spills of the register form (measured faster on causal tiles, which are short; on full rows
-    // the extra LDS reads cost more than the spills).  16-byte aligned, so that the 1 KB aligned
-    // stages keep the first 64 KB (the LDS instructions' offset field).
-    constexpr bool kVLds = D == 256 && CAUSAL;
-    __shared__ __attribute__((aligned(16))) char v_raw[kVLds ? kBN * D * 2 : 16];
 
     int head, ktile;
     work_item(blockIdx.x, n_ktiles, nx, head, ktile);
@@ -444,10 +438,8 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv4_kernel(
     const bool keys_ok = kw0 < Nk;
 
     // K and V of the lane's key: B operands of S = Q K^T and of dO V^T - D = dP - D, whose
-    // accumulator starts from -D, so that dS = P (dP - D) is one multiply per element.  d = 256: V
-    // from its LDS copy instead of registers (causal).
-    constexpr int NVR = kVLds ? 1 : NKS;
-    bf16x8 kf[NKS], vf[NVR];
+    // accumulator starts from -D, so that dS = P (dP - D) is one multiply per element
+    bf16x8 kf[NKS], vf[NKS];
     {
         const __amdgpu_buffer_rsrc_t rk = make_rsrc(K + hoff, (uint32_t)Nk * D * 2);
         const __amdgpu_buffer_rsrc_t rv = make_rsrc(V + hoff, (uint32_t)Nk * D * 2);
@@ -455,13 +447,10 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv4_kernel(
         for (int ks = 0; ks < NKS; ++ks) {
             const uint32_t byte = (uint32_t)(key * D + 16 * ks + 8 * h) * 2u;
             kf[ks] = __builtin_bit_cast(bf16x8, buffer_load16(rk, byte));
-            if constexpr (!kVLds) vf[ks] = __builtin_bit_cast(bf16x8, buffer_load16(rv, byte));
+            vf[ks] = __builtin_bit_cast(bf16x8, buffer_load16(rv, byte));
         }
-        // each wave copies its own 32 rows of V (rows past Nk read as zeros); its first wait on
-        // its loads precedes every read
-        if constexpr (kVLds) load_tile_lds<D, 1, 32>(rv, (lds_char *)v_raw + w * 32 * 2 * D, kw0, 0, lane);
     }
-    f32x16 av[NDB], ak[NDB];  // dV^T and -dK^T: columns 32 db .. 32 db + 31, the lane's key
+    f32x16 av[NDB], ak[NDB];  // dV^T and dK^T / scale: columns 32 db .. 32 db + 31, the lane's key
 #pragma unroll
     for (int i = 0; i < NDB; ++i) {
         av[i] = zero16();
@@ -483,23 +472,6 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv4_kernel(
         asm volatile("" : "+v"(ao[kst]));
     }
     auto a_off = [&](int kst) __attribute__((always_inline)) { return ao[kst % NAO] + (kst / NAO) * 32 * NAO; };
-    // V fragments (causal d = 256): rows c32 of the wave's 32-row block of the V copy, the same swizzled
-    // positions as ao, relative to the first stage so that the offset field stays small
-    int vo[kVLds ? NAO : 1];
-    if constexpr (kVLds) {
-        const int vbase = (int)((lds_char *)v_raw - (lds_char *)q0_raw) + w * 32 * 2 * D;
-#pragma unroll
-        for (int kst = 0; kst < NAO; ++kst) {
-            vo[kst] = ao[kst] + vbase;
-            asm volatile("" : "+v"(vo[kst]));
-        }
-    }
-    auto v_frag = [&](int kst) __attribute__((always_inline)) {
-        if constexpr (kVLds)
-            return lds_read16((lds_char *)q0_raw, vo[kst % NAO] + (kst / NAO) * 32 * NAO);
-        else
-            return vf[kst];
-    };
     {
         const int G4 = lane >> 4, s16 = lane & 15;
         const int tr = 4 * (G4 >> 1) + (s16 >> 2);
@@ -561,31 +533,26 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv4_kernel(
                     dp[4 * g + u] = d4[u];
                 }
             }
-            // first products: S and D - dP as two interleaved chains; fragment c is Q (even c) or
-            // dO (odd c) rows for reduction step c / 2, fetched PF instructions ahead
+            // first products: S - lse / scale and dP - D as two interleaved chains with VGPR
+            // accumulators (the AGPRs all hold dV and dK); fragment c is Q (even c) or dO (odd c)
+            // rows for reduction step c / 2, fetched PF instructions ahead
             constexpr int PF = 2, N1 = 2 * NKS;
             auto fetch1 = [&](auto C) __attribute__((always_inline)) {
                 constexpr int c = decltype(C)::value;
                 return lds_read16((c & 1) ? gl : ql, a_off(c >> 1));
             };
-            bf16x8 fr[PF + 1], vr[PF + 1];  // vr: V fragments of the dP chunks (causal d = 256)
-            static_for<0, PF>([&](auto F) __attribute__((always_inline)) {
-                constexpr int f = decltype(F)::value;
-                fr[f] = fetch1(F);
-                if constexpr (kVLds && (f & 1)) vr[f] = v_frag(f >> 1);
-            });
+            bf16x8 fr[PF + 1];
+            static_for<0, PF>([&](auto F) __attribute__((always_inline)) { fr[decltype(F)::value] = fetch1(F); });
             static_for<0, N1>([&](auto C) __attribute__((always_inline)) {
                 constexpr int c = decltype(C)::value;
-                if constexpr (c + PF < N1) {
-                    fr[(c + PF) % (PF + 1)] = fetch1(std::integral_constant<int, c + PF>{});
-                    if constexpr (kVLds && ((c + PF) & 1)) vr[(c + PF) % (PF + 1)] = v_frag((c + PF) >> 1);
-                }
+                if constexpr (c + PF < N1) fr[(c + PF) % (PF + 1)] = fetch1(std::integral_constant<int, c + PF>{});
                 if constexpr (c & 1)
-                    dp = mfma(fr[c % (PF + 1)], kVLds ? vr[c % (PF + 1)] : v_frag(c >> 1), dp);
+                    mfma_vgpr(dp, fr[c % (PF + 1)], vf[c >> 1]);
                 else
-                    sc = mfma(fr[c % (PF + 1)], kf[c >> 1], sc);
+                    mfma_vgpr(sc, fr[c % (PF + 1)], kf[c >> 1]);
                 __builtin_amdgcn_sched_barrier(0);
             });
+            mfma_vgpr_settle(sc, dp);
             if (CAUSAL && (qs + off < kw0 + 31)) {
                 // scores of queries before this lane's key -> -inf (P = 0)
 #pragma unroll
@@ -625,8 +592,8 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv4_kernel(
                     av[db] = mfma(fr[n % (PF + 1)], pb[t], av[db]);
                 else
                     ak[db] = mfma(fr[n % (PF + 1)], sb[t], ak[db]);
-                // vector work under the products: P of the second group and -dS of the first during
-                // dV over the first group, -dS of the second during dV over the second
+                // vector work under the products: P of the second group and dS of the first during
+                // dV over the first group, dS of the second during dV over the second
                 if constexpr (n < NDB) {
                     static_for<8 + n * 8 / NDB, 8 + (n + 1) * 8 / NDB>(form_p);
                     static_for<n * 8 / NDB, (n + 1) * 8 / NDB>(form_ds);

@@ -40,6 +40,52 @@ __device__ __forceinline__ f32x16 mfma(bf16x8 a, bf16x8 b, f32x16 c)
     return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
 
+// The same instruction with its accumulator in VGPRs, c += a b.  In a kernel with up to 512
+// registers per lane the compiler gives every matrix instruction AGPR accumulators; where the AGPRs
+// all hold long-lived sums, a short chain whose result the vector units read then evicts some of
+// those sums to VGPRs and back around every chain.  Written as assembly, the compiler's hazard
+// recognizer does not see it, so the waits it would insert are explicit: two wait states before it
+// for a vector write of a source just before (its loads are waited for by the compiler's counters,
+// which do see the operands), and mfma_vgpr_settle after the chain, before any instruction reads or
+// writes the accumulator.  Consecutive instructions of one chain (the same accumulator registers
+// in full) need no wait states.
+__device__ __forceinline__ void mfma_vgpr(f32x16 &c, bf16x8 a, bf16x8 b)
+{
+    asm volatile("s_nop 1\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(c) : "v"(a), "v"(b));
+}
+
+// c = a b (the accumulator starts from zero, an inline constant)
+__device__ __forceinline__ void mfma_vgpr_zero(f32x16 &c, bf16x8 a, bf16x8 b)
+{
+    asm volatile("s_nop 1\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, 0" : "=&v"(c) : "v"(a), "v"(b));
+}
+
+// 20 wait states (the most that a 16-pass matrix instruction's VGPR result needs before a vector
+// read or write), ordered after the chains that produce x and y and before any use of them
+__device__ __forceinline__ void mfma_vgpr_settle(f32x16 &x, f32x16 &y)
+{
+    asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 3" : "+v"(x), "+v"(y));
+}
+
+// acc *= alpha for an accumulator that lives in AGPRs, element by element through one VGPR, so
+// that the compiler has no reason to move the accumulator out of the AGPRs.  The reads of results
+// of earlier matrix instructions and the writes before later ones are hazards the compiler cannot
+// see here: agpr_settle before and after a run of these.
+__device__ __forceinline__ void scale_agpr(f32x16 &acc, float alpha)
+{
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+        float x = acc[r], t;
+        asm volatile("v_accvgpr_read_b32 %1, %0\n\tv_mul_f32 %1, %1, %2\n\tv_accvgpr_write_b32 %0, %1"
+                     : "+a"(x), "=&v"(t)
+                     : "v"(alpha));
+        acc[r] = x;
+    }
+}
+
+// 20 wait states
+__device__ __forceinline__ void agpr_settle() { asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 3" ::: "memory"); }
+
 __device__ __forceinline__ f32x16 zero16()
 {
     f32x16 z;

@@ -270,10 +270,19 @@ __global__ __launch_bounds__(64 * fwd_waves<D>(), fwd_min_blocks<D>()) void fwd_
                     m_run = m_new;
                     msc = (m_run == -__builtin_inff()) ? 0.f : m_run * c_log2;
                     l_run *= alpha;
+                    if constexpr (D >= 192) {
+                        // O stays in AGPRs (a multiply there would move all of it to VGPRs and
+                        // back around every step, not only in this rare branch)
+                        agpr_settle();
 #pragma unroll
-                    for (int db = 0; db < NDB; ++db) {
+                        for (int db = 0; db < NDB; ++db) scale_agpr(oacc[db], alpha);
+                        agpr_settle();
+                    } else {
 #pragma unroll
-                        for (int r = 0; r < 16; ++r) oacc[db][r] *= alpha;
+                        for (int db = 0; db < NDB; ++db) {
+#pragma unroll
+                            for (int r = 0; r < 16; ++r) oacc[db][r] *= alpha;
+                        }
                     }
                 }
                 // One step is NC chunks, each one matrix instruction plus a slice of vector work:
@@ -300,7 +309,10 @@ __global__ __launch_bounds__(64 * fwd_waves<D>(), fwd_min_blocks<D>()) void fwd_
                         return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
                     }
                 };
-                if constexpr (!last) {
+                // d >= 192 (AGPRs hold O): the score chains accumulate in VGPRs, the first instruction
+                // of each from zero
+                constexpr bool kVS = D >= 192;
+                if constexpr (!last && !kVS) {
                     nxt[0] = zero16();
                     nxt[1] = zero16();
                 }
@@ -320,7 +332,14 @@ __global__ __launch_bounds__(64 * fwd_waves<D>(), fwd_min_blocks<D>()) void fwd_
                         fr[(c + PF) % (PF + 1)] = fetch(std::integral_constant<int, c + PF>{});
                     if constexpr (is_s(c)) {
                         constexpr int s = c < NS / 2 ? c : c - NPV / 2;
-                        if constexpr (!last) nxt[s & 1] = mfma(fr[c % (PF + 1)], qf[s >> 1], nxt[s & 1]);
+                        if constexpr (last) {
+                        } else if constexpr (!kVS) {
+                            nxt[s & 1] = mfma(fr[c % (PF + 1)], qf[s >> 1], nxt[s & 1]);
+                        } else {
+                            if constexpr (s < 2) mfma_vgpr_zero(nxt[s & 1], fr[c % (PF + 1)], qf[s >> 1]);
+                            else mfma_vgpr(nxt[s & 1], fr[c % (PF + 1)], qf[s >> 1]);
+                            if constexpr (s == NS - 1) mfma_vgpr_settle(nxt[0], nxt[1]);
+                        }
                     } else {
                         const bf16x8 fc = fr[c % (PF + 1)];
                         constexpr int p = c < NS / 2 + NPV / 2 ? c - NS / 2 : c - NS;
