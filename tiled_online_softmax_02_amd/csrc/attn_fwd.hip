@@ -9,9 +9,10 @@
 // end.  S and P never leave the chip.
 //
 // gfx950 mapping:
-//   * one workgroup of 8 waves (d = 128) or 4 waves (d = 64) per block of query
-//     rows; each wave owns 32 rows and holds their Q fragments in VGPRs for the
-//     whole loop;
+//   * one workgroup of 8 waves (d = 128) or 4 waves (d = 64, 192, 256) per block
+//     of query rows; each wave owns 32 rows and holds their Q fragments in VGPRs
+//     for the whole loop; at d = 192 and 256 one wave per SIMD, with the O
+//     accumulators in AGPRs and the score chains in VGPRs (mfma_vgpr);
 //   * key/value blocks of 64 rows are double-buffered through swizzled LDS tiles
 //     filled by direct global->LDS buffer loads (rows past the end read as zeros, no
 //     staging registers, no LDS store instructions); K runs one block ahead of V, so
@@ -332,10 +333,9 @@ __global__ __launch_bounds__(64 * fwd_waves<D>(), fwd_min_blocks<D>()) void fwd_
                         fr[(c + PF) % (PF + 1)] = fetch(std::integral_constant<int, c + PF>{});
                     if constexpr (is_s(c)) {
                         constexpr int s = c < NS / 2 ? c : c - NPV / 2;
-                        if constexpr (last) {
-                        } else if constexpr (!kVS) {
+                        if constexpr (!last && !kVS) {
                             nxt[s & 1] = mfma(fr[c % (PF + 1)], qf[s >> 1], nxt[s & 1]);
-                        } else {
+                        } else if constexpr (!last) {
                             if constexpr (s < 2) mfma_vgpr_zero(nxt[s & 1], fr[c % (PF + 1)], qf[s >> 1]);
                             else mfma_vgpr(nxt[s & 1], fr[c % (PF + 1)], qf[s >> 1]);
                             if constexpr (s == NS - 1) mfma_vgpr_settle(nxt[0], nxt[1]);
